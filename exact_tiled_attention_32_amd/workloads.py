@@ -1,0 +1,116 @@
+"""Seeded synthetic inputs for exact attention.
+
+This module is the one piece shared by the HIP path's callers (tests, bench)
+and the oracle's callers: it draws the inputs and holds none of the method's
+arithmetic. All values are iid N(0, 1) from ``torch.Generator('cpu')``, drawn
+in fp32 and rounded to bf16 (round-to-nearest-even) for the bf16 workloads, so
+the GPU and the oracle consume the same bits.
+
+The workloads stand in, by shape only, for the pages' benchmarks (BERT-large
+at sequence length 512, GPT-2 at 1K, Long Range Arena at 16K and 64K); no
+dataset or trained weight is involved.
+
+Generation order per workload: Q, K, V, dO, then the key-padding lengths.
+"""
+from __future__ import annotations
+
+import math
+from dataclasses import dataclass, field
+
+import torch
+
+__all__ = ["Workload", "WORKLOADS", "generate", "sparse_block_rule", "make_case"]
+
+
+@dataclass(frozen=True)
+class Workload:
+    name: str
+    B: int
+    H: int
+    N: int
+    d: int
+    dtype: str            # "f32" or "bf16"
+    seed: int
+    causal: bool = False
+    padding: bool = False  # key-padding lengths L_b ~ U{N/2 .. N} inclusive
+    sparse: bool = False   # block mask from ``sparse_block_rule``
+    mask_block: int = 128
+    backward: bool = True
+    description: str = field(default="", compare=False)
+
+    @property
+    def scale(self) -> float:
+        return 1.0 / math.sqrt(self.d)
+
+
+WORKLOADS = {
+    "single_head_f32": Workload(
+        "single_head_f32", 1, 1, 128, 64, "f32", 1001, backward=False,
+        description="single-head forward, fp32, B=1 H=1 N=128 d=64, no mask"),
+    "bert_padded": Workload(
+        "bert_padded", 8, 16, 512, 64, "bf16", 1002, padding=True,
+        description="BERT-large-shaped self-attention, bf16 fwd+bwd, B=8 H=16 N=512 d=64, "
+                    "key padding with L_b uniform in [256, 512]"),
+    "gpt2_causal": Workload(
+        "gpt2_causal", 8, 12, 1024, 64, "bf16", 1003, causal=True,
+        description="GPT-2-shaped causal attention, bf16 fwd+bwd, B=8 H=12 N=1024 d=64"),
+    "long_causal_d64": Workload(
+        "long_causal_d64", 1, 16, 16384, 64, "bf16", 1004, causal=True,
+        description="long-sequence causal attention, bf16 fwd+bwd, B=1 H=16 N=16384 d=64"),
+    "long_causal_d128": Workload(
+        "long_causal_d128", 1, 16, 16384, 128, "bf16", 1014, causal=True,
+        description="long-sequence causal attention, bf16 fwd+bwd, B=1 H=16 N=16384 d=128"),
+    "block_sparse_64k": Workload(
+        "block_sparse_64k", 1, 8, 65536, 64, "bf16", 1005, sparse=True,
+        description="block-sparse attention, bf16 fwd+bwd, B=1 H=8 N=65536 d=64, 128x128 blocks, "
+                    "block (i,j) kept iff |i-j| <= 1 or j mod 16 == 0"),
+}
+
+
+def sparse_block_rule(n_blocks: int) -> torch.Tensor:
+    """uint8 [n_blocks, n_blocks]: 1 where |i - j| <= 1 or j % 16 == 0."""
+    i = torch.arange(n_blocks).view(-1, 1)
+    j = torch.arange(n_blocks).view(1, -1)
+    return (((i - j).abs() <= 1) | (j % 16 == 0)).to(torch.uint8)
+
+
+def _draw(gen, shape, dtype):
+    x = torch.randn(shape, generator=gen, dtype=torch.float32)
+    return x if dtype == "f32" else x.to(torch.bfloat16)
+
+
+def generate(w: Workload, *, with_grad_out: bool | None = None) -> dict:
+    """CPU tensors for a workload: q, k, v, (do), kv_len (int32 or None), block_mask (uint8 or None)."""
+    gen = torch.Generator("cpu").manual_seed(w.seed)
+    shape = (w.B, w.H, w.N, w.d)
+    q = _draw(gen, shape, w.dtype)
+    k = _draw(gen, shape, w.dtype)
+    v = _draw(gen, shape, w.dtype)
+    need_do = w.backward if with_grad_out is None else with_grad_out
+    do = _draw(gen, shape, w.dtype) if need_do else None
+    kv_len = None
+    if w.padding:
+        kv_len = torch.randint(w.N // 2, w.N + 1, (w.B,), generator=gen, dtype=torch.int64).to(torch.int32)
+    block_mask = None
+    if w.sparse:
+        block_mask = sparse_block_rule(-(-w.N // w.mask_block))
+    return {"q": q, "k": k, "v": v, "do": do, "kv_len": kv_len, "block_mask": block_mask,
+            "scale": w.scale, "causal": w.causal, "mask_block": w.mask_block}
+
+
+def make_case(B: int, H: int, N: int, d: int, *, dtype: str = "bf16", seed: int = 0,
+              causal: bool = False, kv_len=None, block_mask=None, mask_block: int = 128,
+              magnitude: float = 1.0) -> dict:
+    """A small seeded case for the parity sweep. ``kv_len`` may be a list of ints."""
+    gen = torch.Generator("cpu").manual_seed(seed)
+    shape = (B, H, N, d)
+
+    def draw():
+        x = torch.randn(shape, generator=gen, dtype=torch.float32) * magnitude
+        return x if dtype == "f32" else x.to(torch.bfloat16)
+
+    q, k, v, do = draw(), draw(), draw(), draw()
+    kl = None if kv_len is None else torch.tensor(kv_len, dtype=torch.int32)
+    bm = None if block_mask is None else torch.as_tensor(block_mask, dtype=torch.uint8)
+    return {"q": q, "k": k, "v": v, "do": do, "kv_len": kl, "block_mask": bm,
+            "scale": 1.0 / math.sqrt(d), "causal": causal, "mask_block": mask_block}

@@ -1,0 +1,190 @@
+"""Plain, slow fp64 CPU oracle of exact scaled-dot-product attention.
+
+TEST INFRASTRUCTURE ONLY. Nothing on the product path may import, call or run
+this module: only the tests, ``__graft_entry__.smoke()`` and the ``cpu_baseline``
+leg of ``bench.py`` use it. It shares no code with the HIP path (no kernels,
+headers, helpers, tables or pre/post-processing); both sides see the same
+seeded inputs and nothing else.
+
+What it computes, and where the pages define it
+------------------------------------------------
+* Forward — aiwiki.page "FlashAttention", section "Attention and the memory
+  bottleneck": the output is the row-wise softmax of the scaled score matrix
+  ``Q K^T / sqrt(d)`` applied to ``V``; masks restrict which query–key pairs
+  may interact. The scale is a caller argument (the configs use 1/sqrt(d)).
+  The same page, section "Tiling and online normalization", states that the
+  tiled algorithm reaches this plain result up to floating-point reordering,
+  so the oracle is the plain definition: it materialises the score rows,
+  takes a two-pass (max, then sum) softmax and multiplies by V. It does NOT
+  use the online (running max / running sum) recurrence.
+* Row statistics — sendsoonai.com "FlashAttention: IO-aware explained",
+  section "Recomputation and IO complexity": only the per-row softmax
+  statistics (m, l) are kept. The oracle reports them in the combined form
+  ``lse_i = m_i + ln l_i`` (natural log, since the page's update equations
+  use e^x), i.e. ``lse_i = ln sum_{j allowed} exp(scale * q_i . k_j)``.
+* Masks — aiwiki "FlashAttention", sections "Attention and the memory
+  bottleneck" (masks restrict pairs) and "Software integration and
+  limitations" (causal masks, variable-length sequences); legiblepapers.com
+  "Fast and Memory Efficient Exact Attention", summary paragraph (block-sparse
+  attention skips the zero blocks of a predefined block mask). The allowed set
+  is the AND of the three predicates:
+      causal:   j <= i                       (square self-attention)
+      padding:  j <  L_b                     (key padding per batch entry)
+      block:    mask[i // mb][j // mb] != 0  (block-sparse, mb = mask block)
+  Query rows are never masked; a row with no allowed key has O = 0,
+  lse = -inf and zero gradient (the pages are silent; plainest reading).
+* Backward — the pages say only that the backward is simplified analytically
+  and recomputes the attention matrix from the saved statistics
+  (cochat.ai audit of "FlashAttention: Fast and Memory-Efficient Exact
+  Attention with IO-Awareness", quoted App. B.2/B.4 and Theorem 5 proof). The
+  oracle is the chain rule of the definition, written out with the softmax
+  Jacobian (no rowsum(dO*O) shortcut):
+      dV = P^T dO
+      dP = dO V^T
+      dS_ij = P_ij (dP_ij - sum_k P_ik dP_ik)
+      dQ = scale * dS K
+      dK = scale * dS^T Q
+
+Evaluation order: rows are processed in independent chunks (each row of the
+definition depends only on its own query), and for a chunk only the key
+columns that at least one of its rows may attend to are gathered. A dropped
+column has P = 0 exactly, so both are exact rewrites of the definition, not
+reorderings of any sum over allowed keys.
+"""
+from __future__ import annotations
+
+import numpy as np
+
+__all__ = [
+    "allowed_pairs",
+    "forward_rows",
+    "attention_forward",
+    "attention_backward",
+]
+
+_ROW_CHUNK = 256
+
+
+def _as_f64(x) -> np.ndarray:
+    """Exact widening of the caller's values (fp32 / bf16-as-fp32) to fp64."""
+    if hasattr(x, "detach"):  # a torch tensor: go through float32, exact for bf16/fp32
+        x = x.detach().to("cpu").float().numpy()
+    return np.asarray(x, dtype=np.float64)
+
+
+def allowed_pairs(rows: np.ndarray, n_keys: int, *, causal: bool, kv_len_b,
+                  block_mask, mask_block: int) -> np.ndarray:
+    """Boolean [len(rows), n_keys]: may query ``i`` attend to key ``j``.
+
+    The AND of the causal (j <= i), key-padding (j < L_b) and block-mask
+    (mask[i // mb][j // mb] != 0) predicates; see the module docstring for the
+    passages that define each.
+    """
+    rows = np.asarray(rows, dtype=np.int64)
+    cols = np.arange(n_keys, dtype=np.int64)
+    allow = np.ones((rows.size, n_keys), dtype=bool)
+    if causal:
+        allow &= cols[None, :] <= rows[:, None]
+    if kv_len_b is not None:
+        allow &= cols[None, :] < int(kv_len_b)
+    if block_mask is not None:
+        bm = np.asarray(block_mask) != 0
+        allow &= bm[rows[:, None] // mask_block, cols[None, :] // mask_block]
+    return allow
+
+
+def forward_rows(q_rows: np.ndarray, k: np.ndarray, v: np.ndarray, scale: float,
+                 allow: np.ndarray):
+    """Exact attention for a set of query rows of one (batch, head).
+
+    q_rows [R, d], k [Nk, d], v [Nk, dv], allow [R, Nk] -> (O [R, dv], lse [R]).
+    Two-pass softmax of the materialised score rows (aiwiki "FlashAttention",
+    section "Attention and the memory bottleneck").
+    """
+    cols = np.nonzero(allow.any(axis=0))[0]
+    R = q_rows.shape[0]
+    out = np.zeros((R, v.shape[1]), dtype=np.float64)
+    lse = np.full(R, -np.inf, dtype=np.float64)
+    if cols.size == 0:
+        return out, lse
+    a = allow[:, cols]
+    s = scale * (q_rows @ k[cols].T)                 # scores S = scale * Q K^T
+    s = np.where(a, s, -np.inf)                      # masked pairs leave the softmax
+    m = s.max(axis=1)                                # pass 1: row maximum
+    live = np.isfinite(m)                            # rows with at least one allowed key
+    m_safe = np.where(live, m, 0.0)
+    e = np.exp(s - m_safe[:, None])                  # exp(-inf) = 0 for masked pairs
+    l = e.sum(axis=1)                                # pass 2: row sum
+    p = np.where(live[:, None], e / np.where(live, l, 1.0)[:, None], 0.0)
+    out[:] = p @ v[cols]
+    lse[live] = m[live] + np.log(l[live])
+    return out, lse
+
+
+def attention_forward(q, k, v, scale: float, *, causal: bool = False, kv_len=None,
+                      block_mask=None, mask_block: int = 128, row_chunk: int = _ROW_CHUNK):
+    """O, lse for q/k/v of shape [B, H, N, d] (any float dtype, widened to fp64).
+
+    kv_len: None or length-B integers (key padding). block_mask: None or a 2-D
+    array [ceil(N/mb), ceil(N/mb)] shared by every (b, h), nonzero = keep.
+    Returns O [B, H, N, d] fp64 and lse [B, H, N] fp64 (natural log).
+    """
+    q, k, v = _as_f64(q), _as_f64(k), _as_f64(v)
+    B, H, N, _ = q.shape
+    out = np.zeros(q.shape[:3] + (v.shape[3],), dtype=np.float64)
+    lse = np.full((B, H, N), -np.inf, dtype=np.float64)
+    lens = None if kv_len is None else [int(x) for x in np.asarray(kv_len).reshape(-1)]
+    for b in range(B):
+        for r0 in range(0, N, row_chunk):
+            rows = np.arange(r0, min(N, r0 + row_chunk))
+            allow = allowed_pairs(rows, k.shape[2], causal=causal,
+                                  kv_len_b=None if lens is None else lens[b],
+                                  block_mask=block_mask, mask_block=mask_block)
+            for h in range(H):
+                o_r, l_r = forward_rows(q[b, h, rows], k[b, h], v[b, h], scale, allow)
+                out[b, h, rows] = o_r
+                lse[b, h, rows] = l_r
+    return out, lse
+
+
+def attention_backward(q, k, v, dout, scale: float, *, causal: bool = False, kv_len=None,
+                       block_mask=None, mask_block: int = 128, heads=None,
+                       row_chunk: int = _ROW_CHUNK):
+    """dQ, dK, dV of L = sum(O * dO) for the forward above, all fp64.
+
+    The probabilities are recomputed from the definition (two-pass softmax);
+    the softmax Jacobian-vector product is written out in full. ``heads``
+    optionally restricts the work to a list of (b, h) pairs (the other entries
+    of the returned arrays stay zero): used to sample one head of a large
+    workload.
+    """
+    q, k, v, dout = _as_f64(q), _as_f64(k), _as_f64(v), _as_f64(dout)
+    B, H, N, d = q.shape
+    dq = np.zeros_like(q)
+    dk = np.zeros_like(k)
+    dv = np.zeros_like(v)
+    lens = None if kv_len is None else [int(x) for x in np.asarray(kv_len).reshape(-1)]
+    pairs = [(b, h) for b in range(B) for h in range(H)] if heads is None else list(heads)
+    for b, h in pairs:
+        for r0 in range(0, N, row_chunk):
+            rows = np.arange(r0, min(N, r0 + row_chunk))
+            allow = allowed_pairs(rows, k.shape[2], causal=causal,
+                                  kv_len_b=None if lens is None else lens[b],
+                                  block_mask=block_mask, mask_block=mask_block)
+            cols = np.nonzero(allow.any(axis=0))[0]
+            if cols.size == 0:
+                continue
+            a = allow[:, cols]
+            kc, vc, qr, dor = k[b, h, cols], v[b, h, cols], q[b, h, rows], dout[b, h, rows]
+            s = np.where(a, scale * (qr @ kc.T), -np.inf)
+            m = s.max(axis=1)
+            live = np.isfinite(m)
+            e = np.exp(s - np.where(live, m, 0.0)[:, None])
+            l = e.sum(axis=1)
+            p = np.where(live[:, None], e / np.where(live, l, 1.0)[:, None], 0.0)
+            dv[b, h, cols] += p.T @ dor                        # dV = P^T dO
+            dp = dor @ vc.T                                    # dP = dO V^T
+            ds = p * (dp - (p * dp).sum(axis=1, keepdims=True))  # softmax Jacobian
+            dq[b, h, rows] = scale * (ds @ kc)                 # dQ = scale dS K
+            dk[b, h, cols] += scale * (ds.T @ qr)              # dK = scale dS^T Q
+    return dq, dk, dv

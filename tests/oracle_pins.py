@@ -1,0 +1,359 @@
+"""Pins of the fp64 oracle against facts the pages and the mathematics fix.
+
+Every pin takes the oracle module as an argument, so the same battery runs
+against the real oracle (all must pass) and against copies with a planted
+mistake (at least one must fail; see test_oracle_mutations.py).
+
+None of the pins re-types the oracle's formula. Each checks something the
+definition implies by other means:
+  * closed forms (Q = 0 -> mean of the allowed values, ln |A_i|; one-hot keys;
+    causal row 0),
+  * invariants (permutation equivariance, shift invariance, linearity in V,
+    rows of P summing to one, exposed through V = I),
+  * central finite differences of the oracle's own forward (backward pins),
+  * an independent library routine (torch scaled_dot_product_attention in
+    float64 on the CPU, with autograd for the gradients),
+  * brute-force scalar loops on tiny inputs (math.fsum over Python floats).
+
+The allowed sets used by the expected values are built here, from the mask
+rules stated in the pages (aiwiki "FlashAttention": causal and variable-length
+masks; legiblepapers "Fast and Memory Efficient Exact Attention": predefined
+block mask), not by calling the oracle's helper.
+"""
+from __future__ import annotations
+
+import math
+
+import numpy as np
+import torch
+
+RNG = np.random.default_rng
+
+
+# ----------------------------------------------------------------------------------
+# independent construction of the allowed set (scalar rules, Python loops)
+# ----------------------------------------------------------------------------------
+def allowed_lists(N, causal=False, kv_len_b=None, block_mask=None, mb=1):
+    """For each query row i, the sorted list of keys j it may attend to."""
+    out = []
+    for i in range(N):
+        js = []
+        for j in range(N):
+            if causal and j > i:
+                continue
+            if kv_len_b is not None and j >= kv_len_b:
+                continue
+            if block_mask is not None and not block_mask[i // mb][j // mb]:
+                continue
+            js.append(j)
+        out.append(js)
+    return out
+
+
+def dense_bool(lists, N):
+    a = np.zeros((len(lists), N), dtype=bool)
+    for i, js in enumerate(lists):
+        a[i, js] = True
+    return a
+
+
+MASK_CASES = [
+    # (name, N, causal, kv_len list per batch, block mask (list of lists) or None, mb)
+    ("none", 9, False, None, None, 1),
+    ("causal", 9, True, None, None, 1),
+    ("padding", 9, False, [5, 9], None, 1),
+    ("block", 12, False, None, [[1, 0, 1], [0, 1, 0], [1, 1, 0]], 4),
+    ("causal+padding+block", 12, True, [7, 12], [[1, 0, 1], [1, 1, 0], [1, 0, 1]], 4),
+]
+
+
+def _fwd(orc, q, k, v, scale, causal, kv_len, bm, mb):
+    return orc.attention_forward(q, k, v, scale, causal=causal, kv_len=kv_len,
+                                 block_mask=None if bm is None else np.array(bm), mask_block=mb)
+
+
+def _bwd(orc, q, k, v, do, scale, causal, kv_len, bm, mb):
+    return orc.attention_backward(q, k, v, do, scale, causal=causal, kv_len=kv_len,
+                                  block_mask=None if bm is None else np.array(bm), mask_block=mb)
+
+
+# ----------------------------------------------------------------------------------
+# closed forms
+# ----------------------------------------------------------------------------------
+def pin_zero_query(orc):
+    """Q = 0: every allowed score is 0, so O_i = mean of the allowed v_j and lse_i = ln |A_i|."""
+    for name, N, causal, kv, bm, mb in MASK_CASES:
+        B = 1 if kv is None else len(kv)
+        rng = RNG(11)
+        d = 3
+        q = np.zeros((B, 2, N, d))
+        k = rng.standard_normal((B, 2, N, d))
+        v = rng.standard_normal((B, 2, N, d))
+        o, lse = _fwd(orc, q, k, v, 0.7, causal, kv, bm, mb)
+        for b in range(B):
+            lists = allowed_lists(N, causal, None if kv is None else kv[b], bm, mb)
+            for h in range(2):
+                for i, js in enumerate(lists):
+                    if not js:
+                        continue
+                    exp_o = [math.fsum(v[b, h, j, c] for j in js) / len(js) for c in range(d)]
+                    assert np.allclose(o[b, h, i], exp_o, rtol=0, atol=1e-12), (name, b, h, i)
+                    assert abs(lse[b, h, i] - math.log(len(js))) < 1e-12, (name, b, h, i)
+    # scale = 0 with a random Q is the same closed form
+    rng = RNG(12)
+    q, k, v = (rng.standard_normal((1, 1, 7, 4)) for _ in range(3))
+    o, lse = orc.attention_forward(q, k, v, 0.0, causal=True)
+    for i in range(7):
+        assert np.allclose(o[0, 0, i], v[0, 0, : i + 1].mean(axis=0), atol=1e-12)
+        assert abs(lse[0, 0, i] - math.log(i + 1)) < 1e-12
+
+
+def pin_one_hot_keys(orc):
+    """k_j = e_{h(j)}, q_i = t e_{g(i)}: the softmax has two levels, exp(a) and 1, a = scale*t."""
+    N, d, t, scale = 10, 4, 3.0, 0.5
+    hj = [j % d for j in range(N)]
+    gi = [(3 * i + 1) % d for i in range(N)]
+    k = np.zeros((1, 1, N, d))
+    q = np.zeros((1, 1, N, d))
+    for j in range(N):
+        k[0, 0, j, hj[j]] = 1.0
+    for i in range(N):
+        q[0, 0, i, gi[i]] = t
+    v = RNG(13).standard_normal((1, 1, N, 2))
+    a = scale * t
+    for causal in (False, True):
+        o, lse = orc.attention_forward(q, k, v, scale, causal=causal)
+        for i in range(N):
+            js = range(i + 1) if causal else range(N)
+            w = {j: (math.exp(a) if hj[j] == gi[i] else 1.0) for j in js}
+            z = math.fsum(w.values())
+            for c in range(2):
+                exp_o = math.fsum(w[j] * v[0, 0, j, c] for j in js) / z
+                assert abs(o[0, 0, i, c] - exp_o) < 1e-12, (causal, i, c)
+            assert abs(lse[0, 0, i] - math.log(z)) < 1e-12, (causal, i)
+
+
+def pin_causal_row0(orc):
+    """Causal row 0 attends only to key 0: O_0 = v_0, lse_0 = scale q_0.k_0, dQ_0 = 0."""
+    rng = RNG(14)
+    q, k, v, do = (rng.standard_normal((2, 2, 6, 5)) for _ in range(4))
+    o, lse = orc.attention_forward(q, k, v, 0.3, causal=True)
+    dq, _, _ = orc.attention_backward(q, k, v, do, 0.3, causal=True)
+    for b in range(2):
+        for h in range(2):
+            assert np.allclose(o[b, h, 0], v[b, h, 0], atol=1e-15)
+            dot = math.fsum(float(x) * float(y) for x, y in zip(q[b, h, 0], k[b, h, 0]))
+            assert abs(lse[b, h, 0] - 0.3 * dot) < 1e-13
+            assert np.all(dq[b, h, 0] == 0.0)
+
+
+def pin_empty_rows(orc):
+    """A row with no allowed key: O = 0, lse = -inf; no gradient flows through it."""
+    rng = RNG(15)
+    q, k, v, do = (rng.standard_normal((2, 1, 5, 3)) for _ in range(4))
+    o, lse = orc.attention_forward(q, k, v, 0.5, kv_len=[0, 2])
+    dq, dk, dv = orc.attention_backward(q, k, v, do, 0.5, kv_len=[0, 2])
+    assert np.all(o[0] == 0) and np.all(np.isneginf(lse[0]))
+    assert np.all(dq[0] == 0) and np.all(dk[0] == 0) and np.all(dv[0] == 0)
+    assert np.all(np.isfinite(lse[1])) and np.all(dk[1, :, 2:] == 0) and np.all(dv[1, :, 2:] == 0)
+    # a block mask with an all-zero block row empties those rows too
+    bm = np.array([[1, 0], [0, 0]])
+    o, lse = orc.attention_forward(q[:1], k[:1], v[:1], 0.5, block_mask=bm, mask_block=3)
+    assert np.all(o[0, 0, 3:] == 0) and np.all(np.isneginf(lse[0, 0, 3:]))
+    assert np.all(np.isfinite(lse[0, 0, :3]))
+
+
+# ----------------------------------------------------------------------------------
+# invariants
+# ----------------------------------------------------------------------------------
+def pin_identity_values(orc):
+    """V = I exposes P as O: rows sum to 1, P_ij / P_ik = exp(s_ij - s_ik), lse_i = s_ij - ln P_ij."""
+    for name, N, causal, kv, bm, mb in MASK_CASES:
+        B = 1 if kv is None else len(kv)
+        rng = RNG(16)
+        d = 4
+        q = rng.standard_normal((B, 1, N, d)) * 2
+        k = rng.standard_normal((B, 1, N, d))
+        v = np.broadcast_to(np.eye(N), (B, 1, N, N)).copy()
+        scale = 0.6
+        p, lse = _fwd(orc, q, k, v, scale, causal, kv, bm, mb)
+        for b in range(B):
+            lists = allowed_lists(N, causal, None if kv is None else kv[b], bm, mb)
+            for i, js in enumerate(lists):
+                row = p[b, 0, i]
+                if not js:
+                    assert np.all(row == 0)
+                    continue
+                assert abs(math.fsum(row) - 1.0) < 1e-12, (name, b, i)
+                off = [j for j in range(N) if j not in js]
+                assert np.all(row[off] == 0.0), (name, b, i)
+                s = {j: scale * math.fsum(float(x) * float(y) for x, y in zip(q[b, 0, i], k[b, 0, j]))
+                     for j in js}
+                j0 = js[0]
+                for j in js:
+                    assert abs(row[j] / row[j0] - math.exp(s[j] - s[j0])) < 1e-11 * math.exp(s[j] - s[j0])
+                    assert abs(lse[b, 0, i] - (s[j] - math.log(row[j]))) < 1e-11
+
+
+def pin_permutation_equivariance(orc):
+    """Non-causal, unmasked: permuting the rows of K and V leaves O, lse, dQ unchanged and permutes dK, dV."""
+    rng = RNG(17)
+    q, k, v, do = (rng.standard_normal((1, 2, 11, 5)) for _ in range(4))
+    perm = rng.permutation(11)
+    o1, l1 = orc.attention_forward(q, k, v, 0.4)
+    o2, l2 = orc.attention_forward(q, k[:, :, perm], v[:, :, perm], 0.4)
+    assert np.allclose(o1, o2, atol=1e-13) and np.allclose(l1, l2, atol=1e-13)
+    g1 = orc.attention_backward(q, k, v, do, 0.4)
+    g2 = orc.attention_backward(q, k[:, :, perm], v[:, :, perm], do, 0.4)
+    assert np.allclose(g1[0], g2[0], atol=1e-12)
+    assert np.allclose(g1[1][:, :, perm], g2[1], atol=1e-12)
+    assert np.allclose(g1[2][:, :, perm], g2[2], atol=1e-12)
+    # permuting the query rows permutes every per-row output
+    o3, l3 = orc.attention_forward(q[:, :, perm], k, v, 0.4)
+    assert np.allclose(o1[:, :, perm], o3, atol=1e-13) and np.allclose(l1[:, :, perm], l3, atol=1e-13)
+
+
+def pin_shift_invariance(orc):
+    """K <- K + c (same c for every key) leaves O unchanged and shifts lse_i by scale q_i.c."""
+    rng = RNG(18)
+    q, k, v = (rng.standard_normal((1, 1, 8, 3)) for _ in range(3))
+    c = np.array([0.7, -1.3, 2.1])
+    for causal in (False, True):
+        o1, l1 = orc.attention_forward(q, k, v, 0.9, causal=causal)
+        o2, l2 = orc.attention_forward(q, k + c, v, 0.9, causal=causal)
+        assert np.allclose(o1, o2, atol=1e-12)
+        assert np.allclose(l2 - l1, 0.9 * (q @ c), atol=1e-12)
+
+
+def pin_linearity_in_v(orc):
+    rng = RNG(19)
+    q, k, v1, v2 = (rng.standard_normal((1, 2, 9, 4)) for _ in range(4))
+    for causal in (False, True):
+        o1, _ = orc.attention_forward(q, k, v1, 0.5, causal=causal)
+        o2, _ = orc.attention_forward(q, k, v2, 0.5, causal=causal)
+        o3, _ = orc.attention_forward(q, k, 2.5 * v1 - 0.75 * v2, 0.5, causal=causal)
+        assert np.allclose(o3, 2.5 * o1 - 0.75 * o2, atol=1e-12)
+
+
+# ----------------------------------------------------------------------------------
+# backward: finite differences of the oracle's own forward
+# ----------------------------------------------------------------------------------
+def pin_finite_differences(orc):
+    """Central differences of L = sum(O * dO) (h = 1e-6) against dQ, dK, dV, every mask type."""
+    for name, N, causal, kv, bm, mb in MASK_CASES:
+        B = 1 if kv is None else len(kv)
+        rng = RNG(20)
+        d = 3
+        q, k, v, do = (rng.standard_normal((B, 1, N, d)) for _ in range(4))
+        scale = 0.8
+        grads = _bwd(orc, q, k, v, do, scale, causal, kv, bm, mb)
+
+        def loss(qq, kk, vv):
+            o, _ = _fwd(orc, qq, kk, vv, scale, causal, kv, bm, mb)
+            return float(np.sum(o * do))
+
+        hstep = 1e-6
+        for which, g in zip(range(3), grads):
+            base = [q, k, v]
+            num = np.zeros_like(g)
+            it = np.nditer(base[which], flags=["multi_index"])
+            for _ in it:
+                idx = it.multi_index
+                args_p = [x.copy() for x in base]
+                args_m = [x.copy() for x in base]
+                args_p[which][idx] += hstep
+                args_m[which][idx] -= hstep
+                num[idx] = (loss(*args_p) - loss(*args_m)) / (2 * hstep)
+            err = np.max(np.abs(num - g)) / max(1.0, np.max(np.abs(g)))
+            assert err < 1e-7, (name, "qkv"[which], err)
+
+
+def pin_lse_gradient(orc):
+    """d(sum_i lse_i)/dq_i = scale sum_j P_ij k_j, i.e. scale times the forward with V := K."""
+    rng = RNG(21)
+    q, k = (rng.standard_normal((1, 1, 7, 3)) for _ in range(2))
+    scale = 0.7
+    for causal in (False, True):
+        o_k, _ = orc.attention_forward(q, k, k, scale, causal=causal)
+        hstep = 1e-6
+        for i in range(7):
+            for c in range(3):
+                qp, qm = q.copy(), q.copy()
+                qp[0, 0, i, c] += hstep
+                qm[0, 0, i, c] -= hstep
+                lp = orc.attention_forward(qp, k, k, scale, causal=causal)[1].sum()
+                lm = orc.attention_forward(qm, k, k, scale, causal=causal)[1].sum()
+                assert abs((lp - lm) / (2 * hstep) - scale * o_k[0, 0, i, c]) < 1e-7
+
+
+# ----------------------------------------------------------------------------------
+# independent library routine: torch SDPA in float64 on the CPU, autograd gradients
+# ----------------------------------------------------------------------------------
+def _sdpa(q, k, v, do, scale, allow):
+    tq, tk, tv = (torch.tensor(x, dtype=torch.float64, requires_grad=True) for x in (q, k, v))
+    out = torch.nn.functional.scaled_dot_product_attention(
+        tq, tk, tv, attn_mask=torch.tensor(allow), scale=scale)
+    out.backward(torch.tensor(do, dtype=torch.float64))
+    return out.detach().numpy(), tq.grad.numpy(), tk.grad.numpy(), tv.grad.numpy()
+
+
+def pin_library_sdpa(orc, magnitude=1.0):
+    """Agreement with torch's scaled_dot_product_attention (float64, CPU) on rows with >= 1 allowed key."""
+    for name, N, causal, kv, bm, mb in MASK_CASES:
+        B = 1 if kv is None else len(kv)
+        rng = RNG(22)
+        d = 5
+        q, k, v, do = (rng.standard_normal((B, 3, N, d)) * magnitude for _ in range(4))
+        scale = 1 / math.sqrt(d)
+        o, _ = _fwd(orc, q, k, v, scale, causal, kv, bm, mb)
+        dq, dk, dv = _bwd(orc, q, k, v, do, scale, causal, kv, bm, mb)
+        for b in range(B):
+            lists = allowed_lists(N, causal, None if kv is None else kv[b], bm, mb)
+            allow = dense_bool(lists, N)
+            live = allow.any(axis=1)
+            # SDPA returns NaN on fully masked rows; feed it only the live rows' queries
+            ro, rdq, rdk, rdv = _sdpa(q[b][:, live], k[b], v[b], do[b][:, live], scale, allow[live])
+            tol = 1e-10 * max(1.0, magnitude)
+            assert np.allclose(o[b][:, live], ro, atol=tol, rtol=1e-10), name
+            assert np.allclose(dq[b][:, live], rdq, atol=tol, rtol=1e-9), name
+            assert np.allclose(dk[b], rdk, atol=tol, rtol=1e-9), name
+            assert np.allclose(dv[b], rdv, atol=tol, rtol=1e-9), name
+
+
+def pin_large_magnitude(orc):
+    """Inputs x30 (scores in the hundreds): still finite and equal to the library routine."""
+    pin_library_sdpa(orc, magnitude=30.0)
+
+
+def pin_block_rule_medium(orc):
+    """N = 2048 with causal + block mask (mb = 128) + padding against SDPA on a dense boolean mask."""
+    N, d, mb = 2048, 8, 128
+    nb = N // mb
+    bm = [[1 if (abs(i - j) <= 1 or j % 5 == 0) else 0 for j in range(nb)] for i in range(nb)]
+    rng = RNG(23)
+    q, k, v, do = (rng.standard_normal((1, 1, N, d)) for _ in range(4))
+    scale = 1 / math.sqrt(d)
+    o, lse = orc.attention_forward(q, k, v, scale, causal=True, kv_len=[1900],
+                                   block_mask=np.array(bm), mask_block=mb)
+    ii = np.arange(N)[:, None]
+    jj = np.arange(N)[None, :]
+    allow = (jj <= ii) & (jj < 1900) & np.kron(np.array(bm, dtype=bool), np.ones((mb, mb), dtype=bool))
+    ro, _, _, _ = _sdpa(q[0], k[0], v[0], do[0], scale, allow)
+    assert np.allclose(o[0], ro, atol=1e-11)
+
+
+ALL_PINS = [
+    pin_zero_query,
+    pin_one_hot_keys,
+    pin_causal_row0,
+    pin_empty_rows,
+    pin_identity_values,
+    pin_permutation_equivariance,
+    pin_shift_invariance,
+    pin_linearity_in_v,
+    pin_finite_differences,
+    pin_lse_gradient,
+    pin_library_sdpa,
+    pin_large_magnitude,
+    pin_block_rule_medium,
+]

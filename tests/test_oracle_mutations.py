@@ -1,0 +1,69 @@
+"""Plant plausible mistakes in copies of the oracle; the pin battery must catch every one.
+
+Each mutant is the oracle's source with one textual change (a dropped term, a
+wrong sign, index or operand), executed as a fresh module. This shows the pins
+are strong enough that such a mistake in the oracle could not pass unnoticed.
+"""
+import os
+import types
+
+import pytest
+
+from tests.oracle_pins import ALL_PINS
+
+SRC = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))), "oracle", "attention.py")
+
+MUTANTS = {
+    "fwd_scale_dropped": ("s = scale * (q_rows @ k[cols].T)", "s = (q_rows @ k[cols].T)"),
+    "fwd_keys_reversed": ("s = scale * (q_rows @ k[cols].T)", "s = scale * (q_rows @ k[cols][::-1].T)"),
+    "fwd_values_from_keys": ("out[:] = p @ v[cols]", "out[:] = p @ v[cols][::-1]"),
+    "causal_off_by_one": ("cols[None, :] <= rows[:, None]", "cols[None, :] < rows[:, None] + 2"),
+    "causal_flipped": ("cols[None, :] <= rows[:, None]", "cols[None, :] >= rows[:, None]"),
+    "padding_off_by_one": ("cols[None, :] < int(kv_len_b)", "cols[None, :] <= int(kv_len_b)"),
+    "block_mask_transposed": ("bm[rows[:, None] // mask_block, cols[None, :] // mask_block]",
+                              "bm[cols[None, :] // mask_block, rows[:, None] // mask_block]"),
+    "lse_log2": ("lse[live] = m[live] + np.log(l[live])", "lse[live] = m[live] + np.log2(l[live])"),
+    "lse_missing_max": ("lse[live] = m[live] + np.log(l[live])", "lse[live] = np.log(l[live])"),
+    "no_max_subtraction": ("e = np.exp(s - m_safe[:, None])", "e = np.exp(s)"),
+    "normaliser_dropped": ("p = np.where(live[:, None], e / np.where(live, l, 1.0)[:, None], 0.0)\n    out",
+                           "p = np.where(live[:, None], e, 0.0)\n    out"),
+    "bwd_jacobian_sign": ("ds = p * (dp - (p * dp)", "ds = p * (dp + (p * dp)"),
+    "bwd_jacobian_term_dropped": ("ds = p * (dp - (p * dp).sum(axis=1, keepdims=True))", "ds = p * dp"),
+    "bwd_dk_scale_dropped": ("dk[b, h, cols] += scale * (ds.T @ qr)", "dk[b, h, cols] += (ds.T @ qr)"),
+    "bwd_dq_scale_dropped": ("dq[b, h, rows] = scale * (ds @ kc)", "dq[b, h, rows] = (ds @ kc)"),
+    "bwd_dv_wrong_operand": ("dv[b, h, cols] += p.T @ dor", "dv[b, h, cols] += p.T @ qr"),
+    "bwd_dp_wrong_operand": ("dp = dor @ vc.T", "dp = dor @ kc.T"),
+    "bwd_dk_wrong_operand": ("dk[b, h, cols] += scale * (ds.T @ qr)", "dk[b, h, cols] += scale * (ds.T @ dor)"),
+    "bwd_scale_dropped_in_recompute": ("s = np.where(a, scale * (qr @ kc.T), -np.inf)",
+                                       "s = np.where(a, (qr @ kc.T), -np.inf)"),
+    "bwd_causal_ignored": ("allow = allowed_pairs(rows, k.shape[2], causal=causal,\n"
+                           "                                  kv_len_b=None if lens is None else lens[b],\n"
+                           "                                  block_mask=block_mask, mask_block=mask_block)\n"
+                           "            cols",
+                           "allow = allowed_pairs(rows, k.shape[2], causal=False,\n"
+                           "                                  kv_len_b=None if lens is None else lens[b],\n"
+                           "                                  block_mask=block_mask, mask_block=mask_block)\n"
+                           "            cols"),
+}
+
+
+def _mutant(old, new):
+    with open(SRC) as f:
+        text = f.read()
+    assert text.count(old) >= 1, f"mutation anchor not found: {old!r}"
+    mod = types.ModuleType("oracle_mutant")
+    exec(compile(text.replace(old, new, 1), "oracle_mutant", "exec"), mod.__dict__)
+    return mod
+
+
+@pytest.mark.parametrize("name", sorted(MUTANTS))
+def test_pins_catch_mutant(name):
+    mod = _mutant(*MUTANTS[name])
+    caught = []
+    for pin in ALL_PINS:
+        try:
+            pin(mod)
+        except Exception as e:  # an assertion or a crash both count as caught
+            caught.append((pin.__name__, type(e).__name__))
+            break
+    assert caught, f"no pin catches mutant {name}"

@@ -1,0 +1,10 @@
+"""The fp64 oracle against its pins (closed forms, invariants, finite differences, torch SDPA)."""
+import pytest
+
+import oracle
+from tests.oracle_pins import ALL_PINS
+
+
+@pytest.mark.parametrize("pin", ALL_PINS, ids=[p.__name__ for p in ALL_PINS])
+def test_oracle_pin(pin):
+    pin(oracle)
