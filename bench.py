@@ -1,0 +1,279 @@
+"""Benchmark of the exact tiled attention hot path on one MI355X.
+
+A step is one pass of the whole hot path over the long-sequence causal workload
+(B=1, H=16, N=16384, bf16, causal, at d=64 and at d=128): for each head dimension
+the forward (O, lse) and the backward (pre-pass, main kernel, dQ conversion) through
+the C ABI, on inputs already resident in device memory.
+
+FLOP convention: forward 4*B*H*N^2*d, halved for causal; backward 2.5x the forward
+(five products per score tile instead of two). value = FLOP per step / time per step.
+
+Prints ONE JSON line (the metric line). `--report FILE` additionally times every
+workload (forward and backward separately) and writes a per-workload JSON.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_BF16_TFLOPS = 2500.0  # MI355X dense bf16 MFMA
+PEAK_HBM_GBS = 8000.0
+METRIC = "attention fwd+bwd TFLOP/s (bf16, causal) and % of MI355X bf16 MFMA peak"
+STEP_WORKLOADS = ("long_causal_d64", "long_causal_d128")
+
+
+def attn_flops(w, kept_fraction=None) -> float:
+    """Forward FLOP of a workload under the convention above."""
+    f = 4.0 * w.B * w.H * w.N * w.N * w.d
+    if w.causal:
+        f /= 2
+    if kept_fraction is not None:
+        f *= kept_fraction
+    return f
+
+
+class Runner:
+    """Device-resident inputs, outputs and workspace for one workload."""
+
+    def __init__(self, fa, w, dev):
+        import torch
+        from exact_tiled_attention_32_amd import workloads
+        self.fa, self.w = fa, w
+        x = workloads.generate(w)
+        self.q, self.k, self.v = (x[n].to(dev) for n in ("q", "k", "v"))
+        self.do = x["do"].to(dev) if x["do"] is not None else None
+        self.kv = None if x["kv_len"] is None else x["kv_len"].to(dev)
+        self.mask = None if x["block_mask"] is None else x["block_mask"].to(dev)
+        self.scale = x["scale"]
+        self.o = torch.empty_like(self.q)
+        self.lse = torch.empty(self.q.shape[:3], dtype=torch.float32, device=dev)
+        if w.backward:
+            self.dq, self.dk, self.dv = (torch.empty_like(self.q) for _ in range(3))
+            self.ws = torch.empty(fa.fa_bwd_workspace_bytes(w.B, w.H, w.N, w.d), dtype=torch.uint8, device=dev)
+        self.kept = None
+        if self.mask is not None:
+            self.kept = float(x["block_mask"].double().mean())
+
+    def fwd(self):
+        if self.mask is not None:
+            self.fa.fa_fwd_blocksparse(self.q, self.k, self.v, self.scale, self.mask, self.w.mask_block,
+                                       self.w.causal, self.kv, o=self.o, lse=self.lse)
+        else:
+            self.fa.fa_fwd(self.q, self.k, self.v, self.scale, self.w.causal, self.kv, o=self.o, lse=self.lse)
+
+    def bwd(self):
+        self.fa.fa_bwd(self.q, self.k, self.v, self.o, self.do, self.lse, self.scale, self.w.causal, self.kv,
+                       self.mask, self.w.mask_block, dq=self.dq, dk=self.dk, dv=self.dv, workspace=self.ws)
+
+
+class KernelClock:
+    """HIP events recorded by the library around the dominant kernel of each call."""
+
+    def __init__(self):
+        self.pairs = {}
+
+    def arm(self, fa, name):
+        import torch
+        s, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        # torch creates the HIP event at its first record; the library then re-records it
+        # around the kernel launch on the same stream
+        s.record()
+        e.record()
+        self.pairs.setdefault(name, []).append((s, e))
+        fa.fa_time_next_kernel(s, e)
+
+    def mean_ms(self, name):
+        ps = self.pairs.get(name, [])
+        return sum(s.elapsed_time(e) for s, e in ps) / len(ps) if ps else float("nan")
+
+
+def kernel_source_digest() -> str:
+    h = hashlib.sha256()
+    for f in ("fa_device.h", "fa_bwd.hip", "fa_fwd.hip"):
+        with open(os.path.join(ROOT, "exact_tiled_attention_32_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def load_traffic(kernel: str):
+    """HBM bytes per launch from the committed rocprofv3 counter summary, if it was taken on
+    the current kernel sources; else None."""
+    path = os.path.join(ROOT, "profiles", "hbm_traffic.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        t = json.load(f)
+    entry = t.get("kernels", {}).get(kernel)
+    if not entry or entry.get("source_digest") != kernel_source_digest():
+        return None
+    return entry.get("bytes_per_launch")
+
+
+def cpu_baseline(target_s: float = 12.0) -> dict:
+    """The fp64 oracle on a bounded sample of the step's workload: head (0, 0), the last R
+    query rows (full causal prefix), forward + backward, for d = 64 and d = 128."""
+    import numpy as np
+    import oracle
+    from exact_tiled_attention_32_amd import workloads
+    try:
+        from threadpoolctl import threadpool_info
+        blas_threads = max((i.get("num_threads", 1) for i in threadpool_info()), default=1)
+    except Exception:  # noqa: BLE001
+        blas_threads = os.cpu_count() or 1
+
+    heads = {}
+    for name in STEP_WORKLOADS:
+        w = workloads.WORKLOADS[name]
+        x = workloads.generate(w)
+        heads[name] = (w, *(x[n][0:1, 0:1].float().numpy().astype(np.float64) for n in ("q", "k", "v", "do")))
+
+    def run(R):
+        flop, t0 = 0.0, time.perf_counter()
+        for name in STEP_WORKLOADS:
+            w, q, k, v, do = heads[name]
+            rows = np.arange(w.N - R, w.N)
+            allow = oracle.allowed_pairs(rows, w.N, causal=True, kv_len_b=None, block_mask=None, mask_block=128)
+            oracle.forward_rows(q[0, 0, rows], k[0, 0], v[0, 0], w.scale, allow)
+            oracle.attention_backward(q, k, v, do, w.scale, causal=True, rows=rows)
+            pairs = float(np.sum(rows + 1))
+            flop += 3.5 * 4.0 * w.d * pairs
+        return flop, time.perf_counter() - t0
+
+    R = 128
+    flop, dt = run(R)
+    N = workloads.WORKLOADS[STEP_WORKLOADS[0]].N
+    R = int(min(N, max(128, R * target_s / max(dt, 1e-3))))
+    R = max(128, (R // 128) * 128)
+    flop, dt = run(R)
+    return {"value": flop / dt / 1e12, "unit": "TFLOP/s", "cores": int(blas_threads), "kind": "oracle",
+            "sample": f"fp64 NumPy oracle, head (b=0,h=0) of the step's workloads (d=64 and d=128), the last {R} "
+                      f"query rows of N=16384 with their full causal prefix, forward + backward; "
+                      f"{flop / 1e9:.1f} GFLOP (same FLOP convention) in {dt:.1f} s"}
+
+
+def time_step(fa, runners, steps, warmup):
+    import torch
+    for _ in range(warmup):
+        for r in runners:
+            r.fwd()
+            r.bwd()
+    torch.cuda.synchronize()
+    clock = KernelClock()
+    t0 = torch.cuda.Event(enable_timing=True)
+    t1 = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t0.record()
+    for _ in range(steps):
+        for r in runners:
+            clock.arm(fa, f"fwd_d{r.w.d}")
+            r.fwd()
+            clock.arm(fa, f"bwd_main_d{r.w.d}")
+            r.bwd()
+    t1.record()
+    torch.cuda.synchronize()
+    return t0.elapsed_time(t1) / steps, clock
+
+
+def report_all(fa, dev, path, steps=10, warmup=3):
+    """Per-workload fwd / bwd timing (not the metric line)."""
+    import torch
+    from exact_tiled_attention_32_amd import workloads
+    out = {}
+    for name, w in workloads.WORKLOADS.items():
+        r = Runner(fa, w, dev)
+        kept = r.kept
+        ff = attn_flops(w, kept)
+        res = {"shape": [w.B, w.H, w.N, w.d], "dtype": w.dtype, "causal": w.causal, "padding": w.padding,
+               "sparse": w.sparse, "fwd_gflop": ff / 1e9}
+        if kept is not None:
+            res["kept_block_fraction"] = kept
+        for phase in ("fwd", "bwd") if w.backward else ("fwd",):
+            fn = r.fwd if phase == "fwd" else r.bwd
+            for _ in range(warmup):
+                fn()
+            torch.cuda.synchronize()
+            clock = KernelClock()
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a.record()
+            for _ in range(steps):
+                clock.arm(fa, phase)
+                fn()
+            b.record()
+            torch.cuda.synchronize()
+            ms = a.elapsed_time(b) / steps
+            flop = ff * (2.5 if phase == "bwd" else 1.0)
+            hbm = 2 * w.B * w.H * w.N * w.d * (4 if phase == "fwd" else 8) * (2 if w.dtype == "bf16" else 4)
+            res[phase] = {"ms": ms, "tflops": flop / ms / 1e9, "frac_of_peak": flop / ms / 1e9 / PEAK_BF16_TFLOPS,
+                          "main_kernel_ms": clock.mean_ms(phase),
+                          "compulsory_hbm_gbs": hbm / 2 / ms / 1e6}
+        out[name] = res
+        print(f"[report] {name}: " + json.dumps({k: v for k, v in res.items() if k in ("fwd", "bwd")}), flush=True)
+        del r
+        torch.cuda.empty_cache()
+    with open(path, "w") as f:
+        json.dump(out, f, indent=1)
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--report", default=None, help="also time every workload and write this JSON file")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only: this build has no multi-GPU path (got --gpus {args.gpus}); "
+              "attention heads are independent, see the sharding note in DESIGN.md", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import exact_tiled_attention_32_amd as fa
+    from exact_tiled_attention_32_amd import workloads
+    fa.load()
+    dev = "cuda:0"
+    runners = [Runner(fa, workloads.WORKLOADS[n], dev) for n in STEP_WORKLOADS]
+    ms, clock = time_step(fa, runners, args.steps, args.warmup)
+    step_flop = sum(3.5 * attn_flops(r.w) for r in runners)
+    value = step_flop / (ms * 1e-3) / 1e12
+
+    per = {}
+    for r in runners:
+        f = attn_flops(r.w)
+        per[f"d{r.w.d}"] = {"fwd_kernel_ms": clock.mean_ms(f"fwd_d{r.w.d}"),
+                            "fwd_tflops": f / clock.mean_ms(f"fwd_d{r.w.d}") / 1e9,
+                            "bwd_main_kernel_ms": clock.mean_ms(f"bwd_main_d{r.w.d}"),
+                            "bwd_main_tflops": 2.5 * f / clock.mean_ms(f"bwd_main_d{r.w.d}") / 1e9}
+    # dominant kernel: the one with the largest time per step
+    cands = [(clock.mean_ms(f"{k}_d{r.w.d}"), k, r) for r in runners for k in ("fwd", "bwd_main")]
+    dom_ms, dom_kind, dom_r = max(cands, key=lambda c: c[0])
+    dom_flop = attn_flops(dom_r.w) * (2.5 if dom_kind == "bwd_main" else 1.0)
+    dom_name = f"{dom_kind}_d{dom_r.w.d}"
+    achieved = dom_flop / dom_ms / 1e9
+    roofline = {"bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                "frac": round(achieved / PEAK_BF16_TFLOPS, 4), "traffic": load_traffic(dom_name),
+                "kernel": dom_name, "kernel_ms": round(dom_ms, 4),
+                "algorithmic_tflop_per_launch": round(dom_flop / 1e12, 4)}
+    line = {"metric": METRIC, "value": round(value, 2), "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps,
+            "warmup": args.warmup, "ms_per_step": round(ms, 4), "higher_is_better": True, "scaling": "weak",
+            "vs_baseline": None, "dtype": "bf16", "data": "synthetic (iid N(0,1), seeded)",
+            "config": {"workload": "long-sequence causal attention fwd+bwd, B=1 H=16 N=16384, d=64 and d=128",
+                       "B": 1, "H": 16, "N": 16384, "d": [64, 128], "causal": True},
+            "frac_of_peak": round(value / PEAK_BF16_TFLOPS, 4), "per_head_dim": per, "roofline": roofline}
+    if args.report:
+        report_all(fa, dev, args.report)
+    if not args.no_cpu_baseline:
+        line["cpu_baseline"] = cpu_baseline()
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,211 @@
+"""Exact tiled attention on AMD Instinct MI355X (gfx950): Python binding of libfa.so.
+
+The binding only marshals arguments: it checks tensor shapes, dtypes, devices and
+contiguity, allocates outputs with PyTorch when the caller passes none, and calls the
+C ABI declared in ``include/fa.h`` through ctypes on the current HIP stream. Every step
+of the computation runs in the library's HIP kernels; there is no fallback. If the
+library is not built, every entry point raises.
+
+Entry points (same names as the C ABI):
+    fa_fwd(q, k, v, scale, causal=False, kv_len=None, o=None, lse=None) -> (o, lse)
+    fa_fwd_blocksparse(q, k, v, scale, block_mask, mask_block=128, causal=False,
+                       kv_len=None, o=None, lse=None) -> (o, lse)
+    fa_bwd_workspace_bytes(B, H, N, d) -> int
+    fa_bwd(q, k, v, o, dout, lse, scale, causal=False, kv_len=None, block_mask=None,
+           mask_block=128, dq=None, dk=None, dv=None, workspace=None) -> (dq, dk, dv)
+    fa_status_string(status) -> str
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch
+
+__all__ = [
+    "FA_F32", "FA_BF16", "FA_OK", "FA_ERR_INVALID", "FA_ERR_UNSUPPORTED", "FA_ERR_HIP",
+    "FAError", "lib_path", "load", "fa_fwd", "fa_fwd_blocksparse", "fa_bwd",
+    "fa_bwd_workspace_bytes", "fa_time_next_kernel", "fa_status_string", "EXPORTED_SYMBOLS",
+]
+
+FA_F32, FA_BF16 = 0, 1
+FA_OK, FA_ERR_INVALID, FA_ERR_UNSUPPORTED, FA_ERR_HIP = 0, 1, 2, 3
+
+EXPORTED_SYMBOLS = ("fa_fwd", "fa_fwd_blocksparse", "fa_bwd_workspace_bytes", "fa_bwd",
+                    "fa_time_next_kernel", "fa_status_string", "fa_last_error")
+
+_LIB = None
+
+
+class FAError(RuntimeError):
+    def __init__(self, status: int, message: str):
+        super().__init__(f"{message} (status {status})")
+        self.status = status
+
+
+def lib_path() -> str:
+    return os.path.join(os.path.dirname(os.path.abspath(__file__)), "libfa.so")
+
+
+def load() -> ctypes.CDLL:
+    """Load libfa.so once. Raises if it has not been built."""
+    global _LIB
+    if _LIB is not None:
+        return _LIB
+    path = lib_path()
+    if not os.path.exists(path):
+        raise RuntimeError(f"HIP attention library missing: {path} (run __graft_entry__.build())")
+    lib = ctypes.CDLL(path)
+    P, I, F, S = ctypes.c_void_p, ctypes.c_int, ctypes.c_float, ctypes.c_size_t
+    lib.fa_fwd.argtypes = [I, I, I, I, I, P, P, P, P, P, F, I, P, P]
+    lib.fa_fwd.restype = I
+    lib.fa_fwd_blocksparse.argtypes = [I, I, I, I, I, P, P, P, P, P, F, I, P, P, I, P]
+    lib.fa_fwd_blocksparse.restype = I
+    lib.fa_bwd_workspace_bytes.argtypes = [I, I, I, I]
+    lib.fa_bwd_workspace_bytes.restype = S
+    lib.fa_bwd.argtypes = [I, I, I, I, I, P, P, P, P, P, P, P, P, P, F, I, P, P, I, P, S, P]
+    lib.fa_bwd.restype = I
+    lib.fa_status_string.argtypes = [I]
+    lib.fa_status_string.restype = ctypes.c_char_p
+    lib.fa_time_next_kernel.argtypes = [P, P]
+    lib.fa_time_next_kernel.restype = None
+    lib.fa_last_error.argtypes = []
+    lib.fa_last_error.restype = ctypes.c_char_p
+    _LIB = lib
+    return lib
+
+
+def fa_time_next_kernel(start: "torch.cuda.Event", stop: "torch.cuda.Event") -> None:
+    """Measurement hook: the next call on this thread records the two (timing-enabled)
+    events around its dominant kernel on its stream. Pass None, None to clear."""
+    lib = load()
+    if start is None or stop is None:
+        lib.fa_time_next_kernel(None, None)
+    else:
+        lib.fa_time_next_kernel(ctypes.c_void_p(start.cuda_event), ctypes.c_void_p(stop.cuda_event))
+
+
+def fa_status_string(status: int) -> str:
+    return load().fa_status_string(int(status)).decode()
+
+
+def _check(status: int) -> None:
+    if status != FA_OK:
+        lib = load()
+        raise FAError(status, f"{lib.fa_status_string(status).decode()}: {lib.fa_last_error().decode()}")
+
+
+def _dtype_code(t: torch.Tensor) -> int:
+    if t.dtype == torch.bfloat16:
+        return FA_BF16
+    if t.dtype == torch.float32:
+        return FA_F32
+    raise TypeError(f"unsupported dtype {t.dtype}; expected bfloat16 or float32")
+
+
+def _dev_tensor(t: torch.Tensor, name: str, like: torch.Tensor | None = None) -> torch.Tensor:
+    if not isinstance(t, torch.Tensor) or not t.is_cuda:
+        raise TypeError(f"{name} must be a device tensor")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous ([B, H, N, d] row-major)")
+    if like is not None and (t.shape != like.shape or t.dtype != like.dtype or t.device != like.device):
+        raise ValueError(f"{name} must match q in shape, dtype and device")
+    return t
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(device: torch.device):
+    return ctypes.c_void_p(torch.cuda.current_stream(device).cuda_stream)
+
+
+def _kv_len(kv_len, q):
+    if kv_len is None:
+        return None
+    kv = _dev_tensor(kv_len, "kv_len")
+    if kv.dtype != torch.int32 or kv.shape != (q.shape[0],) or kv.device != q.device:
+        raise ValueError("kv_len must be an int32 device tensor of shape [B]")
+    return kv
+
+
+def _mask(block_mask, q, mask_block):
+    if block_mask is None:
+        return None
+    m = _dev_tensor(block_mask, "block_mask")
+    nb = -(-q.shape[2] // int(mask_block)) if mask_block > 0 else 0
+    if m.dtype != torch.uint8 or m.shape != (nb, nb) or m.device != q.device:
+        raise ValueError(f"block_mask must be a uint8 device tensor of shape [{nb}, {nb}]")
+    return m
+
+
+def _fwd_common(q, k, v, o, lse):
+    q = _dev_tensor(q, "q")
+    if q.dim() != 4:
+        raise ValueError("q must be [B, H, N, d]")
+    _dev_tensor(k, "k", q)
+    _dev_tensor(v, "v", q)
+    B, H, N, d = q.shape
+    o = torch.empty_like(q) if o is None else _dev_tensor(o, "o", q)
+    if lse is None:
+        lse = torch.empty((B, H, N), dtype=torch.float32, device=q.device)
+    elif lse.shape != (B, H, N) or lse.dtype != torch.float32 or not lse.is_contiguous():
+        raise ValueError("lse must be a contiguous float32 tensor [B, H, N]")
+    return q, o, lse
+
+
+def fa_fwd(q, k, v, scale: float, causal: bool = False, kv_len=None, o=None, lse=None):
+    """O and lse (natural log) of exact attention; see ``fa_fwd`` in include/fa.h."""
+    lib = load()
+    q, o, lse = _fwd_common(q, k, v, o, lse)
+    kv = _kv_len(kv_len, q)
+    B, H, N, d = q.shape
+    _check(lib.fa_fwd(_dtype_code(q), B, H, N, d, _ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse),
+                      float(scale), int(bool(causal)), _ptr(kv), _stream(q.device)))
+    return o, lse
+
+
+def fa_fwd_blocksparse(q, k, v, scale: float, block_mask, mask_block: int = 128, causal: bool = False,
+                       kv_len=None, o=None, lse=None):
+    """Block-sparse forward; see ``fa_fwd_blocksparse`` in include/fa.h."""
+    lib = load()
+    q, o, lse = _fwd_common(q, k, v, o, lse)
+    kv = _kv_len(kv_len, q)
+    m = _mask(block_mask, q, mask_block)
+    if m is None:
+        raise ValueError("block_mask is required")
+    B, H, N, d = q.shape
+    _check(lib.fa_fwd_blocksparse(_dtype_code(q), B, H, N, d, _ptr(q), _ptr(k), _ptr(v), _ptr(o),
+                                  _ptr(lse), float(scale), int(bool(causal)), _ptr(kv), _ptr(m),
+                                  int(mask_block), _stream(q.device)))
+    return o, lse
+
+
+def fa_bwd_workspace_bytes(B: int, H: int, N: int, d: int) -> int:
+    return int(load().fa_bwd_workspace_bytes(int(B), int(H), int(N), int(d)))
+
+
+def fa_bwd(q, k, v, o, dout, lse, scale: float, causal: bool = False, kv_len=None, block_mask=None,
+           mask_block: int = 128, dq=None, dk=None, dv=None, workspace=None):
+    """dQ, dK, dV; see ``fa_bwd`` in include/fa.h. ``workspace`` is a uint8 device tensor."""
+    lib = load()
+    q = _dev_tensor(q, "q")
+    for name, t in (("k", k), ("v", v), ("o", o), ("dout", dout)):
+        _dev_tensor(t, name, q)
+    B, H, N, d = q.shape
+    if lse.shape != (B, H, N) or lse.dtype != torch.float32 or not lse.is_contiguous():
+        raise ValueError("lse must be a contiguous float32 tensor [B, H, N]")
+    dq = torch.empty_like(q) if dq is None else _dev_tensor(dq, "dq", q)
+    dk = torch.empty_like(q) if dk is None else _dev_tensor(dk, "dk", q)
+    dv = torch.empty_like(q) if dv is None else _dev_tensor(dv, "dv", q)
+    kv = _kv_len(kv_len, q)
+    m = _mask(block_mask, q, mask_block)
+    need = fa_bwd_workspace_bytes(B, H, N, d)
+    if workspace is None:
+        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+    _check(lib.fa_bwd(_dtype_code(q), B, H, N, d, _ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(dout),
+                      _ptr(lse), _ptr(dq), _ptr(dk), _ptr(dv), float(scale), int(bool(causal)), _ptr(kv),
+                      _ptr(m), int(mask_block), _ptr(workspace), int(workspace.numel()),
+                      _stream(q.device)))
+    return dq, dk, dv

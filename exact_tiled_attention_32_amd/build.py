@@ -1,0 +1,63 @@
+"""Builds libfa.so (the C-ABI attention library) for gfx950 with hipcc, in-tree.
+
+    python -m exact_tiled_attention_32_amd.build
+
+Each .hip file compiles to its own object in parallel, then one shared link.
+"""
+from __future__ import annotations
+
+import os
+import shutil
+import subprocess
+import sys
+from concurrent.futures import ThreadPoolExecutor
+
+PKG = os.path.dirname(os.path.abspath(__file__))
+ROOT = os.path.dirname(PKG)
+CSRC = os.path.join(PKG, "csrc")
+INCLUDE = os.path.join(ROOT, "include")
+BUILD = os.path.join(PKG, "_build")
+LIB = os.path.join(PKG, "libfa.so")
+SOURCES = ["fa_api.hip", "fa_fwd.hip", "fa_bwd.hip"]
+
+HIPCC = os.environ.get("HIPCC", shutil.which("hipcc") or "/opt/rocm/bin/hipcc")
+ARCH = "gfx950"
+FLAGS = [
+    f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC",
+    # keep hipcc from forming packed fp32 instructions (v_pk_*_f32)
+    "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    "-munsafe-fp-atomics",
+    f"-I{INCLUDE}", f"-I{CSRC}",
+    "-Wall", "-Wno-unused-result",
+]
+
+
+def _compile(src: str) -> str:
+    obj = os.path.join(BUILD, os.path.splitext(src)[0] + ".o")
+    cmd = [HIPCC, *FLAGS, "-c", os.path.join(CSRC, src), "-o", obj]
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    out = "\n".join(x for x in (r.stdout + r.stderr).splitlines() if "packed-fp32-ops" not in x)
+    if r.returncode != 0:
+        raise RuntimeError(f"hipcc failed for {src}:\n{out}")
+    if out.strip():
+        print(out, file=sys.stderr)
+    return obj
+
+
+def build(verbose: bool = True) -> str:
+    os.makedirs(BUILD, exist_ok=True)
+    with ThreadPoolExecutor(max_workers=len(SOURCES)) as ex:
+        objs = list(ex.map(_compile, SOURCES))
+    tmp = LIB + ".tmp"
+    cmd = [HIPCC, f"--offload-arch={ARCH}", "-shared", "-fPIC", *objs, "-o", tmp]
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    if r.returncode != 0:
+        raise RuntimeError(f"link failed:\n{r.stdout}{r.stderr}")
+    os.replace(tmp, LIB)
+    if verbose:
+        print(f"built {LIB}")
+    return LIB
+
+
+if __name__ == "__main__":
+    build()

@@ -1,0 +1,206 @@
+// C-ABI layer: argument validation, workspace sizing and dispatch to the kernels.
+// Declared in include/fa.h. Every check happens on the host before any HIP call, so an
+// invalid request launches nothing and writes nothing.
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+
+#include "fa.h"
+#include "fa_launch.h"
+
+namespace {
+
+thread_local char g_last_error[256] = "";
+thread_local fa::KernelTimer g_timer;
+
+// Hands out (and clears) the pending measurement events of this thread.
+fa::KernelTimer take_timer() {
+  fa::KernelTimer t = g_timer;
+  g_timer = fa::KernelTimer{};
+  return t;
+}
+
+fa_status fail(fa_status s, const char* fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(g_last_error, sizeof(g_last_error), fmt, ap);
+  va_end(ap);
+  return s;
+}
+
+bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+
+size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
+
+// Shared validation of the sizes and the tensor pointers.
+fa_status check_common(fa_dtype dt, int B, int H, int N, int d, float scale) {
+  if (dt != FA_F32 && dt != FA_BF16) return fail(FA_ERR_INVALID, "unknown dtype %d", (int)dt);
+  if (B <= 0 || H <= 0 || N <= 0 || d <= 0)
+    return fail(FA_ERR_INVALID, "sizes must be positive (B=%d H=%d N=%d d=%d)", B, H, N, d);
+  const long double elems = (long double)B * H * N * d;
+  if (elems * 4 > (long double)(1ull << 62)) return fail(FA_ERR_INVALID, "tensor size overflows");
+  const long long wgs = (long long)B * H * ((N + fa::kFwdRowsPerWG - 1) / fa::kFwdRowsPerWG);
+  if (wgs > 0x7fffffffLL) return fail(FA_ERR_INVALID, "grid too large (B*H*ceil(N/128) > 2^31-1)");
+  if (!std::isfinite(scale)) return fail(FA_ERR_INVALID, "scale must be finite");
+  if (d != 64 && d != 128) return fail(FA_ERR_UNSUPPORTED, "head dimension %d not built (64, 128)", d);
+  return FA_OK;
+}
+
+fa_status check_tensor(const void* p, const char* name, size_t align) {
+  if (p == nullptr) return fail(FA_ERR_INVALID, "%s is NULL", name);
+  if (!aligned(p, align)) return fail(FA_ERR_INVALID, "%s is not %zu-byte aligned", name, align);
+  return FA_OK;
+}
+
+#define FA_TRY(expr)                 \
+  do {                               \
+    fa_status _s = (expr);           \
+    if (_s != FA_OK) return _s;      \
+  } while (0)
+
+fa_status check_mask(const uint8_t* mask, int mask_block, int N, int tile_keys) {
+  if (mask == nullptr) return fail(FA_ERR_INVALID, "block_mask is NULL");
+  if (mask_block <= 0 || mask_block % fa::kFwdRowsPerWG != 0)
+    return fail(FA_ERR_INVALID, "mask_block must be a positive multiple of 128 (got %d)", mask_block);
+  if ((N + tile_keys - 1) / tile_keys > fa::kMaxTileList)
+    return fail(FA_ERR_UNSUPPORTED, "block-sparse path supports at most %d key tiles (N=%d)",
+                fa::kMaxTileList, N);
+  return FA_OK;
+}
+
+fa_status fwd_impl(fa_dtype dt, int B, int H, int N, int d, const void* q, const void* k,
+                   const void* v, void* o, float* lse, float scale, int causal,
+                   const int32_t* kv_len, const uint8_t* mask, int mask_block, bool sparse,
+                   hipStream_t stream) {
+  FA_TRY(check_common(dt, B, H, N, d, scale));
+  FA_TRY(check_tensor(q, "q", 16));
+  FA_TRY(check_tensor(k, "k", 16));
+  FA_TRY(check_tensor(v, "v", 16));
+  FA_TRY(check_tensor(o, "o", 16));
+  FA_TRY(check_tensor(lse, "lse", 4));
+  if (kv_len && !aligned(kv_len, 4)) return fail(FA_ERR_INVALID, "kv_len is not 4-byte aligned");
+  if (sparse)
+    FA_TRY(check_mask(mask, mask_block, N, dt == FA_BF16 ? fa::kFwdTileKeysBF16 : fa::kFwdTileKeysF32));
+
+  fa::FwdArgs a{};
+  a.q = q;
+  a.k = k;
+  a.v = v;
+  a.o = o;
+  a.lse = lse;
+  a.kv_len = kv_len;
+  a.mask = sparse ? mask : nullptr;
+  a.B = B;
+  a.H = H;
+  a.N = N;
+  a.mb = sparse ? mask_block : 0;
+  a.nb = sparse ? (N + mask_block - 1) / mask_block : 0;
+  a.ntq = (N + fa::kFwdRowsPerWG - 1) / fa::kFwdRowsPerWG;
+  a.causal = causal ? 1 : 0;
+  const float sabs = std::fabs(scale);
+  // The online maximum needs a positive exponent scale. A negative scale is applied by
+  // negating Q (exact); a zero scale by zeroing Q (every allowed score is then 0).
+  a.qmul = scale > 0.f ? 1.f : (scale < 0.f ? -1.f : 0.f);
+  a.c2 = scale != 0.f ? sabs * 1.4426950408889634f : 1.4426950408889634f;
+  a.sc_abs = sabs;
+  hipError_t e = fa::launch_fwd(a, dt, d, stream, take_timer());
+  if (e != hipSuccess) return fail(FA_ERR_HIP, "forward launch failed: %s", hipGetErrorString(e));
+  return FA_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+fa_status fa_fwd(fa_dtype dt, int B, int H, int N, int d, const void* q, const void* k,
+                 const void* v, void* o, float* lse, float scale, int causal,
+                 const int32_t* kv_len, hipStream_t stream) {
+  return fwd_impl(dt, B, H, N, d, q, k, v, o, lse, scale, causal, kv_len, nullptr, 0, false, stream);
+}
+
+fa_status fa_fwd_blocksparse(fa_dtype dt, int B, int H, int N, int d, const void* q,
+                             const void* k, const void* v, void* o, float* lse, float scale,
+                             int causal, const int32_t* kv_len, const uint8_t* block_mask,
+                             int mask_block, hipStream_t stream) {
+  return fwd_impl(dt, B, H, N, d, q, k, v, o, lse, scale, causal, kv_len, block_mask, mask_block,
+                  true, stream);
+}
+
+size_t fa_bwd_workspace_bytes(int B, int H, int N, int d) {
+  if (B <= 0 || H <= 0 || N <= 0 || d <= 0) return 0;
+  const long double rows = (long double)B * H * N;
+  if (rows * d * 4 > (long double)(1ull << 62)) return 0;
+  const size_t r = (size_t)B * H * N;
+  return align256(r * sizeof(float)) + align256(r * (size_t)d * sizeof(float));
+}
+
+fa_status fa_bwd(fa_dtype dt, int B, int H, int N, int d, const void* q, const void* k,
+                 const void* v, const void* o, const void* dout, const float* lse, void* dq,
+                 void* dk, void* dv, float scale, int causal, const int32_t* kv_len,
+                 const uint8_t* block_mask, int mask_block, void* workspace,
+                 size_t workspace_bytes, hipStream_t stream) {
+  FA_TRY(check_common(dt, B, H, N, d, scale));
+  if (dt != FA_BF16) return fail(FA_ERR_UNSUPPORTED, "backward is built for bf16 only");
+  FA_TRY(check_tensor(q, "q", 16));
+  FA_TRY(check_tensor(k, "k", 16));
+  FA_TRY(check_tensor(v, "v", 16));
+  FA_TRY(check_tensor(o, "o", 16));
+  FA_TRY(check_tensor(dout, "dout", 16));
+  FA_TRY(check_tensor(lse, "lse", 4));
+  FA_TRY(check_tensor(dq, "dq", 16));
+  FA_TRY(check_tensor(dk, "dk", 16));
+  FA_TRY(check_tensor(dv, "dv", 16));
+  if (kv_len && !aligned(kv_len, 4)) return fail(FA_ERR_INVALID, "kv_len is not 4-byte aligned");
+  if (block_mask) FA_TRY(check_mask(block_mask, mask_block, N, fa::kFwdTileKeysBF16));
+  const size_t need = fa_bwd_workspace_bytes(B, H, N, d);
+  if (workspace == nullptr) return fail(FA_ERR_INVALID, "workspace is NULL");
+  if (!aligned(workspace, 256)) return fail(FA_ERR_INVALID, "workspace is not 256-byte aligned");
+  if (workspace_bytes < need)
+    return fail(FA_ERR_INVALID, "workspace too small: %zu bytes given, %zu needed", workspace_bytes, need);
+
+  fa::BwdArgs a{};
+  a.q = q;
+  a.k = k;
+  a.v = v;
+  a.o = o;
+  a.dout = dout;
+  a.lse = lse;
+  a.dq = dq;
+  a.dk = dk;
+  a.dv = dv;
+  const size_t rows = (size_t)B * H * N;
+  a.dsum = reinterpret_cast<float*>(workspace);
+  a.dq_acc = reinterpret_cast<float*>(reinterpret_cast<char*>(workspace) + align256(rows * sizeof(float)));
+  a.kv_len = kv_len;
+  a.mask = block_mask;
+  a.B = B;
+  a.H = H;
+  a.N = N;
+  a.mb = block_mask ? mask_block : 0;
+  a.nb = block_mask ? (N + mask_block - 1) / mask_block : 0;
+  a.causal = causal ? 1 : 0;
+  a.scale = scale;
+  a.c2s = scale * 1.4426950408889634f;
+  hipError_t e = fa::launch_bwd(a, d, stream, take_timer());
+  if (e != hipSuccess) return fail(FA_ERR_HIP, "backward launch failed: %s", hipGetErrorString(e));
+  return FA_OK;
+}
+
+void fa_time_next_kernel(hipEvent_t start, hipEvent_t stop) {
+  g_timer = (start && stop) ? fa::KernelTimer{start, stop} : fa::KernelTimer{};
+}
+
+const char* fa_status_string(fa_status s) {
+  switch (s) {
+    case FA_OK: return "FA_OK";
+    case FA_ERR_INVALID: return "FA_ERR_INVALID: invalid argument";
+    case FA_ERR_UNSUPPORTED: return "FA_ERR_UNSUPPORTED: request not implemented by this build";
+    case FA_ERR_HIP: return "FA_ERR_HIP: HIP runtime error";
+  }
+  return "unknown fa_status";
+}
+
+const char* fa_last_error(void) { return g_last_error; }
+
+}  // extern "C"

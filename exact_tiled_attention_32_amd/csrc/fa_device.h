@@ -1,0 +1,102 @@
+// Device-side building blocks shared by the forward and backward kernels (gfx950 only).
+//
+// MFMA operand layouts used throughout (v_mfma_f32_32x32x16_bf16, wave64), lane l, half
+// h = l / 32:
+//   A (32 x 16, M x K): lane holds A[m = l % 32][k = 8h .. 8h + 7]
+//   B (16 x 32, K x N): lane holds B[k = 8h .. 8h + 7][n = l % 32]
+//   C (32 x 32):        register i holds C[m = 8(i/4) + 4h + (i%4)][n = l % 32]
+// fp32 variant v_mfma_f32_32x32x2_f32: A lane holds A[l % 32][h], B holds B[h][l % 32],
+// C as above.
+//
+// LDS tiles of bf16 rows (K, V, Q, dO) are stored row-major with the 16-byte chunks of
+// each row XOR-swizzled: physical chunk = chunk ^ swz(row),
+//   swz(row) = ((row & 3) << 1) | ((row >> 2) & 1),
+// which keeps (a) 16-byte reads of the same chunk by 8 consecutive rows and (b) the
+// transpose reads, which take 4 consecutive rows x 32 bytes, free of bank conflicts.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace fa {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef short i16x4 __attribute__((ext_vector_type(4)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+
+#define FA_LDS __attribute__((address_space(3)))
+
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kNegInf = -__builtin_inff();
+
+__device__ __forceinline__ int lane_id() { return threadIdx.x & 63; }
+
+__device__ __forceinline__ f32x16 mfma32(bf16x8 a, bf16x8 b, f32x16 c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+}
+
+__device__ __forceinline__ f32x16 mfma32_f32(float a, float b, f32x16 c) {
+  return __builtin_amdgcn_mfma_f32_32x32x2f32(a, b, c, 0, 0, 0);
+}
+
+__device__ __forceinline__ int swz(int row) { return ((row & 3) << 1) | ((row >> 2) & 1); }
+
+// Byte offset of element (row, col) in a swizzled bf16 tile with D columns.
+template <int D>
+__device__ __forceinline__ int tile_off(int row, int col) {
+  return row * (D * 2) + (((col >> 3) ^ swz(row)) << 4) + ((col & 7) << 1);
+}
+
+// 16-byte read of 8 consecutive bf16 (col multiple of 8) from a swizzled tile.
+template <int D>
+__device__ __forceinline__ bf16x8 lds_read8(const FA_LDS char* tile, int row, int col) {
+  return *reinterpret_cast<const FA_LDS bf16x8*>(tile + tile_off<D>(row, col));
+}
+
+// Transpose read (ds_read_b64_tr_b16). Within each 16-lane group, lane 4r + c supplies
+// the address of row r, columns 4c .. 4c + 3 of a 4 x 16 block of 16-bit elements, and
+// lane j of the group receives column j: (row 0, row 1, row 2, row 3).
+__device__ __forceinline__ bf16x4 lds_read_tr(const FA_LDS char* addr) {
+  i16x4 r = __builtin_amdgcn_ds_read_tr16_b64_v4i16((FA_LDS i16x4*)addr);
+  return __builtin_bit_cast(bf16x4, r);
+}
+
+// MFMA A operand "X^T" (M = column index of X, K = row index of X) for the 32 columns
+// [col0, col0 + 32) and the 8 rows {r0 + 4h + 0..3, r0 + 8 + 4h + 0..3} of a swizzled tile
+// X: lane l receives X[those rows][col0 + l % 32]. This is the row permutation that the
+// accumulator layout of a 32 x 32 MFMA block hands to the next product (registers
+// 8t .. 8t + 7 of a C tile cover rows 16t + {4h..4h+3, 8+4h..8+4h+3}).
+template <int D>
+__device__ __forceinline__ bf16x8 lds_read_tr8(const FA_LDS char* tile, int r0, int col0) {
+  const int l = lane_id();
+  const int h = l >> 5;
+  const int j = l & 15;
+  const int rr = j >> 2;                          // row inside the 4-row block
+  const int cc = col0 + ((l >> 4) & 1) * 16 + (j & 3) * 4;
+  bf16x4 lo = lds_read_tr(tile + tile_off<D>(r0 + 4 * h + rr, cc));
+  bf16x4 hi = lds_read_tr(tile + tile_off<D>(r0 + 8 + 4 * h + rr, cc));
+  return __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+}
+
+// Pack 8 fp32 accumulator values (registers base .. base + 7) into a bf16 MFMA operand,
+// round-to-nearest-even.
+__device__ __forceinline__ bf16x8 pack8(const f32x16& c, int base) {
+  bf16x8 r;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) r[i] = (__bf16)c[base + i];
+  return r;
+}
+
+__device__ __forceinline__ float wave_xor32(float x) { return __shfl_xor(x, 32); }
+
+__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+
+// 16-byte global load/store helpers (addresses 16-byte aligned).
+__device__ __forceinline__ u32x4 gload16(const void* p) { return *reinterpret_cast<const u32x4*>(p); }
+__device__ __forceinline__ void lds_store16(FA_LDS char* p, u32x4 v) { *reinterpret_cast<FA_LDS u32x4*>(p) = v; }
+
+}  // namespace fa

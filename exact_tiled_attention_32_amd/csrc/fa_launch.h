@@ -1,0 +1,65 @@
+// Internal interface between the C-ABI layer (fa_api.hip) and the kernel files.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "fa.h"
+
+namespace fa {
+
+// Forward arguments, already validated by the host layer.
+struct FwdArgs {
+  const void* q;
+  const void* k;
+  const void* v;
+  void* o;
+  float* lse;
+  const int32_t* kv_len;  // nullptr: every key valid
+  const uint8_t* mask;    // nullptr: dense
+  int B, H, N;
+  int mb;                 // mask block side (multiple of 128) when mask != nullptr
+  int nb;                 // mask blocks per side
+  int ntq;                // query tiles per (b, h)
+  int causal;
+  float c2;               // |scale| * log2(e), or log2(e) when scale == 0 (exp2 domain)
+  float sc_abs;           // |scale|: lse = m * |scale| + ln l
+  float qmul;             // +1, -1 (negative scale) or 0 (zero scale), applied to Q exactly
+};
+
+// Backward arguments, already validated by the host layer.
+struct BwdArgs {
+  const void* q;
+  const void* k;
+  const void* v;
+  const void* o;
+  const void* dout;
+  const float* lse;
+  void* dq;
+  void* dk;
+  void* dv;
+  float* dsum;            // workspace: D = rowsum(dO * O), [B,H,N]
+  float* dq_acc;          // workspace: fp32 dQ accumulator, [B,H,N,d]
+  const int32_t* kv_len;
+  const uint8_t* mask;
+  int B, H, N, mb, nb;
+  int causal;
+  float scale;            // signed softmax scale
+  float c2s;              // scale * log2(e)
+};
+
+constexpr int kFwdRowsPerWG = 128;
+constexpr int kFwdTileKeysBF16 = 64;
+constexpr int kFwdTileKeysF32 = 32;
+constexpr int kMaxTileList = 4096;
+
+// Optional events recorded around the dominant kernel of a call (may be nullptr).
+struct KernelTimer {
+  hipEvent_t start = nullptr;
+  hipEvent_t stop = nullptr;
+};
+
+hipError_t launch_fwd(const FwdArgs& a, fa_dtype dt, int d, hipStream_t stream, const KernelTimer& tm);
+hipError_t launch_bwd(const BwdArgs& a, int d, hipStream_t stream, const KernelTimer& tm);
+
+}  // namespace fa

@@ -100,16 +100,20 @@ def generate(w: Workload, *, with_grad_out: bool | None = None) -> dict:
 
 def make_case(B: int, H: int, N: int, d: int, *, dtype: str = "bf16", seed: int = 0,
               causal: bool = False, kv_len=None, block_mask=None, mask_block: int = 128,
-              magnitude: float = 1.0) -> dict:
-    """A small seeded case for the parity sweep. ``kv_len`` may be a list of ints."""
+              q_magnitude: float = 1.0) -> dict:
+    """A small seeded case for the parity sweep. ``kv_len`` may be a list of ints.
+
+    ``q_magnitude`` multiplies Q before rounding: large values give scores with a
+    standard deviation of about ``q_magnitude`` (scale = 1/sqrt(d)).
+    """
     gen = torch.Generator("cpu").manual_seed(seed)
     shape = (B, H, N, d)
 
-    def draw():
-        x = torch.randn(shape, generator=gen, dtype=torch.float32) * magnitude
+    def draw(mult=1.0):
+        x = torch.randn(shape, generator=gen, dtype=torch.float32) * mult
         return x if dtype == "f32" else x.to(torch.bfloat16)
 
-    q, k, v, do = draw(), draw(), draw(), draw()
+    q, k, v, do = draw(q_magnitude), draw(), draw(), draw()
     kl = None if kv_len is None else torch.tensor(kv_len, dtype=torch.int32)
     bm = None if block_mask is None else torch.as_tensor(block_mask, dtype=torch.uint8)
     return {"q": q, "k": k, "v": v, "do": do, "kv_len": kl, "block_mask": bm,

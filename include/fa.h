@@ -1,0 +1,153 @@
+/*
+ * fa.h — C ABI of the exact tiled attention library for AMD Instinct MI355X (gfx950).
+ *
+ * What the library computes
+ *   Exact scaled-dot-product attention, per (batch b, head h):
+ *       O = softmax(scale * Q K^T) V            (row-wise softmax over keys)
+ *   as defined in aiwiki.page "FlashAttention", section "Attention and the memory
+ *   bottleneck" (masks restrict which query-key pairs interact), computed by the tiled
+ *   online-softmax method of the same page, section "Tiling and online normalization",
+ *   so the N x N score matrix never reaches device memory. Only the per-row log-sum-exp
+ *       lse_i = ln sum_{j allowed} exp(scale * q_i . k_j)
+ *   is kept (sendsoonai.com "FlashAttention: IO-aware explained", section
+ *   "Recomputation and IO complexity": only the softmax statistics are stored), and the
+ *   backward pass recomputes each score tile from it.
+ *
+ * Allowed pairs (all predicates combine with AND)
+ *   causal       : key j <= query i (square self-attention, queries and keys share N)
+ *   kv_len       : key j <  kv_len[b] (key padding; aiwiki "FlashAttention", section
+ *                  "Software integration and limitations": variable-length sequences)
+ *   block_mask   : block_mask[i / mask_block][j / mask_block] != 0 (legiblepapers.com
+ *                  "Fast and Memory Efficient Exact Attention", summary: block-sparse
+ *                  attention skips the zero blocks of a predefined block mask)
+ *   Query rows are never masked. A row with no allowed key yields O = 0, lse = -inf and a
+ *   zero dQ row.
+ *
+ * Conventions shared by every entry point
+ *   - Tensors q, k, v, o, dout, dq, dk, dv are DEVICE pointers owned by the caller, laid out
+ *     [B, H, N, d] row-major (d contiguous), all of the same dtype, 16-byte aligned.
+ *     lse is a device float array [B, H, N] (natural log), 4-byte aligned.
+ *     kv_len, when not NULL, is a device int32 array [B]; values are clamped to [0, N].
+ *     block_mask, when used, is a device uint8 array [nb, nb] row-major with
+ *     nb = ceil(N / mask_block), shared by every (b, h).
+ *   - Every call validates its arguments synchronously on the host, before touching the
+ *     device. On any error nothing is launched and no output is written.
+ *   - Work is enqueued asynchronously on `stream` (NULL = the default stream). The library
+ *     allocates no device memory and keeps no per-call state: calls are re-entrant and
+ *     thread-safe. Faults during execution surface at the caller's stream synchronisation.
+ *   - bf16 (FA_BF16): d in {64, 128}, forward and backward. fp32 (FA_F32): d in {64, 128},
+ *     forward only.
+ */
+#ifndef EXACT_TILED_ATTENTION_FA_H
+#define EXACT_TILED_ATTENTION_FA_H
+
+#include <stddef.h>
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  FA_F32 = 0,  /* IEEE fp32 tensors */
+  FA_BF16 = 1  /* bfloat16 tensors; arithmetic accumulates in fp32 */
+} fa_dtype;
+
+typedef enum {
+  FA_OK = 0,
+  FA_ERR_INVALID = 1,     /* bad argument: NULL or misaligned pointer, non-positive or
+                             overflowing size, NaN/Inf scale, mask without a valid
+                             mask_block, workspace missing or too small */
+  FA_ERR_UNSUPPORTED = 2, /* a valid request this build does not implement (dtype / d
+                             combination, backward in fp32, too many mask blocks); the
+                             caller may fall back to another implementation */
+  FA_ERR_HIP = 3          /* the HIP runtime reported an error at launch */
+} fa_status;
+
+/*
+ * Forward pass: O and lse.
+ *   dt        element type of q, k, v, o
+ *   B, H, N, d  batch, heads, sequence length (queries = keys), head dimension
+ *   q, k, v   inputs [B,H,N,d] (read only)
+ *   o         output [B,H,N,d]
+ *   lse       output [B,H,N] fp32, natural-log log-sum-exp of the scaled scores of each row
+ *   scale     multiplier of q.k inside the softmax (1/sqrt(d) for standard attention)
+ *   causal    nonzero: key j allowed only for j <= i
+ *   kv_len    NULL (every key valid) or device int32 [B] of valid key counts
+ * Online-softmax update of aiwiki "FlashAttention", section "Tiling and online
+ * normalization" (running max, rescaled running sum and accumulator, final O = u / l).
+ */
+fa_status fa_fwd(fa_dtype dt, int B, int H, int N, int d,
+                 const void* q, const void* k, const void* v,
+                 void* o, float* lse,
+                 float scale, int causal, const int32_t* kv_len,
+                 hipStream_t stream);
+
+/*
+ * Block-sparse forward: as fa_fwd, and additionally every key tile whose mask block is
+ * zero is skipped without being read (legiblepapers.com "Fast and Memory Efficient Exact
+ * Attention", summary paragraph). O is written for every row.
+ *   block_mask  device uint8 [nb, nb], nb = ceil(N / mask_block), nonzero = keep
+ *   mask_block  side of a square mask block; a positive multiple of 128; nb <= 4096
+ */
+fa_status fa_fwd_blocksparse(fa_dtype dt, int B, int H, int N, int d,
+                             const void* q, const void* k, const void* v,
+                             void* o, float* lse,
+                             float scale, int causal, const int32_t* kv_len,
+                             const uint8_t* block_mask, int mask_block,
+                             hipStream_t stream);
+
+/*
+ * Bytes of device workspace fa_bwd needs: the per-row D = rowsum(dO * O) (fp32 [B,H,N])
+ * and the fp32 dQ accumulator [B,H,N,d], each 256-byte aligned. Linear in N (the
+ * backward keeps O(N) extra memory; cochat.ai audit of "FlashAttention: Fast and
+ * Memory-Efficient Exact Attention with IO-Awareness", quoted backward-pass memory claim).
+ * Returns 0 for non-positive or overflowing sizes.
+ */
+size_t fa_bwd_workspace_bytes(int B, int H, int N, int d);
+
+/*
+ * Backward pass: dQ, dK, dV of L = sum(O * dout) (bf16 only).
+ *   q, k, v, o, lse   the inputs and outputs of the matching forward call (same mask
+ *                     arguments); o and lse are read, not recomputed
+ *   dout              upstream gradient [B,H,N,d]
+ *   dq, dk, dv        outputs [B,H,N,d]
+ *   block_mask        NULL (dense) or as in fa_fwd_blocksparse; mask_block ignored if NULL
+ *   workspace         device memory of at least fa_bwd_workspace_bytes(B,H,N,d) bytes,
+ *                     256-byte aligned, owned by the caller; its contents on entry do not
+ *                     matter and are overwritten
+ * Structure (cochat.ai audit, quoted Theorem 5 proof / App. C): each key/value tile is
+ * loaded once and its dK, dV stay on chip while query tiles stream past; dQ is
+ * accumulated in fp32 across key tiles. The score tile is recomputed from q, k and lse.
+ */
+fa_status fa_bwd(fa_dtype dt, int B, int H, int N, int d,
+                 const void* q, const void* k, const void* v,
+                 const void* o, const void* dout, const float* lse,
+                 void* dq, void* dk, void* dv,
+                 float scale, int causal, const int32_t* kv_len,
+                 const uint8_t* block_mask, int mask_block,
+                 void* workspace, size_t workspace_bytes,
+                 hipStream_t stream);
+
+/*
+ * Measurement hook. When both events are non-NULL, the next fa_fwd, fa_fwd_blocksparse or
+ * fa_bwd call on the calling thread that passes validation records `start` on its stream
+ * immediately before launching its dominant kernel (the forward kernel, or the backward
+ * main kernel) and `stop` immediately after it, then forgets both events. Passing NULL
+ * clears a pending request. The events are owned by the caller.
+ */
+void fa_time_next_kernel(hipEvent_t start, hipEvent_t stop);
+
+/* Static English name of a status code. */
+const char* fa_status_string(fa_status s);
+
+/* Human-readable reason for the last non-OK status returned on the calling thread
+ * (static per-thread storage, valid until the next call on that thread). */
+const char* fa_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* EXACT_TILED_ATTENTION_FA_H */

@@ -148,15 +148,17 @@ def attention_forward(q, k, v, scale: float, *, causal: bool = False, kv_len=Non
 
 
 def attention_backward(q, k, v, dout, scale: float, *, causal: bool = False, kv_len=None,
-                       block_mask=None, mask_block: int = 128, heads=None,
+                       block_mask=None, mask_block: int = 128, heads=None, rows=None,
                        row_chunk: int = _ROW_CHUNK):
     """dQ, dK, dV of L = sum(O * dO) for the forward above, all fp64.
 
     The probabilities are recomputed from the definition (two-pass softmax);
     the softmax Jacobian-vector product is written out in full. ``heads``
-    optionally restricts the work to a list of (b, h) pairs (the other entries
-    of the returned arrays stay zero): used to sample one head of a large
-    workload.
+    optionally restricts the work to a list of (b, h) pairs, and ``rows`` to a
+    sorted list of query rows: only those rows get dQ, and dK / dV then hold
+    the contributions of those rows alone (exact for every key that no other
+    row may attend to). Entries outside the restriction stay zero. Both serve
+    to sample a large workload.
     """
     q, k, v, dout = _as_f64(q), _as_f64(k), _as_f64(v), _as_f64(dout)
     B, H, N, d = q.shape
@@ -165,9 +167,10 @@ def attention_backward(q, k, v, dout, scale: float, *, causal: bool = False, kv_
     dv = np.zeros_like(v)
     lens = None if kv_len is None else [int(x) for x in np.asarray(kv_len).reshape(-1)]
     pairs = [(b, h) for b in range(B) for h in range(H)] if heads is None else list(heads)
+    all_rows = np.arange(N) if rows is None else np.asarray(rows, dtype=np.int64)
     for b, h in pairs:
-        for r0 in range(0, N, row_chunk):
-            rows = np.arange(r0, min(N, r0 + row_chunk))
+        for r0 in range(0, all_rows.size, row_chunk):
+            rows = all_rows[r0:r0 + row_chunk]
             allow = allowed_pairs(rows, k.shape[2], causal=causal,
                                   kv_len_b=None if lens is None else lens[b],
                                   block_mask=block_mask, mask_block=mask_block)

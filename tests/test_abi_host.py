@@ -1,0 +1,139 @@
+"""Host-side tests of the C ABI: the library loads, exports what include/fa.h declares,
+sizes its workspace linearly in N, and rejects invalid requests before touching a device.
+
+No call here reaches a kernel launch: every request fails validation on the host, so
+the tests run without a GPU (fake, well-aligned pointer values are never dereferenced).
+"""
+import ctypes
+import os
+import re
+
+import pytest
+
+import exact_tiled_attention_32_amd as fa
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "fa.h")
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(fa.lib_path()):
+        from exact_tiled_attention_32_amd import build
+        build.build(verbose=False)
+    return fa.load()
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(fa_[a-z_]+)\s*\(", text)))
+
+
+def test_exports_every_declared_symbol(lib):
+    names = declared_functions()
+    assert set(names) == set(fa.EXPORTED_SYMBOLS), names
+    for n in names:
+        assert getattr(lib, n) is not None
+
+
+def test_workspace_bytes_linear_in_n(lib):
+    # exact formula: align256(rows * 4) + align256(rows * d * 4)
+    for B, H, N, d in [(1, 1, 1, 64), (8, 16, 512, 64), (1, 16, 16384, 128), (1, 8, 65536, 64)]:
+        rows = B * H * N
+        al = lambda x: (x + 255) // 256 * 256
+        assert fa.fa_bwd_workspace_bytes(B, H, N, d) == al(rows * 4) + al(rows * d * 4)
+    # O(N): doubling N doubles the workspace (no N^2 term)
+    assert fa.fa_bwd_workspace_bytes(1, 1, 32768, 64) == 2 * fa.fa_bwd_workspace_bytes(1, 1, 16384, 64)
+    assert fa.fa_bwd_workspace_bytes(0, 1, 1, 64) == 0
+    assert fa.fa_bwd_workspace_bytes(1, 1, -5, 64) == 0
+
+
+def test_status_strings(lib):
+    for s in (fa.FA_OK, fa.FA_ERR_INVALID, fa.FA_ERR_UNSUPPORTED, fa.FA_ERR_HIP):
+        assert fa.fa_status_string(s).startswith("FA_")
+    assert fa.fa_status_string(99) == "unknown fa_status"
+
+
+P = 0x10000  # fake, 256-byte aligned device address; never dereferenced
+
+
+def fwd(lib, dt=fa.FA_BF16, B=1, H=1, N=128, d=64, q=P, k=P, v=P, o=P, lse=P, scale=0.125,
+        causal=0, kv_len=None):
+    c = ctypes.c_void_p
+    return lib.fa_fwd(dt, B, H, N, d, c(q), c(k), c(v), c(o), c(lse), scale, causal,
+                      None if kv_len is None else c(kv_len), None)
+
+
+def fwd_sparse(lib, mask=P, mb=128, **kw):
+    c = ctypes.c_void_p
+    return lib.fa_fwd_blocksparse(kw.get("dt", fa.FA_BF16), 1, 1, kw.get("N", 256), 64, c(P), c(P), c(P),
+                                  c(P), c(P), 0.125, 0, None, None if mask is None else c(mask), mb, None)
+
+
+def bwd(lib, dt=fa.FA_BF16, N=128, d=64, ws=P, ws_bytes=None, mask=None, mb=128, dq=P, scale=0.125):
+    c = ctypes.c_void_p
+    need = fa.fa_bwd_workspace_bytes(1, 1, N, d) if ws_bytes is None else ws_bytes
+    return lib.fa_bwd(dt, 1, 1, N, d, c(P), c(P), c(P), c(P), c(P), c(P), c(dq), c(P), c(P), scale, 0, None,
+                      None if mask is None else c(mask), mb, None if ws is None else c(ws), need, None)
+
+
+@pytest.mark.parametrize("kwargs, status", [
+    (dict(q=0), fa.FA_ERR_INVALID),
+    (dict(o=0), fa.FA_ERR_INVALID),
+    (dict(lse=0), fa.FA_ERR_INVALID),
+    (dict(k=P + 8), fa.FA_ERR_INVALID),          # not 16-byte aligned
+    (dict(lse=P + 2), fa.FA_ERR_INVALID),        # not 4-byte aligned
+    (dict(kv_len=P + 1), fa.FA_ERR_INVALID),
+    (dict(B=0), fa.FA_ERR_INVALID),
+    (dict(N=-3), fa.FA_ERR_INVALID),
+    (dict(H=1 << 30, N=1 << 30), fa.FA_ERR_INVALID),  # size overflow
+    (dict(scale=float("nan")), fa.FA_ERR_INVALID),
+    (dict(scale=float("inf")), fa.FA_ERR_INVALID),
+    (dict(dt=7), fa.FA_ERR_INVALID),
+    (dict(d=96), fa.FA_ERR_UNSUPPORTED),
+    (dict(d=32), fa.FA_ERR_UNSUPPORTED),
+    (dict(dt=fa.FA_F32, d=80), fa.FA_ERR_UNSUPPORTED),
+])
+def test_fwd_rejects(lib, kwargs, status):
+    assert fwd(lib, **kwargs) == status
+    assert lib.fa_last_error().decode()
+
+
+@pytest.mark.parametrize("kwargs, status", [
+    (dict(mask=None), fa.FA_ERR_INVALID),
+    (dict(mb=0), fa.FA_ERR_INVALID),
+    (dict(mb=100), fa.FA_ERR_INVALID),
+    (dict(mb=64), fa.FA_ERR_INVALID),
+    (dict(N=4096 * 64 + 1), fa.FA_ERR_UNSUPPORTED),  # key-tile list capacity
+])
+def test_fwd_blocksparse_rejects(lib, kwargs, status):
+    assert fwd_sparse(lib, **kwargs) == status
+
+
+@pytest.mark.parametrize("kwargs, status", [
+    (dict(dt=fa.FA_F32), fa.FA_ERR_UNSUPPORTED),
+    (dict(ws=None), fa.FA_ERR_INVALID),
+    (dict(ws=P + 16), fa.FA_ERR_INVALID),
+    (dict(ws_bytes=1024), fa.FA_ERR_INVALID),
+    (dict(dq=0), fa.FA_ERR_INVALID),
+    (dict(mask=P, mb=96), fa.FA_ERR_INVALID),
+    (dict(scale=float("nan")), fa.FA_ERR_INVALID),
+    (dict(d=256), fa.FA_ERR_UNSUPPORTED),
+])
+def test_bwd_rejects(lib, kwargs, status):
+    assert bwd(lib, **kwargs) == status
+
+
+def test_binding_refuses_cpu_tensors(lib):
+    import torch
+    x = torch.zeros(1, 1, 4, 64, dtype=torch.bfloat16)
+    with pytest.raises(TypeError):
+        fa.fa_fwd(x, x, x, 0.125)
+
+
+def test_binding_fails_loudly_without_library(monkeypatch, tmp_path):
+    monkeypatch.setattr(fa, "_LIB", None)
+    monkeypatch.setattr(fa, "lib_path", lambda: str(tmp_path / "missing.so"))
+    with pytest.raises(RuntimeError, match="missing"):
+        fa.load()
