@@ -28,6 +28,7 @@ PEAK_BF16_TFLOPS = 2500.0  # MI355X dense bf16 MFMA
 PEAK_HBM_GBS = 8000.0
 METRIC = "attention fwd+bwd TFLOP/s (bf16, causal) and % of MI355X bf16 MFMA peak"
 STEP_WORKLOADS = ("long_causal_d64", "long_causal_d128")
+CALIBRATION_BYTES = 256 << 20
 
 
 def attn_flops(w, kept_fraction=None) -> float:
@@ -229,6 +230,9 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--report", default=None, help="also time every workload and write this JSON file")
+    ap.add_argument("--pmc-pass", action="store_true",
+                    help="for rocprofv3 --pmc: one 256 MiB device copy (counter calibration), then one "
+                         "untimed pass of the step; prints no metric line")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only: this build has no multi-GPU path (got --gpus {args.gpus}); "
@@ -241,6 +245,17 @@ def main():
     fa.load()
     dev = "cuda:0"
     runners = [Runner(fa, workloads.WORKLOADS[n], dev) for n in STEP_WORKLOADS]
+    if args.pmc_pass:
+        src = torch.ones(CALIBRATION_BYTES // 4, dtype=torch.float32, device=dev)
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        dst.copy_(src)  # reads and writes exactly CALIBRATION_BYTES each
+        for r in runners:
+            r.fwd()
+            r.bwd()
+        torch.cuda.synchronize()
+        print(f"pmc pass done: calibration copy of {CALIBRATION_BYTES} bytes, one step", flush=True)
+        return
     ms, clock = time_step(fa, runners, args.steps, args.warmup)
     step_flop = sum(3.5 * attn_flops(r.w) for r in runners)
     value = step_flop / (ms * 1e-3) / 1e12

@@ -53,6 +53,13 @@ def build(verbose: bool = True) -> str:
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"link failed:\n{r.stdout}{r.stderr}")
+    # A kernel whose host-side instantiation failed leaves an undefined launch stub that
+    # only shows when the library is loaded: load it here so the build fails instead.
+    import ctypes
+    try:
+        ctypes.CDLL(tmp)
+    except OSError as e:
+        raise RuntimeError(f"built library does not load: {e}") from e
     os.replace(tmp, LIB)
     if verbose:
         print(f"built {LIB}")

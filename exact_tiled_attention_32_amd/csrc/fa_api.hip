@@ -81,7 +81,7 @@ fa_status fwd_impl(fa_dtype dt, int B, int H, int N, int d, const void* q, const
   FA_TRY(check_tensor(lse, "lse", 4));
   if (kv_len && !aligned(kv_len, 4)) return fail(FA_ERR_INVALID, "kv_len is not 4-byte aligned");
   if (sparse)
-    FA_TRY(check_mask(mask, mask_block, N, dt == FA_BF16 ? fa::kFwdTileKeysBF16 : fa::kFwdTileKeysF32));
+    FA_TRY(check_mask(mask, mask_block, N, dt == FA_BF16 ? fa::fwd_tile_keys_bf16(d) : fa::kFwdTileKeysF32));
 
   fa::FwdArgs a{};
   a.q = q;
@@ -96,7 +96,8 @@ fa_status fwd_impl(fa_dtype dt, int B, int H, int N, int d, const void* q, const
   a.N = N;
   a.mb = sparse ? mask_block : 0;
   a.nb = sparse ? (N + mask_block - 1) / mask_block : 0;
-  a.ntq = (N + fa::kFwdRowsPerWG - 1) / fa::kFwdRowsPerWG;
+  const int rows_per_wg = dt == FA_BF16 ? fa::kFwdRowsPerWGBF16 : fa::kFwdRowsPerWG;
+  a.ntq = (N + rows_per_wg - 1) / rows_per_wg;
   a.causal = causal ? 1 : 0;
   const float sabs = std::fabs(scale);
   // The online maximum needs a positive exponent scale. A negative scale is applied by
@@ -152,7 +153,7 @@ fa_status fa_bwd(fa_dtype dt, int B, int H, int N, int d, const void* q, const v
   FA_TRY(check_tensor(dk, "dk", 16));
   FA_TRY(check_tensor(dv, "dv", 16));
   if (kv_len && !aligned(kv_len, 4)) return fail(FA_ERR_INVALID, "kv_len is not 4-byte aligned");
-  if (block_mask) FA_TRY(check_mask(block_mask, mask_block, N, fa::kFwdTileKeysBF16));
+  if (block_mask) FA_TRY(check_mask(block_mask, mask_block, N, fa::bwd_query_step(d)));
   const size_t need = fa_bwd_workspace_bytes(B, H, N, d);
   if (workspace == nullptr) return fail(FA_ERR_INVALID, "workspace is NULL");
   if (!aligned(workspace, 256)) return fail(FA_ERR_INVALID, "workspace is not 256-byte aligned");

@@ -8,11 +8,16 @@
 // fp32 variant v_mfma_f32_32x32x2_f32: A lane holds A[l % 32][h], B holds B[h][l % 32],
 // C as above.
 //
-// LDS tiles of bf16 rows (K, V, Q, dO) are stored row-major with the 16-byte chunks of
-// each row XOR-swizzled: physical chunk = chunk ^ swz(row),
-//   swz(row) = ((row & 3) << 1) | ((row >> 2) & 1),
-// which keeps (a) 16-byte reads of the same chunk by 8 consecutive rows and (b) the
-// transpose reads, which take 4 consecutive rows x 32 bytes, free of bank conflicts.
+// LDS tiles of bf16 rows (K, V, Q, dO, dS^T) are stored row-major with the 16-byte chunks
+// of each row XOR-swizzled: physical chunk = chunk ^ swz<D>(row). The LDS has 64 banks of
+// 4 bytes and serves 16 lanes per cycle; the swizzle keeps both access patterns the
+// kernels use free of bank conflicts:
+//   (a) 16-byte reads of one logical chunk by 16 consecutive rows (MFMA row operands), and
+//   (b) transpose reads, where 16 lanes take 4 consecutive rows x 32 bytes.
+//   D = 128 (16 chunks / 256-byte row):  swz = ((row & 3) << 2) | ((row >> 2) & 3)
+//   D = 64  (8 chunks / 128-byte row, two rows per bank line):
+//                                        swz = (((row >> 1) & 1) << 2) | ((row >> 2) & 3)
+// swz depends on row & 15 only, so moving by a multiple of 16 rows is a plain offset.
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -43,13 +48,22 @@ __device__ __forceinline__ f32x16 mfma32_f32(float a, float b, f32x16 c) {
   return __builtin_amdgcn_mfma_f32_32x32x2f32(a, b, c, 0, 0, 0);
 }
 
-__device__ __forceinline__ int swz(int row) { return ((row & 3) << 1) | ((row >> 2) & 1); }
+template <int D>
+__device__ __forceinline__ int swz(int row) {
+  static_assert(D == 32 || D == 64 || D == 128, "tile width");
+  if constexpr (D == 128) return ((row & 3) << 2) | ((row >> 2) & 3);
+  else if constexpr (D == 64) return (((row >> 1) & 1) << 2) | ((row >> 2) & 3);
+  else return (row >> 2) & 3;  // 4 chunks / 64-byte row, four rows per bank line
+}
 
 // Byte offset of element (row, col) in a swizzled bf16 tile with D columns.
 template <int D>
 __device__ __forceinline__ int tile_off(int row, int col) {
-  return row * (D * 2) + (((col >> 3) ^ swz(row)) << 4) + ((col & 7) << 1);
+  return row * (D * 2) + (((col >> 3) ^ swz<D>(row)) << 4) + ((col & 7) << 1);
 }
+
+// 16-byte LDS read at a precomputed address.
+__device__ __forceinline__ bf16x8 lds_ld8(const FA_LDS char* p) { return *reinterpret_cast<const FA_LDS bf16x8*>(p); }
 
 // 16-byte read of 8 consecutive bf16 (col multiple of 8) from a swizzled tile.
 template <int D>
@@ -82,6 +96,22 @@ __device__ __forceinline__ bf16x8 lds_read_tr8(const FA_LDS char* tile, int r0, 
   return __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
 }
 
+// The two per-lane addresses of lds_read_tr8<D>(tile, 0, col0), tile-relative. Adding
+// 16 t * 2D bytes to both gives the read at r0 = 16 t (swz<D> depends on row & 15 only).
+template <int D>
+__device__ __forceinline__ void tr8_offsets(int col0, int& lo, int& hi) {
+  const int l = lane_id();
+  const int h = l >> 5;
+  const int j = l & 15;
+  const int cc = col0 + ((l >> 4) & 1) * 16 + (j & 3) * 4;
+  lo = tile_off<D>(4 * h + (j >> 2), cc);
+  hi = tile_off<D>(8 + 4 * h + (j >> 2), cc);
+}
+
+__device__ __forceinline__ bf16x8 lds_tr8(const FA_LDS char* lo, const FA_LDS char* hi) {
+  return __builtin_shufflevector(lds_read_tr(lo), lds_read_tr(hi), 0, 1, 2, 3, 4, 5, 6, 7);
+}
+
 // Pack 8 fp32 accumulator values (registers base .. base + 7) into a bf16 MFMA operand,
 // round-to-nearest-even.
 __device__ __forceinline__ bf16x8 pack8(const f32x16& c, int base) {
@@ -92,6 +122,15 @@ __device__ __forceinline__ bf16x8 pack8(const f32x16& c, int base) {
 }
 
 __device__ __forceinline__ float wave_xor32(float x) { return __shfl_xor(x, 32); }
+
+// The value held by the lane 32 positions away (the other half of the wave), through
+// v_permlane32_swap: for lanes < 32 the second result is the upper half's value, for
+// lanes >= 32 the first result is the lower half's value.
+__device__ __forceinline__ float other_half(float x) {
+  const int xi = __builtin_bit_cast(int, x);
+  const auto r = __builtin_amdgcn_permlane32_swap(xi, xi, false, false);
+  return __builtin_bit_cast(float, lane_id() < 32 ? (int)r[1] : (int)r[0]);
+}
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 

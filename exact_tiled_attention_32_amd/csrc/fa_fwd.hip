@@ -22,6 +22,8 @@
 //     row's maximum grew by more than 2^8 in the exp2 domain, which keeps every
 //     probability below 256 and leaves the result exact up to rounding (u and l always
 //     share the same reference maximum).
+#include <type_traits>
+
 #include "fa_device.h"
 #include "fa_launch.h"
 
@@ -57,6 +59,11 @@ __device__ int build_tile_list(uint16_t* list, int* wcount, const uint8_t* mask,
   return count;
 }
 
+// Ordering hints for the scheduler (masks of __builtin_amdgcn_sched_group_barrier).
+constexpr int kSchedMfma = 0x008;
+constexpr int kSchedValu = 0x002;
+constexpr int kSchedDsRead = 0x100;
+
 template <int D>
 __global__ __launch_bounds__(kThreads, 2) void fwd_bf16_kernel(FwdArgs a) {
   constexpr int CH = D / 8;                    // 16-byte chunks per row
@@ -64,6 +71,10 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_bf16_kernel(FwdArgs a) {
   constexpr int TILE = kBC * D * 2;            // bytes of one K or V tile
   constexpr int KS = D / 16;                   // k-steps of the score product
   constexpr int MD = D / 32;                   // 32-row blocks of O^T
+  constexpr int KB = kBC / 32;                 // 32-key blocks of a score tile
+  constexpr int PS = kBC / 16;                 // k-steps of the O^T product
+  // LDS: K buffers [0, 2 TILE), V buffers [2 TILE, 4 TILE). The score product runs one
+  // tile ahead of the value product, so step t reads K(t+1) and V(t).
   __shared__ __attribute__((aligned(16))) char smem[4 * TILE];
   __shared__ uint16_t tlist[kMaxTiles];
   __shared__ int wcount[4];
@@ -87,128 +98,179 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_bf16_kernel(FwdArgs a) {
   const int ntk = (hi + kBC - 1) / kBC;
   int ntiles = ntk;
   if (a.mask) ntiles = build_tile_list(tlist, wcount, a.mask, q0 / a.mb, a.nb, a.mb, ntk, kBC);
+  // Key tile of step t, clamped so that the look-ahead of the last steps stays valid.
+  auto tile_at = [&](int t) {
+    const int tc = min(t, max(ntiles - 1, 0));
+    return a.mask ? (int)tlist[tc] : tc;
+  };
 
   // Q fragments: B operand of S^T = K Q^T, lane holds Q[qi][16 ks + 8h .. +7].
   bf16x8 qf[KS];
+  {
+    const __bf16* qrow = Q + (size_t)min(qi, a.N - 1) * D + 8 * h;
 #pragma unroll
-  for (int ks = 0; ks < KS; ++ks) {
-    if (qi < a.N) {
-      qf[ks] = __builtin_bit_cast(bf16x8, gload16(Q + (size_t)qi * D + 16 * ks + 8 * h));
-      if (a.qmul != 1.0f) {
+    for (int ks = 0; ks < KS; ++ks) qf[ks] = __builtin_bit_cast(bf16x8, gload16(qrow + 16 * ks));
+    const float qm = qi < a.N ? a.qmul : 0.f;
+    if (qm != 1.0f) {
 #pragma unroll
-        for (int e = 0; e < 8; ++e) qf[ks][e] = (__bf16)((float)qf[ks][e] * a.qmul);
-      }
-    } else {
-      qf[ks] = bf16x8{};
+      for (int ks = 0; ks < KS; ++ks)
+#pragma unroll
+        for (int e = 0; e < 8; ++e) qf[ks][e] = (__bf16)((float)qf[ks][e] * qm);
     }
   }
+
+  // Per-lane LDS byte offsets, tile-relative, fixed for the whole kernel.
+  int k_off[KS];             // S^T A operand: K row ql, columns 16 ks + 8h (+32 kb rows)
+#pragma unroll
+  for (int ks = 0; ks < KS; ++ks) k_off[ks] = tile_off<D>(ql, 16 * ks + 8 * h);
+  int v_lo[MD], v_hi[MD];    // V^T transpose reads for d-block md (+16 st rows)
+#pragma unroll
+  for (int md = 0; md < MD; ++md) tr8_offsets<D>(32 * md, v_lo[md], v_hi[md]);
+  // Tile staging: thread chunk c covers row tid / CH + c * (kThreads / CH); that row step
+  // is a multiple of 16, so one swizzled offset serves every chunk.
+  constexpr int GROWS = kThreads / CH;
+  static_assert(GROWS % 16 == 0, "row step must keep the swizzle");
+  const int g_row0 = tid / CH, g_col0 = (tid % CH) * 8;
+  const int st_off0 = tile_off<D>(g_row0, g_col0);
 
   f32x16 o[MD];
 #pragma unroll
   for (int md = 0; md < MD; ++md) o[md] = f32x16{};
-  float m_run = kNegInf, l_run = 0.f;
+  float m_run = kNegInf, l_run = 0.f, moff = 0.f;
   const float c2 = a.c2;
 
+  // Branch-free load pipeline, so the compiler can count outstanding loads exactly: rows
+  // past N read row N-1 and are zeroed when stored.
   u32x4 kr[NCH], vr[NCH];
-  auto gload_tile = [&](int jt) {
-    const int key0 = jt * kBC;
+  bool kval[NCH], vval[NCH];
+  auto gload_k = [&](int jt) {
 #pragma unroll
     for (int c = 0; c < NCH; ++c) {
-      const int id = tid + kThreads * c;
-      const int row = id / CH, col = (id % CH) * 8;
-      const int key = key0 + row;
-      if (key < a.N) {
-        kr[c] = gload16(K + (size_t)key * D + col);
-        vr[c] = gload16(V + (size_t)key * D + col);
-      } else {
-        kr[c] = u32x4{};
-        vr[c] = u32x4{};
-      }
+      const int key = jt * kBC + g_row0 + c * GROWS;
+      kval[c] = key < a.N;
+      kr[c] = gload16(K + (size_t)min(key, a.N - 1) * D + g_col0);
     }
   };
-  auto lds_store_tile = [&](int buf) {
-    FA_LDS char* kb = (FA_LDS char*)smem + buf * 2 * TILE;
-    FA_LDS char* vb = kb + TILE;
+  auto gload_v = [&](int jt) {
 #pragma unroll
     for (int c = 0; c < NCH; ++c) {
-      const int id = tid + kThreads * c;
-      const int row = id / CH, col = (id % CH) * 8;
-      lds_store16(kb + tile_off<D>(row, col), kr[c]);
-      lds_store16(vb + tile_off<D>(row, col), vr[c]);
+      const int key = jt * kBC + g_row0 + c * GROWS;
+      vval[c] = key < a.N;
+      vr[c] = gload16(V + (size_t)min(key, a.N - 1) * D + g_col0);
     }
   };
+  FA_LDS char* const lds0 = (FA_LDS char*)smem;
+  auto store_k = [&](int buf) {
+#pragma unroll
+    for (int c = 0; c < NCH; ++c)
+      lds_store16(lds0 + buf * TILE + st_off0 + c * GROWS * 2 * D, kval[c] ? kr[c] : u32x4{});
+  };
+  auto store_v = [&](int buf) {
+#pragma unroll
+    for (int c = 0; c < NCH; ++c)
+      lds_store16(lds0 + (2 + buf) * TILE + st_off0 + c * GROWS * 2 * D, vval[c] ? vr[c] : u32x4{});
+  };
 
-  if (ntiles > 0) {
-    gload_tile(a.mask ? tlist[0] : 0);
-    lds_store_tile(0);
-  }
-  __syncthreads();
-
-  for (int t = 0; t < ntiles; ++t) {
-    const int jt = a.mask ? tlist[t] : t;
-    const int buf = t & 1;
-    if (t + 1 < ntiles) gload_tile(a.mask ? tlist[t + 1] : t + 1);
-
+  // Score tile S^T = K Q^T of the K tile at `kb` (MFMA phase only).
+  auto scores = [&](const FA_LDS char* kb, f32x16 (&s)[KB]) {
+#pragma unroll
+    for (int kbk = 0; kbk < KB; ++kbk) {
+      s[kbk] = f32x16{};
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks) s[kbk] = mfma32(lds_ld8(kb + k_off[ks] + kbk * 32 * 2 * D), qf[ks], s[kbk]);
+    }
+  };
+  // Masking of an edge tile, its row maximum and the lazy rescale (a wave-uniform branch).
+  auto rowmax_update = [&](int jt, f32x16 (&s)[KB]) {
     const int key0 = jt * kBC;
-    // A wave whose queries all precede the tile (causal) has nothing to do here.
-    const bool active = !(a.causal && key0 > q0 + 32 * w + 31);
-    if (active) {
-      const FA_LDS char* kb = (const FA_LDS char*)smem + buf * 2 * TILE;
-      const FA_LDS char* vb = kb + TILE;
-      f32x16 s[2];
+    if ((key0 + kBC > kv_end) || (a.causal && key0 + kBC - 1 > q0 + 32 * w)) {
 #pragma unroll
-      for (int mb = 0; mb < 2; ++mb) {
-        s[mb] = f32x16{};
-#pragma unroll
-        for (int ks = 0; ks < KS; ++ks)
-          s[mb] = mfma32(lds_read8<D>(kb, 32 * mb + ql, 16 * ks + 8 * h), qf[ks], s[mb]);
-      }
-      const bool edge = (key0 + kBC > kv_end) || (a.causal && key0 + kBC - 1 > q0 + 32 * w);
-      if (edge) {
-#pragma unroll
-        for (int mb = 0; mb < 2; ++mb)
-#pragma unroll
-          for (int i = 0; i < 16; ++i) {
-            const int key = key0 + 32 * mb + 8 * (i >> 2) + 4 * h + (i & 3);
-            if (key >= kv_end || (a.causal && key > qi)) s[mb][i] = kNegInf;
-          }
-      }
-      float tmax = kNegInf;
-#pragma unroll
-      for (int mb = 0; mb < 2; ++mb)
-#pragma unroll
-        for (int i = 0; i < 16; ++i) tmax = fmaxf(tmax, s[mb][i]);
-      tmax = fmaxf(tmax, wave_xor32(tmax));
-      const float mcand = fmaxf(m_run, tmax);
-      const bool need = (mcand - m_run) * c2 > kRescaleLog2;
-      if (__ballot(need)) {
-        const float alpha = need ? fast_exp2((m_run - mcand) * c2) : 1.0f;
-        if (need) m_run = mcand;
-        l_run *= alpha;
-#pragma unroll
-        for (int md = 0; md < MD; ++md) o[md] *= alpha;
-      }
-      const float moff = (m_run == kNegInf) ? 0.f : m_run * c2;
-#pragma unroll
-      for (int mb = 0; mb < 2; ++mb)
+      for (int kbk = 0; kbk < KB; ++kbk)
 #pragma unroll
         for (int i = 0; i < 16; ++i) {
-          const float p = fast_exp2(__builtin_fmaf(s[mb][i], c2, -moff));
-          s[mb][i] = p;
-          l_run += p;
+          const int key = key0 + 32 * kbk + 8 * (i >> 2) + 4 * h + (i & 3);
+          if (key >= kv_end || (a.causal && key > qi)) s[kbk][i] = kNegInf;
         }
-#pragma unroll
-      for (int st = 0; st < 4; ++st) {
-        const bf16x8 bp = pack8(s[st >> 1], 8 * (st & 1));
-#pragma unroll
-        for (int md = 0; md < MD; ++md) o[md] = mfma32(lds_read_tr8<D>(vb, 16 * st, 32 * md), bp, o[md]);
-      }
     }
-    if (t + 1 < ntiles) lds_store_tile(buf ^ 1);
+    float tmax = kNegInf;
+#pragma unroll
+    for (int kbk = 0; kbk < KB; ++kbk)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) tmax = fmaxf(tmax, s[kbk][i]);
+    tmax = fmaxf(tmax, other_half(tmax));
+    const float mcand = fmaxf(m_run, tmax);
+    const bool need = (mcand - m_run) * c2 > kRescaleLog2;
+    if (__ballot(need)) {
+      const float alpha = need ? fast_exp2((m_run - mcand) * c2) : 1.0f;
+      if (need) m_run = mcand;
+      l_run *= alpha;
+#pragma unroll
+      for (int md = 0; md < MD; ++md) o[md] *= alpha;
+    }
+    moff = (m_run == kNegInf) ? 0.f : m_run * c2;
+  };
+
+  f32x16 sa[KB], sb[KB];
+  if (ntiles > 0) {
+    gload_k(tile_at(0));
+    gload_v(tile_at(0));
+    store_k(0);
+    store_v(0);
+    gload_k(tile_at(1));
+    store_k(1);
     __syncthreads();
+    scores(lds0, sa);
+    rowmax_update(tile_at(0), sa);
+    __syncthreads();  // step 0 overwrites K buffer 0
   }
 
-  const float l_tot = l_run + wave_xor32(l_run);
+  // Step t: S(t+1) from K buffer (t+1)&1 interleaved with the probabilities of tile t;
+  // then O^T += V^T P^T from V buffer t&1; then stage K(t+2), V(t+1) and find the
+  // maximum of tile t+1.
+  auto step = [&](auto bufc, f32x16 (&cur)[KB], f32x16 (&nxt)[KB], int t) {
+    constexpr int BUF = decltype(bufc)::value;
+    const FA_LDS char* kb = lds0 + (BUF ^ 1) * TILE;
+    const FA_LDS char* vb = lds0 + (2 + BUF) * TILE;
+    gload_k(tile_at(t + 2));
+    gload_v(tile_at(t + 1));
+    // -- region A: score MFMAs of the next tile, exp/sum/pack of this tile
+    scores(kb, nxt);
+    bf16x8 pb[PS];
+    float lsum = 0.f;
+#pragma unroll
+    for (int kbk = 0; kbk < KB; ++kbk)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        const float p = fast_exp2(__builtin_fmaf(cur[kbk][i], c2, -moff));
+        lsum += p;
+        pb[2 * kbk + (i >> 3)][i & 7] = (__bf16)p;
+      }
+    __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 4, 0);
+#pragma unroll
+    for (int k = 0; k < KB * KS; ++k) {
+      __builtin_amdgcn_sched_group_barrier(kSchedMfma, 1, 0);
+      if (k + 4 < KB * KS) __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(kSchedValu, 7, 0);
+    }
+    l_run += lsum;
+    // -- region B: O^T += V^T P^T
+#pragma unroll
+    for (int st = 0; st < PS; ++st)
+#pragma unroll
+      for (int md = 0; md < MD; ++md)
+        o[md] = mfma32(lds_tr8(vb + v_lo[md] + st * 16 * 2 * D, vb + v_hi[md] + st * 16 * 2 * D), pb[st], o[md]);
+    // -- stage the tiles two and one steps ahead; prepare tile t+1
+    store_k(BUF);
+    store_v(BUF ^ 1);
+    if (t + 1 < ntiles) rowmax_update(tile_at(t + 1), nxt);
+    __syncthreads();
+  };
+  for (int t = 0; t < ntiles; t += 2) {
+    step(std::integral_constant<int, 0>{}, sa, sb, t);
+    if (t + 1 < ntiles) step(std::integral_constant<int, 1>{}, sb, sa, t + 1);
+  }
+
+  const float l_tot = l_run + other_half(l_run);
   if (qi < a.N) {
     const float inv = l_tot > 0.f ? 1.0f / l_tot : 0.f;
     __bf16* O = reinterpret_cast<__bf16*>(a.o) + hoff + (size_t)qi * D;

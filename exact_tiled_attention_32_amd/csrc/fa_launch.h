@@ -48,10 +48,14 @@ struct BwdArgs {
   float c2s;              // scale * log2(e)
 };
 
-constexpr int kFwdRowsPerWG = 128;
-constexpr int kFwdTileKeysBF16 = 64;
+constexpr int kFwdRowsPerWG = 128;       // fp32 forward; also the mask-block granularity
+constexpr int kFwdRowsPerWGBF16 = 128;   // bf16 forward: 4 waves x 32 query rows
+// Keys per tile of the bf16 forward (its block-sparse tile list holds N / that).
+constexpr int fwd_tile_keys_bf16(int) { return 64; }
 constexpr int kFwdTileKeysF32 = 32;
 constexpr int kMaxTileList = 4096;
+// Query rows per inner step of the backward main kernel (its tile list holds N / step).
+constexpr int bwd_query_step(int d) { return d == 128 ? 32 : 64; }
 
 // Optional events recorded around the dominant kernel of a call (may be nullptr).
 struct KernelTimer {
