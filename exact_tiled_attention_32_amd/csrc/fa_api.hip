@@ -132,8 +132,7 @@ size_t fa_bwd_workspace_bytes(int B, int H, int N, int d) {
   if (B <= 0 || H <= 0 || N <= 0 || d <= 0) return 0;
   const long double rows = (long double)B * H * N;
   if (rows * d * 4 > (long double)(1ull << 62)) return 0;
-  const size_t r = (size_t)B * H * N;
-  return align256(r * sizeof(float)) + align256(r * (size_t)d * sizeof(float));
+  return align256((size_t)B * H * N * sizeof(float));
 }
 
 fa_status fa_bwd(fa_dtype dt, int B, int H, int N, int d, const void* q, const void* k,
@@ -153,7 +152,7 @@ fa_status fa_bwd(fa_dtype dt, int B, int H, int N, int d, const void* q, const v
   FA_TRY(check_tensor(dk, "dk", 16));
   FA_TRY(check_tensor(dv, "dv", 16));
   if (kv_len && !aligned(kv_len, 4)) return fail(FA_ERR_INVALID, "kv_len is not 4-byte aligned");
-  if (block_mask) FA_TRY(check_mask(block_mask, mask_block, N, fa::bwd_query_step(d)));
+  if (block_mask) FA_TRY(check_mask(block_mask, mask_block, N, fa::kBwdMinTile));
   const size_t need = fa_bwd_workspace_bytes(B, H, N, d);
   if (workspace == nullptr) return fail(FA_ERR_INVALID, "workspace is NULL");
   if (!aligned(workspace, 256)) return fail(FA_ERR_INVALID, "workspace is not 256-byte aligned");
@@ -170,9 +169,7 @@ fa_status fa_bwd(fa_dtype dt, int B, int H, int N, int d, const void* q, const v
   a.dq = dq;
   a.dk = dk;
   a.dv = dv;
-  const size_t rows = (size_t)B * H * N;
   a.dsum = reinterpret_cast<float*>(workspace);
-  a.dq_acc = reinterpret_cast<float*>(reinterpret_cast<char*>(workspace) + align256(rows * sizeof(float)));
   a.kv_len = kv_len;
   a.mask = block_mask;
   a.B = B;

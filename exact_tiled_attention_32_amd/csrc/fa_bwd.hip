@@ -8,14 +8,17 @@
 // O = softmax(scale Q K^T) V:
 //     P = exp(scale S - lse),  dV = P^T dO,  dP = dO V^T,  dS = P o (dP - D),
 //     dK = scale dS^T Q,       dQ = scale dS K,     with D_i = sum_j P_ij dP_ij = dO_i . O_i.
-// Loop order follows the quoted Theorem 5 proof (App. C): each key/value tile is loaded
-// once and its dK, dV accumulate on chip while query tiles stream past; dQ is read and
-// written once per key tile, here as fp32 atomic adds into a workspace accumulator.
+// Loop order for dK, dV follows the quoted Theorem 5 proof (App. C): each key/value tile
+// is loaded once and its dK, dV accumulate on chip while query tiles stream past. The
+// proof's dQ updates (one read/write pass over dQ per key tile) would be fp32 atomics
+// here; on MI355X those are performed past the per-XCD L2 and run at ~1.3 TB/s, which
+// bounded the whole backward. dQ is therefore computed by its own query-major kernel that
+// recomputes the score tile (two more products per tile, no atomics).
 //
 // Three launches on the caller's stream:
-//   1. bwd_pre:     D = rowsum(dO o O) in fp32, and dQ_acc = 0
-//   2. bwd_main:    one workgroup per (b, h, 128-key tile); 4 waves, 32 keys each
-//   3. bwd_dq_out:  dQ = scale * dQ_acc, rounded to bf16
+//   1. bwd_pre:   D = rowsum(dO o O) in fp32
+//   2. bwd_dkdv:  one workgroup per (b, h, 128-key tile); 8 waves (two per SIMD)
+//   3. bwd_dq:    one workgroup per (b, h, 128-query tile); 4 waves, one query per lane
 #include <type_traits>
 
 #include "fa_device.h"
@@ -27,13 +30,9 @@ namespace {
 
 constexpr int kThreads = 256;
 constexpr int kBK = 128;  // keys per workgroup (32 per wave)
-// Query rows per inner step: 64 at d = 64; 32 at d = 128, where the register-resident K, V,
-// dK^T and dV^T already take 192 registers per lane.
-template <int D>
-constexpr int query_step() { return D == 128 ? 32 : 64; }
 
 // ---------------------------------------------------------------------------------------
-// 1. D = rowsum(dO o O), zero the dQ accumulator. Each thread owns 8 columns of one row.
+// 1. D = rowsum(dO o O). Each thread owns 8 columns of one row.
 // ---------------------------------------------------------------------------------------
 template <int D>
 __global__ __launch_bounds__(kThreads) void bwd_pre_kernel(BwdArgs a) {
@@ -48,68 +47,74 @@ __global__ __launch_bounds__(kThreads) void bwd_pre_kernel(BwdArgs a) {
     const bf16x8 dv = __builtin_bit_cast(bf16x8, gload16(reinterpret_cast<const __bf16*>(a.dout) + row * D + c0));
 #pragma unroll
     for (int e = 0; e < 8; ++e) acc += (float)ov[e] * (float)dv[e];
-    f32x4* dst = reinterpret_cast<f32x4*>(a.dq_acc + row * D + c0);
-    dst[0] = f32x4{};
-    dst[1] = f32x4{};
   }
 #pragma unroll
   for (int off = LPR / 2; off > 0; off >>= 1) acc += __shfl_xor(acc, off);
   if (row < rows && (gid % LPR) == 0) a.dsum[row] = acc;
 }
 
-// Key-tile list helper for the block-sparse path: query tiles [i0, ntq) whose mask block
-// in column `cb` is nonzero.
-__device__ int build_qtile_list(uint16_t* list, int* wcount, const uint8_t* mask, int cb, int nb,
-                                int mb, int i0, int ntq, int bq) {
+// ---------------------------------------------------------------------------------------
+// 2. dK / dV kernel: one workgroup per (b, h, 128-key tile), 8 waves (two per SIMD).
+//    Wave w owns key group kg = w % 4 (keys 32 kg .. 32 kg + 31 of the tile) and query half
+//    qh = w / 4 of each query step (QBW 32-row blocks: the step is 64 rows at d = 128 and
+//    128 rows at d = 64). Orientation (v_mfma_f32_32x32x16_bf16):
+//   S, dP   = Q K^T, dO V^T   (M = the wave's queries, N = its 32 keys): Q/dO rows and K/V
+//             rows are 16-byte LDS reads.
+//   dV^T   += dO^T P          (M = d, N = keys): dO^T from transpose reads, P straight
+//   dK^T   += Q^T dS           from the accumulator (same layout trick as the forward).
+//   At the end the two query halves' dK^T, dV^T partials are summed through LDS.
+// ---------------------------------------------------------------------------------------
+constexpr int kMainThreads = 512;
+// s_waitcnt immediate for vmcnt(0), expcnt and lgkmcnt left free (gfx9 encoding).
+constexpr int kWaitVmcnt0 = 0x0F70;
+
+template <int D>
+constexpr int main_query_step() { return D == 128 ? 64 : 128; }
+
+// Query tiles [i0, ntq) whose mask block in column `cb` is nonzero (block-sparse path).
+__device__ int build_qtile_list512(uint16_t* list, int* wcount, const uint8_t* mask, int cb, int nb,
+                                   int mb, int i0, int ntq, int bq) {
   const int tid = threadIdx.x, w = tid >> 6, l = tid & 63;
   int count = 0;
-  for (int base = i0; base < ntq; base += kThreads) {
+  for (int base = i0; base < ntq; base += kMainThreads) {
     const int i = base + tid;
     const bool keep = i < ntq && mask[(size_t)((i * bq) / mb) * nb + cb] != 0;
     const uint64_t bal = __ballot(keep);
     const int pre = __popcll(bal & ((1ull << l) - 1ull));
     if (l == 0) wcount[w] = __popcll(bal);
     __syncthreads();
-    int off = count;
-    for (int k = 0; k < w; ++k) off += wcount[k];
+    int off = count, tot = 0;
+    for (int k = 0; k < 8; ++k) {
+      off += k < w ? wcount[k] : 0;
+      tot += wcount[k];
+    }
     if (keep) list[off + pre] = (uint16_t)i;
-    count += wcount[0] + wcount[1] + wcount[2] + wcount[3];
+    count += tot;
     __syncthreads();
   }
   return count;
 }
 
-// ---------------------------------------------------------------------------------------
-// 2. Main kernel. Orientation (v_mfma_f32_32x32x16_bf16):
-//   S, dP   = Q K^T, dO V^T   (M = queries, N = the wave's 32 keys): K, V rows are
-//             register-resident B operands; Q, dO rows are 16-byte LDS reads.
-//   dV^T   += dO^T P          (M = d, N = keys): dO^T from transpose reads, P straight
-//   dK^T   += Q^T dS           from the accumulator (same layout trick as the forward).
-//   dQ     += dS K            (M = queries, N = d, K = the 128 keys of the workgroup):
-//             dS goes through LDS as dS^T [key][query]; both operands are transpose
-//             reads; the result is added to the fp32 workspace with global atomics.
-// ---------------------------------------------------------------------------------------
 template <int D>
-__global__ __launch_bounds__(kThreads, 1) void bwd_main_kernel(BwdArgs a) {
-  constexpr int BQ = query_step<D>();
-  constexpr int QB = BQ / 32;          // 32-query blocks per step
+__global__ __launch_bounds__(kMainThreads, 1) void bwd_dkdv_kernel(BwdArgs a) {
+  constexpr int BQ = main_query_step<D>();
+  constexpr int QBW = BQ / 64;         // 32-query blocks per wave per step
   constexpr int KS = D / 16;           // k-steps over d
   constexpr int MD = D / 32;           // 32-row blocks of dK^T / dV^T
   constexpr int QT = BQ * D * 2;       // bytes of a Q or dO tile
-  constexpr int KT = kBK * D * 2;      // bytes of the K tile
-  constexpr int ST = kBK * BQ * 2;     // bytes of the dS^T tile
-  constexpr int QCH = BQ * (D / 8) / kThreads;   // 16-byte chunks per thread per Q/dO tile
-  constexpr int KCH = kBK * (D / 8) / kThreads;  // 16-byte chunks per thread for K
-  // dQ[BQ][D] = dS K has QB * MD = 4 blocks of 32 x 32: one per wave.
-  static_assert(QB * MD == 4, "one dQ block per wave");
-  __shared__ __attribute__((aligned(16))) char smem[KT + 4 * QT + ST];
+  constexpr int KT = kBK * D * 2;      // bytes of the K or V tile
+  constexpr int NDMA = QT / (kMainThreads * 16);     // DMA instructions per wave per Q/dO tile
+  constexpr int RPB = 1024 / (2 * D);                 // rows per 1 KB DMA block
+  constexpr int KCH = kBK * (D / 8) / kMainThreads;  // 16-byte chunks per thread per K/V tile
+  static_assert(2 * kBK * D * 4 <= 2 * KT + 4 * QT, "dK/dV reduction fits in LDS");
+  __shared__ __attribute__((aligned(16))) char smem[2 * KT + 4 * QT];
   __shared__ __attribute__((aligned(16))) float stats[2][2][BQ];  // [buf][lse2 | D][row]
   __shared__ uint16_t qlist[kMaxTileList];
-  __shared__ int wcount[4];
+  __shared__ int wcount[8];
 
   FA_LDS char* const kt = (FA_LDS char*)smem;
-  FA_LDS char* const qbuf = kt + KT;      // [buf][Q | dO]
-  FA_LDS char* const st = qbuf + 4 * QT;  // dS^T [128 keys][BQ queries]
+  FA_LDS char* const vt = kt + KT;
+  FA_LDS char* const qbuf = vt + KT;      // [buf][Q | dO]
 
   const int BH = a.B * a.H;
   const int bh = blockIdx.x % BH;
@@ -117,7 +122,9 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_main_kernel(BwdArgs a) {
   const int b = bh / a.H;
   const int k0 = jt * kBK;
   const int tid = threadIdx.x, w = tid >> 6, l = tid & 63, h = l >> 5, kl = l & 31;
-  const int key = k0 + 32 * w + kl;     // the key this lane's accumulator columns refer to
+  const int kg = w & 3, qh = w >> 2;
+  const int key = k0 + 32 * kg + kl;    // the key this lane's accumulator columns refer to
+  const int qw0 = 32 * QBW * qh;        // the wave's first query row inside a step
   const size_t hoff = (size_t)bh * a.N * D;
   const __bf16* __restrict__ Q = reinterpret_cast<const __bf16*>(a.q) + hoff;
   const __bf16* __restrict__ K = reinterpret_cast<const __bf16*>(a.k) + hoff;
@@ -125,64 +132,51 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_main_kernel(BwdArgs a) {
   const __bf16* __restrict__ dO = reinterpret_cast<const __bf16*>(a.dout) + hoff;
   const float* __restrict__ lse = a.lse + (size_t)bh * a.N;
   const float* __restrict__ dsum = a.dsum + (size_t)bh * a.N;
-  float* __restrict__ dqa = a.dq_acc + hoff;
 
   int kv_end = a.N;
   if (a.kv_len) kv_end = min(max(a.kv_len[b], 0), a.N);
   const int ntq = (a.N + BQ - 1) / BQ;
   const int i0 = a.causal ? k0 / BQ : 0;
   int nq = k0 < kv_end ? ntq - i0 : 0;  // key tile entirely padded: no work, zero dK/dV
-  if (a.mask && nq > 0) nq = build_qtile_list(qlist, wcount, a.mask, k0 / a.mb, a.nb, a.mb, i0, ntq, BQ);
+  if (a.mask && nq > 0) nq = build_qtile_list512(qlist, wcount, a.mask, k0 / a.mb, a.nb, a.mb, i0, ntq, BQ);
 
-  // Register-resident K and V rows: B operands of S = Q K^T and dP = dO V^T.
-  bf16x8 kf[KS], vf[KS];
-  {
-    const size_t row = (size_t)min(key, a.N - 1) * D + 8 * h;
-#pragma unroll
-    for (int ks = 0; ks < KS; ++ks) {
-      kf[ks] = __builtin_bit_cast(bf16x8, gload16(K + row + 16 * ks));
-      vf[ks] = __builtin_bit_cast(bf16x8, gload16(V + row + 16 * ks));
-      if (key >= a.N) {
-        kf[ks] = bf16x8{};
-        vf[ks] = bf16x8{};
-      }
-    }
-  }
-  // K tile through LDS once, to give each wave the B operand of its dQ block:
-  // K[128 keys][32 md_q + l % 32] in the accumulator row order (8 k-steps of 16 keys).
+  // K and V tiles stay in LDS for the whole kernel (rows past N are zero).
 #pragma unroll
   for (int c = 0; c < KCH; ++c) {
-    const int id = tid + kThreads * c;
+    const int id = tid + kMainThreads * c;
     const int row = id / (D / 8), col = (id % (D / 8)) * 8;
-    const int kk = k0 + row;
-    lds_store16(kt + tile_off<D>(row, col), kk < a.N ? gload16(K + (size_t)kk * D + col) : u32x4{});
-  }
-  const int md_q = w % MD;   // the wave's dQ block: d-block md_q of query block qb_q
-  const int qb_q = w / MD;
-  __syncthreads();
-  bf16x8 kq[kBK / 16];
-  {
-    int lo, hi;
-    tr8_offsets<D>(32 * md_q, lo, hi);
-#pragma unroll
-    for (int kk = 0; kk < kBK / 16; ++kk) kq[kk] = lds_tr8(kt + lo + kk * 16 * 2 * D, kt + hi + kk * 16 * 2 * D);
+    const int kk = min(k0 + row, a.N - 1);
+    const bool ok = k0 + row < a.N;
+    const u32x4 kv = gload16(K + (size_t)kk * D + col);
+    const u32x4 vv = gload16(V + (size_t)kk * D + col);
+    lds_store16(kt + tile_off<D>(row, col), ok ? kv : u32x4{});
+    lds_store16(vt + tile_off<D>(row, col), ok ? vv : u32x4{});
   }
 
-  // Per-lane LDS byte offsets, fixed for the whole kernel.
-  int row_off[KS];          // Q / dO row operand: row kl, columns 16 ks + 8h (+32 qb2 rows)
-#pragma unroll
-  for (int ks = 0; ks < KS; ++ks) row_off[ks] = tile_off<D>(kl, 16 * ks + 8 * h);
-  int tr_lo[MD], tr_hi[MD];  // Q^T / dO^T transpose reads for d-block md (+16 s4 rows)
-#pragma unroll
-  for (int md = 0; md < MD; ++md) tr8_offsets<D>(32 * md, tr_lo[md], tr_hi[md]);
-  int ds_lo, ds_hi;          // dS^T transpose reads for the wave's dQ query block (+16 kk rows)
-  tr8_offsets<BQ>(32 * qb_q, ds_lo, ds_hi);
-  // Q / dO tile staging: thread chunk c covers row tid / (D/8) + c * QROWS, column
-  // (tid % (D/8)) * 8; QROWS is a multiple of 16, so one swizzled offset serves every chunk.
-  const int q_row0 = tid / (D / 8), q_col0 = (tid % (D / 8)) * 8;
-  const int qs_off0 = tile_off<D>(q_row0, q_col0);
-  constexpr int QROWS = kThreads * 8 / D;
-  static_assert(QROWS % 16 == 0, "row step must keep the swizzle");
+  // Per-lane LDS byte offsets, fixed for the whole kernel. Within a swizzled row the
+  // offsets of chunk c and of chunk c ^ m differ by an XOR with 16 m, so one base register
+  // per operand family serves every k-step and d-block (the XOR only touches bits below
+  // the row stride).
+  const int row_off0 = tile_off<D>(qw0 + kl, 8 * h);  // Q / dO row operand, k-step 0
+  int ro0 = row_off0;
+  auto row_off = [&](int ks) { return ro0 ^ (32 * ks); };
+  // The K / V row operand (row 32 kg + kl) has the same swizzle (both rows agree mod 16),
+  // so it is the Q / dO offset moved by whole rows.
+  const int kv_shift = (32 * kg - qw0) * 2 * D;
+  int tr_lo0, tr_hi0;        // Q^T / dO^T transpose reads of d-block 0 (+16 s4 rows)
+  tr8_offsets<D>(0, tr_lo0, tr_hi0);
+  int tl0 = tr_lo0, th0 = tr_hi0;
+  auto tr_lo = [&](int md) { return tl0 ^ (64 * md); };
+  auto tr_hi = [&](int md) { return th0 ^ (64 * md); };
+  // Q / dO staging by direct global -> LDS loads: each wave instruction fills 1 KB, lane
+  // i the 16 bytes at offset 16 i, so lane i fetches the chunk whose swizzled slot that
+  // is. Rows past N (last query tile only) read row N-1; they get P = 0 through the
+  // staged lse (+inf), so their values never reach a result.
+  // Lane l of DMA block c covers row (8c + w) RPB + l / (D/8); the block rows are a
+  // multiple of 16 apart, so the swizzled column is the same for every block.
+  const int dma_row0 = w * RPB + l / (D / 8);
+  const int dma_col = ((l % (D / 8)) ^ swz<D>(dma_row0)) * 8;
+  static_assert((8 * RPB) % 16 == 0, "DMA block step must keep the swizzle");
 
   f32x16 dkt[MD], dvt[MD];
 #pragma unroll
@@ -191,35 +185,27 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_main_kernel(BwdArgs a) {
     dvt[md] = f32x16{};
   }
 
-  // Branch-free load pipeline (see the forward kernel): rows past N read row N-1 and are
-  // zeroed when stored; the last step prefetches a valid tile it does not use.
-  u32x4 qr[QCH], dr[QCH];
-  bool qvalid[QCH];
   float sr = 0.f;
   bool svalid = false;
-  auto gload_q = [&](int it) {
+  auto stage_q = [&](int it, int buf) {
     const int q0 = it * BQ;
+    FA_LDS char* qb = qbuf + buf * 2 * QT;
 #pragma unroll
-    for (int c = 0; c < QCH; ++c) {
-      const int qq = q0 + q_row0 + c * QROWS;
-      qvalid[c] = qq < a.N;
-      const size_t row = (size_t)min(qq, a.N - 1) * D + q_col0;
-      qr[c] = gload16(Q + row);
-      dr[c] = gload16(dO + row);
+    for (int c = 0; c < NDMA; ++c) {
+      const size_t row = (size_t)min(q0 + dma_row0 + c * 8 * RPB, a.N - 1) * D + dma_col;
+      FA_LDS char* blk = qb + (c * 8 + w) * 1024;
+      // (the builtin takes a non-const pointer; without the cast the host pass silently
+      // drops the kernel's launch stub)
+      __builtin_amdgcn_global_load_lds((void*)(Q + row), (FA_LDS void*)blk, 16, 0, 0);
+      __builtin_amdgcn_global_load_lds((void*)(dO + row), (FA_LDS void*)(blk + QT), 16, 0, 0);
     }
-    // threads [0, BQ) stage lse (exp2 domain), threads [BQ, 2 BQ) stage D
-    const int qq = q0 + (tid & (BQ - 1));
+    // threads [0, BQ) stage lse, threads [BQ, 2 BQ) stage D
+    const int qq = q0 + (tid % BQ);
     svalid = qq < a.N;
     const float* src = tid < BQ ? lse : dsum;
     sr = src[min(qq, a.N - 1)];
   };
-  auto lds_store_q = [&](int buf) {
-    FA_LDS char* qb = qbuf + buf * 2 * QT;
-#pragma unroll
-    for (int c = 0; c < QCH; ++c) {
-      lds_store16(qb + qs_off0 + c * QROWS * 2 * D, qvalid[c] ? qr[c] : u32x4{});
-      lds_store16(qb + QT + qs_off0 + c * QROWS * 2 * D, qvalid[c] ? dr[c] : u32x4{});
-    }
+  auto store_stats = [&](int buf) {
     if (tid < 2 * BQ) {
       float v;
       if (tid < BQ) {
@@ -228,100 +214,111 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_main_kernel(BwdArgs a) {
       } else {
         v = svalid ? sr : 0.f;
       }
-      stats[buf][tid / BQ][tid & (BQ - 1)] = v;
+      stats[buf][tid / BQ][tid % BQ] = v;
     }
   };
-  // Query tiles are visited last-first: the workgroups of one head that run together
-  // then update the same dQ tile at about the same time, so it stays in L2.
+  // Wait for this wave's staging loads before the barrier that publishes the staged tile.
+  auto wait_loads = [&]() { __builtin_amdgcn_s_waitcnt(kWaitVmcnt0); };
+  // Query tiles are visited last-first, so the workgroups of one head that run together
+  // add into the same dQ tile at about the same time.
   auto tile_at = [&](int t) { return a.mask ? (int)qlist[nq - 1 - t] : i0 + nq - 1 - t; };
 
-  gload_q(nq > 0 ? tile_at(0) : 0);
-  lds_store_q(0);
+  stage_q(nq > 0 ? tile_at(0) : 0, 0);
+  wait_loads();
+  store_stats(0);
   __syncthreads();
+  asm volatile("" ::: "memory");
 
   auto step = [&](auto bufc, int t) {
     constexpr int BUF = decltype(bufc)::value;
     const int it = tile_at(t);
     const int q0 = it * BQ;
-    gload_q(tile_at(min(t + 1, nq - 1)));
+    // buffer BUF ^ 1 was last read in step t - 1: stream the next query tile into it
+    stage_q(tile_at(min(t + 1, nq - 1)), BUF ^ 1);
+    // Opaque copies of the offset bases: keeps the compiler from hoisting every derived
+    // offset out of the loop into its own register.
+    ro0 = row_off0;
+    tl0 = tr_lo0;
+    th0 = tr_hi0;
+    asm volatile("" : "+v"(ro0), "+v"(tl0), "+v"(th0));
     const FA_LDS char* qb = qbuf + BUF * 2 * QT;
     const FA_LDS char* db = qb + QT;
 
-    // S = Q K^T and dP = dO V^T for the wave's 32 keys, QB 32-query blocks.
-    f32x16 s[QB], dp[QB];
+    // S = Q K^T and dP = dO V^T: the wave's QBW query blocks x its 32 keys.
+    f32x16 s[QBW], dp[QBW];
 #pragma unroll
-    for (int qb2 = 0; qb2 < QB; ++qb2) {
-      s[qb2] = f32x16{};
-      dp[qb2] = f32x16{};
+    for (int b2 = 0; b2 < QBW; ++b2) {
+      s[b2] = f32x16{};
+      dp[b2] = f32x16{};
+    }
 #pragma unroll
-      for (int ks = 0; ks < KS; ++ks) {
-        s[qb2] = mfma32(lds_ld8(qb + row_off[ks] + qb2 * 32 * 2 * D), kf[ks], s[qb2]);
-        dp[qb2] = mfma32(lds_ld8(db + row_off[ks] + qb2 * 32 * 2 * D), vf[ks], dp[qb2]);
+    for (int ks = 0; ks < KS; ++ks) {
+      const bf16x8 kf = lds_ld8(kt + kv_shift + row_off(ks));
+      const bf16x8 vf = lds_ld8(vt + kv_shift + row_off(ks));
+#pragma unroll
+      for (int b2 = 0; b2 < QBW; ++b2) {
+        s[b2] = mfma32(lds_ld8(qb + row_off(ks) + b2 * 32 * 2 * D), kf, s[b2]);
+        dp[b2] = mfma32(lds_ld8(db + row_off(ks) + b2 * 32 * 2 * D), vf, dp[b2]);
       }
     }
     // P = exp2(S * scale * log2e - lse * log2e); masked pairs -> 0; dS = P (dP - D).
-    const bool edge = (k0 + 32 * w + 31 >= kv_end) || (a.causal && k0 + 32 * w + 31 > q0);
+    const bool edge = (k0 + 32 * kg + 31 >= kv_end) || (a.causal && k0 + 32 * kg + 31 > q0 + qw0);
 #pragma unroll
-    for (int qb2 = 0; qb2 < QB; ++qb2)
+    for (int b2 = 0; b2 < QBW; ++b2)
 #pragma unroll
       for (int g = 0; g < 4; ++g) {
-        const int qr0 = 32 * qb2 + 8 * g + 4 * h;
+        const int qr0 = qw0 + 32 * b2 + 8 * g + 4 * h;
         const f32x4 l2 = *reinterpret_cast<const f32x4*>(&stats[BUF][0][qr0]);
         const f32x4 dd = *reinterpret_cast<const f32x4*>(&stats[BUF][1][qr0]);
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
           const int i = 4 * g + e;
-          float p = fast_exp2(__builtin_fmaf(s[qb2][i], a.c2s, -l2[e]));
+          float p = fast_exp2(__builtin_fmaf(s[b2][i], a.c2s, -l2[e]));
           if (edge && (key >= kv_end || (a.causal && key > q0 + qr0 + e))) p = 0.f;
-          s[qb2][i] = p;
-          dp[qb2][i] = p * (dp[qb2][i] - dd[e]);
+          s[b2][i] = p;
+          dp[b2][i] = p * (dp[b2][i] - dd[e]);
         }
       }
     // dV^T += dO^T P, dK^T += Q^T dS (16 queries per k-step).
 #pragma unroll
-    for (int s4 = 0; s4 < BQ / 16; ++s4) {
+    for (int s4 = 0; s4 < 2 * QBW; ++s4) {
       const bf16x8 pb = pack8(s[s4 >> 1], 8 * (s4 & 1));
       const bf16x8 sb = pack8(dp[s4 >> 1], 8 * (s4 & 1));
+      const int ro = (qw0 + 16 * s4) * 2 * D;
 #pragma unroll
       for (int md = 0; md < MD; ++md) {
-        const int ro = s4 * 16 * 2 * D;
-        dvt[md] = mfma32(lds_tr8(db + tr_lo[md] + ro, db + tr_hi[md] + ro), pb, dvt[md]);
-        dkt[md] = mfma32(lds_tr8(qb + tr_lo[md] + ro, qb + tr_hi[md] + ro), sb, dkt[md]);
+        dvt[md] = mfma32(lds_tr8(db + tr_lo(md) + ro, db + tr_hi(md) + ro), pb, dvt[md]);
+        dkt[md] = mfma32(lds_tr8(qb + tr_lo(md) + ro, qb + tr_hi(md) + ro), sb, dkt[md]);
       }
     }
-    // dS^T -> LDS: lane writes 4 consecutive queries of its key per (block, group).
-#pragma unroll
-    for (int qb2 = 0; qb2 < QB; ++qb2)
-#pragma unroll
-      for (int g = 0; g < 4; ++g) {
-        bf16x4 v4;
-#pragma unroll
-        for (int e = 0; e < 4; ++e) v4[e] = (__bf16)dp[qb2][4 * g + e];
-        *reinterpret_cast<FA_LDS bf16x4*>(st + tile_off<BQ>(32 * w + kl, 32 * qb2 + 8 * g + 4 * h)) = v4;
-      }
+    // Wait for the staged tile, publish it and its statistics.
+    wait_loads();
+    store_stats(BUF ^ 1);
     __syncthreads();
-    // dQ[q0 .. q0 + BQ)[:] += dS K over the 128 keys: this wave's 32 x 32 block.
-    f32x16 acc = f32x16{};
-#pragma unroll
-    for (int kk = 0; kk < kBK / 16; ++kk)
-      acc = mfma32(lds_tr8(st + ds_lo + kk * 16 * 2 * BQ, st + ds_hi + kk * 16 * 2 * BQ), kq[kk], acc);
-    // Stage the next query tile before issuing the atomics: waiting for its loads then
-    // does not also wait for this step's atomics (the memory counter is in-order).
-    lds_store_q(BUF ^ 1);
-#pragma unroll
-    for (int i = 0; i < 16; ++i) {
-      const int qq = q0 + 32 * qb_q + 8 * (i >> 2) + 4 * h + (i & 3);
-      if (qq < a.N) unsafeAtomicAdd(dqa + (size_t)qq * D + 32 * md_q + kl, acc[i]);
-    }
-    __syncthreads();
+    asm volatile("" ::: "memory");
   };
   for (int t = 0; t < nq; t += 2) {
     step(std::integral_constant<int, 0>{}, t);
     if (t + 1 < nq) step(std::integral_constant<int, 1>{}, t + 1);
   }
 
-  // dK = scale * (dK^T)^T, dV = (dV^T)^T: lane writes 4 consecutive columns of its key.
-  if (key < a.N) {
+  wait_loads();  // the last step's look-ahead staging must land before LDS is reused
+  __syncthreads();
+  // Sum the two query halves' partials through LDS (all tiles are free now): the upper
+  // half stores dK^T, dV^T in fp32 in its accumulator layout, the lower half adds them.
+  float* red = reinterpret_cast<float*>(smem);
+  const int red_off = kg * (2 * MD * 16 * 64) + l;  // [kg][2 MD][16 regs][64 lanes]
+  if (qh == 1) {
+#pragma unroll
+    for (int md = 0; md < MD; ++md)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        red[red_off + ((2 * md) * 16 + i) * 64] = dkt[md][i];
+        red[red_off + ((2 * md + 1) * 16 + i) * 64] = dvt[md][i];
+      }
+  }
+  __syncthreads();
+  if (qh == 0 && key < a.N) {
     __bf16* dK = reinterpret_cast<__bf16*>(a.dk) + hoff + (size_t)key * D;
     __bf16* dV = reinterpret_cast<__bf16*>(a.dv) + hoff + (size_t)key * D;
 #pragma unroll
@@ -331,8 +328,9 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_main_kernel(BwdArgs a) {
         bf16x4 kv4, vv4;
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
-          kv4[e] = (__bf16)(dkt[md][4 * g + e] * a.scale);
-          vv4[e] = (__bf16)dvt[md][4 * g + e];
+          const int i = 4 * g + e;
+          kv4[e] = (__bf16)((dkt[md][i] + red[red_off + ((2 * md) * 16 + i) * 64]) * a.scale);
+          vv4[e] = (__bf16)(dvt[md][i] + red[red_off + ((2 * md + 1) * 16 + i) * 64]);
         }
         *reinterpret_cast<bf16x4*>(dK + 32 * md + 8 * g + 4 * h) = kv4;
         *reinterpret_cast<bf16x4*>(dV + 32 * md + 8 * g + 4 * h) = vv4;
@@ -341,20 +339,199 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_main_kernel(BwdArgs a) {
 }
 
 // ---------------------------------------------------------------------------------------
-// 3. dQ = scale * dQ_acc -> bf16 (8 elements per thread).
+// 3. dQ kernel: one workgroup per (b, h, 128-query tile), 4 waves of 32 queries; key tiles
+//    of 64 keys stream through double-buffered LDS. The orientation is the forward's:
+//    scores are formed transposed so each lane owns one query and lse, D are per-lane
+//    scalars.
+//   S^T, dP^T = K Q^T, V dO^T   (A = K / V rows from LDS, B = the wave's Q / dO rows held
+//                                 in registers)
+//   dS^T      = P^T o (dP^T - D),  P^T = exp2(S^T scale log2e - lse log2e)
+//   dQ^T     += K^T dS^T          (A = K^T transpose reads, B = dS^T from the accumulator)
+//   dQ = scale dQ^T^T, written once in bf16.
 // ---------------------------------------------------------------------------------------
-__global__ __launch_bounds__(kThreads) void bwd_dq_out_kernel(BwdArgs a, size_t n8) {
-  const size_t gid = (size_t)blockIdx.x * kThreads + threadIdx.x;
-  if (gid >= n8) return;
-  const f32x4* src = reinterpret_cast<const f32x4*>(a.dq_acc) + 2 * gid;
-  const f32x4 x0 = src[0], x1 = src[1];
-  bf16x8 r;
-#pragma unroll
-  for (int e = 0; e < 4; ++e) {
-    r[e] = (__bf16)(x0[e] * a.scale);
-    r[4 + e] = (__bf16)(x1[e] * a.scale);
+constexpr int kDqRows = 128;  // query rows per workgroup
+constexpr int kDqKeys = 64;   // keys per tile
+
+template <int D>
+__global__ __launch_bounds__(kThreads, 2) void bwd_dq_kernel(BwdArgs a) {
+  constexpr int CH = D / 8;                     // 16-byte chunks per row
+  constexpr int TILE = kDqKeys * D * 2;         // bytes of one K or V tile
+  constexpr int NCH = kDqKeys * CH / kThreads;  // chunks per thread per tensor
+  constexpr int KS = D / 16;                    // k-steps over d
+  constexpr int MD = D / 32;                    // 32-row blocks of dQ^T
+  constexpr int KB = kDqKeys / 32;              // 32-key blocks of a tile
+  constexpr int PS = kDqKeys / 16;              // k-steps of the dQ^T product
+  __shared__ __attribute__((aligned(16))) char smem[4 * TILE];  // [buf][K | V]
+  __shared__ uint16_t tlist[kMaxTileList];
+  __shared__ int wcount[4];
+
+  const int BH = a.B * a.H;
+  const int bh = blockIdx.x % BH;
+  const int ntq = (a.N + kDqRows - 1) / kDqRows;
+  const int qt = ntq - 1 - blockIdx.x / BH;     // longest (causal) tiles first
+  const int b = bh / a.H;
+  const int q0 = qt * kDqRows;
+  const int tid = threadIdx.x, w = tid >> 6, l = tid & 63, h = l >> 5, ql = l & 31;
+  const int qi = q0 + 32 * w + ql;
+  const size_t hoff = (size_t)bh * a.N * D;
+  const __bf16* __restrict__ Q = reinterpret_cast<const __bf16*>(a.q) + hoff;
+  const __bf16* __restrict__ K = reinterpret_cast<const __bf16*>(a.k) + hoff;
+  const __bf16* __restrict__ V = reinterpret_cast<const __bf16*>(a.v) + hoff;
+  const __bf16* __restrict__ dO = reinterpret_cast<const __bf16*>(a.dout) + hoff;
+
+  int kv_end = a.N;
+  if (a.kv_len) kv_end = min(max(a.kv_len[b], 0), a.N);
+  int hi = kv_end;
+  if (a.causal) hi = min(hi, q0 + kDqRows);
+  const int ntk = (hi + kDqKeys - 1) / kDqKeys;
+  int ntiles = ntk;
+  if (a.mask) {
+    // key tiles of this query tile's mask row (128 rows never straddle two mask rows)
+    const int rb = q0 / a.mb;
+    int count = 0;
+    for (int base = 0; base < ntk; base += kThreads) {
+      const int j = base + tid;
+      const bool keep = j < ntk && a.mask[(size_t)rb * a.nb + (j * kDqKeys) / a.mb] != 0;
+      const uint64_t bal = __ballot(keep);
+      const int pre = __popcll(bal & ((1ull << l) - 1ull));
+      if (l == 0) wcount[w] = __popcll(bal);
+      __syncthreads();
+      int off = count;
+      for (int i = 0; i < w; ++i) off += wcount[i];
+      if (keep) tlist[off + pre] = (uint16_t)j;
+      count += wcount[0] + wcount[1] + wcount[2] + wcount[3];
+      __syncthreads();
+    }
+    ntiles = count;
   }
-  reinterpret_cast<bf16x8*>(a.dq)[gid] = r;
+
+  // The wave's Q and dO rows (B operands), and its row statistics in the exp2 domain.
+  bf16x8 qf[KS], df[KS];
+  {
+    const size_t row = (size_t)min(qi, a.N - 1) * D + 8 * h;
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+      qf[ks] = __builtin_bit_cast(bf16x8, gload16(Q + row + 16 * ks));
+      df[ks] = __builtin_bit_cast(bf16x8, gload16(dO + row + 16 * ks));
+    }
+  }
+  const float lse_v = a.lse[(size_t)bh * a.N + min(qi, a.N - 1)];
+  // an empty row (lse = -inf) and a row past N get lse2 = +inf, so P = 0 there
+  const float lse2 = (qi >= a.N || lse_v == kNegInf) ? __builtin_inff() : lse_v * kLog2e;
+  const float dval = a.dsum[(size_t)bh * a.N + min(qi, a.N - 1)];
+
+  // Per-lane LDS byte offsets (XOR-derived per k-step / d-block, see the dK/dV kernel).
+  const int k_off0 = tile_off<D>(ql, 8 * h);  // K / V row operand, k-step 0 (+32 kb rows)
+  int t_lo0, t_hi0;                             // K^T transpose reads of d-block 0 (+16 st rows)
+  tr8_offsets<D>(0, t_lo0, t_hi0);
+  constexpr int GROWS = kThreads / CH;
+  static_assert(GROWS % 16 == 0, "row step must keep the swizzle");
+  const int g_row0 = tid / CH, g_col0 = (tid % CH) * 8;
+  const int st_off0 = tile_off<D>(g_row0, g_col0);
+
+  f32x16 dq[MD];
+#pragma unroll
+  for (int md = 0; md < MD; ++md) dq[md] = f32x16{};
+
+  // Branch-free register prefetch of the next K, V tile (rows past N zeroed on store).
+  u32x4 kr[NCH], vr[NCH];
+  bool kval[NCH];
+  auto tile_at = [&](int t) {
+    const int tc = min(t, max(ntiles - 1, 0));
+    return a.mask ? (int)tlist[tc] : tc;
+  };
+  auto gload_kv = [&](int jt) {
+#pragma unroll
+    for (int c = 0; c < NCH; ++c) {
+      const int key = jt * kDqKeys + g_row0 + c * GROWS;
+      kval[c] = key < a.N;
+      const size_t row = (size_t)min(key, a.N - 1) * D + g_col0;
+      kr[c] = gload16(K + row);
+      vr[c] = gload16(V + row);
+    }
+  };
+  FA_LDS char* const lds0 = (FA_LDS char*)smem;
+  auto store_kv = [&](int buf) {
+#pragma unroll
+    for (int c = 0; c < NCH; ++c) {
+      FA_LDS char* p = lds0 + buf * 2 * TILE + st_off0 + c * GROWS * 2 * D;
+      lds_store16(p, kval[c] ? kr[c] : u32x4{});
+      lds_store16(p + TILE, kval[c] ? vr[c] : u32x4{});
+    }
+  };
+
+  gload_kv(tile_at(0));
+  store_kv(0);
+  __syncthreads();
+
+  int ko0 = k_off0, tl0 = t_lo0, th0 = t_hi0;
+  auto step = [&](auto bufc, int t) {
+    constexpr int BUF = decltype(bufc)::value;
+    const FA_LDS char* kb = lds0 + BUF * 2 * TILE;
+    const FA_LDS char* vb = kb + TILE;
+    const int jt = tile_at(t);
+    gload_kv(tile_at(t + 1));
+    // opaque offset bases: keep the derived offsets from being hoisted into registers
+    ko0 = k_off0;
+    tl0 = t_lo0;
+    th0 = t_hi0;
+    asm volatile("" : "+v"(ko0), "+v"(tl0), "+v"(th0));
+    const int key0 = jt * kDqKeys;
+    // A wave whose queries all precede the tile (causal) has nothing to do here.
+    if (!(a.causal && key0 > q0 + 32 * w + 31)) {
+      f32x16 s[KB], dp[KB];
+#pragma unroll
+      for (int kbk = 0; kbk < KB; ++kbk) {
+        s[kbk] = f32x16{};
+        dp[kbk] = f32x16{};
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) {
+          const int o = (ko0 ^ (32 * ks)) + kbk * 32 * 2 * D;
+          s[kbk] = mfma32(lds_ld8(kb + o), qf[ks], s[kbk]);
+          dp[kbk] = mfma32(lds_ld8(vb + o), df[ks], dp[kbk]);
+        }
+      }
+      const bool edge = (key0 + kDqKeys > kv_end) || (a.causal && key0 + kDqKeys - 1 > q0 + 32 * w);
+      bf16x8 dsb[PS];
+#pragma unroll
+      for (int kbk = 0; kbk < KB; ++kbk)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+          float p = fast_exp2(__builtin_fmaf(s[kbk][i], a.c2s, -lse2));
+          if (edge) {
+            const int key = key0 + 32 * kbk + 8 * (i >> 2) + 4 * h + (i & 3);
+            if (key >= kv_end || (a.causal && key > qi)) p = 0.f;
+          }
+          dsb[2 * kbk + (i >> 3)][i & 7] = (__bf16)(p * (dp[kbk][i] - dval));
+        }
+#pragma unroll
+      for (int st = 0; st < PS; ++st)
+#pragma unroll
+        for (int md = 0; md < MD; ++md) {
+          const int ro = st * 16 * 2 * D;
+          dq[md] = mfma32(lds_tr8(kb + (tl0 ^ (64 * md)) + ro, kb + (th0 ^ (64 * md)) + ro), dsb[st], dq[md]);
+        }
+    }
+    store_kv(BUF ^ 1);
+    __syncthreads();
+  };
+  for (int t = 0; t < ntiles; t += 2) {
+    step(std::integral_constant<int, 0>{}, t);
+    if (t + 1 < ntiles) step(std::integral_constant<int, 1>{}, t + 1);
+  }
+
+  if (qi < a.N) {
+    __bf16* dQ = reinterpret_cast<__bf16*>(a.dq) + hoff + (size_t)qi * D;
+#pragma unroll
+    for (int md = 0; md < MD; ++md)
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        bf16x4 v4;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) v4[e] = (__bf16)(dq[md][4 * g + e] * a.scale);
+        *reinterpret_cast<bf16x4*>(dQ + 32 * md + 8 * g + 4 * h) = v4;
+      }
+  }
 }
 
 }  // namespace
@@ -364,20 +541,20 @@ hipError_t launch_bwd(const BwdArgs& a, int d, hipStream_t stream, const KernelT
   const size_t pre_threads = rows * (size_t)(d / 8);
   const dim3 block(kThreads);
   const dim3 gpre((unsigned)((pre_threads + kThreads - 1) / kThreads));
-  const dim3 gmain((unsigned)(((a.N + kBK - 1) / kBK) * a.B * a.H));
-  const size_t n8 = rows * (size_t)d / 8;
-  const dim3 gout((unsigned)((n8 + kThreads - 1) / kThreads));
+  const dim3 gdkdv((unsigned)(((a.N + kBK - 1) / kBK) * a.B * a.H)), bdkdv(kMainThreads);
+  const dim3 gdq((unsigned)(((a.N + kDqRows - 1) / kDqRows) * a.B * a.H));
   if (d == 64) hipLaunchKernelGGL(bwd_pre_kernel<64>, gpre, block, 0, stream, a);
   else hipLaunchKernelGGL(bwd_pre_kernel<128>, gpre, block, 0, stream, a);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   if (tm.start) (void)hipEventRecord(tm.start, stream);
-  if (d == 64) hipLaunchKernelGGL(bwd_main_kernel<64>, gmain, block, 0, stream, a);
-  else hipLaunchKernelGGL(bwd_main_kernel<128>, gmain, block, 0, stream, a);
+  if (d == 64) hipLaunchKernelGGL(bwd_dkdv_kernel<64>, gdkdv, bdkdv, 0, stream, a);
+  else hipLaunchKernelGGL(bwd_dkdv_kernel<128>, gdkdv, bdkdv, 0, stream, a);
   e = hipGetLastError();
   if (tm.stop) (void)hipEventRecord(tm.stop, stream);
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(bwd_dq_out_kernel, gout, block, 0, stream, a, n8);
+  if (d == 64) hipLaunchKernelGGL(bwd_dq_kernel<64>, gdq, block, 0, stream, a);
+  else hipLaunchKernelGGL(bwd_dq_kernel<128>, gdq, block, 0, stream, a);
   return hipGetLastError();
 }
 

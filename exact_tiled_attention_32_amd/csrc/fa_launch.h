@@ -39,7 +39,6 @@ struct BwdArgs {
   void* dk;
   void* dv;
   float* dsum;            // workspace: D = rowsum(dO * O), [B,H,N]
-  float* dq_acc;          // workspace: fp32 dQ accumulator, [B,H,N,d]
   const int32_t* kv_len;
   const uint8_t* mask;
   int B, H, N, mb, nb;
@@ -54,8 +53,9 @@ constexpr int kFwdRowsPerWGBF16 = 128;   // bf16 forward: 4 waves x 32 query row
 constexpr int fwd_tile_keys_bf16(int) { return 64; }
 constexpr int kFwdTileKeysF32 = 32;
 constexpr int kMaxTileList = 4096;
-// Query rows per inner step of the backward main kernel (its tile list holds N / step).
-constexpr int bwd_query_step(int d) { return d == 128 ? 32 : 64; }
+// Smallest tile of the backward kernels (64 keys per dQ-kernel tile, 64 or 128 query
+// rows per dK/dV step); their block-sparse tile lists hold at most N / 64 entries.
+constexpr int kBwdMinTile = 64;
 
 // Optional events recorded around the dominant kernel of a call (may be nullptr).
 struct KernelTimer {

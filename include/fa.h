@@ -89,7 +89,7 @@ fa_status fa_fwd(fa_dtype dt, int B, int H, int N, int d,
  * zero is skipped without being read (legiblepapers.com "Fast and Memory Efficient Exact
  * Attention", summary paragraph). O is written for every row.
  *   block_mask  device uint8 [nb, nb], nb = ceil(N / mask_block), nonzero = keep
- *   mask_block  side of a square mask block; a positive multiple of 128; nb <= 4096
+ *   mask_block  side of a square mask block; a positive multiple of 128
  */
 fa_status fa_fwd_blocksparse(fa_dtype dt, int B, int H, int N, int d,
                              const void* q, const void* k, const void* v,
@@ -99,11 +99,10 @@ fa_status fa_fwd_blocksparse(fa_dtype dt, int B, int H, int N, int d,
                              hipStream_t stream);
 
 /*
- * Bytes of device workspace fa_bwd needs: the per-row D = rowsum(dO * O) (fp32 [B,H,N])
- * and the fp32 dQ accumulator [B,H,N,d], each 256-byte aligned. Linear in N (the
- * backward keeps O(N) extra memory; cochat.ai audit of "FlashAttention: Fast and
- * Memory-Efficient Exact Attention with IO-Awareness", quoted backward-pass memory claim).
- * Returns 0 for non-positive or overflowing sizes.
+ * Bytes of device workspace fa_bwd needs: the per-row D = rowsum(dO * O) (fp32 [B,H,N],
+ * rounded up to 256 bytes). Linear in N (the backward keeps O(N) extra memory; cochat.ai
+ * audit of "FlashAttention: Fast and Memory-Efficient Exact Attention with IO-Awareness",
+ * quoted backward-pass memory claim). Returns 0 for non-positive or overflowing sizes.
  */
 size_t fa_bwd_workspace_bytes(int B, int H, int N, int d);
 
@@ -118,8 +117,9 @@ size_t fa_bwd_workspace_bytes(int B, int H, int N, int d);
  *                     256-byte aligned, owned by the caller; its contents on entry do not
  *                     matter and are overwritten
  * Structure (cochat.ai audit, quoted Theorem 5 proof / App. C): each key/value tile is
- * loaded once and its dK, dV stay on chip while query tiles stream past; dQ is
- * accumulated in fp32 across key tiles. The score tile is recomputed from q, k and lse.
+ * loaded once and its dK, dV stay on chip while query tiles stream past. dQ is computed by
+ * a second, query-major pass that keeps dQ on chip while key tiles stream past. Both
+ * recompute the score tile from q, k and lse. No atomics: results are deterministic.
  */
 fa_status fa_bwd(fa_dtype dt, int B, int H, int N, int d,
                  const void* q, const void* k, const void* v,
