@@ -2,11 +2,13 @@
 
 A step is one pass of the whole hot path over the long-sequence causal workload
 (B=1, H=16, N=16384, bf16, causal, at d=64 and at d=128): for each head dimension
-the forward (O, lse) and the backward (pre-pass, main kernel, dQ conversion) through
+the forward (O, lse) and the backward (D pre-pass, dK/dV kernel, dQ kernel) through
 the C ABI, on inputs already resident in device memory.
 
 FLOP convention: forward 4*B*H*N^2*d, halved for causal; backward 2.5x the forward
 (five products per score tile instead of two). value = FLOP per step / time per step.
+The backward's dK/dV kernel performs four of the five products (2.0x the forward); its
+dQ kernel the fifth, plus a recomputation of two that the convention does not count.
 
 Prints ONE JSON line (the metric line). `--report FILE` additionally times every
 workload (forward and backward separately) and writes a per-workload JSON.
@@ -28,6 +30,8 @@ PEAK_BF16_TFLOPS = 2500.0  # MI355X dense bf16 MFMA
 PEAK_HBM_GBS = 8000.0
 METRIC = "attention fwd+bwd TFLOP/s (bf16, causal) and % of MI355X bf16 MFMA peak"
 STEP_WORKLOADS = ("long_causal_d64", "long_causal_d128")
+# Algorithmic FLOP of each timed kernel, as a multiple of the forward FLOP.
+KERNEL_FLOP_FACTOR = {"fwd": 1.0, "bwd_dkdv": 2.0}
 CALIBRATION_BYTES = 256 << 20
 
 
@@ -94,6 +98,63 @@ class KernelClock:
     def mean_ms(self, name):
         ps = self.pairs.get(name, [])
         return sum(s.elapsed_time(e) for s, e in ps) / len(ps) if ps else float("nan")
+
+
+KERNEL_NAMES = {  # demangled kernel -> short name used by the bench and the traffic file
+    "fwd_bf16_kernel<64>": "fwd_d64", "fwd_bf16_kernel<128>": "fwd_d128",
+    "bwd_dkdv_kernel<64>": "bwd_dkdv_d64", "bwd_dkdv_kernel<128>": "bwd_dkdv_d128",
+    "bwd_dq_kernel<64>": "bwd_dq_d64", "bwd_dq_kernel<128>": "bwd_dq_d128",
+    "bwd_pre_kernel<64>": "bwd_pre_d64", "bwd_pre_kernel<128>": "bwd_pre_d128",
+}
+
+
+def summarize_pmc(fetch_csv: str, write_csv: str, out_path: str) -> dict:
+    """HBM bytes per dispatch from two rocprofv3 --pmc runs of `bench.py --pmc-pass`
+    (FETCH_SIZE, then WRITE_SIZE; KiB per dispatch), each scaled by the factor that makes
+    the 256 MiB calibration copy read and write exactly its size."""
+    import csv
+
+    def load(path, counter):
+        per = {}
+        for row in csv.DictReader(open(path)):
+            if row["Counter_Name"] != counter:
+                continue
+            key = (int(row["Dispatch_Id"]), row["Kernel_Name"])
+            per[key] = per.get(key, 0.0) + float(row["Counter_Value"]) * 1024.0
+        return per
+
+    fetch, write = load(fetch_csv, "FETCH_SIZE"), load(write_csv, "WRITE_SIZE")
+
+    def calib(per):
+        vals = [v for (d, n), v in per.items() if "copyBuffer" in n]
+        if not vals:
+            raise RuntimeError("calibration copy not found in the counter file")
+        return CALIBRATION_BYTES / vals[0]
+
+    ff, fw = calib(fetch), calib(write)
+
+    def short(name):
+        for k, v in KERNEL_NAMES.items():
+            if k in name:
+                return v
+        return None
+
+    def by_kernel(per, factor):
+        out = {}
+        for (d, n), v in sorted(per.items()):
+            s = short(n)
+            if s:
+                out.setdefault(s, []).append(v * factor)
+        return {k: sum(v) / len(v) for k, v in out.items()}
+
+    fb, wb = by_kernel(fetch, ff), by_kernel(write, fw)
+    digest = kernel_source_digest()
+    res = {"calibration": {"copy_bytes": CALIBRATION_BYTES, "fetch_factor": ff, "write_factor": fw},
+           "kernels": {k: {"fetch_bytes": fb[k], "write_bytes": wb.get(k, 0.0),
+                           "bytes_per_launch": fb[k] + wb.get(k, 0.0), "source_digest": digest} for k in fb}}
+    with open(out_path, "w") as f:
+        json.dump(res, f, indent=1)
+    return res
 
 
 def kernel_source_digest() -> str:
@@ -176,7 +237,7 @@ def time_step(fa, runners, steps, warmup):
         for r in runners:
             clock.arm(fa, f"fwd_d{r.w.d}")
             r.fwd()
-            clock.arm(fa, f"bwd_main_d{r.w.d}")
+            clock.arm(fa, f"bwd_dkdv_d{r.w.d}")
             r.bwd()
     t1.record()
     torch.cuda.synchronize()
@@ -230,10 +291,16 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--report", default=None, help="also time every workload and write this JSON file")
+    ap.add_argument("--summarize-pmc", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
+                    help="write profiles/hbm_traffic.json from two rocprofv3 counter files and exit")
     ap.add_argument("--pmc-pass", action="store_true",
                     help="for rocprofv3 --pmc: one 256 MiB device copy (counter calibration), then one "
                          "untimed pass of the step; prints no metric line")
     args = ap.parse_args()
+    if args.summarize_pmc:
+        res = summarize_pmc(*args.summarize_pmc, os.path.join(ROOT, "profiles", "hbm_traffic.json"))
+        print(json.dumps(res, indent=1))
+        return
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only: this build has no multi-GPU path (got --gpus {args.gpus}); "
               "attention heads are independent, see the sharding note in DESIGN.md", file=sys.stderr)
@@ -263,14 +330,13 @@ def main():
     per = {}
     for r in runners:
         f = attn_flops(r.w)
-        per[f"d{r.w.d}"] = {"fwd_kernel_ms": clock.mean_ms(f"fwd_d{r.w.d}"),
-                            "fwd_tflops": f / clock.mean_ms(f"fwd_d{r.w.d}") / 1e9,
-                            "bwd_main_kernel_ms": clock.mean_ms(f"bwd_main_d{r.w.d}"),
-                            "bwd_main_tflops": 2.5 * f / clock.mean_ms(f"bwd_main_d{r.w.d}") / 1e9}
+        per[f"d{r.w.d}"] = {k + "_kernel_ms": round(clock.mean_ms(f"{k}_d{r.w.d}"), 4) for k in KERNEL_FLOP_FACTOR}
+        per[f"d{r.w.d}"].update({k + "_tflops": round(KERNEL_FLOP_FACTOR[k] * f / clock.mean_ms(f"{k}_d{r.w.d}") / 1e9, 1)
+                                 for k in KERNEL_FLOP_FACTOR})
     # dominant kernel: the one with the largest time per step
-    cands = [(clock.mean_ms(f"{k}_d{r.w.d}"), k, r) for r in runners for k in ("fwd", "bwd_main")]
+    cands = [(clock.mean_ms(f"{k}_d{r.w.d}"), k, r) for r in runners for k in KERNEL_FLOP_FACTOR]
     dom_ms, dom_kind, dom_r = max(cands, key=lambda c: c[0])
-    dom_flop = attn_flops(dom_r.w) * (2.5 if dom_kind == "bwd_main" else 1.0)
+    dom_flop = attn_flops(dom_r.w) * KERNEL_FLOP_FACTOR[dom_kind]
     dom_name = f"{dom_kind}_d{dom_r.w.d}"
     achieved = dom_flop / dom_ms / 1e9
     roofline = {"bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",

@@ -106,22 +106,28 @@ __global__ __launch_bounds__(kMainThreads, 1) void bwd_dkdv_kernel(BwdArgs a) {
   constexpr int NDMA = QT / (kMainThreads * 16);     // DMA instructions per wave per Q/dO tile
   constexpr int RPB = 1024 / (2 * D);                 // rows per 1 KB DMA block
   constexpr int KCH = kBK * (D / 8) / kMainThreads;  // 16-byte chunks per thread per K/V tile
-  static_assert(2 * kBK * D * 4 <= 2 * KT + 4 * QT, "dK/dV reduction fits in LDS");
-  __shared__ __attribute__((aligned(16))) char smem[2 * KT + 4 * QT];
+  // LDS: the two Q | dO staging buffers and the K | V tile are separate arrays. The
+  // compiler can then tell that the direct global -> LDS loads into one buffer do not
+  // touch the other, and does not wait for them before reading it.
+  __shared__ __attribute__((aligned(16))) char qd0[2 * QT];
+  __shared__ __attribute__((aligned(16))) char qd1[2 * QT];
+  __shared__ __attribute__((aligned(16))) char kvt[2 * KT];
   __shared__ __attribute__((aligned(16))) float stats[2][2][BQ];  // [buf][lse2 | D][row]
   __shared__ uint16_t qlist[kMaxTileList];
   __shared__ int wcount[8];
-
-  FA_LDS char* const kt = (FA_LDS char*)smem;
+  FA_LDS char* const kt = (FA_LDS char*)kvt;
   FA_LDS char* const vt = kt + KT;
-  FA_LDS char* const qbuf = vt + KT;      // [buf][Q | dO]
+  // After the loop the upper query half hands its partials over through LDS: dK^T of key
+  // group kg in kvt, dV^T in the Q | dO buffer kg / 2.
+  constexpr int RED = MD * 16 * 64;  // floats per key group and tensor
+  static_assert(4 * RED * 4 <= 2 * KT && 2 * RED * 4 <= 2 * QT, "dK/dV reduction fits in LDS");
 
   const int BH = a.B * a.H;
   const int bh = blockIdx.x % BH;
   const int jt = blockIdx.x / BH;       // key tile; small j (most causal work) first
   const int b = bh / a.H;
   const int k0 = jt * kBK;
-  const int tid = threadIdx.x, w = tid >> 6, l = tid & 63, h = l >> 5, kl = l & 31;
+  const int tid = threadIdx.x, w = wave_id(), l = tid & 63, h = l >> 5, kl = l & 31;
   const int kg = w & 3, qh = w >> 2;
   const int key = k0 + 32 * kg + kl;    // the key this lane's accumulator columns refer to
   const int qw0 = 32 * QBW * qh;        // the wave's first query row inside a step
@@ -138,7 +144,8 @@ __global__ __launch_bounds__(kMainThreads, 1) void bwd_dkdv_kernel(BwdArgs a) {
   const int ntq = (a.N + BQ - 1) / BQ;
   const int i0 = a.causal ? k0 / BQ : 0;
   int nq = k0 < kv_end ? ntq - i0 : 0;  // key tile entirely padded: no work, zero dK/dV
-  if (a.mask && nq > 0) nq = build_qtile_list512(qlist, wcount, a.mask, k0 / a.mb, a.nb, a.mb, i0, ntq, BQ);
+  if (a.mask && nq > 0)
+    nq = __builtin_amdgcn_readfirstlane(build_qtile_list512(qlist, wcount, a.mask, k0 / a.mb, a.nb, a.mb, i0, ntq, BQ));
 
   // K and V tiles stay in LDS for the whole kernel (rows past N are zero).
 #pragma unroll
@@ -157,17 +164,17 @@ __global__ __launch_bounds__(kMainThreads, 1) void bwd_dkdv_kernel(BwdArgs a) {
   // offsets of chunk c and of chunk c ^ m differ by an XOR with 16 m, so one base register
   // per operand family serves every k-step and d-block (the XOR only touches bits below
   // the row stride).
+  // Adding a multiple of 32 rows (8 KB at d = 128, 4 KB at d = 64) leaves the XOR-ed bits
+  // alone, so the wave's row shifts are folded into the bases.
   const int row_off0 = tile_off<D>(qw0 + kl, 8 * h);  // Q / dO row operand, k-step 0
-  int ro0 = row_off0;
-  auto row_off = [&](int ks) { return ro0 ^ (32 * ks); };
   // The K / V row operand (row 32 kg + kl) has the same swizzle (both rows agree mod 16),
-  // so it is the Q / dO offset moved by whole rows.
-  const int kv_shift = (32 * kg - qw0) * 2 * D;
+  // so it is the Q / dO offset moved by whole rows, into the K tile.
+  const int kv_off0 = row_off0 + (32 * kg - qw0) * 2 * D;
   int tr_lo0, tr_hi0;        // Q^T / dO^T transpose reads of d-block 0 (+16 s4 rows)
   tr8_offsets<D>(0, tr_lo0, tr_hi0);
-  int tl0 = tr_lo0, th0 = tr_hi0;
-  auto tr_lo = [&](int md) { return tl0 ^ (64 * md); };
-  auto tr_hi = [&](int md) { return th0 ^ (64 * md); };
+  tr_lo0 += qw0 * 2 * D;
+  tr_hi0 += qw0 * 2 * D;
+  int ro0 = row_off0, ko0 = kv_off0, tl0 = tr_lo0, th0 = tr_hi0;
   // Q / dO staging by direct global -> LDS loads: each wave instruction fills 1 KB, lane
   // i the 16 bytes at offset 16 i, so lane i fetches the chunk whose swizzled slot that
   // is. Rows past N (last query tile only) read row N-1; they get P = 0 through the
@@ -187,9 +194,9 @@ __global__ __launch_bounds__(kMainThreads, 1) void bwd_dkdv_kernel(BwdArgs a) {
 
   float sr = 0.f;
   bool svalid = false;
-  auto stage_q = [&](int it, int buf) {
+  auto stage_q = [&](int it, auto bufc) {
     const int q0 = it * BQ;
-    FA_LDS char* qb = qbuf + buf * 2 * QT;
+    FA_LDS char* qb = (FA_LDS char*)(decltype(bufc)::value ? qd1 : qd0);
 #pragma unroll
     for (int c = 0; c < NDMA; ++c) {
       const size_t row = (size_t)min(q0 + dma_row0 + c * 8 * RPB, a.N - 1) * D + dma_col;
@@ -221,9 +228,11 @@ __global__ __launch_bounds__(kMainThreads, 1) void bwd_dkdv_kernel(BwdArgs a) {
   auto wait_loads = [&]() { __builtin_amdgcn_s_waitcnt(kWaitVmcnt0); };
   // Query tiles are visited last-first, so the workgroups of one head that run together
   // add into the same dQ tile at about the same time.
-  auto tile_at = [&](int t) { return a.mask ? (int)qlist[nq - 1 - t] : i0 + nq - 1 - t; };
+  auto tile_at = [&](int t) {
+    return a.mask ? __builtin_amdgcn_readfirstlane((int)qlist[nq - 1 - t]) : i0 + nq - 1 - t;
+  };
 
-  stage_q(nq > 0 ? tile_at(0) : 0, 0);
+  stage_q(nq > 0 ? tile_at(0) : 0, std::integral_constant<int, 0>{});
   wait_loads();
   store_stats(0);
   __syncthreads();
@@ -234,14 +243,15 @@ __global__ __launch_bounds__(kMainThreads, 1) void bwd_dkdv_kernel(BwdArgs a) {
     const int it = tile_at(t);
     const int q0 = it * BQ;
     // buffer BUF ^ 1 was last read in step t - 1: stream the next query tile into it
-    stage_q(tile_at(min(t + 1, nq - 1)), BUF ^ 1);
+    stage_q(tile_at(min(t + 1, nq - 1)), std::integral_constant<int, BUF ^ 1>{});
     // Opaque copies of the offset bases: keeps the compiler from hoisting every derived
     // offset out of the loop into its own register.
     ro0 = row_off0;
+    ko0 = kv_off0;
     tl0 = tr_lo0;
     th0 = tr_hi0;
-    asm volatile("" : "+v"(ro0), "+v"(tl0), "+v"(th0));
-    const FA_LDS char* qb = qbuf + BUF * 2 * QT;
+    asm volatile("" : "+v"(ro0), "+v"(ko0), "+v"(tl0), "+v"(th0));
+    const FA_LDS char* qb = (const FA_LDS char*)(BUF ? qd1 : qd0);
     const FA_LDS char* db = qb + QT;
 
     // S = Q K^T and dP = dO V^T: the wave's QBW query blocks x its 32 keys.
@@ -251,18 +261,35 @@ __global__ __launch_bounds__(kMainThreads, 1) void bwd_dkdv_kernel(BwdArgs a) {
       s[b2] = f32x16{};
       dp[b2] = f32x16{};
     }
-#pragma unroll
-    for (int ks = 0; ks < KS; ++ks) {
-      const bf16x8 kf = lds_ld8(kt + kv_shift + row_off(ks));
-      const bf16x8 vf = lds_ld8(vt + kv_shift + row_off(ks));
+    // Software-pipelined: the operands of k-step ks + 1 are requested before the products
+    // of k-step ks are issued (the scheduling barrier keeps that order).
+    struct SOps {
+      bf16x8 k, v, q[QBW], d[QBW];
+    };
+    auto load_s = [&](int ks, SOps& o) {
+      const int qo = ro0 ^ (32 * ks), ko = ko0 ^ (32 * ks);
+      o.k = lds_ld8(kt + ko);
+      o.v = lds_ld8(vt + ko);
 #pragma unroll
       for (int b2 = 0; b2 < QBW; ++b2) {
-        s[b2] = mfma32(lds_ld8(qb + row_off(ks) + b2 * 32 * 2 * D), kf, s[b2]);
-        dp[b2] = mfma32(lds_ld8(db + row_off(ks) + b2 * 32 * 2 * D), vf, dp[b2]);
+        o.q[b2] = lds_ld8(qb + qo + b2 * 32 * 2 * D);
+        o.d[b2] = lds_ld8(db + qo + b2 * 32 * 2 * D);
+      }
+    };
+    SOps so[2];
+    load_s(0, so[0]);
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+      if (ks + 1 < KS) load_s(ks + 1, so[(ks + 1) & 1]);
+      __builtin_amdgcn_sched_barrier(0);
+      const SOps& o = so[ks & 1];
+#pragma unroll
+      for (int b2 = 0; b2 < QBW; ++b2) {
+        s[b2] = mfma32(o.q[b2], o.k, s[b2]);
+        dp[b2] = mfma32(o.d[b2], o.v, dp[b2]);
       }
     }
-    // P = exp2(S * scale * log2e - lse * log2e); masked pairs -> 0; dS = P (dP - D).
-    const bool edge = (k0 + 32 * kg + 31 >= kv_end) || (a.causal && k0 + 32 * kg + 31 > q0 + qw0);
+    // P = exp2(S * scale * log2e - lse * log2e), dS = P (dP - D).
 #pragma unroll
     for (int b2 = 0; b2 < QBW; ++b2)
 #pragma unroll
@@ -273,23 +300,53 @@ __global__ __launch_bounds__(kMainThreads, 1) void bwd_dkdv_kernel(BwdArgs a) {
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
           const int i = 4 * g + e;
-          float p = fast_exp2(__builtin_fmaf(s[b2][i], a.c2s, -l2[e]));
-          if (edge && (key >= kv_end || (a.causal && key > q0 + qr0 + e))) p = 0.f;
+          const float p = fast_exp2(__builtin_fmaf(s[b2][i], a.c2s, -l2[e]));
           s[b2][i] = p;
           dp[b2][i] = p * (dp[b2][i] - dd[e]);
         }
       }
+    // Tiles that cross the causal diagonal or the key padding (a wave-uniform test): the
+    // masked pairs get P = dS = 0, by selection, so whatever was computed there is dropped.
+    if ((k0 + 32 * kg + 31 >= kv_end) || (a.causal && k0 + 32 * kg + 31 > q0 + qw0)) {
+#pragma unroll
+      for (int b2 = 0; b2 < QBW; ++b2)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+          const int qrow = q0 + qw0 + 32 * b2 + 8 * (i >> 2) + 4 * h + (i & 3);
+          const bool masked = key >= kv_end || (a.causal && key > qrow);
+          s[b2][i] = masked ? 0.f : s[b2][i];
+          dp[b2][i] = masked ? 0.f : dp[b2][i];
+        }
+    }
     // dV^T += dO^T P, dK^T += Q^T dS (16 queries per k-step).
+    // Pipelined like the score products: transpose reads of item j + 1 (item = 16-query
+    // step s4 x d-block md) are requested before the products of item j.
+    bf16x8 pb[2 * QBW], sb[2 * QBW];
 #pragma unroll
     for (int s4 = 0; s4 < 2 * QBW; ++s4) {
-      const bf16x8 pb = pack8(s[s4 >> 1], 8 * (s4 & 1));
-      const bf16x8 sb = pack8(dp[s4 >> 1], 8 * (s4 & 1));
-      const int ro = (qw0 + 16 * s4) * 2 * D;
+      pb[s4] = pack8(s[s4 >> 1], 8 * (s4 & 1));
+      sb[s4] = pack8(dp[s4 >> 1], 8 * (s4 & 1));
+    }
+    constexpr int NJ = 2 * QBW * MD;
+    struct TOps {
+      bf16x8 d, q;
+    };
+    auto load_t = [&](int j, TOps& o) {
+      const int s4 = j / MD, md = j % MD;
+      const int ro = 16 * s4 * 2 * D;
+      const int lo = (tl0 ^ (64 * md)) + ro, hi = (th0 ^ (64 * md)) + ro;
+      o.d = lds_tr8(db + lo, db + hi);
+      o.q = lds_tr8(qb + lo, qb + hi);
+    };
+    TOps to[2];
+    load_t(0, to[0]);
 #pragma unroll
-      for (int md = 0; md < MD; ++md) {
-        dvt[md] = mfma32(lds_tr8(db + tr_lo(md) + ro, db + tr_hi(md) + ro), pb, dvt[md]);
-        dkt[md] = mfma32(lds_tr8(qb + tr_lo(md) + ro, qb + tr_hi(md) + ro), sb, dkt[md]);
-      }
+    for (int j = 0; j < NJ; ++j) {
+      if (j + 1 < NJ) load_t(j + 1, to[(j + 1) & 1]);
+      __builtin_amdgcn_sched_barrier(0);
+      const int s4 = j / MD, md = j % MD;
+      dvt[md] = mfma32(to[j & 1].d, pb[s4], dvt[md]);
+      dkt[md] = mfma32(to[j & 1].q, sb[s4], dkt[md]);
     }
     // Wait for the staged tile, publish it and its statistics.
     wait_loads();
@@ -306,15 +363,16 @@ __global__ __launch_bounds__(kMainThreads, 1) void bwd_dkdv_kernel(BwdArgs a) {
   __syncthreads();
   // Sum the two query halves' partials through LDS (all tiles are free now): the upper
   // half stores dK^T, dV^T in fp32 in its accumulator layout, the lower half adds them.
-  float* red = reinterpret_cast<float*>(smem);
-  const int red_off = kg * (2 * MD * 16 * 64) + l;  // [kg][2 MD][16 regs][64 lanes]
+  // [MD][16 regs][64 lanes] per key group
+  float* const kred = reinterpret_cast<float*>(kvt) + kg * RED + l;
+  float* const vred = reinterpret_cast<float*>(kg < 2 ? qd0 : qd1) + (kg & 1) * RED + l;
   if (qh == 1) {
 #pragma unroll
     for (int md = 0; md < MD; ++md)
 #pragma unroll
       for (int i = 0; i < 16; ++i) {
-        red[red_off + ((2 * md) * 16 + i) * 64] = dkt[md][i];
-        red[red_off + ((2 * md + 1) * 16 + i) * 64] = dvt[md][i];
+        kred[(md * 16 + i) * 64] = dkt[md][i];
+        vred[(md * 16 + i) * 64] = dvt[md][i];
       }
   }
   __syncthreads();
@@ -329,8 +387,8 @@ __global__ __launch_bounds__(kMainThreads, 1) void bwd_dkdv_kernel(BwdArgs a) {
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
           const int i = 4 * g + e;
-          kv4[e] = (__bf16)((dkt[md][i] + red[red_off + ((2 * md) * 16 + i) * 64]) * a.scale);
-          vv4[e] = (__bf16)(dvt[md][i] + red[red_off + ((2 * md + 1) * 16 + i) * 64]);
+          kv4[e] = (__bf16)((dkt[md][i] + kred[(md * 16 + i) * 64]) * a.scale);
+          vv4[e] = (__bf16)(dvt[md][i] + vred[(md * 16 + i) * 64]);
         }
         *reinterpret_cast<bf16x4*>(dK + 32 * md + 8 * g + 4 * h) = kv4;
         *reinterpret_cast<bf16x4*>(dV + 32 * md + 8 * g + 4 * h) = vv4;
@@ -348,20 +406,27 @@ __global__ __launch_bounds__(kMainThreads, 1) void bwd_dkdv_kernel(BwdArgs a) {
 //   dS^T      = P^T o (dP^T - D),  P^T = exp2(S^T scale log2e - lse log2e)
 //   dQ^T     += K^T dS^T          (A = K^T transpose reads, B = dS^T from the accumulator)
 //   dQ = scale dQ^T^T, written once in bf16.
+//   K and V tiles are staged by direct buffer -> LDS loads bounded at row N (rows past the
+//   end arrive as zeros), one tile ahead, so no staging registers are needed.
 // ---------------------------------------------------------------------------------------
 constexpr int kDqRows = 128;  // query rows per workgroup
 constexpr int kDqKeys = 64;   // keys per tile
 
 template <int D>
 __global__ __launch_bounds__(kThreads, 2) void bwd_dq_kernel(BwdArgs a) {
-  constexpr int CH = D / 8;                     // 16-byte chunks per row
-  constexpr int TILE = kDqKeys * D * 2;         // bytes of one K or V tile
-  constexpr int NCH = kDqKeys * CH / kThreads;  // chunks per thread per tensor
-  constexpr int KS = D / 16;                    // k-steps over d
-  constexpr int MD = D / 32;                    // 32-row blocks of dQ^T
-  constexpr int KB = kDqKeys / 32;              // 32-key blocks of a tile
-  constexpr int PS = kDqKeys / 16;              // k-steps of the dQ^T product
-  __shared__ __attribute__((aligned(16))) char smem[4 * TILE];  // [buf][K | V]
+  constexpr int CH = D / 8;                         // 16-byte chunks per row
+  constexpr int TILE = kDqKeys * D * 2;             // bytes of one K or V tile
+  constexpr int KS = D / 16;                        // k-steps over d
+  constexpr int MD = D / 32;                        // 32-row blocks of dQ^T
+  constexpr int KB = kDqKeys / 32;                  // 32-key blocks of a tile
+  constexpr int PS = kDqKeys / 16;                  // k-steps of the dQ^T product
+  constexpr int RPB = 1024 / (2 * D);               // tile rows per 1 KB staging block
+  constexpr int NDMA = TILE / (kThreads * 16);      // staging instructions per wave per tensor
+  static_assert((4 * RPB) % 16 == 0, "staging block step must keep the swizzle");
+  // One array per buffer, so that the staging loads into one buffer are known not to
+  // touch the other (no wait for them before reading it).
+  __shared__ __attribute__((aligned(16))) char kv0[2 * TILE];  // K | V, buffer 0
+  __shared__ __attribute__((aligned(16))) char kv1[2 * TILE];  // K | V, buffer 1
   __shared__ uint16_t tlist[kMaxTileList];
   __shared__ int wcount[4];
 
@@ -371,7 +436,7 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dq_kernel(BwdArgs a) {
   const int qt = ntq - 1 - blockIdx.x / BH;     // longest (causal) tiles first
   const int b = bh / a.H;
   const int q0 = qt * kDqRows;
-  const int tid = threadIdx.x, w = tid >> 6, l = tid & 63, h = l >> 5, ql = l & 31;
+  const int tid = threadIdx.x, w = wave_id(), l = tid & 63, h = l >> 5, ql = l & 31;
   const int qi = q0 + 32 * w + ql;
   const size_t hoff = (size_t)bh * a.N * D;
   const __bf16* __restrict__ Q = reinterpret_cast<const __bf16*>(a.q) + hoff;
@@ -402,7 +467,7 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dq_kernel(BwdArgs a) {
       count += wcount[0] + wcount[1] + wcount[2] + wcount[3];
       __syncthreads();
     }
-    ntiles = count;
+    ntiles = __builtin_amdgcn_readfirstlane(count);
   }
 
   // The wave's Q and dO rows (B operands), and its row statistics in the exp2 domain.
@@ -419,58 +484,58 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dq_kernel(BwdArgs a) {
   // an empty row (lse = -inf) and a row past N get lse2 = +inf, so P = 0 there
   const float lse2 = (qi >= a.N || lse_v == kNegInf) ? __builtin_inff() : lse_v * kLog2e;
   const float dval = a.dsum[(size_t)bh * a.N + min(qi, a.N - 1)];
+  // The fragments are read in every step: let them land here, so that no wait for them is
+  // left inside the loop.
+  __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
 
   // Per-lane LDS byte offsets (XOR-derived per k-step / d-block, see the dK/dV kernel).
   const int k_off0 = tile_off<D>(ql, 8 * h);  // K / V row operand, k-step 0 (+32 kb rows)
   int t_lo0, t_hi0;                             // K^T transpose reads of d-block 0 (+16 st rows)
   tr8_offsets<D>(0, t_lo0, t_hi0);
-  constexpr int GROWS = kThreads / CH;
-  static_assert(GROWS % 16 == 0, "row step must keep the swizzle");
-  const int g_row0 = tid / CH, g_col0 = (tid % CH) * 8;
-  const int st_off0 = tile_off<D>(g_row0, g_col0);
+  // Staging: instruction c of wave w fills 1 KB block 4c + w of a tile, lane l the 16
+  // bytes at 16 l: tile row (4c + w) RPB + l / CH, physical chunk l % CH, which holds the
+  // logical chunk (l % CH) ^ swz(row); the row step 4 RPB keeps swz unchanged.
+  const int dma_row0 = w * RPB + l / CH;
+  const int dma_col = ((l % CH) ^ swz<D>(dma_row0)) * 8;
+  int dma_off[NDMA];
+#pragma unroll
+  for (int c = 0; c < NDMA; ++c) dma_off[c] = ((dma_row0 + 4 * RPB * c) * D + dma_col) * 2;
 
   f32x16 dq[MD];
 #pragma unroll
   for (int md = 0; md < MD; ++md) dq[md] = f32x16{};
 
-  // Branch-free register prefetch of the next K, V tile (rows past N zeroed on store).
-  u32x4 kr[NCH], vr[NCH];
-  bool kval[NCH];
   auto tile_at = [&](int t) {
     const int tc = min(t, max(ntiles - 1, 0));
-    return a.mask ? (int)tlist[tc] : tc;
+    return a.mask ? __builtin_amdgcn_readfirstlane((int)tlist[tc]) : tc;
   };
-  auto gload_kv = [&](int jt) {
+  auto stage = [&](int jt, auto bufc) {
+    const int key0 = jt * kDqKeys;
+    const uint32_t bytes = (uint32_t)max(a.N - key0, 0) * (uint32_t)(D * 2);
+    const auto rk = make_rsrc(K + (size_t)key0 * D, bytes);
+    const auto rv = make_rsrc(V + (size_t)key0 * D, bytes);
+    FA_LDS char* base = (FA_LDS char*)(decltype(bufc)::value ? kv1 : kv0);
 #pragma unroll
-    for (int c = 0; c < NCH; ++c) {
-      const int key = jt * kDqKeys + g_row0 + c * GROWS;
-      kval[c] = key < a.N;
-      const size_t row = (size_t)min(key, a.N - 1) * D + g_col0;
-      kr[c] = gload16(K + row);
-      vr[c] = gload16(V + row);
-    }
-  };
-  FA_LDS char* const lds0 = (FA_LDS char*)smem;
-  auto store_kv = [&](int buf) {
-#pragma unroll
-    for (int c = 0; c < NCH; ++c) {
-      FA_LDS char* p = lds0 + buf * 2 * TILE + st_off0 + c * GROWS * 2 * D;
-      lds_store16(p, kval[c] ? kr[c] : u32x4{});
-      lds_store16(p + TILE, kval[c] ? vr[c] : u32x4{});
+    for (int c = 0; c < NDMA; ++c) {
+      FA_LDS char* blk = base + (4 * c + w) * 1024;
+      const int voff = dma_off[c];  // (a local copy: see the forward's staging)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rk, (FA_LDS void*)blk, 16, voff, 0, 0, 0);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rv, (FA_LDS void*)(blk + TILE), 16, voff, 0, 0, 0);
     }
   };
 
-  gload_kv(tile_at(0));
-  store_kv(0);
+  stage(tile_at(0), std::integral_constant<int, 0>{});
+  __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
   __syncthreads();
 
   int ko0 = k_off0, tl0 = t_lo0, th0 = t_hi0;
   auto step = [&](auto bufc, int t) {
     constexpr int BUF = decltype(bufc)::value;
-    const FA_LDS char* kb = lds0 + BUF * 2 * TILE;
+    const FA_LDS char* kb = (const FA_LDS char*)(BUF ? kv1 : kv0);
     const FA_LDS char* vb = kb + TILE;
     const int jt = tile_at(t);
-    gload_kv(tile_at(t + 1));
+    // buffer BUF ^ 1 was last read in step t - 1: stream the next tile into it
+    stage(tile_at(t + 1), std::integral_constant<int, BUF ^ 1>{});
     // opaque offset bases: keep the derived offsets from being hoisted into registers
     ko0 = k_off0;
     tl0 = t_lo0;
@@ -479,40 +544,75 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dq_kernel(BwdArgs a) {
     const int key0 = jt * kDqKeys;
     // A wave whose queries all precede the tile (causal) has nothing to do here.
     if (!(a.causal && key0 > q0 + 32 * w + 31)) {
+      // S^T, dP^T: items (ks, kb) with the key block innermost, so that four independent
+      // accumulations alternate; each item's K / V rows are requested one item ahead.
       f32x16 s[KB], dp[KB];
 #pragma unroll
       for (int kbk = 0; kbk < KB; ++kbk) {
         s[kbk] = f32x16{};
         dp[kbk] = f32x16{};
-#pragma unroll
-        for (int ks = 0; ks < KS; ++ks) {
-          const int o = (ko0 ^ (32 * ks)) + kbk * 32 * 2 * D;
-          s[kbk] = mfma32(lds_ld8(kb + o), qf[ks], s[kbk]);
-          dp[kbk] = mfma32(lds_ld8(vb + o), df[ks], dp[kbk]);
-        }
       }
-      const bool edge = (key0 + kDqKeys > kv_end) || (a.causal && key0 + kDqKeys - 1 > q0 + 32 * w);
-      bf16x8 dsb[PS];
+      constexpr int NI = KS * KB;
+      struct SOps {
+        bf16x8 k, v;
+      };
+      auto load_s = [&](int it, SOps& o) {
+        const int ks = it / KB, kbk = it % KB;
+        const int off = (ko0 ^ (32 * ks)) + kbk * 32 * 2 * D;
+        o.k = lds_ld8(kb + off);
+        o.v = lds_ld8(vb + off);
+      };
+      SOps so[2];
+      load_s(0, so[0]);
+#pragma unroll
+      for (int it = 0; it < NI; ++it) {
+        if (it + 1 < NI) load_s(it + 1, so[(it + 1) & 1]);
+        __builtin_amdgcn_sched_barrier(0);
+        const int ks = it / KB, kbk = it % KB;
+        s[kbk] = mfma32(so[it & 1].k, qf[ks], s[kbk]);
+        dp[kbk] = mfma32(so[it & 1].v, df[ks], dp[kbk]);
+      }
 #pragma unroll
       for (int kbk = 0; kbk < KB; ++kbk)
 #pragma unroll
         for (int i = 0; i < 16; ++i) {
-          float p = fast_exp2(__builtin_fmaf(s[kbk][i], a.c2s, -lse2));
-          if (edge) {
+          const float p = fast_exp2(__builtin_fmaf(s[kbk][i], a.c2s, -lse2));
+          dp[kbk][i] = p * (dp[kbk][i] - dval);
+        }
+      // Tiles that cross the causal diagonal or the key padding (a wave-uniform test):
+      // masked pairs get dS = 0 by selection.
+      if ((key0 + kDqKeys > kv_end) || (a.causal && key0 + kDqKeys - 1 > q0 + 32 * w)) {
+#pragma unroll
+        for (int kbk = 0; kbk < KB; ++kbk)
+#pragma unroll
+          for (int i = 0; i < 16; ++i) {
             const int key = key0 + 32 * kbk + 8 * (i >> 2) + 4 * h + (i & 3);
-            if (key >= kv_end || (a.causal && key > qi)) p = 0.f;
+            dp[kbk][i] = (key >= kv_end || (a.causal && key > qi)) ? 0.f : dp[kbk][i];
           }
-          dsb[2 * kbk + (i >> 3)][i & 7] = (__bf16)(p * (dp[kbk][i] - dval));
-        }
+      }
+      bf16x8 dsb[PS];
 #pragma unroll
-      for (int st = 0; st < PS; ++st)
+      for (int kbk = 0; kbk < KB; ++kbk)
 #pragma unroll
-        for (int md = 0; md < MD; ++md) {
-          const int ro = st * 16 * 2 * D;
-          dq[md] = mfma32(lds_tr8(kb + (tl0 ^ (64 * md)) + ro, kb + (th0 ^ (64 * md)) + ro), dsb[st], dq[md]);
-        }
+        for (int i = 0; i < 16; ++i) dsb[2 * kbk + (i >> 3)][i & 7] = (__bf16)dp[kbk][i];
+      // dQ^T += K^T dS^T: items (st, md), transpose reads one item ahead.
+      constexpr int NJ = PS * MD;
+      bf16x8 kt8[2];
+      auto load_t = [&](int j) {
+        const int st = j / MD, md = j % MD;
+        const int ro = st * 16 * 2 * D;
+        return lds_tr8(kb + (tl0 ^ (64 * md)) + ro, kb + (th0 ^ (64 * md)) + ro);
+      };
+      kt8[0] = load_t(0);
+#pragma unroll
+      for (int j = 0; j < NJ; ++j) {
+        if (j + 1 < NJ) kt8[(j + 1) & 1] = load_t(j + 1);
+        __builtin_amdgcn_sched_barrier(0);
+        dq[j % MD] = mfma32(kt8[j & 1], dsb[j / MD], dq[j % MD]);
+      }
     }
-    store_kv(BUF ^ 1);
+    // the next tile has landed (this wave's part): publish it
+    __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
     __syncthreads();
   };
   for (int t = 0; t < ntiles; t += 2) {

@@ -40,6 +40,21 @@ constexpr float kNegInf = -__builtin_inff();
 
 __device__ __forceinline__ int lane_id() { return threadIdx.x & 63; }
 
+// Index of the calling wave in its workgroup, as a wave-uniform (scalar) value: branches
+// that depend on it stay scalar branches instead of per-lane exec masking.
+__device__ __forceinline__ int wave_id() { return __builtin_amdgcn_readfirstlane(threadIdx.x >> 6); }
+
+// Raw buffer resource over [base, base + bytes). Loads through it at a byte offset >= bytes
+// return zero instead of touching memory (the hardware range check of raw buffers), which
+// zero-fills tiles that run past the end of a sequence without any per-lane test.
+// Word 3 selects 32-bit data format, as for every gfx9-family raw buffer.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, 0x00020000);
+}
+__device__ __forceinline__ u32x4 bload16(__amdgpu_buffer_rsrc_t r, int byte_off) {
+  return __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, byte_off, 0, 0));
+}
+
 __device__ __forceinline__ f32x16 mfma32(bf16x8 a, bf16x8 b, f32x16 c) {
   return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
 }

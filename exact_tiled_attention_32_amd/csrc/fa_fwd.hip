@@ -63,19 +63,27 @@ __device__ int build_tile_list(uint16_t* list, int* wcount, const uint8_t* mask,
 constexpr int kSchedMfma = 0x008;
 constexpr int kSchedValu = 0x002;
 constexpr int kSchedDsRead = 0x100;
+// s_waitcnt immediate for vmcnt(0), expcnt and lgkmcnt left free (gfx9 encoding).
+constexpr int kWaitVmcnt0 = 0x0F70;
 
 template <int D>
 __global__ __launch_bounds__(kThreads, 2) void fwd_bf16_kernel(FwdArgs a) {
   constexpr int CH = D / 8;                    // 16-byte chunks per row
-  constexpr int NCH = kBC * CH / kThreads;     // chunks per thread per tensor
   constexpr int TILE = kBC * D * 2;            // bytes of one K or V tile
   constexpr int KS = D / 16;                   // k-steps of the score product
   constexpr int MD = D / 32;                   // 32-row blocks of O^T
   constexpr int KB = kBC / 32;                 // 32-key blocks of a score tile
   constexpr int PS = kBC / 16;                 // k-steps of the O^T product
-  // LDS: K buffers [0, 2 TILE), V buffers [2 TILE, 4 TILE). The score product runs one
-  // tile ahead of the value product, so step t reads K(t+1) and V(t).
-  __shared__ __attribute__((aligned(16))) char smem[4 * TILE];
+  constexpr int RPB = 1024 / (2 * D);          // tile rows per 1 KB staging block
+  constexpr int NDMA = TILE / (kThreads * 16); // staging instructions per wave per tile
+  static_assert((4 * RPB) % 16 == 0, "staging block step must keep the swizzle");
+  // LDS: two K and two V buffers, each its own array so that the staging loads into one
+  // buffer are known not to touch the others (no wait for them before reading those).
+  // The score product runs one tile ahead of the value product: step t reads K(t+1), V(t).
+  __shared__ __attribute__((aligned(16))) char kb0[TILE];
+  __shared__ __attribute__((aligned(16))) char kb1[TILE];
+  __shared__ __attribute__((aligned(16))) char vb0[TILE];
+  __shared__ __attribute__((aligned(16))) char vb1[TILE];
   __shared__ uint16_t tlist[kMaxTiles];
   __shared__ int wcount[4];
 
@@ -84,7 +92,7 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_bf16_kernel(FwdArgs a) {
   const int qt = a.ntq - 1 - blockIdx.x / BH;  // longest (causal) tiles first
   const int b = bh / a.H;
   const int q0 = qt * kBR;
-  const int tid = threadIdx.x, w = tid >> 6, l = tid & 63, h = l >> 5, ql = l & 31;
+  const int tid = threadIdx.x, w = wave_id(), l = tid & 63, h = l >> 5, ql = l & 31;
   const int qi = q0 + 32 * w + ql;
   const size_t hoff = (size_t)bh * a.N * D;
   const __bf16* __restrict__ Q = reinterpret_cast<const __bf16*>(a.q) + hoff;
@@ -97,11 +105,12 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_bf16_kernel(FwdArgs a) {
   if (a.causal) hi = min(hi, q0 + kBR);
   const int ntk = (hi + kBC - 1) / kBC;
   int ntiles = ntk;
-  if (a.mask) ntiles = build_tile_list(tlist, wcount, a.mask, q0 / a.mb, a.nb, a.mb, ntk, kBC);
+  if (a.mask)
+    ntiles = __builtin_amdgcn_readfirstlane(build_tile_list(tlist, wcount, a.mask, q0 / a.mb, a.nb, a.mb, ntk, kBC));
   // Key tile of step t, clamped so that the look-ahead of the last steps stays valid.
   auto tile_at = [&](int t) {
     const int tc = min(t, max(ntiles - 1, 0));
-    return a.mask ? (int)tlist[tc] : tc;
+    return a.mask ? __builtin_amdgcn_readfirstlane((int)tlist[tc]) : tc;
   };
 
   // Q fragments: B operand of S^T = K Q^T, lane holds Q[qi][16 ks + 8h .. +7].
@@ -117,6 +126,9 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_bf16_kernel(FwdArgs a) {
 #pragma unroll
         for (int e = 0; e < 8; ++e) qf[ks][e] = (__bf16)((float)qf[ks][e] * qm);
     }
+    // The fragments are read in every step: let them land here, so that no wait for them
+    // is left inside the loop.
+    __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
   }
 
   // Per-lane LDS byte offsets, tile-relative, fixed for the whole kernel.
@@ -126,12 +138,15 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_bf16_kernel(FwdArgs a) {
   int v_lo[MD], v_hi[MD];    // V^T transpose reads for d-block md (+16 st rows)
 #pragma unroll
   for (int md = 0; md < MD; ++md) tr8_offsets<D>(32 * md, v_lo[md], v_hi[md]);
-  // Tile staging: thread chunk c covers row tid / CH + c * (kThreads / CH); that row step
-  // is a multiple of 16, so one swizzled offset serves every chunk.
-  constexpr int GROWS = kThreads / CH;
-  static_assert(GROWS % 16 == 0, "row step must keep the swizzle");
-  const int g_row0 = tid / CH, g_col0 = (tid % CH) * 8;
-  const int st_off0 = tile_off<D>(g_row0, g_col0);
+  // Tile staging by direct buffer -> LDS loads bounded at row N (rows past the end arrive
+  // as zeros): instruction c of wave w fills 1 KB block 4c + w of a tile, lane l the 16
+  // bytes at 16 l: tile row (4c + w) RPB + l / CH, physical chunk l % CH, which holds the
+  // logical chunk (l % CH) ^ swz(row); the row step 4 RPB keeps swz unchanged.
+  const int dma_row0 = w * RPB + l / CH;
+  const int dma_col = ((l % CH) ^ swz<D>(dma_row0)) * 8;
+  int dma_off[NDMA];
+#pragma unroll
+  for (int c = 0; c < NDMA; ++c) dma_off[c] = ((dma_row0 + 4 * RPB * c) * D + dma_col) * 2;
 
   f32x16 o[MD];
 #pragma unroll
@@ -139,37 +154,21 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_bf16_kernel(FwdArgs a) {
   float m_run = kNegInf, l_run = 0.f, moff = 0.f;
   const float c2 = a.c2;
 
-  // Branch-free load pipeline, so the compiler can count outstanding loads exactly: rows
-  // past N read row N-1 and are zeroed when stored.
-  u32x4 kr[NCH], vr[NCH];
-  bool kval[NCH], vval[NCH];
-  auto gload_k = [&](int jt) {
+  auto stage = [&](const __bf16* base, int jt, FA_LDS char* buf) {
+    const int key0 = jt * kBC;
+    const auto r = make_rsrc(base + (size_t)key0 * D, (uint32_t)max(a.N - key0, 0) * (uint32_t)(D * 2));
 #pragma unroll
-    for (int c = 0; c < NCH; ++c) {
-      const int key = jt * kBC + g_row0 + c * GROWS;
-      kval[c] = key < a.N;
-      kr[c] = gload16(K + (size_t)min(key, a.N - 1) * D + g_col0);
+    for (int c = 0; c < NDMA; ++c) {
+      // (an array element passed straight to the builtin makes the host pass silently drop
+      // the kernel's launch stub; a local copy does not)
+      const int voff = dma_off[c];
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (FA_LDS void*)(buf + (4 * c + w) * 1024), 16, voff, 0, 0, 0);
     }
   };
-  auto gload_v = [&](int jt) {
-#pragma unroll
-    for (int c = 0; c < NCH; ++c) {
-      const int key = jt * kBC + g_row0 + c * GROWS;
-      vval[c] = key < a.N;
-      vr[c] = gload16(V + (size_t)min(key, a.N - 1) * D + g_col0);
-    }
-  };
-  FA_LDS char* const lds0 = (FA_LDS char*)smem;
-  auto store_k = [&](int buf) {
-#pragma unroll
-    for (int c = 0; c < NCH; ++c)
-      lds_store16(lds0 + buf * TILE + st_off0 + c * GROWS * 2 * D, kval[c] ? kr[c] : u32x4{});
-  };
-  auto store_v = [&](int buf) {
-#pragma unroll
-    for (int c = 0; c < NCH; ++c)
-      lds_store16(lds0 + (2 + buf) * TILE + st_off0 + c * GROWS * 2 * D, vval[c] ? vr[c] : u32x4{});
-  };
+  FA_LDS char* const kbuf0 = (FA_LDS char*)kb0;
+  FA_LDS char* const kbuf1 = (FA_LDS char*)kb1;
+  FA_LDS char* const vbuf0 = (FA_LDS char*)vb0;
+  FA_LDS char* const vbuf1 = (FA_LDS char*)vb1;
 
   // Score tile S^T = K Q^T of the K tile at `kb` (MFMA phase only).
   auto scores = [&](const FA_LDS char* kb, f32x16 (&s)[KB]) {
@@ -212,14 +211,12 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_bf16_kernel(FwdArgs a) {
 
   f32x16 sa[KB], sb[KB];
   if (ntiles > 0) {
-    gload_k(tile_at(0));
-    gload_v(tile_at(0));
-    store_k(0);
-    store_v(0);
-    gload_k(tile_at(1));
-    store_k(1);
+    stage(K, tile_at(0), kbuf0);
+    stage(V, tile_at(0), vbuf0);
+    stage(K, tile_at(1), kbuf1);
+    __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
     __syncthreads();
-    scores(lds0, sa);
+    scores(kbuf0, sa);
     rowmax_update(tile_at(0), sa);
     __syncthreads();  // step 0 overwrites K buffer 0
   }
@@ -229,10 +226,12 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_bf16_kernel(FwdArgs a) {
   // maximum of tile t+1.
   auto step = [&](auto bufc, f32x16 (&cur)[KB], f32x16 (&nxt)[KB], int t) {
     constexpr int BUF = decltype(bufc)::value;
-    const FA_LDS char* kb = lds0 + (BUF ^ 1) * TILE;
-    const FA_LDS char* vb = lds0 + (2 + BUF) * TILE;
-    gload_k(tile_at(t + 2));
-    gload_v(tile_at(t + 1));
+    const FA_LDS char* kb = BUF ? kbuf0 : kbuf1;
+    const FA_LDS char* vb = BUF ? vbuf1 : vbuf0;
+    // K buffer BUF held tile t (read in step t - 1), V buffer BUF ^ 1 tile t - 1 (read in
+    // step t - 1): stream K(t+2) and V(t+1) into them; they land by the end of the step.
+    stage(K, tile_at(t + 2), BUF ? kbuf1 : kbuf0);
+    stage(V, tile_at(t + 1), BUF ? vbuf0 : vbuf1);
     // -- region A: score MFMAs of the next tile, exp/sum/pack of this tile
     scores(kb, nxt);
     bf16x8 pb[PS];
@@ -253,16 +252,23 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_bf16_kernel(FwdArgs a) {
       __builtin_amdgcn_sched_group_barrier(kSchedValu, 7, 0);
     }
     l_run += lsum;
-    // -- region B: O^T += V^T P^T
+    // -- region B: O^T += V^T P^T, items (st, md), transpose reads one item ahead
+    constexpr int NJ = PS * MD;
+    bf16x8 vt8[2];
+    auto load_v = [&](int j) {
+      const int st = j / MD, md = j % MD;
+      return lds_tr8(vb + v_lo[md] + st * 16 * 2 * D, vb + v_hi[md] + st * 16 * 2 * D);
+    };
+    vt8[0] = load_v(0);
 #pragma unroll
-    for (int st = 0; st < PS; ++st)
-#pragma unroll
-      for (int md = 0; md < MD; ++md)
-        o[md] = mfma32(lds_tr8(vb + v_lo[md] + st * 16 * 2 * D, vb + v_hi[md] + st * 16 * 2 * D), pb[st], o[md]);
-    // -- stage the tiles two and one steps ahead; prepare tile t+1
-    store_k(BUF);
-    store_v(BUF ^ 1);
+    for (int j = 0; j < NJ; ++j) {
+      if (j + 1 < NJ) vt8[(j + 1) & 1] = load_v(j + 1);
+      __builtin_amdgcn_sched_barrier(0);
+      o[j % MD] = mfma32(vt8[j & 1], pb[j / MD], o[j % MD]);
+    }
+    // -- prepare tile t+1; the staged tiles must have landed before the barrier
     if (t + 1 < ntiles) rowmax_update(tile_at(t + 1), nxt);
+    __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
     __syncthreads();
   };
   for (int t = 0; t < ntiles; t += 2) {
@@ -303,7 +309,7 @@ __global__ __launch_bounds__(kThreads) void fwd_f32_kernel(FwdArgs a) {
   const int qt = a.ntq - 1 - blockIdx.x / BH;
   const int b = bh / a.H;
   const int q0 = qt * kBR;
-  const int tid = threadIdx.x, w = tid >> 6, l = tid & 63, h = l >> 5, ql = l & 31;
+  const int tid = threadIdx.x, w = wave_id(), l = tid & 63, h = l >> 5, ql = l & 31;
   const int qi = q0 + 32 * w + ql;
   const size_t hoff = (size_t)bh * a.N * D;
   const float* __restrict__ Q = reinterpret_cast<const float*>(a.q) + hoff;
@@ -316,7 +322,8 @@ __global__ __launch_bounds__(kThreads) void fwd_f32_kernel(FwdArgs a) {
   if (a.causal) hi = min(hi, q0 + kBR);
   const int ntk = (hi + BC - 1) / BC;
   int ntiles = ntk;
-  if (a.mask) ntiles = build_tile_list(tlist, wcount, a.mask, q0 / a.mb, a.nb, a.mb, ntk, BC);
+  if (a.mask)
+    ntiles = __builtin_amdgcn_readfirstlane(build_tile_list(tlist, wcount, a.mask, q0 / a.mb, a.nb, a.mb, ntk, BC));
 
   float qf[D / 2];
 #pragma unroll
@@ -329,7 +336,7 @@ __global__ __launch_bounds__(kThreads) void fwd_f32_kernel(FwdArgs a) {
   const float c2 = a.c2;
 
   for (int t = 0; t < ntiles; ++t) {
-    const int jt = a.mask ? tlist[t] : t;
+    const int jt = a.mask ? __builtin_amdgcn_readfirstlane((int)tlist[t]) : t;
     const int key0 = jt * BC;
     for (int e = tid; e < BC * D; e += kThreads) {
       const int row = e / D, col = e % D;

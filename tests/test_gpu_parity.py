@@ -172,6 +172,16 @@ def test_forward_deterministic(gpu_lib):
     assert torch.equal(a["o"], b["o"]) and torch.equal(a["lse"], b["lse"])
 
 
+@pytest.mark.parametrize("d", [64, 128])
+def test_backward_deterministic(gpu_lib, d):
+    """The backward accumulates without atomics: repeated calls are bitwise identical."""
+    case = workloads.make_case(2, 3, 700, d, seed=5, causal=True, kv_len=[700, 450])
+    a = gpu_run(gpu_lib, case)
+    b = gpu_run(gpu_lib, case)
+    for n in ("dq", "dk", "dv"):
+        assert torch.equal(a[n], b[n]), n
+
+
 def test_blocksparse_pattern(gpu_lib):
     """Changing K, V inside blocks masked for query block r leaves block r's O and lse bitwise
     unchanged; keys no query block keeps get dK = dV = 0 exactly."""
