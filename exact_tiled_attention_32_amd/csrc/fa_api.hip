@@ -132,7 +132,7 @@ size_t fa_bwd_workspace_bytes(int B, int H, int N, int d) {
   if (B <= 0 || H <= 0 || N <= 0 || d <= 0) return 0;
   const long double rows = (long double)B * H * N;
   if (rows * d * 4 > (long double)(1ull << 62)) return 0;
-  return align256((size_t)B * H * N * sizeof(float));
+  return align256((size_t)B * H * N * sizeof(float)) + fa::kMaxKeyTiles * sizeof(uint32_t);
 }
 
 fa_status fa_bwd(fa_dtype dt, int B, int H, int N, int d, const void* q, const void* k,
@@ -170,6 +170,9 @@ fa_status fa_bwd(fa_dtype dt, int B, int H, int N, int d, const void* q, const v
   a.dk = dk;
   a.dv = dv;
   a.dsum = reinterpret_cast<float*>(workspace);
+  a.order = block_mask ? reinterpret_cast<uint32_t*>(reinterpret_cast<char*>(workspace) +
+                                                     align256((size_t)B * H * N * sizeof(float)))
+                       : nullptr;
   a.kv_len = kv_len;
   a.mask = block_mask;
   a.B = B;

@@ -29,7 +29,7 @@ namespace fa {
 namespace {
 
 constexpr int kThreads = 256;
-constexpr int kBK = 128;  // keys per workgroup (32 per wave)
+constexpr int kBK = kBwdKeyTile;  // keys per dK/dV workgroup (32 per wave)
 
 // ---------------------------------------------------------------------------------------
 // 1. D = rowsum(dO o O). Each thread owns 8 columns of one row.
@@ -51,6 +51,67 @@ __global__ __launch_bounds__(kThreads) void bwd_pre_kernel(BwdArgs a) {
 #pragma unroll
   for (int off = LPR / 2; off > 0; off >>= 1) acc += __shfl_xor(acc, off);
   if (row < rows && (gid % LPR) == 0) a.dsum[row] = acc;
+}
+
+// ---------------------------------------------------------------------------------------
+// 1b. Block-sparse only: the order in which the dK/dV workgroups take their key tiles, most
+//     kept mask blocks first. The work of a key tile is proportional to the kept blocks of
+//     its mask column; a column kept for every query block (a "global" column) can take
+//     far longer than the rest, and started last it would set the end of the launch.
+//     One workgroup: column counts into LDS, then a bitonic sort of (count, tile) keys.
+// ---------------------------------------------------------------------------------------
+__global__ __launch_bounds__(kThreads) void bwd_order_kernel(const uint8_t* __restrict__ mask, int nb, int mb,
+                                                             int ntk, uint32_t* __restrict__ order) {
+  __shared__ uint32_t cnt[kMaxKeyTiles];   // kept blocks per mask column (nb <= ntk)
+  __shared__ uint32_t keys[kMaxKeyTiles];
+  const int tid = threadIdx.x;
+  for (int c = tid; c < nb; c += kThreads) cnt[c] = 0;
+  __syncthreads();
+  if (nb % 16 == 0 && (reinterpret_cast<uintptr_t>(mask) & 15) == 0) {
+    // 16 columns per thread and 16-byte loads: column group g = tid % G, every R-th row
+    const int G = nb / 16, R = kThreads / G;
+    if (tid < G * R) {
+      const int g = tid % G;
+      uint32_t n[16] = {};
+      for (int r = tid / G; r < nb; r += R) {
+        const u32x4 v = gload16(mask + (size_t)r * nb + 16 * g);
+#pragma unroll
+        for (int i = 0; i < 16; ++i) n[i] += ((v[i >> 2] >> (8 * (i & 3))) & 0xFFu) != 0;
+      }
+#pragma unroll
+      for (int i = 0; i < 16; ++i) atomicAdd(&cnt[16 * g + i], n[i]);
+    }
+  } else {
+    // any width: each thread sums its columns down the rows
+    for (int c = tid; c < nb; c += kThreads) {
+      uint32_t n = 0;
+      for (int r = 0; r < nb; ++r) n += mask[(size_t)r * nb + c] != 0;
+      cnt[c] = n;
+    }
+  }
+  __syncthreads();
+  int P = 1;
+  while (P < ntk) P <<= 1;
+  // ascending order of (0xFFFF - count) << 16 | tile: most blocks first, ties by tile
+  for (int j = tid; j < P; j += kThreads)
+    keys[j] = j < ntk ? ((0xFFFFu - min(cnt[(j * kBwdKeyTile) / mb], 0xFFFFu)) << 16) | (uint32_t)j : 0xFFFFFFFFu;
+  __syncthreads();
+  for (int k = 2; k <= P; k <<= 1)
+    for (int j = k >> 1; j > 0; j >>= 1) {
+      for (int i = tid; i < P; i += kThreads) {
+        const int x = i ^ j;
+        if (x > i) {
+          const uint32_t a = keys[i], b = keys[x];
+          const bool up = (i & k) == 0;
+          if ((a > b) == up) {
+            keys[i] = b;
+            keys[x] = a;
+          }
+        }
+      }
+      __syncthreads();
+    }
+  for (int i = tid; i < ntk; i += kThreads) order[i] = keys[i] & 0xFFFFu;
 }
 
 // ---------------------------------------------------------------------------------------
@@ -124,7 +185,9 @@ __global__ __launch_bounds__(kMainThreads, 1) void bwd_dkdv_kernel(BwdArgs a) {
 
   const int BH = a.B * a.H;
   const int bh = blockIdx.x % BH;
-  const int jt = blockIdx.x / BH;       // key tile; small j (most causal work) first
+  // key tile: small j (most causal work) first, or the block-sparse order (most kept
+  // blocks first)
+  const int jt = a.order ? (int)a.order[blockIdx.x / BH] : (int)(blockIdx.x / BH);
   const int b = bh / a.H;
   const int k0 = jt * kBK;
   const int tid = threadIdx.x, w = wave_id(), l = tid & 63, h = l >> 5, kl = l & 31;
@@ -647,6 +710,12 @@ hipError_t launch_bwd(const BwdArgs& a, int d, hipStream_t stream, const KernelT
   else hipLaunchKernelGGL(bwd_pre_kernel<128>, gpre, block, 0, stream, a);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
+  if (a.order) {
+    hipLaunchKernelGGL(bwd_order_kernel, dim3(1), block, 0, stream, a.mask, a.nb, a.mb,
+                       (a.N + kBK - 1) / kBK, a.order);
+    e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
   if (tm.start) (void)hipEventRecord(tm.start, stream);
   if (d == 64) hipLaunchKernelGGL(bwd_dkdv_kernel<64>, gdkdv, bdkdv, 0, stream, a);
   else hipLaunchKernelGGL(bwd_dkdv_kernel<128>, gdkdv, bdkdv, 0, stream, a);

@@ -39,6 +39,7 @@ struct BwdArgs {
   void* dk;
   void* dv;
   float* dsum;            // workspace: D = rowsum(dO * O), [B,H,N]
+  uint32_t* order;        // workspace: dK/dV key tiles, most mask blocks first (block-sparse)
   const int32_t* kv_len;
   const uint8_t* mask;
   int B, H, N, mb, nb;
@@ -56,6 +57,9 @@ constexpr int kMaxTileList = 4096;
 // Smallest tile of the backward kernels (64 keys per dQ-kernel tile, 64 or 128 query
 // rows per dK/dV step); their block-sparse tile lists hold at most N / 64 entries.
 constexpr int kBwdMinTile = 64;
+// Keys per dK/dV workgroup, and the capacity of the block-sparse key-tile order.
+constexpr int kBwdKeyTile = 128;
+constexpr int kMaxKeyTiles = kMaxTileList * kBwdMinTile / kBwdKeyTile;
 
 // Optional events recorded around the dominant kernel of a call (may be nullptr).
 struct KernelTimer {

@@ -100,7 +100,7 @@ fa_status fa_fwd_blocksparse(fa_dtype dt, int B, int H, int N, int d,
 
 /*
  * Bytes of device workspace fa_bwd needs: the per-row D = rowsum(dO * O) (fp32 [B,H,N],
- * rounded up to 256 bytes). Linear in N (the backward keeps O(N) extra memory; cochat.ai
+ * rounded up to 256 bytes), then 8 KB for the block-sparse order of the key tiles. Linear in N (the backward keeps O(N) extra memory; cochat.ai
  * audit of "FlashAttention: Fast and Memory-Efficient Exact Attention with IO-Awareness",
  * quoted backward-pass memory claim). Returns 0 for non-positive or overflowing sizes.
  */
