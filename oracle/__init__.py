@@ -9,4 +9,5 @@ from .attention import (  # noqa: F401
     attention_backward,
     attention_forward,
     forward_rows,
+    kvcache_forward,
 )

@@ -33,6 +33,14 @@ What it computes, and where the pages define it
       block:    mask[i // mb][j // mb] != 0  (block-sparse, mb = mask block)
   Query rows are never masked; a row with no allowed key has O = 0,
   lse = -inf and zero gradient (the pages are silent; plainest reading).
+* Decode against a key/value cache — aiwiki "FlashAttention", section "Software
+  integration and limitations", lists inference with cached keys and values
+  among the interfaces but defines no semantics. Plainest reading, used by
+  ``kvcache_forward``: Nq new queries are the last Nq positions of a sequence
+  whose first L_b keys and values are in the cache (the new tokens' own keys
+  included); query i sits at position L_b - Nq + i and, when causal, attends
+  key j iff j <= L_b - Nq + i; always j < L_b. With Nq = Nk = L_b this is the
+  square causal mask above.
 * Backward — the pages say only that the backward is simplified analytically
   and recomputes the attention matrix from the saved statistics
   (cochat.ai audit of "FlashAttention: Fast and Memory-Efficient Exact
@@ -60,6 +68,7 @@ __all__ = [
     "forward_rows",
     "attention_forward",
     "attention_backward",
+    "kvcache_forward",
 ]
 
 _ROW_CHUNK = 256
@@ -191,3 +200,29 @@ def attention_backward(q, k, v, dout, scale: float, *, causal: bool = False, kv_
             dq[b, h, rows] = scale * (ds @ kc)                 # dQ = scale dS K
             dk[b, h, cols] += scale * (ds.T @ qr)              # dK = scale dS^T Q
     return dq, dk, dv
+
+
+def kvcache_forward(q, k, v, scale: float, *, causal: bool = False, kv_len=None):
+    """O, lse of Nq queries against a key/value cache (module docstring, "Decode").
+
+    q [B, H, Nq, d]; k, v [B, H, Nk, d]; kv_len None (L_b = Nk) or length-B integers,
+    clamped to [0, Nk]. Query i of batch b attends key j iff j < L_b and, if causal,
+    j <= L_b - Nq + i. Returns O [B, H, Nq, d] and lse [B, H, Nq] in fp64; a query with
+    no allowed key gets O = 0, lse = -inf.
+    """
+    q, k, v = _as_f64(q), _as_f64(k), _as_f64(v)
+    B, H, Nq, _ = q.shape
+    Nk = k.shape[2]
+    out = np.zeros(q.shape[:3] + (v.shape[3],), dtype=np.float64)
+    lse = np.full((B, H, Nq), -np.inf, dtype=np.float64)
+    lens = [Nk] * B if kv_len is None else [min(max(int(x), 0), Nk) for x in np.asarray(kv_len).reshape(-1)]
+    cols = np.arange(Nk, dtype=np.int64)
+    for b in range(B):
+        L = lens[b]
+        allow = np.broadcast_to(cols[None, :] < L, (Nq, Nk)).copy()
+        if causal:
+            pos = L - Nq + np.arange(Nq, dtype=np.int64)      # absolute query positions
+            allow &= cols[None, :] <= pos[:, None]
+        for h in range(H):
+            out[b, h], lse[b, h] = forward_rows(q[b, h], k[b, h], v[b, h], scale, allow)
+    return out, lse

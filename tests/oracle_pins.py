@@ -12,7 +12,8 @@ definition implies by other means:
     rows of P summing to one, exposed through V = I),
   * central finite differences of the oracle's own forward (backward pins),
   * an independent library routine (torch scaled_dot_product_attention in
-    float64 on the CPU, with autograd for the gradients),
+    float64 on the CPU, with autograd for the gradients), also for the decode
+    function on a bottom-right mask built here,
   * brute-force scalar loops on tiny inputs (math.fsum over Python floats).
 
 The allowed sets used by the expected values are built here, from the mask
@@ -342,6 +343,78 @@ def pin_block_rule_medium(orc):
     assert np.allclose(o[0], ro, atol=1e-11)
 
 
+# ----------------------------------------------------------------------------------
+# decode against a key/value cache (kvcache_forward)
+# ----------------------------------------------------------------------------------
+def _cache_allowed(Nq, Nk, L, causal):
+    """Scalar rule: query i (position L - Nq + i) may see key j < L, and j <= L - Nq + i
+    when causal."""
+    a = np.zeros((Nq, Nk), dtype=bool)
+    for i in range(Nq):
+        for j in range(Nk):
+            if j >= L:
+                continue
+            if causal and j > L - Nq + i:
+                continue
+            a[i, j] = True
+    return a
+
+
+def pin_kvcache_zero_query(orc):
+    """Q = 0: every allowed key has the same score, so O_i is the mean of the values the
+    query may see and lse_i = ln(count); with causal alignment query i sees the first
+    L - Nq + i + 1 keys (none when that is <= 0)."""
+    rng = RNG(31)
+    B, H, Nq, Nk, d = 3, 2, 5, 19, 4
+    lens = [19, 7, 3]
+    q = np.zeros((B, H, Nq, d))
+    k, v = rng.standard_normal((B, H, Nk, d)), rng.standard_normal((B, H, Nk, d))
+    for causal in (False, True):
+        o, lse = orc.kvcache_forward(q, k, v, 0.37, causal=causal, kv_len=lens)
+        for b, L in enumerate(lens):
+            for i in range(Nq):
+                n = min(L, L - Nq + i + 1) if causal else L
+                for h in range(H):
+                    if n <= 0:
+                        assert np.all(o[b, h, i] == 0) and np.isneginf(lse[b, h, i])
+                    else:
+                        assert np.allclose(o[b, h, i], v[b, h, :n].mean(axis=0), atol=1e-13)
+                        assert abs(lse[b, h, i] - math.log(n)) < 1e-13
+
+
+def pin_kvcache_single_query(orc):
+    """Nq = 1 (one decode step): the query sees every cached key, causal or not; checked
+    against a brute-force scalar softmax."""
+    rng = RNG(32)
+    Nk, d, L = 23, 3, 17
+    q, k, v = rng.standard_normal((1, 1, 1, d)), rng.standard_normal((1, 1, Nk, d)), rng.standard_normal((1, 1, Nk, d))
+    for causal in (False, True):
+        o, lse = orc.kvcache_forward(q, k, v, 0.8, causal=causal, kv_len=[L])
+        sc = [0.8 * math.fsum(q[0, 0, 0, t] * k[0, 0, j, t] for t in range(d)) for j in range(L)]
+        m = max(sc)
+        w = [math.exp(x - m) for x in sc]
+        z = math.fsum(w)
+        ref = [math.fsum(w[j] * v[0, 0, j, t] for j in range(L)) / z for t in range(d)]
+        assert np.allclose(o[0, 0, 0], ref, atol=1e-13)
+        assert abs(lse[0, 0, 0] - (m + math.log(z))) < 1e-12
+
+
+def pin_kvcache_library_sdpa(orc):
+    """Agreement with torch SDPA (float64) on the explicitly built bottom-right mask."""
+    rng = RNG(33)
+    B, H, Nq, Nk, d = 2, 2, 6, 40, 5
+    lens = [40, 29]
+    q = rng.standard_normal((B, H, Nq, d))
+    k, v = rng.standard_normal((B, H, Nk, d)), rng.standard_normal((B, H, Nk, d))
+    for causal in (False, True):
+        o, _ = orc.kvcache_forward(q, k, v, 0.45, causal=causal, kv_len=lens)
+        for b, L in enumerate(lens):
+            allow = _cache_allowed(Nq, Nk, L, causal)
+            live = allow.any(axis=1)
+            ro, _, _, _ = _sdpa(q[b][:, live], k[b], v[b], np.zeros_like(q[b][:, live]), 0.45, allow[live])
+            assert np.allclose(o[b][:, live], ro, atol=1e-12), (causal, b)
+
+
 ALL_PINS = [
     pin_zero_query,
     pin_one_hot_keys,
@@ -356,4 +429,7 @@ ALL_PINS = [
     pin_library_sdpa,
     pin_large_magnitude,
     pin_block_rule_medium,
+    pin_kvcache_zero_query,
+    pin_kvcache_single_query,
+    pin_kvcache_library_sdpa,
 ]

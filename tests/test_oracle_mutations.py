@@ -36,6 +36,12 @@ MUTANTS = {
     "bwd_dk_wrong_operand": ("dk[b, h, cols] += scale * (ds.T @ qr)", "dk[b, h, cols] += scale * (ds.T @ dor)"),
     "bwd_scale_dropped_in_recompute": ("s = np.where(a, scale * (qr @ kc.T), -np.inf)",
                                        "s = np.where(a, (qr @ kc.T), -np.inf)"),
+    "kvcache_causal_top_left": ("allow &= cols[None, :] <= pos[:, None]",
+                                "allow &= cols[None, :] <= np.arange(Nq)[:, None]"),
+    "kvcache_causal_off_by_one": ("pos = L - Nq + np.arange(Nq, dtype=np.int64)",
+                                  "pos = L - Nq - 1 + np.arange(Nq, dtype=np.int64)"),
+    "kvcache_length_ignored": ("allow = np.broadcast_to(cols[None, :] < L, (Nq, Nk)).copy()",
+                               "allow = np.ones((Nq, Nk), dtype=bool)"),
     "bwd_causal_ignored": ("allow = allowed_pairs(rows, k.shape[2], causal=causal,\n"
                            "                                  kv_len_b=None if lens is None else lens[b],\n"
                            "                                  block_mask=block_mask, mask_block=mask_block)\n"
