@@ -10,8 +10,14 @@ FLOP convention: forward 4*B*H*N^2*d, halved for causal; backward 2.5x the forwa
 The backward's dK/dV kernel performs four of the five products (2.0x the forward); its
 dQ kernel the fifth, plus a recomputation of two that the convention does not count.
 
+The key/value-cache forward (a few queries against a long cache, HBM-bound) is timed
+outside the step on its decode workloads and reported under "kvcache_decode": algorithmic
+bytes = every valid cached key and value read once plus Q and O, divided by the time of the
+whole call (key-split kernel and merge).
+
 Prints ONE JSON line (the metric line). `--report FILE` additionally times every
-workload (forward and backward separately) and writes a per-workload JSON.
+workload (forward and backward separately) and writes a per-workload JSON;
+`--decode-only` times only the decode workloads (for profiling them).
 """
 from __future__ import annotations
 
@@ -105,6 +111,8 @@ KERNEL_NAMES = {  # demangled kernel -> short name used by the bench and the tra
     "bwd_dkdv_kernel<64>": "bwd_dkdv_d64", "bwd_dkdv_kernel<128>": "bwd_dkdv_d128",
     "bwd_dq_kernel<64>": "bwd_dq_d64", "bwd_dq_kernel<128>": "bwd_dq_d128",
     "bwd_pre_kernel<64>": "bwd_pre_d64", "bwd_pre_kernel<128>": "bwd_pre_d128",
+    "kvc_split_kernel<64>": "kvc_split_d64", "kvc_split_kernel<128>": "kvc_split_d128",
+    "kvc_merge_kernel<64>": "kvc_merge_d64", "kvc_merge_kernel<128>": "kvc_merge_d128",
 }
 
 
@@ -244,6 +252,52 @@ def time_step(fa, runners, steps, warmup):
     return t0.elapsed_time(t1) / steps, clock
 
 
+def decode_bytes(w, kv_len) -> float:
+    """Algorithmic HBM bytes of one cache-forward call: every valid cached key and value
+    read once (bf16), the queries read and the outputs written once."""
+    lens = [w.Nk] * w.B if kv_len is None else [min(max(int(x), 0), w.Nk) for x in kv_len.tolist()]
+    return 2.0 * 2 * w.H * w.d * sum(lens) + 2.0 * 2 * w.B * w.H * w.Nq * w.d
+
+
+def report_decode(fa, w, dev, steps, warmup) -> dict:
+    """Cache-forward timing of one decode workload: whole call and key-split kernel."""
+    import torch
+    from exact_tiled_attention_32_amd import workloads
+    x = workloads.generate_decode(w)
+    q, k, v = (x[n].to(dev) for n in ("q", "k", "v"))
+    kv = None if x["kv_len"] is None else x["kv_len"].to(dev)
+    o = torch.empty_like(q)
+    lse = torch.empty(q.shape[:3], dtype=torch.float32, device=dev)
+    ws = torch.empty(fa.fa_fwd_kvcache_workspace_bytes(w.B, w.H, w.Nq, w.Nk, w.d), dtype=torch.uint8, device=dev)
+
+    def call():
+        fa.fa_fwd_kvcache(q, k, v, x["scale"], w.causal, kv, o=o, lse=lse, workspace=ws)
+
+    for _ in range(warmup):
+        call()
+    torch.cuda.synchronize()
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a.record()
+    for _ in range(steps):
+        call()
+    b.record()
+    torch.cuda.synchronize()
+    ms = a.elapsed_time(b) / steps
+    # second pass with the library's events around the key-split kernel (their records
+    # add gaps between launches, so the whole-call time above is taken without them)
+    clock = KernelClock()
+    for _ in range(steps):
+        clock.arm(fa, "split")
+        call()
+    torch.cuda.synchronize()
+    split_ms = clock.mean_ms("split")
+    nbytes = decode_bytes(w, x["kv_len"])
+    return {"shape": {"B": w.B, "H": w.H, "Nq": w.Nq, "Nk": w.Nk, "d": w.d}, "causal": w.causal,
+            "padding": w.padding, "algorithmic_bytes": nbytes, "ms": ms, "split_kernel_ms": split_ms,
+            "gbs": nbytes / ms / 1e6, "split_kernel_gbs": nbytes / split_ms / 1e6,
+            "frac_of_hbm_peak": nbytes / ms / 1e6 / PEAK_HBM_GBS}
+
+
 def report_all(fa, dev, path, steps=10, warmup=3):
     """Per-workload fwd / bwd timing (not the metric line)."""
     import torch
@@ -280,6 +334,11 @@ def report_all(fa, dev, path, steps=10, warmup=3):
         print(f"[report] {name}: " + json.dumps({k: v for k, v in res.items() if k in ("fwd", "bwd")}), flush=True)
         del r
         torch.cuda.empty_cache()
+    for name, w in workloads.DECODE_WORKLOADS.items():
+        out[name] = report_decode(fa, w, dev, steps, warmup)
+        print(f"[report] {name}: " + json.dumps({k: out[name][k] for k in ("ms", "split_kernel_ms", "gbs")}),
+              flush=True)
+        torch.cuda.empty_cache()
     with open(path, "w") as f:
         json.dump(out, f, indent=1)
 
@@ -293,6 +352,8 @@ def main():
     ap.add_argument("--report", default=None, help="also time every workload and write this JSON file")
     ap.add_argument("--summarize-pmc", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
                     help="write profiles/hbm_traffic.json from two rocprofv3 counter files and exit")
+    ap.add_argument("--decode-only", action="store_true",
+                    help="time only the key/value-cache forward on the decode workloads and print them")
     ap.add_argument("--pmc-pass", action="store_true",
                     help="for rocprofv3 --pmc: one 256 MiB device copy (counter calibration), then one "
                          "untimed pass of the step; prints no metric line")
@@ -303,7 +364,7 @@ def main():
         return
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only: this build has no multi-GPU path (got --gpus {args.gpus}); "
-              "attention heads are independent, see the sharding note in DESIGN.md", file=sys.stderr)
+              "attention heads are independent, so a multi-GPU run would split B*H across GPUs", file=sys.stderr)
         sys.exit(2)
 
     import torch
@@ -311,6 +372,10 @@ def main():
     from exact_tiled_attention_32_amd import workloads
     fa.load()
     dev = "cuda:0"
+    if args.decode_only:
+        for name, w in workloads.DECODE_WORKLOADS.items():
+            print(json.dumps({"workload": name, **report_decode(fa, w, dev, args.steps, args.warmup)}), flush=True)
+        return
     runners = [Runner(fa, workloads.WORKLOADS[n], dev) for n in STEP_WORKLOADS]
     if args.pmc_pass:
         src = torch.ones(CALIBRATION_BYTES // 4, dtype=torch.float32, device=dev)
@@ -349,6 +414,16 @@ def main():
             "config": {"workload": "long-sequence causal attention fwd+bwd, B=1 H=16 N=16384, d=64 and d=128",
                        "B": 1, "H": 16, "N": 16384, "d": [64, 128], "causal": True},
             "frac_of_peak": round(value / PEAK_BF16_TFLOPS, 4), "per_head_dim": per, "roofline": roofline}
+    # the key/value-cache forward (HBM-bound) on its decode workloads, outside the step
+    dec = {}
+    for name, w in workloads.DECODE_WORKLOADS.items():
+        r = report_decode(fa, w, dev, 20, 5)
+        dec[name] = {"ms": round(r["ms"], 4), "split_kernel_ms": round(r["split_kernel_ms"], 4),
+                     "gbs": round(r["gbs"], 1), "frac_of_hbm_peak": round(r["frac_of_hbm_peak"], 4),
+                     "algorithmic_mb": round(r["algorithmic_bytes"] / 1e6, 1)}
+        del r
+        torch.cuda.empty_cache()
+    line["kvcache_decode"] = dec
     if args.report:
         report_all(fa, dev, args.report)
     if not args.no_cpu_baseline:

@@ -10,6 +10,9 @@ Entry points (same names as the C ABI):
     fa_fwd(q, k, v, scale, causal=False, kv_len=None, o=None, lse=None) -> (o, lse)
     fa_fwd_blocksparse(q, k, v, scale, block_mask, mask_block=128, causal=False,
                        kv_len=None, o=None, lse=None) -> (o, lse)
+    fa_fwd_kvcache_workspace_bytes(B, H, Nq, Nk, d) -> int
+    fa_fwd_kvcache(q, k_cache, v_cache, scale, causal=False, kv_len=None, o=None, lse=None,
+                   workspace=None) -> (o, lse)
     fa_bwd_workspace_bytes(B, H, N, d) -> int
     fa_bwd(q, k, v, o, dout, lse, scale, causal=False, kv_len=None, block_mask=None,
            mask_block=128, dq=None, dk=None, dv=None, workspace=None) -> (dq, dk, dv)
@@ -25,13 +28,14 @@ import torch
 __all__ = [
     "FA_F32", "FA_BF16", "FA_OK", "FA_ERR_INVALID", "FA_ERR_UNSUPPORTED", "FA_ERR_HIP",
     "FAError", "lib_path", "load", "fa_fwd", "fa_fwd_blocksparse", "fa_bwd",
-    "fa_bwd_workspace_bytes", "fa_time_next_kernel", "fa_status_string", "EXPORTED_SYMBOLS",
+    "fa_bwd_workspace_bytes", "fa_fwd_kvcache", "fa_fwd_kvcache_workspace_bytes", "fa_time_next_kernel", "fa_status_string", "EXPORTED_SYMBOLS",
 ]
 
 FA_F32, FA_BF16 = 0, 1
 FA_OK, FA_ERR_INVALID, FA_ERR_UNSUPPORTED, FA_ERR_HIP = 0, 1, 2, 3
 
 EXPORTED_SYMBOLS = ("fa_fwd", "fa_fwd_blocksparse", "fa_bwd_workspace_bytes", "fa_bwd",
+                    "fa_fwd_kvcache_workspace_bytes", "fa_fwd_kvcache",
                     "fa_time_next_kernel", "fa_status_string", "fa_last_error")
 
 _LIB = None
@@ -65,6 +69,10 @@ def load() -> ctypes.CDLL:
     lib.fa_bwd_workspace_bytes.restype = S
     lib.fa_bwd.argtypes = [I, I, I, I, I, P, P, P, P, P, P, P, P, P, F, I, P, P, I, P, S, P]
     lib.fa_bwd.restype = I
+    lib.fa_fwd_kvcache_workspace_bytes.argtypes = [I, I, I, I, I]
+    lib.fa_fwd_kvcache_workspace_bytes.restype = S
+    lib.fa_fwd_kvcache.argtypes = [I, I, I, I, I, I, P, P, P, P, P, F, I, P, P, S, P]
+    lib.fa_fwd_kvcache.restype = I
     lib.fa_status_string.argtypes = [I]
     lib.fa_status_string.restype = ctypes.c_char_p
     lib.fa_time_next_kernel.argtypes = [P, P]
@@ -209,3 +217,37 @@ def fa_bwd(q, k, v, o, dout, lse, scale: float, causal: bool = False, kv_len=Non
                       _ptr(m), int(mask_block), _ptr(workspace), int(workspace.numel()),
                       _stream(q.device)))
     return dq, dk, dv
+
+
+def fa_fwd_kvcache_workspace_bytes(B: int, H: int, Nq: int, Nk: int, d: int) -> int:
+    return int(load().fa_fwd_kvcache_workspace_bytes(int(B), int(H), int(Nq), int(Nk), int(d)))
+
+
+def fa_fwd_kvcache(q, k_cache, v_cache, scale: float, causal: bool = False, kv_len=None, o=None,
+                   lse=None, workspace=None):
+    """Queries [B, H, Nq, d] against a key/value cache [B, H, Nk, d]; see ``fa_fwd_kvcache``
+    in include/fa.h. ``workspace`` is a uint8 device tensor."""
+    lib = load()
+    q = _dev_tensor(q, "q")
+    if q.dim() != 4:
+        raise ValueError("q must be [B, H, Nq, d]")
+    k_cache = _dev_tensor(k_cache, "k_cache")
+    _dev_tensor(v_cache, "v_cache", k_cache)
+    B, H, Nq, d = q.shape
+    Nk = k_cache.shape[2]
+    if (k_cache.dim() != 4 or k_cache.shape[0] != B or k_cache.shape[1] != H or k_cache.shape[3] != d
+            or k_cache.dtype != q.dtype or k_cache.device != q.device):
+        raise ValueError("k_cache and v_cache must be [B, H, Nk, d] of q's dtype and device")
+    o = torch.empty_like(q) if o is None else _dev_tensor(o, "o", q)
+    if lse is None:
+        lse = torch.empty((B, H, Nq), dtype=torch.float32, device=q.device)
+    elif lse.shape != (B, H, Nq) or lse.dtype != torch.float32 or not lse.is_contiguous():
+        raise ValueError("lse must be a contiguous float32 tensor [B, H, Nq]")
+    kv = _kv_len(kv_len, q)
+    if workspace is None:
+        need = fa_fwd_kvcache_workspace_bytes(B, H, Nq, Nk, d)
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=q.device)
+    _check(lib.fa_fwd_kvcache(_dtype_code(q), B, H, Nq, Nk, d, _ptr(q), _ptr(k_cache), _ptr(v_cache),
+                              _ptr(o), _ptr(lse), float(scale), int(bool(causal)), _ptr(kv),
+                              _ptr(workspace), int(workspace.numel()), _stream(q.device)))
+    return o, lse

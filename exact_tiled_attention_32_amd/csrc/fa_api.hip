@@ -110,6 +110,20 @@ fa_status fwd_impl(fa_dtype dt, int B, int H, int N, int d, const void* q, const
   return FA_OK;
 }
 
+// Workspace layout of the key/value-cache forward: part_u, part_m, part_l (each 256-byte
+// aligned). Returns 0 for invalid sizes.
+size_t kvcache_ws(int B, int H, int Nq, int Nk, int d, size_t* off_m, size_t* off_l) {
+  if (B <= 0 || H <= 0 || Nq <= 0 || Nk <= 0 || d <= 0) return 0;
+  if ((long double)B * H * (long double)(Nq > Nk ? Nq : Nk) * d * 4 > (long double)(1ull << 62)) return 0;
+  int chunk = 0, units = 0;
+  fa::kvcache_split_plan(B, H, Nk, d, &chunk, &units);
+  const size_t rows = (size_t)B * H * units * Nq;
+  const size_t su = align256(rows * d * sizeof(float)), sm = align256(rows * sizeof(float));
+  if (off_m) *off_m = su;
+  if (off_l) *off_l = su + sm;
+  return su + 2 * sm;
+}
+
 }  // namespace
 
 extern "C" {
@@ -185,6 +199,64 @@ fa_status fa_bwd(fa_dtype dt, int B, int H, int N, int d, const void* q, const v
   a.c2s = scale * 1.4426950408889634f;
   hipError_t e = fa::launch_bwd(a, d, stream, take_timer());
   if (e != hipSuccess) return fail(FA_ERR_HIP, "backward launch failed: %s", hipGetErrorString(e));
+  return FA_OK;
+}
+
+size_t fa_fwd_kvcache_workspace_bytes(int B, int H, int Nq, int Nk, int d) {
+  return kvcache_ws(B, H, Nq, Nk, d, nullptr, nullptr);
+}
+
+fa_status fa_fwd_kvcache(fa_dtype dt, int B, int H, int Nq, int Nk, int d, const void* q,
+                         const void* k_cache, const void* v_cache, void* o, float* lse,
+                         float scale, int causal, const int32_t* kv_len, void* workspace,
+                         size_t workspace_bytes, hipStream_t stream) {
+  if (dt != FA_F32 && dt != FA_BF16) return fail(FA_ERR_INVALID, "unknown dtype %d", (int)dt);
+  if (B <= 0 || H <= 0 || Nq <= 0 || Nk <= 0 || d <= 0)
+    return fail(FA_ERR_INVALID, "sizes must be positive (B=%d H=%d Nq=%d Nk=%d d=%d)", B, H, Nq, Nk, d);
+  if (!std::isfinite(scale)) return fail(FA_ERR_INVALID, "scale must be finite");
+  size_t off_m = 0, off_l = 0;
+  const size_t need = kvcache_ws(B, H, Nq, Nk, d, &off_m, &off_l);
+  if (need == 0) return fail(FA_ERR_INVALID, "tensor size overflows");
+  if (dt != FA_BF16) return fail(FA_ERR_UNSUPPORTED, "key/value-cache forward is built for bf16 only");
+  if (d != 64 && d != 128) return fail(FA_ERR_UNSUPPORTED, "head dimension %d not built (64, 128)", d);
+  if (Nq > fa::kDecMaxQueries)
+    return fail(FA_ERR_UNSUPPORTED, "at most %d queries per (b, h) (got Nq=%d)", fa::kDecMaxQueries, Nq);
+  FA_TRY(check_tensor(q, "q", 16));
+  FA_TRY(check_tensor(k_cache, "k_cache", 16));
+  FA_TRY(check_tensor(v_cache, "v_cache", 16));
+  FA_TRY(check_tensor(o, "o", 16));
+  FA_TRY(check_tensor(lse, "lse", 4));
+  if (kv_len && !aligned(kv_len, 4)) return fail(FA_ERR_INVALID, "kv_len is not 4-byte aligned");
+  if (workspace == nullptr) return fail(FA_ERR_INVALID, "workspace is NULL");
+  if (!aligned(workspace, 256)) return fail(FA_ERR_INVALID, "workspace is not 256-byte aligned");
+  if (workspace_bytes < need)
+    return fail(FA_ERR_INVALID, "workspace too small: %zu bytes given, %zu needed", workspace_bytes, need);
+
+  fa::DecArgs a{};
+  fa::kvcache_split_plan(B, H, Nk, d, &a.chunk, &a.units);
+  if ((long long)a.units / fa::kvcache_split_waves(d) * B * H > 0x7fffffffLL || (long long)B * H * Nq > 0x7fffffffLL)
+    return fail(FA_ERR_INVALID, "grid too large (B*H*units/waves or B*H*Nq > 2^31-1)");
+  a.q = q;
+  a.k = k_cache;
+  a.v = v_cache;
+  a.o = o;
+  a.lse = lse;
+  a.kv_len = kv_len;
+  char* ws = reinterpret_cast<char*>(workspace);
+  a.part_u = reinterpret_cast<float*>(ws);
+  a.part_m = reinterpret_cast<float*>(ws + off_m);
+  a.part_l = reinterpret_cast<float*>(ws + off_l);
+  a.B = B;
+  a.H = H;
+  a.Nq = Nq;
+  a.Nk = Nk;
+  a.causal = causal ? 1 : 0;
+  const float sabs = std::fabs(scale);
+  a.qmul = scale > 0.f ? 1.f : (scale < 0.f ? -1.f : 0.f);
+  a.c2 = scale != 0.f ? sabs * 1.4426950408889634f : 1.4426950408889634f;
+  a.sc_abs = sabs;
+  hipError_t e = fa::launch_kvcache(a, d, stream, take_timer());
+  if (e != hipSuccess) return fail(FA_ERR_HIP, "key/value-cache forward launch failed: %s", hipGetErrorString(e));
   return FA_OK;
 }
 

@@ -48,6 +48,31 @@ struct BwdArgs {
   float c2s;              // scale * log2(e)
 };
 
+// Key/value-cache forward arguments, already validated by the host layer.
+struct DecArgs {
+  const void* q;          // [B, H, Nq, d]
+  const void* k;          // [B, H, Nk, d]
+  const void* v;
+  void* o;                // [B, H, Nq, d]
+  float* lse;             // [B, H, Nq]
+  const int32_t* kv_len;  // nullptr: every cached key valid
+  float* part_u;          // workspace: [B, H, units, Nq, d] unnormalised partial outputs
+  float* part_m;          // workspace: [B, H, units, Nq] partial maxima (raw q.k units)
+  float* part_l;          // workspace: [B, H, units, Nq] partial sums
+  int B, H, Nq, Nk;
+  int chunk;              // keys per unit (a multiple of the 32-key tile)
+  int units;              // units per (b, h), a multiple of the waves per workgroup
+  int causal;
+  float c2, sc_abs, qmul; // as in FwdArgs
+};
+
+constexpr int kDecMaxQueries = 32;
+
+// Split of the cached keys into units: chunk keys each, units per (b, h).
+void kvcache_split_plan(int B, int H, int Nk, int d, int* chunk, int* units);
+// Waves (units) per workgroup of the key-split kernel for head dimension d.
+int kvcache_split_waves(int d);
+
 constexpr int kFwdRowsPerWG = 128;       // fp32 forward; also the mask-block granularity
 constexpr int kFwdRowsPerWGBF16 = 128;   // bf16 forward: 4 waves x 32 query rows
 // Keys per tile of the bf16 forward (its block-sparse tile list holds N / that).
@@ -69,5 +94,6 @@ struct KernelTimer {
 
 hipError_t launch_fwd(const FwdArgs& a, fa_dtype dt, int d, hipStream_t stream, const KernelTimer& tm);
 hipError_t launch_bwd(const BwdArgs& a, int d, hipStream_t stream, const KernelTimer& tm);
+hipError_t launch_kvcache(const DecArgs& a, int d, hipStream_t stream, const KernelTimer& tm);
 
 }  // namespace fa

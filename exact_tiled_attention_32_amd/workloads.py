@@ -10,7 +10,9 @@ The workloads stand in, by shape only, for the pages' benchmarks (BERT-large
 at sequence length 512, GPT-2 at 1K, Long Range Arena at 16K and 64K); no
 dataset or trained weight is involved.
 
-Generation order per workload: Q, K, V, dO, then the key-padding lengths.
+Generation order per workload: Q, K, V, dO, then the key-padding lengths. Decode
+workloads (a few queries against a key/value cache): Q [B, H, Nq, d], then the cache's
+K and V [B, H, Nk, d], then the cache lengths.
 """
 from __future__ import annotations
 
@@ -19,7 +21,8 @@ from dataclasses import dataclass, field
 
 import torch
 
-__all__ = ["Workload", "WORKLOADS", "generate", "sparse_block_rule", "make_case"]
+__all__ = ["Workload", "WORKLOADS", "generate", "sparse_block_rule", "make_case",
+           "DecodeWorkload", "DECODE_WORKLOADS", "generate_decode", "make_decode_case"]
 
 
 @dataclass(frozen=True)
@@ -118,3 +121,57 @@ def make_case(B: int, H: int, N: int, d: int, *, dtype: str = "bf16", seed: int 
     bm = None if block_mask is None else torch.as_tensor(block_mask, dtype=torch.uint8)
     return {"q": q, "k": k, "v": v, "do": do, "kv_len": kl, "block_mask": bm,
             "scale": 1.0 / math.sqrt(d), "causal": causal, "mask_block": mask_block}
+
+
+@dataclass(frozen=True)
+class DecodeWorkload:
+    """Nq new queries per (b, h) against a cache of Nk keys and values."""
+    name: str
+    B: int
+    H: int
+    Nq: int
+    Nk: int
+    d: int
+    seed: int
+    causal: bool = False
+    padding: bool = False  # cache lengths L_b ~ U{Nk/2 .. Nk} inclusive
+    description: str = field(default="", compare=False)
+
+    @property
+    def scale(self) -> float:
+        return 1.0 / math.sqrt(self.d)
+
+
+DECODE_WORKLOADS = {
+    "decode_q1_d128": DecodeWorkload(
+        "decode_q1_d128", 8, 16, 1, 16384, 128, 1101, padding=True,
+        description="single-query decode, bf16, B=8 H=16 Nq=1 against a 16K-entry cache, "
+                    "d=128, cache lengths uniform in [8192, 16384]"),
+    "decode_q16_causal_d64": DecodeWorkload(
+        "decode_q16_causal_d64", 4, 32, 16, 32768, 64, 1102, causal=True, padding=True,
+        description="16 new queries per head (causal among themselves), bf16, B=4 H=32 "
+                    "against a 32K-entry cache, d=64, cache lengths uniform in [16384, 32768]"),
+}
+
+
+def generate_decode(w: DecodeWorkload) -> dict:
+    """CPU bf16 tensors q [B,H,Nq,d], k, v [B,H,Nk,d] and kv_len (int32 or None)."""
+    gen = torch.Generator("cpu").manual_seed(w.seed)
+    q = _draw(gen, (w.B, w.H, w.Nq, w.d), "bf16")
+    k = _draw(gen, (w.B, w.H, w.Nk, w.d), "bf16")
+    v = _draw(gen, (w.B, w.H, w.Nk, w.d), "bf16")
+    kv_len = None
+    if w.padding:
+        kv_len = torch.randint(w.Nk // 2, w.Nk + 1, (w.B,), generator=gen, dtype=torch.int64).to(torch.int32)
+    return {"q": q, "k": k, "v": v, "kv_len": kv_len, "scale": w.scale, "causal": w.causal}
+
+
+def make_decode_case(B: int, H: int, Nq: int, Nk: int, d: int, *, seed: int = 0, causal: bool = False,
+                     kv_len=None, q_magnitude: float = 1.0) -> dict:
+    """A small seeded bf16 decode case; ``kv_len`` may be a list of ints."""
+    gen = torch.Generator("cpu").manual_seed(seed)
+    q = (torch.randn((B, H, Nq, d), generator=gen) * q_magnitude).to(torch.bfloat16)
+    k = torch.randn((B, H, Nk, d), generator=gen).to(torch.bfloat16)
+    v = torch.randn((B, H, Nk, d), generator=gen).to(torch.bfloat16)
+    kl = None if kv_len is None else torch.tensor(kv_len, dtype=torch.int32)
+    return {"q": q, "k": k, "v": v, "kv_len": kl, "scale": 1.0 / math.sqrt(d), "causal": causal}

@@ -36,7 +36,8 @@
  *     allocates no device memory and keeps no per-call state: calls are re-entrant and
  *     thread-safe. Faults during execution surface at the caller's stream synchronisation.
  *   - bf16 (FA_BF16): d in {64, 128}, forward and backward. fp32 (FA_F32): d in {64, 128},
- *     forward only.
+ *     forward only. The key/value-cache forward takes its own query and key counts
+ *     (Nq, Nk) in place of N; its tensors follow the same layout.
  */
 #ifndef EXACT_TILED_ATTENTION_FA_H
 #define EXACT_TILED_ATTENTION_FA_H
@@ -131,11 +132,49 @@ fa_status fa_bwd(fa_dtype dt, int B, int H, int N, int d,
                  hipStream_t stream);
 
 /*
- * Measurement hook. When both events are non-NULL, the next fa_fwd, fa_fwd_blocksparse or
- * fa_bwd call on the calling thread that passes validation records `start` on its stream
- * immediately before launching its dominant kernel (the forward kernel, or the backward
- * main kernel) and `stop` immediately after it, then forgets both events. Passing NULL
- * clears a pending request. The events are owned by the caller.
+ * Bytes of device workspace fa_fwd_kvcache needs for the partial results of its key split:
+ * B*H*units*Nq*(4d + 8) bytes (three regions, each rounded up to 256 bytes), where units
+ * is the number of key ranges each (b, h) is split into, chosen from B, H and Nk (about
+ * 8192 ranges in all, at least 32 keys each). Returns 0 for non-positive or overflowing
+ * sizes.
+ */
+size_t fa_fwd_kvcache_workspace_bytes(int B, int H, int Nq, int Nk, int d);
+
+/*
+ * Forward of a few new queries against a key/value cache (inference decoding; aiwiki
+ * "FlashAttention", section "Software integration and limitations", lists cached keys and
+ * values among the supported interfaces). bf16 only, d in {64, 128}, 1 <= Nq <= 32.
+ *   q                 [B,H,Nq,d]: the queries of the last Nq positions of each sequence
+ *   k_cache, v_cache  [B,H,Nk,d]: cached keys and values; positions >= the valid length
+ *                     are never read into the result (their contents do not matter)
+ *   o                 output [B,H,Nq,d]
+ *   lse               output [B,H,Nq] fp32, natural log
+ *   kv_len            NULL (all Nk cached positions valid) or device int32 [B]: valid
+ *                     length L_b of each sequence, clamped to [0, Nk]
+ *   causal            nonzero: query i (0-based among the Nq) sits at position
+ *                     L_b - Nq + i and attends keys j <= L_b - Nq + i (the mask aligned to
+ *                     the bottom-right corner); zero: it attends every key j < L_b
+ *   workspace         device memory of at least fa_fwd_kvcache_workspace_bytes(B,H,Nq,Nk,d)
+ *                     bytes, 256-byte aligned, owned by the caller, overwritten
+ * Each (b, h) splits its keys into ranges processed in parallel, each with the online
+ * softmax of aiwiki "FlashAttention", section "Tiling and online normalization"; a second
+ * kernel merges the ranges' (max, sum, unnormalised output) with the same update. A query
+ * with no allowed key yields O = 0 and lse = -inf.
+ */
+fa_status fa_fwd_kvcache(fa_dtype dt, int B, int H, int Nq, int Nk, int d,
+                         const void* q, const void* k_cache, const void* v_cache,
+                         void* o, float* lse,
+                         float scale, int causal, const int32_t* kv_len,
+                         void* workspace, size_t workspace_bytes,
+                         hipStream_t stream);
+
+/*
+ * Measurement hook. When both events are non-NULL, the next fa_fwd, fa_fwd_blocksparse,
+ * fa_fwd_kvcache or fa_bwd call on the calling thread that passes validation records
+ * `start` on its stream immediately before launching its dominant kernel (the forward
+ * kernel, the key-split kernel of the cache forward, or the backward main kernel) and
+ * `stop` immediately after it, then forgets both events. Passing NULL clears a pending
+ * request. The events are owned by the caller.
  */
 void fa_time_next_kernel(hipEvent_t start, hipEvent_t stop);
 

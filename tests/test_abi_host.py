@@ -139,3 +139,55 @@ def test_binding_fails_loudly_without_library(monkeypatch, tmp_path):
     monkeypatch.setattr(fa, "lib_path", lambda: str(tmp_path / "missing.so"))
     with pytest.raises(RuntimeError, match="missing"):
         fa.load()
+
+
+def _kvcache_units(B, H, Nk, d):
+    # key ranges per (b, h): about 4096 ranges in all, each a multiple of 32 keys, the
+    # count per (b, h) rounded up to whole workgroups (4 ranges at d=64, 3 at d=128)
+    W = 4 if d == 64 else 3
+    chunk = max(32, -(-(-(-(B * H * Nk) // 4096)) // 32) * 32)
+    units = -(-Nk // chunk)
+    return chunk, -(-units // W) * W
+
+
+@pytest.mark.parametrize("B,H,Nq,Nk,d", [(1, 1, 1, 1, 64), (8, 16, 1, 16384, 128), (4, 32, 16, 32768, 64),
+                                         (2, 3, 5, 70000, 128), (1, 1, 32, 1 << 24, 64)])
+def test_kvcache_workspace_bytes(lib, B, H, Nq, Nk, d):
+    al = lambda x: (x + 255) // 256 * 256
+    chunk, units = _kvcache_units(B, H, Nk, d)
+    assert chunk * units >= Nk and chunk % 32 == 0
+    # the partial results stay bounded: at most ~4096 ranges plus rounding per (b, h)
+    assert B * H * units <= 4096 + 4 * B * H
+    rows = B * H * units * Nq
+    assert fa.fa_fwd_kvcache_workspace_bytes(B, H, Nq, Nk, d) == al(rows * d * 4) + 2 * al(rows * 4)
+    assert fa.fa_fwd_kvcache_workspace_bytes(B, H, 0, Nk, d) == 0
+    assert fa.fa_fwd_kvcache_workspace_bytes(B, H, Nq, -1, d) == 0
+
+
+def kvc(lib, dt=fa.FA_BF16, B=1, H=1, Nq=1, Nk=256, d=64, q=P, k=P, v=P, o=P, lse=P, scale=0.125,
+        kv_len=None, ws=P, ws_bytes=None):
+    c = ctypes.c_void_p
+    need = fa.fa_fwd_kvcache_workspace_bytes(B, H, Nq, Nk, d) if ws_bytes is None else ws_bytes
+    return lib.fa_fwd_kvcache(dt, B, H, Nq, Nk, d, c(q), c(k), c(v), c(o), c(lse), scale, 1,
+                              None if kv_len is None else c(kv_len), None if ws is None else c(ws), need, None)
+
+
+@pytest.mark.parametrize("kwargs, status", [
+    (dict(q=0), fa.FA_ERR_INVALID),
+    (dict(k=P + 8), fa.FA_ERR_INVALID),
+    (dict(lse=P + 2), fa.FA_ERR_INVALID),
+    (dict(kv_len=P + 2), fa.FA_ERR_INVALID),
+    (dict(Nq=0), fa.FA_ERR_INVALID),
+    (dict(Nk=0), fa.FA_ERR_INVALID),
+    (dict(scale=float("nan")), fa.FA_ERR_INVALID),
+    (dict(ws=None), fa.FA_ERR_INVALID),
+    (dict(ws=P + 64), fa.FA_ERR_INVALID),
+    (dict(ws_bytes=1000), fa.FA_ERR_INVALID),
+    (dict(dt=7), fa.FA_ERR_INVALID),
+    (dict(dt=fa.FA_F32), fa.FA_ERR_UNSUPPORTED),
+    (dict(d=96), fa.FA_ERR_UNSUPPORTED),
+    (dict(Nq=33), fa.FA_ERR_UNSUPPORTED),
+])
+def test_kvcache_rejects(lib, kwargs, status):
+    assert kvc(lib, **kwargs) == status
+    assert lib.fa_last_error().decode()

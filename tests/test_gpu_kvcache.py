@@ -1,0 +1,117 @@
+"""Parity of the key/value-cache forward (HIP, through the C ABI) with the fp64 oracle.
+
+Bars (tests/parity.py): bf16 O within 1e-2 after discounting the output's own rounding,
+lse within 1e-3, rows without an allowed key O = 0 and lse = -inf. The sweep spans one to
+several key ranges per (b, h), ragged cache lengths (including 0 and lengths shorter than
+the number of queries) and both mask modes; the named decode workloads run at their full
+sizes and are compared in full (the oracle handles a few queries per head quickly).
+"""
+import sys
+import zlib
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from exact_tiled_attention_32_amd import workloads
+from tests import parity
+
+pytestmark = pytest.mark.gpu
+
+DEV = "cuda:0"
+
+
+def note(msg):
+    print(msg, flush=True)
+    sys.stdout.flush()
+
+
+def gpu_decode(fa, case, workspace=None):
+    q, k, v = (case[n].to(DEV) for n in ("q", "k", "v"))
+    kv = None if case["kv_len"] is None else case["kv_len"].to(DEV)
+    o, lse = fa.fa_fwd_kvcache(q, k, v, case["scale"], case["causal"], kv, workspace=workspace)
+    torch.cuda.synchronize()
+    return o.cpu(), lse.cpu()
+
+
+def check(fa, case, label):
+    note(f"[kvcache] {label}")
+    o, lse = gpu_decode(fa, case)
+    kv = None if case["kv_len"] is None else case["kv_len"].tolist()
+    ref_o, ref_lse = oracle.kvcache_forward(case["q"], case["k"], case["v"], case["scale"],
+                                            causal=case["causal"], kv_len=kv)
+    parity.check_o(o, ref_o, "bf16", f"{label} O")
+    parity.check_lse(lse, ref_lse, f"{label} lse")
+    empty = np.isneginf(ref_lse)
+    if empty.any():
+        assert float(np.abs(o.float().numpy()[empty]).max()) == 0.0, f"{label}: empty rows must be 0"
+    return o, lse
+
+
+SWEEP = []
+for d in (64, 128):
+    for Nq in (1, 4, 16, 32):
+        for Nk, kv in ((1, None), (31, None), (100, [100, 0]), (777, [3, 777]), (2500, [2500, 1234])):
+            for causal in (False, True):
+                if Nq in (4, 32) and Nk in (1, 31):
+                    continue
+                SWEEP.append((f"d{d}_q{Nq}_k{Nk}_{'causal' if causal else 'full'}", d, Nq, Nk, kv, causal))
+
+
+@pytest.mark.parametrize("name,d,Nq,Nk,kv,causal", SWEEP, ids=[c[0] for c in SWEEP])
+def test_sweep(gpu_lib, name, d, Nq, Nk, kv, causal):
+    B = 1 if kv is None else len(kv)
+    case = workloads.make_decode_case(B, 2, Nq, Nk, d, seed=zlib.crc32(name.encode()) % 10007, causal=causal, kv_len=kv)
+    check(gpu_lib, case, name)
+
+
+@pytest.mark.parametrize("d", [64, 128])
+def test_many_key_ranges(gpu_lib, d):
+    # few heads and a long cache: each (b, h) is split into many ranges, so the merge
+    # combines many partial results, some of them empty (the second sequence is short)
+    case = workloads.make_decode_case(2, 3, 5, 70000, d, seed=77 + d, causal=True, kv_len=[70000, 12345])
+    check(gpu_lib, case, f"many_ranges_d{d}")
+
+
+@pytest.mark.parametrize("d", [64, 128])
+def test_large_score_magnitude(gpu_lib, d):
+    # scores with a standard deviation of ~30: ranges reach very different maxima, so the
+    # merge weights span many orders of magnitude and the lazy rescale triggers often
+    case = workloads.make_decode_case(2, 2, 8, 9000, d, seed=5 + d, causal=True, kv_len=[9000, 4000],
+                                      q_magnitude=30.0)
+    check(gpu_lib, case, f"large_scores_d{d}")
+
+
+def test_scale_sign_and_zero(gpu_lib):
+    for scale in (-0.2, 0.0):
+        case = workloads.make_decode_case(2, 2, 3, 600, 64, seed=11, causal=True, kv_len=[600, 2])
+        case["scale"] = scale
+        check(gpu_lib, case, f"scale={scale}")
+
+
+def test_query_count_beyond_cache(gpu_lib):
+    # causal with Nq > L: the first Nq - L queries precede the cache and see nothing
+    case = workloads.make_decode_case(3, 2, 16, 40, 128, seed=3, causal=True, kv_len=[5, 0, 40])
+    check(gpu_lib, case, "nq_beyond_cache")
+
+
+def test_deterministic_and_workspace_reuse(gpu_lib):
+    fa = gpu_lib
+    big = workloads.make_decode_case(2, 4, 7, 20000, 128, seed=21, causal=True, kv_len=[20000, 9000])
+    small = workloads.make_decode_case(1, 2, 3, 500, 128, seed=22, causal=False, kv_len=[450])
+    need = fa.fa_fwd_kvcache_workspace_bytes(2, 4, 7, 20000, 128)
+    assert need >= fa.fa_fwd_kvcache_workspace_bytes(1, 2, 3, 500, 128)
+    ws = torch.full((need,), 0xFF, dtype=torch.uint8, device=DEV)  # stale contents must not matter
+    o1, l1 = gpu_decode(fa, big, ws)
+    o2, l2 = gpu_decode(fa, small, ws)
+    o3, l3 = gpu_decode(fa, big, ws)
+    assert torch.equal(o1, o3) and torch.equal(l1, l3)
+    o4, l4 = gpu_decode(fa, small)
+    assert torch.equal(o2, o4) and torch.equal(l2, l4)
+
+
+@pytest.mark.parametrize("name", list(workloads.DECODE_WORKLOADS))
+def test_decode_workload_full(gpu_lib, name):
+    w = workloads.DECODE_WORKLOADS[name]
+    check(gpu_lib, workloads.generate_decode(w), name)
