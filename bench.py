@@ -134,10 +134,14 @@ def summarize_pmc(fetch_csv: str, write_csv: str, out_path: str) -> dict:
     fetch, write = load(fetch_csv, "FETCH_SIZE"), load(write_csv, "WRITE_SIZE")
 
     def calib(per):
-        vals = [v for (d, n), v in per.items() if "copyBuffer" in n]
+        # the calibration copy is the last device copy before the first library kernel
+        # (the uploads of the inputs come before it)
+        items = sorted(per.items())
+        first = next((i for i, ((d, n), v) in enumerate(items) if "fa::" in n), len(items))
+        vals = [v for (d, n), v in items[:first] if "copyBuffer" in n]
         if not vals:
             raise RuntimeError("calibration copy not found in the counter file")
-        return CALIBRATION_BYTES / vals[0]
+        return CALIBRATION_BYTES / vals[-1]
 
     ff, fw = calib(fetch), calib(write)
 
@@ -163,6 +167,125 @@ def summarize_pmc(fetch_csv: str, write_csv: str, out_path: str) -> dict:
     with open(out_path, "w") as f:
         json.dump(res, f, indent=1)
     return res
+
+
+COUNTER_SETS = {  # one rocprofv3 --pmc pass each (at most 8 SQ, 4 TCC and 2 GRBM counters)
+    "sq": "SQ_BUSY_CU_CYCLES SQ_VALU_MFMA_BUSY_CYCLES SQ_INSTS_MFMA SQ_INSTS_LDS SQ_LDS_BANK_CONFLICT "
+          "SQ_LDS_IDX_ACTIVE SQ_WAVE_CYCLES GRBM_GUI_ACTIVE",
+    "fetch": "FETCH_SIZE",
+    "write": "WRITE_SIZE",
+}
+
+
+def counter_sequence(workloads):
+    """(workload, kernel) of every library dispatch of `--counter-pass`, in launch order."""
+    seq = []
+    for _ in range(2):
+        for name, w in workloads.WORKLOADS.items():
+            seq.append((name, "fwd_f32_kernel<64>" if w.dtype == "f32" else f"fwd_bf16_kernel<{w.d}>"))
+            if w.backward:
+                seq.append((name, f"bwd_pre_kernel<{w.d}>"))
+                if w.sparse:
+                    seq.append((name, "bwd_order_kernel"))
+                seq += [(name, f"bwd_dkdv_kernel<{w.d}>"), (name, f"bwd_dq_kernel<{w.d}>")]
+        for name, w in workloads.DECODE_WORKLOADS.items():
+            seq += [(name, f"kvc_split_kernel<{w.d}>"), (name, f"kvc_merge_kernel<{w.d}>")]
+    return seq
+
+
+def counter_pass(fa, dev):
+    """For rocprofv3: the calibration copy, then every workload's forward and backward and
+    every decode call, twice (the second round is the one summarised)."""
+    import torch
+    from exact_tiled_attention_32_amd import workloads
+    runners = [Runner(fa, w, dev) for w in workloads.WORKLOADS.values()]
+    dec = []
+    for w in workloads.DECODE_WORKLOADS.values():
+        x = workloads.generate_decode(w)
+        q, k, v = (x[n].to(dev) for n in ("q", "k", "v"))
+        kv = None if x["kv_len"] is None else x["kv_len"].to(dev)
+        ws = torch.empty(fa.fa_fwd_kvcache_workspace_bytes(w.B, w.H, w.Nq, w.Nk, w.d), dtype=torch.uint8,
+                         device=dev)
+        dec.append((w, q, k, v, kv, x["scale"], ws))
+    src = torch.ones(CALIBRATION_BYTES // 4, dtype=torch.float32, device=dev)
+    dst = torch.empty_like(src)
+    torch.cuda.synchronize()
+    dst.copy_(src)
+    torch.cuda.synchronize()
+    for _ in range(2):
+        for r in runners:
+            r.fwd()
+            if r.w.backward:
+                r.bwd()
+            torch.cuda.synchronize()
+        for w, q, k, v, kv, scale, ws in dec:
+            fa.fa_fwd_kvcache(q, k, v, scale, w.causal, kv, workspace=ws)
+            torch.cuda.synchronize()
+    print("counter pass done", flush=True)
+
+
+def summarize_counters(sq_csv, fetch_csv, write_csv, trace_csv) -> str:
+    """Markdown table per (workload, kernel) of the second round of `--counter-pass`:
+    duration (kernel trace), HBM bytes and GB/s (FETCH_SIZE, WRITE_SIZE scaled by the
+    calibration copy), MFMA busy and LDS bank conflicts (SQ counters)."""
+    import csv
+    from exact_tiled_attention_32_amd import workloads
+
+    def ours(name):
+        return "fa::" in name or "copyBuffer" in name
+
+    def load(path):
+        per = {}
+        for row in csv.DictReader(open(path)):
+            if not ours(row["Kernel_Name"]):
+                continue
+            d = per.setdefault(int(row["Dispatch_Id"]), {"name": row["Kernel_Name"]})
+            d[row["Counter_Name"]] = d.get(row["Counter_Name"], 0.0) + float(row["Counter_Value"])
+        return [per[k] for k in sorted(per)]
+
+    def calib(rows, counter):
+        # the calibration copy is the last device copy before the first library kernel
+        # (the uploads of the inputs come before it)
+        first = next(i for i, r in enumerate(rows) if "fa::" in r["name"])
+        c = [r for r in rows[:first] if "copyBuffer" in r["name"]]
+        return CALIBRATION_BYTES / (c[-1][counter] * 1024.0)
+
+    sq, fe, wr = load(sq_csv), load(fetch_csv), load(write_csv)
+    ff, fw = calib(fe, "FETCH_SIZE"), calib(wr, "WRITE_SIZE")
+    trace = []
+    for row in csv.DictReader(open(trace_csv)):
+        if "fa::" in row["Kernel_Name"]:
+            trace.append((int(row["Dispatch_Id"]), row["Kernel_Name"],
+                          (int(row["End_Timestamp"]) - int(row["Start_Timestamp"])) * 1e-3))
+    trace.sort()
+    seq = counter_sequence(workloads)
+    strip = lambda rows: [r for r in rows if "copyBuffer" not in r["name"]]
+    sq, fe, wr = strip(sq), strip(fe), strip(wr)
+    for what, rows in (("sq", sq), ("fetch", fe), ("write", wr), ("trace", trace)):
+        if len(rows) != len(seq):
+            raise RuntimeError(f"{what}: {len(rows)} library dispatches, expected {len(seq)}")
+    half = len(seq) // 2
+    lines = ["| workload | kernel | µs | FETCH MB | WRITE MB | HBM GB/s | MFMA busy | LDS bank-conflict cycles "
+             "/ LDS active cycles | MFMA insts | LDS insts | active MHz |", "|---|---|---|---|---|---|---|---|---|---|---|"]
+    for i in range(half, len(seq)):
+        wname, kname = seq[i]
+        name = trace[i][1]
+        if kname.split("<")[0] not in name:
+            raise RuntimeError(f"dispatch {i}: expected {kname}, found {name}")
+        us = trace[i][2]
+        fb, wb = fe[i]["FETCH_SIZE"] * 1024.0 * ff, wr[i]["WRITE_SIZE"] * 1024.0 * fw
+        c = sq[i]
+        # SQ_VALU_MFMA_BUSY_CYCLES and SQ_BUSY_CU_CYCLES are both summed over the CUs; the
+        # MFMA counter adds the nominal issue cycles of each MFMA instruction (32 for a
+        # 32x32x16 bf16 one) over the CU's four SIMDs. Active MHz: GRBM_GUI_ACTIVE summed
+        # over the 8 XCDs, per microsecond of the kernel.
+        mfma = c["SQ_VALU_MFMA_BUSY_CYCLES"] / max(4.0 * c["SQ_BUSY_CU_CYCLES"], 1.0)
+        bank = c["SQ_LDS_BANK_CONFLICT"] / max(c["SQ_LDS_IDX_ACTIVE"], 1.0)
+        lines.append(f"| {wname} | {kname} | {us:.1f} | {fb / 1e6:.1f} | {wb / 1e6:.1f} | "
+                     f"{(fb + wb) / us / 1e3:.0f} | {100 * mfma:.1f} % | {100 * bank:.2f} % | "
+                     f"{c['SQ_INSTS_MFMA']:.3g} | {c['SQ_INSTS_LDS']:.3g} | "
+                     f"{c['GRBM_GUI_ACTIVE'] / 8 / us:.0f} |")
+    return "\n".join(lines)
 
 
 def kernel_source_digest() -> str:
@@ -352,12 +475,20 @@ def main():
     ap.add_argument("--report", default=None, help="also time every workload and write this JSON file")
     ap.add_argument("--summarize-pmc", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
                     help="write profiles/hbm_traffic.json from two rocprofv3 counter files and exit")
+    ap.add_argument("--counter-pass", action="store_true",
+                    help="for rocprofv3 --pmc / --kernel-trace: a calibration copy, then every workload once, "
+                         "twice over; prints no metric line")
+    ap.add_argument("--summarize-counters", nargs=4, metavar=("SQ_CSV", "FETCH_CSV", "WRITE_CSV", "TRACE_CSV"),
+                    help="print the per-kernel counter table of a --counter-pass and exit")
     ap.add_argument("--decode-only", action="store_true",
                     help="time only the key/value-cache forward on the decode workloads and print them")
     ap.add_argument("--pmc-pass", action="store_true",
                     help="for rocprofv3 --pmc: one 256 MiB device copy (counter calibration), then one "
                          "untimed pass of the step; prints no metric line")
     args = ap.parse_args()
+    if args.summarize_counters:
+        print(summarize_counters(*args.summarize_counters))
+        return
     if args.summarize_pmc:
         res = summarize_pmc(*args.summarize_pmc, os.path.join(ROOT, "profiles", "hbm_traffic.json"))
         print(json.dumps(res, indent=1))
@@ -372,6 +503,9 @@ def main():
     from exact_tiled_attention_32_amd import workloads
     fa.load()
     dev = "cuda:0"
+    if args.counter_pass:
+        counter_pass(fa, dev)
+        return
     if args.decode_only:
         for name, w in workloads.DECODE_WORKLOADS.items():
             print(json.dumps({"workload": name, **report_decode(fa, w, dev, args.steps, args.warmup)}), flush=True)
