@@ -10,4 +10,6 @@ from .attention import (  # noqa: F401
     attention_forward,
     forward_rows,
     kvcache_forward,
+    varlen_backward,
+    varlen_forward,
 )

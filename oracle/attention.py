@@ -33,6 +33,19 @@ What it computes, and where the pages define it
       block:    mask[i // mb][j // mb] != 0  (block-sparse, mb = mask block)
   Query rows are never masked; a row with no allowed key has O = 0,
   lse = -inf and zero gradient (the pages are silent; plainest reading).
+* Sliding window — aiwiki "FlashAttention", section "Software integration and
+  limitations", lists sliding-window masks among the interfaces; the cochat.ai
+  audit's citation check of the Longformer reference describes sliding-window
+  attention as each query attending a fixed window of w keys (O(n w) work).
+  Plainest reading: a left extent wl and a right extent wr, each unbounded when
+  negative; key j is allowed for query i iff i - wl <= j <= i + wr (another
+  predicate in the AND above; causal is the same as wr = 0).
+* Variable-length packed sequences — same aiwiki section ("variable-length
+  sequences"). Plainest reading, used by ``varlen_forward`` / ``varlen_backward``:
+  sequences are packed along one token axis, q/k/v of shape [total, H, d], with
+  sequence s owning tokens cu_seqlens[s] .. cu_seqlens[s+1] - 1; attention (and
+  every mask, with positions counted from the sequence's first token) acts
+  within a sequence only. lse is returned as [H, total].
 * Decode against a key/value cache — aiwiki "FlashAttention", section "Software
   integration and limitations", lists inference with cached keys and values
   among the interfaces but defines no semantics. Plainest reading, used by
@@ -69,6 +82,8 @@ __all__ = [
     "attention_forward",
     "attention_backward",
     "kvcache_forward",
+    "varlen_forward",
+    "varlen_backward",
 ]
 
 _ROW_CHUNK = 256
@@ -82,12 +97,14 @@ def _as_f64(x) -> np.ndarray:
 
 
 def allowed_pairs(rows: np.ndarray, n_keys: int, *, causal: bool, kv_len_b,
-                  block_mask, mask_block: int) -> np.ndarray:
+                  block_mask, mask_block: int, window_left: int = -1,
+                  window_right: int = -1) -> np.ndarray:
     """Boolean [len(rows), n_keys]: may query ``i`` attend to key ``j``.
 
-    The AND of the causal (j <= i), key-padding (j < L_b) and block-mask
-    (mask[i // mb][j // mb] != 0) predicates; see the module docstring for the
-    passages that define each.
+    The AND of the causal (j <= i), key-padding (j < L_b), block-mask
+    (mask[i // mb][j // mb] != 0) and sliding-window (i - wl <= j <= i + wr, a
+    negative extent being unbounded) predicates; see the module docstring for
+    the passages that define each.
     """
     rows = np.asarray(rows, dtype=np.int64)
     cols = np.arange(n_keys, dtype=np.int64)
@@ -99,6 +116,10 @@ def allowed_pairs(rows: np.ndarray, n_keys: int, *, causal: bool, kv_len_b,
     if block_mask is not None:
         bm = np.asarray(block_mask) != 0
         allow &= bm[rows[:, None] // mask_block, cols[None, :] // mask_block]
+    if window_left >= 0:
+        allow &= cols[None, :] >= rows[:, None] - window_left
+    if window_right >= 0:
+        allow &= cols[None, :] <= rows[:, None] + window_right
     return allow
 
 
@@ -131,11 +152,13 @@ def forward_rows(q_rows: np.ndarray, k: np.ndarray, v: np.ndarray, scale: float,
 
 
 def attention_forward(q, k, v, scale: float, *, causal: bool = False, kv_len=None,
-                      block_mask=None, mask_block: int = 128, row_chunk: int = _ROW_CHUNK):
+                      block_mask=None, mask_block: int = 128, window_left: int = -1,
+                      window_right: int = -1, row_chunk: int = _ROW_CHUNK):
     """O, lse for q/k/v of shape [B, H, N, d] (any float dtype, widened to fp64).
 
     kv_len: None or length-B integers (key padding). block_mask: None or a 2-D
     array [ceil(N/mb), ceil(N/mb)] shared by every (b, h), nonzero = keep.
+    window_left / window_right: sliding-window extents (negative = unbounded).
     Returns O [B, H, N, d] fp64 and lse [B, H, N] fp64 (natural log).
     """
     q, k, v = _as_f64(q), _as_f64(k), _as_f64(v)
@@ -148,7 +171,8 @@ def attention_forward(q, k, v, scale: float, *, causal: bool = False, kv_len=Non
             rows = np.arange(r0, min(N, r0 + row_chunk))
             allow = allowed_pairs(rows, k.shape[2], causal=causal,
                                   kv_len_b=None if lens is None else lens[b],
-                                  block_mask=block_mask, mask_block=mask_block)
+                                  block_mask=block_mask, mask_block=mask_block,
+                                  window_left=window_left, window_right=window_right)
             for h in range(H):
                 o_r, l_r = forward_rows(q[b, h, rows], k[b, h], v[b, h], scale, allow)
                 out[b, h, rows] = o_r
@@ -157,7 +181,8 @@ def attention_forward(q, k, v, scale: float, *, causal: bool = False, kv_len=Non
 
 
 def attention_backward(q, k, v, dout, scale: float, *, causal: bool = False, kv_len=None,
-                       block_mask=None, mask_block: int = 128, heads=None, rows=None,
+                       block_mask=None, mask_block: int = 128, window_left: int = -1,
+                       window_right: int = -1, heads=None, rows=None,
                        row_chunk: int = _ROW_CHUNK):
     """dQ, dK, dV of L = sum(O * dO) for the forward above, all fp64.
 
@@ -182,7 +207,8 @@ def attention_backward(q, k, v, dout, scale: float, *, causal: bool = False, kv_
             rows = all_rows[r0:r0 + row_chunk]
             allow = allowed_pairs(rows, k.shape[2], causal=causal,
                                   kv_len_b=None if lens is None else lens[b],
-                                  block_mask=block_mask, mask_block=mask_block)
+                                  block_mask=block_mask, mask_block=mask_block,
+                                  window_left=window_left, window_right=window_right)
             cols = np.nonzero(allow.any(axis=0))[0]
             if cols.size == 0:
                 continue
@@ -226,3 +252,50 @@ def kvcache_forward(q, k, v, scale: float, *, causal: bool = False, kv_len=None)
         for h in range(H):
             out[b, h], lse[b, h] = forward_rows(q[b, h], k[b, h], v[b, h], scale, allow)
     return out, lse
+
+
+def _segments(cu_seqlens, total: int):
+    cu = [int(x) for x in np.asarray(cu_seqlens).reshape(-1)]
+    if len(cu) < 2 or cu[0] != 0 or cu[-1] != total or any(b < a for a, b in zip(cu, cu[1:])):
+        raise ValueError("cu_seqlens must start at 0, be nondecreasing and end at the token count")
+    return list(zip(cu[:-1], cu[1:]))
+
+
+def varlen_forward(q, k, v, cu_seqlens, scale: float, *, causal: bool = False,
+                   window_left: int = -1, window_right: int = -1):
+    """O [total, H, d] and lse [H, total] of packed sequences (module docstring).
+
+    q, k, v [total, H, d]; sequence s is tokens cu_seqlens[s] .. cu_seqlens[s+1] - 1
+    and attends within itself, with the causal and sliding-window masks counted from
+    its first token.
+    """
+    q, k, v = _as_f64(q), _as_f64(k), _as_f64(v)
+    total, H, _ = q.shape
+    out = np.zeros((total, H, v.shape[2]), dtype=np.float64)
+    lse = np.full((H, total), -np.inf, dtype=np.float64)
+    for c0, c1 in _segments(cu_seqlens, total):
+        if c1 == c0:
+            continue
+        seq = [x[c0:c1].transpose(1, 0, 2)[None] for x in (q, k, v)]   # [1, H, n, d]
+        o_s, l_s = attention_forward(*seq, scale, causal=causal, window_left=window_left,
+                                     window_right=window_right)
+        out[c0:c1] = o_s[0].transpose(1, 0, 2)
+        lse[:, c0:c1] = l_s[0]
+    return out, lse
+
+
+def varlen_backward(q, k, v, dout, cu_seqlens, scale: float, *, causal: bool = False,
+                    window_left: int = -1, window_right: int = -1):
+    """dQ, dK, dV [total, H, d] of L = sum(O * dout) for ``varlen_forward``."""
+    q, k, v, dout = _as_f64(q), _as_f64(k), _as_f64(v), _as_f64(dout)
+    total = q.shape[0]
+    dq, dk, dv = np.zeros_like(q), np.zeros_like(k), np.zeros_like(v)
+    for c0, c1 in _segments(cu_seqlens, total):
+        if c1 == c0:
+            continue
+        seq = [x[c0:c1].transpose(1, 0, 2)[None] for x in (q, k, v, dout)]
+        g = attention_backward(*seq, scale, causal=causal, window_left=window_left,
+                               window_right=window_right)
+        for dst, src in zip((dq, dk, dv), g):
+            dst[c0:c1] = src[0].transpose(1, 0, 2)
+    return dq, dk, dv

@@ -415,6 +415,138 @@ def pin_kvcache_library_sdpa(orc):
             assert np.allclose(o[b][:, live], ro, atol=1e-12), (causal, b)
 
 
+# ----------------------------------------------------------------------------------
+# sliding window and packed variable-length sequences
+# ----------------------------------------------------------------------------------
+def window_lists(N, causal, wl, wr):
+    """Allowed keys per query under the causal and sliding-window rules (scalar loops)."""
+    out = []
+    for i in range(N):
+        js = []
+        for j in range(N):
+            if causal and j > i:
+                continue
+            if wl >= 0 and j < i - wl:
+                continue
+            if wr >= 0 and j > i + wr:
+                continue
+            js.append(j)
+        out.append(js)
+    return out
+
+
+def _lse_loop(q, k, scale, js):
+    """ln sum_j exp(scale q . k_j) by scalar loops (shifted by the maximum for range)."""
+    if not js:
+        return -math.inf
+    s = [scale * math.fsum(float(a) * float(b) for a, b in zip(q, k[j])) for j in js]
+    m = max(s)
+    return m + math.log(math.fsum(math.exp(x - m) for x in s))
+
+
+WINDOW_CASES = [  # (N, causal, window_left, window_right)
+    (11, False, 3, 2),
+    (11, True, 4, -1),
+    (11, False, -1, 0),
+    (11, False, 0, 5),
+    (11, True, 2, 7),
+    (11, False, 20, 20),
+]
+
+
+def pin_window_library_sdpa(orc):
+    """Sliding windows (with and without causal) against torch SDPA on masks built here."""
+    rng = RNG(40)
+    for N, causal, wl, wr in WINDOW_CASES:
+        d, scale = 4, 0.6
+        q, k, v, do = (rng.standard_normal((2, 2, N, d)) for _ in range(4))
+        o, lse = orc.attention_forward(q, k, v, scale, causal=causal, window_left=wl, window_right=wr)
+        dq, dk, dv = orc.attention_backward(q, k, v, do, scale, causal=causal, window_left=wl,
+                                            window_right=wr)
+        lists = window_lists(N, causal, wl, wr)
+        allow = dense_bool(lists, N)
+        live = allow.any(axis=1)
+        for b in range(2):
+            ro, rdq, rdk, rdv = _sdpa(q[b][:, live], k[b], v[b], do[b][:, live], scale, allow[live])
+            case = (N, causal, wl, wr, b)
+            assert np.allclose(o[b][:, live], ro, atol=1e-12), case
+            assert np.allclose(dq[b][:, live], rdq, atol=1e-11), case
+            assert np.allclose(dk[b], rdk, atol=1e-11), case
+            assert np.allclose(dv[b], rdv, atol=1e-11), case
+            for h in range(2):
+                for i in range(N):
+                    ref = _lse_loop(q[b, h, i], k[b, h], scale, lists[i])
+                    assert (ref == -math.inf and lse[b, h, i] == -math.inf) or abs(lse[b, h, i] - ref) < 1e-12, case
+
+
+def pin_window_self_only(orc):
+    """Left extent 0 with causal (or both extents 0): each query sees only its own key, so
+    O_i = v_i and lse_i = scale q_i . k_i; the same inside every packed sequence."""
+    rng = RNG(41)
+    q, k, v = (rng.standard_normal((1, 2, 9, 3)) for _ in range(3))
+    for causal, wl, wr in ((True, 0, -1), (False, 0, 0)):
+        o, lse = orc.attention_forward(q, k, v, 0.9, causal=causal, window_left=wl, window_right=wr)
+        assert np.allclose(o, v, atol=1e-15)
+        assert np.allclose(lse, 0.9 * np.einsum("bhnd,bhnd->bhn", q, k), atol=1e-14)
+    cu = [0, 3, 3, 8, 9]
+    qp, kp, vp = (rng.standard_normal((9, 2, 3)) for _ in range(3))
+    o, lse = orc.varlen_forward(qp, kp, vp, cu, 0.9, causal=True, window_left=0)
+    assert np.allclose(o, vp, atol=1e-15)
+    assert np.allclose(lse, 0.9 * np.einsum("thd,thd->ht", qp, kp), atol=1e-14)
+
+
+VARLEN_CU = [0, 5, 5, 12, 13, 20]  # lengths 5, 0, 7, 1, 7
+
+
+def pin_varlen_library_sdpa(orc):
+    """Packed sequences: every sequence against torch SDPA on its own slice (forward, lse by
+    scalar loops, gradients), for full, causal and windowed masks."""
+    rng = RNG(42)
+    total, H, d, scale = VARLEN_CU[-1], 2, 3, 0.7
+    q, k, v, do = (rng.standard_normal((total, H, d)) for _ in range(4))
+    for causal, wl, wr in ((False, -1, -1), (True, -1, -1), (False, 2, 1), (True, 3, -1)):
+        o, lse = orc.varlen_forward(q, k, v, VARLEN_CU, scale, causal=causal, window_left=wl, window_right=wr)
+        dq, dk, dv = orc.varlen_backward(q, k, v, do, VARLEN_CU, scale, causal=causal, window_left=wl,
+                                         window_right=wr)
+        assert o.shape == (total, H, d) and lse.shape == (H, total)
+        for c0, c1 in zip(VARLEN_CU[:-1], VARLEN_CU[1:]):
+            n = c1 - c0
+            if n == 0:
+                continue
+            lists = window_lists(n, causal, wl, wr)
+            allow = dense_bool(lists, n)
+            sl = [x[c0:c1].transpose(1, 0, 2) for x in (q, k, v, do)]  # [H, n, d]
+            ro, rdq, rdk, rdv = _sdpa(*sl, scale, allow)
+            case = (causal, wl, wr, c0)
+            assert np.allclose(o[c0:c1].transpose(1, 0, 2), ro, atol=1e-12), case
+            assert np.allclose(dq[c0:c1].transpose(1, 0, 2), rdq, atol=1e-11), case
+            assert np.allclose(dk[c0:c1].transpose(1, 0, 2), rdk, atol=1e-11), case
+            assert np.allclose(dv[c0:c1].transpose(1, 0, 2), rdv, atol=1e-11), case
+            for h in range(H):
+                for i in range(n):
+                    ref = _lse_loop(q[c0 + i, h], k[c0:c1, h], scale, lists[i])
+                    assert abs(lse[h, c0 + i] - ref) < 1e-12, case
+
+
+def pin_varlen_isolation(orc):
+    """Changing one sequence's keys and values changes no other sequence's results."""
+    rng = RNG(43)
+    total, H, d = VARLEN_CU[-1], 2, 3
+    q, k, v, do = (rng.standard_normal((total, H, d)) for _ in range(4))
+    k2, v2 = k.copy(), v.copy()
+    k2[5:12] += 3.0
+    v2[5:12] -= 2.0
+    a = orc.varlen_forward(q, k, v, VARLEN_CU, 0.5, causal=True)
+    b = orc.varlen_forward(q, k2, v2, VARLEN_CU, 0.5, causal=True)
+    ga = orc.varlen_backward(q, k, v, do, VARLEN_CU, 0.5, causal=True)
+    gb = orc.varlen_backward(q, k2, v2, do, VARLEN_CU, 0.5, causal=True)
+    other = np.r_[0:5, 12:20]
+    assert np.array_equal(a[0][other], b[0][other]) and np.array_equal(a[1][:, other], b[1][:, other])
+    for x, y in zip(ga, gb):
+        assert np.array_equal(x[other], y[other])
+    assert not np.allclose(a[0][5:12], b[0][5:12])
+
+
 ALL_PINS = [
     pin_zero_query,
     pin_one_hot_keys,
@@ -432,4 +564,8 @@ ALL_PINS = [
     pin_kvcache_zero_query,
     pin_kvcache_single_query,
     pin_kvcache_library_sdpa,
+    pin_window_library_sdpa,
+    pin_window_self_only,
+    pin_varlen_library_sdpa,
+    pin_varlen_isolation,
 ]

@@ -44,12 +44,29 @@ MUTANTS = {
                                "allow = np.ones((Nq, Nk), dtype=bool)"),
     "bwd_causal_ignored": ("allow = allowed_pairs(rows, k.shape[2], causal=causal,\n"
                            "                                  kv_len_b=None if lens is None else lens[b],\n"
-                           "                                  block_mask=block_mask, mask_block=mask_block)\n"
+                           "                                  block_mask=block_mask, mask_block=mask_block,\n"
+                           "                                  window_left=window_left, window_right=window_right)\n"
                            "            cols",
                            "allow = allowed_pairs(rows, k.shape[2], causal=False,\n"
                            "                                  kv_len_b=None if lens is None else lens[b],\n"
-                           "                                  block_mask=block_mask, mask_block=mask_block)\n"
+                           "                                  block_mask=block_mask, mask_block=mask_block,\n"
+                           "                                  window_left=window_left, window_right=window_right)\n"
                            "            cols"),
+    "window_left_off_by_one": ("allow &= cols[None, :] >= rows[:, None] - window_left",
+                               "allow &= cols[None, :] > rows[:, None] - window_left"),
+    "window_right_ignored": ("allow &= cols[None, :] <= rows[:, None] + window_right",
+                             "allow &= cols[None, :] <= rows[:, None] + window_right + 10**6"),
+    "window_mirrored": ("allow &= cols[None, :] >= rows[:, None] - window_left",
+                        "allow &= cols[None, :] >= rows[:, None] - window_right"),
+    "bwd_window_ignored": ("                                  window_left=window_left, window_right=window_right)\n"
+                           "            cols",
+                           "                                  window_left=-1, window_right=-1)\n"
+                           "            cols"),
+    "varlen_keys_shifted": ("seq = [x[c0:c1].transpose(1, 0, 2)[None] for x in (q, k, v)]",
+                            "seq = [x[c0:c1].transpose(1, 0, 2)[None] for x in (q,)] + "
+                            "[np.roll(x, 1, axis=0)[c0:c1].transpose(1, 0, 2)[None] for x in (k, v)]"),
+    "varlen_lse_misplaced": ("lse[:, c0:c1] = l_s[0]", "lse[:, c0:c1] = l_s[0][:, ::-1]"),
+    "varlen_bwd_dk_dv_swapped": ("for dst, src in zip((dq, dk, dv), g):", "for dst, src in zip((dq, dv, dk), g):"),
 }
 
 
