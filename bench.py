@@ -10,6 +10,10 @@ FLOP convention: forward 4*B*H*N^2*d, halved for causal; backward 2.5x the forwa
 The backward's dK/dV kernel performs four of the five products (2.0x the forward); its
 dQ kernel the fifth, plus a recomputation of two that the convention does not count.
 
+Packed variable-length sequences and the sliding-window mask are timed outside the step
+on their own workloads and reported under "varlen" (FLOP counted exactly over the allowed
+query-key pairs: 4 d per pair forward, 2.5x that backward).
+
 The key/value-cache forward (a few queries against a long cache, HBM-bound) is timed
 outside the step on its decode workloads and reported under "kvcache_decode": algorithmic
 bytes = every valid cached key and value read once plus Q and O, divided by the time of the
@@ -188,6 +192,9 @@ def counter_sequence(workloads):
                 if w.sparse:
                     seq.append((name, "bwd_order_kernel"))
                 seq += [(name, f"bwd_dkdv_kernel<{w.d}>"), (name, f"bwd_dq_kernel<{w.d}>")]
+        for name, w in workloads.VARLEN_WORKLOADS.items():
+            seq += [(name, f"fwd_bf16_kernel<{w.d}>"), (name, f"bwd_pre_kernel<{w.d}>"),
+                    (name, f"bwd_dkdv_kernel<{w.d}>"), (name, f"bwd_dq_kernel<{w.d}>")]
         for name, w in workloads.DECODE_WORKLOADS.items():
             seq += [(name, f"kvc_split_kernel<{w.d}>"), (name, f"kvc_merge_kernel<{w.d}>")]
     return seq
@@ -207,6 +214,11 @@ def counter_pass(fa, dev):
         ws = torch.empty(fa.fa_fwd_kvcache_workspace_bytes(w.B, w.H, w.Nq, w.Nk, w.d), dtype=torch.uint8,
                          device=dev)
         dec.append((w, q, k, v, kv, x["scale"], ws))
+    var = []
+    for w in workloads.VARLEN_WORKLOADS.values():
+        x = workloads.generate_varlen(w)
+        t = {n: x[n].to(dev) for n in ("q", "k", "v", "do", "cu_seqlens")}
+        var.append((w, x, t))
     src = torch.ones(CALIBRATION_BYTES // 4, dtype=torch.float32, device=dev)
     dst = torch.empty_like(src)
     torch.cuda.synchronize()
@@ -217,6 +229,12 @@ def counter_pass(fa, dev):
             r.fwd()
             if r.w.backward:
                 r.bwd()
+            torch.cuda.synchronize()
+        for w, x, t in var:
+            kw = dict(causal=w.causal, window_left=w.window_left, window_right=w.window_right)
+            o, lse = fa.fa_fwd_varlen(t["q"], t["k"], t["v"], t["cu_seqlens"], x["max_seqlen"], x["scale"], **kw)
+            fa.fa_bwd_varlen(t["q"], t["k"], t["v"], o, t["do"], lse, t["cu_seqlens"], x["max_seqlen"], x["scale"],
+                             **kw)
             torch.cuda.synchronize()
         for w, q, k, v, kv, scale, ws in dec:
             fa.fa_fwd_kvcache(q, k, v, scale, w.causal, kv, workspace=ws)
@@ -421,6 +439,56 @@ def report_decode(fa, w, dev, steps, warmup) -> dict:
             "frac_of_hbm_peak": nbytes / ms / 1e6 / PEAK_HBM_GBS}
 
 
+def allowed_pair_count(n: int, causal: bool, wl: int, wr: int) -> int:
+    """Query-key pairs a sequence of n tokens attends under the causal / window rules."""
+    import numpy as np
+    i = np.arange(n, dtype=np.int64)
+    lo = np.maximum(i - wl, 0) if wl >= 0 else np.zeros_like(i)
+    right = 0 if causal else wr
+    hi = np.minimum(i + right, n - 1) if right >= 0 else np.full_like(i, n - 1)
+    return int(np.maximum(hi - lo + 1, 0).sum())
+
+
+def report_varlen(fa, w, dev, steps, warmup) -> dict:
+    """Forward and backward timing of one packed workload. FLOP: 4 d per allowed pair
+    (forward) and 2.5x that (backward), counted exactly over the sequences."""
+    import torch
+    from exact_tiled_attention_32_amd import workloads
+    x = workloads.generate_varlen(w)
+    q, k, v, do = (x[n].to(dev) for n in ("q", "k", "v", "do"))
+    cu = x["cu_seqlens"].to(dev)
+    lens = (x["cu_seqlens"][1:] - x["cu_seqlens"][:-1]).tolist()
+    pairs = sum(allowed_pair_count(n, w.causal, w.window_left, w.window_right) for n in lens)
+    fwd_flop = 4.0 * w.d * w.H * pairs
+    kw = dict(causal=w.causal, window_left=w.window_left, window_right=w.window_right)
+    o = torch.empty_like(q)
+    lse = torch.empty((w.H, q.shape[0]), dtype=torch.float32, device=dev)
+    dq, dk, dv = (torch.empty_like(q) for _ in range(3))
+    ws = torch.empty(fa.fa_bwd_varlen_workspace_bytes(w.H, q.shape[0], w.d), dtype=torch.uint8, device=dev)
+    fns = {
+        "fwd": lambda: fa.fa_fwd_varlen(q, k, v, cu, x["max_seqlen"], x["scale"], o=o, lse=lse, **kw),
+        "bwd": lambda: fa.fa_bwd_varlen(q, k, v, o, do, lse, cu, x["max_seqlen"], x["scale"], dq=dq, dk=dk, dv=dv,
+                                        workspace=ws, **kw),
+    }
+    res = {"sequences": len(lens), "tokens": int(q.shape[0]), "H": w.H, "d": w.d, "causal": w.causal,
+           "window_left": w.window_left, "window_right": w.window_right, "allowed_pairs_per_head": pairs}
+    for phase, fn in fns.items():
+        for _ in range(warmup):
+            fn()
+        torch.cuda.synchronize()
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record()
+        for _ in range(steps):
+            fn()
+        b.record()
+        torch.cuda.synchronize()
+        ms = a.elapsed_time(b) / steps
+        flop = fwd_flop * (2.5 if phase == "bwd" else 1.0)
+        res[phase] = {"ms": round(ms, 4), "tflops": round(flop / ms / 1e9, 1),
+                      "frac_of_peak": round(flop / ms / 1e9 / PEAK_BF16_TFLOPS, 4)}
+    return res
+
+
 def report_all(fa, dev, path, steps=10, warmup=3):
     """Per-workload fwd / bwd timing (not the metric line)."""
     import torch
@@ -456,6 +524,10 @@ def report_all(fa, dev, path, steps=10, warmup=3):
         out[name] = res
         print(f"[report] {name}: " + json.dumps({k: v for k, v in res.items() if k in ("fwd", "bwd")}), flush=True)
         del r
+        torch.cuda.empty_cache()
+    for name, w in workloads.VARLEN_WORKLOADS.items():
+        out[name] = report_varlen(fa, w, dev, steps, warmup)
+        print(f"[report] {name}: " + json.dumps({k: out[name][k] for k in ("fwd", "bwd")}), flush=True)
         torch.cuda.empty_cache()
     for name, w in workloads.DECODE_WORKLOADS.items():
         out[name] = report_decode(fa, w, dev, steps, warmup)
@@ -558,6 +630,9 @@ def main():
         del r
         torch.cuda.empty_cache()
     line["kvcache_decode"] = dec
+    # packed variable-length sequences and the sliding window, outside the step
+    line["varlen"] = {name: report_varlen(fa, w, dev, 10, 3) for name, w in workloads.VARLEN_WORKLOADS.items()}
+    torch.cuda.empty_cache()
     if args.report:
         report_all(fa, dev, args.report)
     if not args.no_cpu_baseline:

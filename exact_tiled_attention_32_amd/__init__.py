@@ -10,6 +10,12 @@ Entry points (same names as the C ABI):
     fa_fwd(q, k, v, scale, causal=False, kv_len=None, o=None, lse=None) -> (o, lse)
     fa_fwd_blocksparse(q, k, v, scale, block_mask, mask_block=128, causal=False,
                        kv_len=None, o=None, lse=None) -> (o, lse)
+    fa_fwd_varlen(q, k, v, cu_seqlens, max_seqlen, scale, causal=False, window_left=-1,
+                  window_right=-1, o=None, lse=None) -> (o, lse)
+    fa_bwd_varlen_workspace_bytes(H, total, d) -> int
+    fa_bwd_varlen(q, k, v, o, dout, lse, cu_seqlens, max_seqlen, scale, causal=False,
+                  window_left=-1, window_right=-1, dq=None, dk=None, dv=None,
+                  workspace=None) -> (dq, dk, dv)
     fa_fwd_kvcache_workspace_bytes(B, H, Nq, Nk, d) -> int
     fa_fwd_kvcache(q, k_cache, v_cache, scale, causal=False, kv_len=None, o=None, lse=None,
                    workspace=None) -> (o, lse)
@@ -28,7 +34,7 @@ import torch
 __all__ = [
     "FA_F32", "FA_BF16", "FA_OK", "FA_ERR_INVALID", "FA_ERR_UNSUPPORTED", "FA_ERR_HIP",
     "FAError", "lib_path", "load", "fa_fwd", "fa_fwd_blocksparse", "fa_bwd",
-    "fa_bwd_workspace_bytes", "fa_fwd_kvcache", "fa_fwd_kvcache_workspace_bytes", "fa_time_next_kernel", "fa_status_string", "EXPORTED_SYMBOLS",
+    "fa_bwd_workspace_bytes", "fa_fwd_varlen", "fa_bwd_varlen", "fa_bwd_varlen_workspace_bytes", "fa_fwd_kvcache", "fa_fwd_kvcache_workspace_bytes", "fa_time_next_kernel", "fa_status_string", "EXPORTED_SYMBOLS",
 ]
 
 FA_F32, FA_BF16 = 0, 1
@@ -36,6 +42,7 @@ FA_OK, FA_ERR_INVALID, FA_ERR_UNSUPPORTED, FA_ERR_HIP = 0, 1, 2, 3
 
 EXPORTED_SYMBOLS = ("fa_fwd", "fa_fwd_blocksparse", "fa_bwd_workspace_bytes", "fa_bwd",
                     "fa_fwd_kvcache_workspace_bytes", "fa_fwd_kvcache",
+                    "fa_fwd_varlen", "fa_bwd_varlen_workspace_bytes", "fa_bwd_varlen",
                     "fa_time_next_kernel", "fa_status_string", "fa_last_error")
 
 _LIB = None
@@ -69,6 +76,12 @@ def load() -> ctypes.CDLL:
     lib.fa_bwd_workspace_bytes.restype = S
     lib.fa_bwd.argtypes = [I, I, I, I, I, P, P, P, P, P, P, P, P, P, F, I, P, P, I, P, S, P]
     lib.fa_bwd.restype = I
+    lib.fa_fwd_varlen.argtypes = [I, I, I, I, I, I, P, P, P, P, P, P, F, I, I, I, P]
+    lib.fa_fwd_varlen.restype = I
+    lib.fa_bwd_varlen_workspace_bytes.argtypes = [I, I, I]
+    lib.fa_bwd_varlen_workspace_bytes.restype = S
+    lib.fa_bwd_varlen.argtypes = [I, I, I, I, I, I, P, P, P, P, P, P, P, P, P, P, F, I, I, I, P, S, P]
+    lib.fa_bwd_varlen.restype = I
     lib.fa_fwd_kvcache_workspace_bytes.argtypes = [I, I, I, I, I]
     lib.fa_fwd_kvcache_workspace_bytes.restype = S
     lib.fa_fwd_kvcache.argtypes = [I, I, I, I, I, I, P, P, P, P, P, F, I, P, P, S, P]
@@ -251,3 +264,66 @@ def fa_fwd_kvcache(q, k_cache, v_cache, scale: float, causal: bool = False, kv_l
                               _ptr(o), _ptr(lse), float(scale), int(bool(causal)), _ptr(kv),
                               _ptr(workspace), int(workspace.numel()), _stream(q.device)))
     return o, lse
+
+
+def _cu_seqlens(cu_seqlens, q):
+    cu = _dev_tensor(cu_seqlens, "cu_seqlens")
+    if cu.dtype != torch.int32 or cu.dim() != 1 or cu.numel() < 2 or cu.device != q.device:
+        raise ValueError("cu_seqlens must be an int32 device tensor of shape [nseq + 1]")
+    return cu
+
+
+def _packed(q):
+    q = _dev_tensor(q, "q")
+    if q.dim() != 3:
+        raise ValueError("packed tensors are [total, H, d]")
+    return q
+
+
+def fa_fwd_varlen(q, k, v, cu_seqlens, max_seqlen: int, scale: float, causal: bool = False,
+                  window_left: int = -1, window_right: int = -1, o=None, lse=None):
+    """Packed variable-length forward; see ``fa_fwd_varlen`` in include/fa.h. q, k, v are
+    [total, H, d]; returns o [total, H, d] and lse [H, total]."""
+    lib = load()
+    q = _packed(q)
+    _dev_tensor(k, "k", q)
+    _dev_tensor(v, "v", q)
+    cu = _cu_seqlens(cu_seqlens, q)
+    total, H, d = q.shape
+    o = torch.empty_like(q) if o is None else _dev_tensor(o, "o", q)
+    if lse is None:
+        lse = torch.empty((H, total), dtype=torch.float32, device=q.device)
+    elif lse.shape != (H, total) or lse.dtype != torch.float32 or not lse.is_contiguous():
+        raise ValueError("lse must be a contiguous float32 tensor [H, total]")
+    _check(lib.fa_fwd_varlen(_dtype_code(q), cu.numel() - 1, H, total, int(max_seqlen), d, _ptr(cu), _ptr(q),
+                             _ptr(k), _ptr(v), _ptr(o), _ptr(lse), float(scale), int(bool(causal)),
+                             int(window_left), int(window_right), _stream(q.device)))
+    return o, lse
+
+
+def fa_bwd_varlen_workspace_bytes(H: int, total: int, d: int) -> int:
+    return int(load().fa_bwd_varlen_workspace_bytes(int(H), int(total), int(d)))
+
+
+def fa_bwd_varlen(q, k, v, o, dout, lse, cu_seqlens, max_seqlen: int, scale: float, causal: bool = False,
+                  window_left: int = -1, window_right: int = -1, dq=None, dk=None, dv=None, workspace=None):
+    """Backward of ``fa_fwd_varlen``; see ``fa_bwd_varlen`` in include/fa.h."""
+    lib = load()
+    q = _packed(q)
+    for name, t in (("k", k), ("v", v), ("o", o), ("dout", dout)):
+        _dev_tensor(t, name, q)
+    cu = _cu_seqlens(cu_seqlens, q)
+    total, H, d = q.shape
+    if lse.shape != (H, total) or lse.dtype != torch.float32 or not lse.is_contiguous():
+        raise ValueError("lse must be a contiguous float32 tensor [H, total]")
+    dq = torch.empty_like(q) if dq is None else _dev_tensor(dq, "dq", q)
+    dk = torch.empty_like(q) if dk is None else _dev_tensor(dk, "dk", q)
+    dv = torch.empty_like(q) if dv is None else _dev_tensor(dv, "dv", q)
+    if workspace is None:
+        workspace = torch.empty(max(fa_bwd_varlen_workspace_bytes(H, total, d), 1), dtype=torch.uint8,
+                                device=q.device)
+    _check(lib.fa_bwd_varlen(_dtype_code(q), cu.numel() - 1, H, total, int(max_seqlen), d, _ptr(cu), _ptr(q),
+                             _ptr(k), _ptr(v), _ptr(o), _ptr(dout), _ptr(lse), _ptr(dq), _ptr(dk), _ptr(dv),
+                             float(scale), int(bool(causal)), int(window_left), int(window_right),
+                             _ptr(workspace), int(workspace.numel()), _stream(q.device)))
+    return dq, dk, dv

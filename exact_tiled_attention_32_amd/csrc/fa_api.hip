@@ -105,8 +105,33 @@ fa_status fwd_impl(fa_dtype dt, int B, int H, int N, int d, const void* q, const
   a.qmul = scale > 0.f ? 1.f : (scale < 0.f ? -1.f : 0.f);
   a.c2 = scale != 0.f ? sabs * 1.4426950408889634f : 1.4426950408889634f;
   a.sc_abs = sabs;
+  a.wl = -1;
+  a.wr = causal ? 0 : -1;
+  a.cu = nullptr;
+  a.rs = d;
+  a.total = 0;
   hipError_t e = fa::launch_fwd(a, dt, d, stream, take_timer());
   if (e != hipSuccess) return fail(FA_ERR_HIP, "forward launch failed: %s", hipGetErrorString(e));
+  return FA_OK;
+}
+
+// Shared validation of the packed variable-length calls.
+fa_status check_varlen(fa_dtype dt, int nseq, int H, int total, int max_seqlen, int d, float scale,
+                       const int32_t* cu, int window_left, int window_right) {
+  if (dt != FA_F32 && dt != FA_BF16) return fail(FA_ERR_INVALID, "unknown dtype %d", (int)dt);
+  if (nseq <= 0 || H <= 0 || total < 0 || max_seqlen < 0 || d <= 0)
+    return fail(FA_ERR_INVALID, "sizes must be positive (nseq=%d H=%d total=%d max_seqlen=%d d=%d)", nseq, H,
+                total, max_seqlen, d);
+  if ((long double)total * H * d * 4 > (long double)(1ull << 62)) return fail(FA_ERR_INVALID, "tensor size overflows");
+  const long long wgs = (long long)nseq * H * ((max_seqlen + fa::kFwdRowsPerWG - 1) / fa::kFwdRowsPerWG);
+  if (wgs > 0x7fffffffLL) return fail(FA_ERR_INVALID, "grid too large (nseq*H*ceil(max_seqlen/128) > 2^31-1)");
+  if (!std::isfinite(scale)) return fail(FA_ERR_INVALID, "scale must be finite");
+  if (cu == nullptr) return fail(FA_ERR_INVALID, "cu_seqlens is NULL");
+  if (!aligned(cu, 4)) return fail(FA_ERR_INVALID, "cu_seqlens is not 4-byte aligned");
+  if (window_left < -1 || window_right < -1)
+    return fail(FA_ERR_INVALID, "window extents must be >= 0, or -1 for unbounded");
+  if (dt != FA_BF16) return fail(FA_ERR_UNSUPPORTED, "packed sequences are built for bf16 only");
+  if (d != 64 && d != 128) return fail(FA_ERR_UNSUPPORTED, "head dimension %d not built (64, 128)", d);
   return FA_OK;
 }
 
@@ -197,6 +222,11 @@ fa_status fa_bwd(fa_dtype dt, int B, int H, int N, int d, const void* q, const v
   a.causal = causal ? 1 : 0;
   a.scale = scale;
   a.c2s = scale * 1.4426950408889634f;
+  a.wl = -1;
+  a.wr = causal ? 0 : -1;
+  a.cu = nullptr;
+  a.rs = d;
+  a.total = 0;
   hipError_t e = fa::launch_bwd(a, d, stream, take_timer());
   if (e != hipSuccess) return fail(FA_ERR_HIP, "backward launch failed: %s", hipGetErrorString(e));
   return FA_OK;
@@ -257,6 +287,99 @@ fa_status fa_fwd_kvcache(fa_dtype dt, int B, int H, int Nq, int Nk, int d, const
   a.sc_abs = sabs;
   hipError_t e = fa::launch_kvcache(a, d, stream, take_timer());
   if (e != hipSuccess) return fail(FA_ERR_HIP, "key/value-cache forward launch failed: %s", hipGetErrorString(e));
+  return FA_OK;
+}
+
+fa_status fa_fwd_varlen(fa_dtype dt, int nseq, int H, int total, int max_seqlen, int d,
+                        const int32_t* cu_seqlens, const void* q, const void* k, const void* v, void* o,
+                        float* lse, float scale, int causal, int window_left, int window_right,
+                        hipStream_t stream) {
+  FA_TRY(check_varlen(dt, nseq, H, total, max_seqlen, d, scale, cu_seqlens, window_left, window_right));
+  if (total == 0 || max_seqlen == 0) return FA_OK;  // no token: nothing to compute
+  FA_TRY(check_tensor(q, "q", 16));
+  FA_TRY(check_tensor(k, "k", 16));
+  FA_TRY(check_tensor(v, "v", 16));
+  FA_TRY(check_tensor(o, "o", 16));
+  FA_TRY(check_tensor(lse, "lse", 4));
+  fa::FwdArgs a{};
+  a.q = q;
+  a.k = k;
+  a.v = v;
+  a.o = o;
+  a.lse = lse;
+  a.B = nseq;
+  a.H = H;
+  a.N = max_seqlen;
+  a.ntq = (max_seqlen + fa::kFwdRowsPerWGBF16 - 1) / fa::kFwdRowsPerWGBF16;
+  a.causal = causal ? 1 : 0;
+  const float sabs = std::fabs(scale);
+  a.qmul = scale > 0.f ? 1.f : (scale < 0.f ? -1.f : 0.f);
+  a.c2 = scale != 0.f ? sabs * 1.4426950408889634f : 1.4426950408889634f;
+  a.sc_abs = sabs;
+  a.wl = window_left;
+  a.wr = causal ? 0 : window_right;
+  a.cu = cu_seqlens;
+  a.rs = H * d;
+  a.total = total;
+  hipError_t e = fa::launch_fwd(a, dt, d, stream, take_timer());
+  if (e != hipSuccess) return fail(FA_ERR_HIP, "forward launch failed: %s", hipGetErrorString(e));
+  return FA_OK;
+}
+
+size_t fa_bwd_varlen_workspace_bytes(int H, int total, int d) {
+  if (H <= 0 || total < 0 || d <= 0) return 0;
+  if ((long double)total * H * d * 4 > (long double)(1ull << 62)) return 0;
+  return align256((size_t)total * H * sizeof(float));
+}
+
+fa_status fa_bwd_varlen(fa_dtype dt, int nseq, int H, int total, int max_seqlen, int d,
+                        const int32_t* cu_seqlens, const void* q, const void* k, const void* v,
+                        const void* o, const void* dout, const float* lse, void* dq, void* dk, void* dv,
+                        float scale, int causal, int window_left, int window_right, void* workspace,
+                        size_t workspace_bytes, hipStream_t stream) {
+  FA_TRY(check_varlen(dt, nseq, H, total, max_seqlen, d, scale, cu_seqlens, window_left, window_right));
+  if (total == 0 || max_seqlen == 0) return FA_OK;
+  FA_TRY(check_tensor(q, "q", 16));
+  FA_TRY(check_tensor(k, "k", 16));
+  FA_TRY(check_tensor(v, "v", 16));
+  FA_TRY(check_tensor(o, "o", 16));
+  FA_TRY(check_tensor(dout, "dout", 16));
+  FA_TRY(check_tensor(lse, "lse", 4));
+  FA_TRY(check_tensor(dq, "dq", 16));
+  FA_TRY(check_tensor(dk, "dk", 16));
+  FA_TRY(check_tensor(dv, "dv", 16));
+  const size_t need = fa_bwd_varlen_workspace_bytes(H, total, d);
+  if (workspace == nullptr) return fail(FA_ERR_INVALID, "workspace is NULL");
+  if (!aligned(workspace, 256)) return fail(FA_ERR_INVALID, "workspace is not 256-byte aligned");
+  if (workspace_bytes < need)
+    return fail(FA_ERR_INVALID, "workspace too small: %zu bytes given, %zu needed", workspace_bytes, need);
+  fa::BwdArgs a{};
+  a.q = q;
+  a.k = k;
+  a.v = v;
+  a.o = o;
+  a.dout = dout;
+  a.lse = lse;
+  a.dq = dq;
+  a.dk = dk;
+  a.dv = dv;
+  a.dsum = reinterpret_cast<float*>(workspace);
+  a.order = nullptr;
+  a.kv_len = nullptr;
+  a.mask = nullptr;
+  a.B = nseq;
+  a.H = H;
+  a.N = max_seqlen;
+  a.causal = causal ? 1 : 0;
+  a.scale = scale;
+  a.c2s = scale * 1.4426950408889634f;
+  a.wl = window_left;
+  a.wr = causal ? 0 : window_right;
+  a.cu = cu_seqlens;
+  a.rs = H * d;
+  a.total = total;
+  hipError_t e = fa::launch_bwd(a, d, stream, take_timer());
+  if (e != hipSuccess) return fail(FA_ERR_HIP, "backward launch failed: %s", hipGetErrorString(e));
   return FA_OK;
 }
 

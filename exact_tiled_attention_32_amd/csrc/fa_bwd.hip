@@ -37,7 +37,9 @@ constexpr int kBK = kBwdKeyTile;  // keys per dK/dV workgroup (32 per wave)
 template <int D>
 __global__ __launch_bounds__(kThreads) void bwd_pre_kernel(BwdArgs a) {
   constexpr int LPR = D / 8;  // lanes per row
-  const size_t rows = (size_t)a.B * a.H * a.N;
+  // Rows of d elements, contiguous in both layouts: [B, H, N] order, or [total, H] order
+  // for packed sequences (whose D goes to [H, total], like their lse).
+  const size_t rows = a.cu ? (size_t)a.total * a.H : (size_t)a.B * a.H * a.N;
   const size_t gid = (size_t)blockIdx.x * kThreads + threadIdx.x;
   const size_t row = gid / LPR;
   const int c0 = (int)(gid % LPR) * 8;
@@ -50,7 +52,10 @@ __global__ __launch_bounds__(kThreads) void bwd_pre_kernel(BwdArgs a) {
   }
 #pragma unroll
   for (int off = LPR / 2; off > 0; off >>= 1) acc += __shfl_xor(acc, off);
-  if (row < rows && (gid % LPR) == 0) a.dsum[row] = acc;
+  if (row < rows && (gid % LPR) == 0) {
+    const size_t at = a.cu ? (row % a.H) * (size_t)a.total + row / a.H : row;
+    a.dsum[at] = acc;
+  }
 }
 
 // ---------------------------------------------------------------------------------------
@@ -194,19 +199,25 @@ __global__ __launch_bounds__(kMainThreads, 1) void bwd_dkdv_kernel(BwdArgs a) {
   const int kg = w & 3, qh = w >> 2;
   const int key = k0 + 32 * kg + kl;    // the key this lane's accumulator columns refer to
   const int qw0 = 32 * QBW * qh;        // the wave's first query row inside a step
-  const size_t hoff = (size_t)bh * a.N * D;
+  const HeadSlice sl = head_slice<D>(a, bh);
+  const int N = sl.N;
+  if (k0 >= N) return;  // a key tile past the end of a shorter sequence (uniform)
+  const size_t hoff = sl.hoff, rs = (size_t)a.rs;
   const __bf16* __restrict__ Q = reinterpret_cast<const __bf16*>(a.q) + hoff;
   const __bf16* __restrict__ K = reinterpret_cast<const __bf16*>(a.k) + hoff;
   const __bf16* __restrict__ V = reinterpret_cast<const __bf16*>(a.v) + hoff;
   const __bf16* __restrict__ dO = reinterpret_cast<const __bf16*>(a.dout) + hoff;
-  const float* __restrict__ lse = a.lse + (size_t)bh * a.N;
-  const float* __restrict__ dsum = a.dsum + (size_t)bh * a.N;
+  const float* __restrict__ lse = a.lse + sl.loff;
+  const float* __restrict__ dsum = a.dsum + sl.loff;
 
-  int kv_end = a.N;
-  if (a.kv_len) kv_end = min(max(a.kv_len[b], 0), a.N);
-  const int ntq = (a.N + BQ - 1) / BQ;
-  const int i0 = a.causal ? k0 / BQ : 0;
-  int nq = k0 < kv_end ? ntq - i0 : 0;  // key tile entirely padded: no work, zero dK/dV
+  int kv_end = N;
+  if (a.kv_len) kv_end = min(max(a.kv_len[b], 0), N);
+  // Query tiles [i0, i1) that may attend to a key of this tile: query i sees key j iff
+  // i - wl <= j <= i + wr, i.e. j - wr <= i <= j + wl.
+  const int ntq = (N + BQ - 1) / BQ;
+  const int i0 = a.wr >= 0 ? max(k0 - a.wr, 0) / BQ : 0;
+  const int i1 = a.wl >= 0 ? min((min(k0 + kBK - 1 + a.wl, N - 1)) / BQ + 1, ntq) : ntq;
+  int nq = k0 < kv_end ? max(i1 - i0, 0) : 0;  // key tile entirely padded: zero dK/dV
   if (a.mask && nq > 0)
     nq = __builtin_amdgcn_readfirstlane(build_qtile_list512(qlist, wcount, a.mask, k0 / a.mb, a.nb, a.mb, i0, ntq, BQ));
 
@@ -215,10 +226,10 @@ __global__ __launch_bounds__(kMainThreads, 1) void bwd_dkdv_kernel(BwdArgs a) {
   for (int c = 0; c < KCH; ++c) {
     const int id = tid + kMainThreads * c;
     const int row = id / (D / 8), col = (id % (D / 8)) * 8;
-    const int kk = min(k0 + row, a.N - 1);
-    const bool ok = k0 + row < a.N;
-    const u32x4 kv = gload16(K + (size_t)kk * D + col);
-    const u32x4 vv = gload16(V + (size_t)kk * D + col);
+    const int kk = min(k0 + row, N - 1);
+    const bool ok = k0 + row < N;
+    const u32x4 kv = gload16(K + (size_t)kk * rs + col);
+    const u32x4 vv = gload16(V + (size_t)kk * rs + col);
     lds_store16(kt + tile_off<D>(row, col), ok ? kv : u32x4{});
     lds_store16(vt + tile_off<D>(row, col), ok ? vv : u32x4{});
   }
@@ -262,7 +273,7 @@ __global__ __launch_bounds__(kMainThreads, 1) void bwd_dkdv_kernel(BwdArgs a) {
     FA_LDS char* qb = (FA_LDS char*)(decltype(bufc)::value ? qd1 : qd0);
 #pragma unroll
     for (int c = 0; c < NDMA; ++c) {
-      const size_t row = (size_t)min(q0 + dma_row0 + c * 8 * RPB, a.N - 1) * D + dma_col;
+      const size_t row = (size_t)min(q0 + dma_row0 + c * 8 * RPB, N - 1) * rs + dma_col;
       FA_LDS char* blk = qb + (c * 8 + w) * 1024;
       // (the builtin takes a non-const pointer; without the cast the host pass silently
       // drops the kernel's launch stub)
@@ -271,9 +282,9 @@ __global__ __launch_bounds__(kMainThreads, 1) void bwd_dkdv_kernel(BwdArgs a) {
     }
     // threads [0, BQ) stage lse, threads [BQ, 2 BQ) stage D
     const int qq = q0 + (tid % BQ);
-    svalid = qq < a.N;
+    svalid = qq < N;
     const float* src = tid < BQ ? lse : dsum;
-    sr = src[min(qq, a.N - 1)];
+    sr = src[min(qq, N - 1)];
   };
   auto store_stats = [&](int buf) {
     if (tid < 2 * BQ) {
@@ -370,13 +381,15 @@ __global__ __launch_bounds__(kMainThreads, 1) void bwd_dkdv_kernel(BwdArgs a) {
       }
     // Tiles that cross the causal diagonal or the key padding (a wave-uniform test): the
     // masked pairs get P = dS = 0, by selection, so whatever was computed there is dropped.
-    if ((k0 + 32 * kg + 31 >= kv_end) || (a.causal && k0 + 32 * kg + 31 > q0 + qw0)) {
+    const int kk0 = k0 + 32 * kg, qa = q0 + qw0;  // the wave's first key and first query
+    if ((kk0 + 31 >= kv_end) || (a.wr >= 0 && kk0 + 31 > qa + a.wr) ||
+        (a.wl >= 0 && kk0 < qa + 32 * QBW - 1 - a.wl)) {
 #pragma unroll
       for (int b2 = 0; b2 < QBW; ++b2)
 #pragma unroll
         for (int i = 0; i < 16; ++i) {
           const int qrow = q0 + qw0 + 32 * b2 + 8 * (i >> 2) + 4 * h + (i & 3);
-          const bool masked = key >= kv_end || (a.causal && key > qrow);
+          const bool masked = key >= kv_end || (a.wr >= 0 && key > qrow + a.wr) || (a.wl >= 0 && key < qrow - a.wl);
           s[b2][i] = masked ? 0.f : s[b2][i];
           dp[b2][i] = masked ? 0.f : dp[b2][i];
         }
@@ -439,9 +452,9 @@ __global__ __launch_bounds__(kMainThreads, 1) void bwd_dkdv_kernel(BwdArgs a) {
       }
   }
   __syncthreads();
-  if (qh == 0 && key < a.N) {
-    __bf16* dK = reinterpret_cast<__bf16*>(a.dk) + hoff + (size_t)key * D;
-    __bf16* dV = reinterpret_cast<__bf16*>(a.dv) + hoff + (size_t)key * D;
+  if (qh == 0 && key < N) {
+    __bf16* dK = reinterpret_cast<__bf16*>(a.dk) + hoff + (size_t)key * rs;
+    __bf16* dV = reinterpret_cast<__bf16*>(a.dv) + hoff + (size_t)key * rs;
 #pragma unroll
     for (int md = 0; md < MD; ++md)
 #pragma unroll
@@ -501,18 +514,23 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dq_kernel(BwdArgs a) {
   const int q0 = qt * kDqRows;
   const int tid = threadIdx.x, w = wave_id(), l = tid & 63, h = l >> 5, ql = l & 31;
   const int qi = q0 + 32 * w + ql;
-  const size_t hoff = (size_t)bh * a.N * D;
+  const HeadSlice sl = head_slice<D>(a, bh);
+  const int N = sl.N;
+  if (q0 >= N) return;  // a query tile past the end of a shorter sequence (uniform)
+  const size_t hoff = sl.hoff, rs = (size_t)a.rs;
   const __bf16* __restrict__ Q = reinterpret_cast<const __bf16*>(a.q) + hoff;
   const __bf16* __restrict__ K = reinterpret_cast<const __bf16*>(a.k) + hoff;
   const __bf16* __restrict__ V = reinterpret_cast<const __bf16*>(a.v) + hoff;
   const __bf16* __restrict__ dO = reinterpret_cast<const __bf16*>(a.dout) + hoff;
 
-  int kv_end = a.N;
-  if (a.kv_len) kv_end = min(max(a.kv_len[b], 0), a.N);
+  int kv_end = N;
+  if (a.kv_len) kv_end = min(max(a.kv_len[b], 0), N);
+  // Key range of the workgroup's rows under the window: tiles [t0, ntk).
   int hi = kv_end;
-  if (a.causal) hi = min(hi, q0 + kDqRows);
+  if (a.wr >= 0) hi = min(hi, q0 + kDqRows + a.wr);
+  const int t0 = a.wl >= 0 ? max(q0 - a.wl, 0) / kDqKeys : 0;
   const int ntk = (hi + kDqKeys - 1) / kDqKeys;
-  int ntiles = ntk;
+  int ntiles = max(ntk - t0, 0);
   if (a.mask) {
     // key tiles of this query tile's mask row (128 rows never straddle two mask rows)
     const int rb = q0 / a.mb;
@@ -536,17 +554,17 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dq_kernel(BwdArgs a) {
   // The wave's Q and dO rows (B operands), and its row statistics in the exp2 domain.
   bf16x8 qf[KS], df[KS];
   {
-    const size_t row = (size_t)min(qi, a.N - 1) * D + 8 * h;
+    const size_t row = (size_t)min(qi, N - 1) * rs + 8 * h;
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) {
       qf[ks] = __builtin_bit_cast(bf16x8, gload16(Q + row + 16 * ks));
       df[ks] = __builtin_bit_cast(bf16x8, gload16(dO + row + 16 * ks));
     }
   }
-  const float lse_v = a.lse[(size_t)bh * a.N + min(qi, a.N - 1)];
+  const float lse_v = a.lse[sl.loff + min(qi, N - 1)];
   // an empty row (lse = -inf) and a row past N get lse2 = +inf, so P = 0 there
-  const float lse2 = (qi >= a.N || lse_v == kNegInf) ? __builtin_inff() : lse_v * kLog2e;
-  const float dval = a.dsum[(size_t)bh * a.N + min(qi, a.N - 1)];
+  const float lse2 = (qi >= N || lse_v == kNegInf) ? __builtin_inff() : lse_v * kLog2e;
+  const float dval = a.dsum[sl.loff + min(qi, N - 1)];
   // The fragments are read in every step: let them land here, so that no wait for them is
   // left inside the loop.
   __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
@@ -562,7 +580,7 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dq_kernel(BwdArgs a) {
   const int dma_col = ((l % CH) ^ swz<D>(dma_row0)) * 8;
   int dma_off[NDMA];
 #pragma unroll
-  for (int c = 0; c < NDMA; ++c) dma_off[c] = ((dma_row0 + 4 * RPB * c) * D + dma_col) * 2;
+  for (int c = 0; c < NDMA; ++c) dma_off[c] = ((dma_row0 + 4 * RPB * c) * a.rs + dma_col) * 2;
 
   f32x16 dq[MD];
 #pragma unroll
@@ -570,13 +588,13 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dq_kernel(BwdArgs a) {
 
   auto tile_at = [&](int t) {
     const int tc = min(t, max(ntiles - 1, 0));
-    return a.mask ? __builtin_amdgcn_readfirstlane((int)tlist[tc]) : tc;
+    return a.mask ? __builtin_amdgcn_readfirstlane((int)tlist[tc]) : t0 + tc;
   };
   auto stage = [&](int jt, auto bufc) {
     const int key0 = jt * kDqKeys;
-    const uint32_t bytes = (uint32_t)max(a.N - key0, 0) * (uint32_t)(D * 2);
-    const auto rk = make_rsrc(K + (size_t)key0 * D, bytes);
-    const auto rv = make_rsrc(V + (size_t)key0 * D, bytes);
+    const uint32_t bytes = (uint32_t)max(N - key0, 0) * (uint32_t)(a.rs * 2);
+    const auto rk = make_rsrc(K + (size_t)key0 * rs, bytes);
+    const auto rv = make_rsrc(V + (size_t)key0 * rs, bytes);
     FA_LDS char* base = (FA_LDS char*)(decltype(bufc)::value ? kv1 : kv0);
 #pragma unroll
     for (int c = 0; c < NDMA; ++c) {
@@ -605,8 +623,9 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dq_kernel(BwdArgs a) {
     th0 = t_hi0;
     asm volatile("" : "+v"(ko0), "+v"(tl0), "+v"(th0));
     const int key0 = jt * kDqKeys;
-    // A wave whose queries all precede the tile (causal) has nothing to do here.
-    if (!(a.causal && key0 > q0 + 32 * w + 31)) {
+    // A wave whose queries all lie outside the tile's window has nothing to do here.
+    const int qw = q0 + 32 * w;
+    if (!((a.wr >= 0 && key0 > qw + 31 + a.wr) || (a.wl >= 0 && key0 + kDqKeys - 1 < qw - a.wl))) {
       // S^T, dP^T: items (ks, kb) with the key block innermost, so that four independent
       // accumulations alternate; each item's K / V rows are requested one item ahead.
       f32x16 s[KB], dp[KB];
@@ -644,13 +663,15 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dq_kernel(BwdArgs a) {
         }
       // Tiles that cross the causal diagonal or the key padding (a wave-uniform test):
       // masked pairs get dS = 0 by selection.
-      if ((key0 + kDqKeys > kv_end) || (a.causal && key0 + kDqKeys - 1 > q0 + 32 * w)) {
+      if ((key0 + kDqKeys > kv_end) || (a.wr >= 0 && key0 + kDqKeys - 1 > qw + a.wr) ||
+          (a.wl >= 0 && key0 < qw + 31 - a.wl)) {
 #pragma unroll
         for (int kbk = 0; kbk < KB; ++kbk)
 #pragma unroll
           for (int i = 0; i < 16; ++i) {
             const int key = key0 + 32 * kbk + 8 * (i >> 2) + 4 * h + (i & 3);
-            dp[kbk][i] = (key >= kv_end || (a.causal && key > qi)) ? 0.f : dp[kbk][i];
+            const bool masked = key >= kv_end || (a.wr >= 0 && key > qi + a.wr) || (a.wl >= 0 && key < qi - a.wl);
+            dp[kbk][i] = masked ? 0.f : dp[kbk][i];
           }
       }
       bf16x8 dsb[PS];
@@ -683,8 +704,8 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dq_kernel(BwdArgs a) {
     if (t + 1 < ntiles) step(std::integral_constant<int, 1>{}, t + 1);
   }
 
-  if (qi < a.N) {
-    __bf16* dQ = reinterpret_cast<__bf16*>(a.dq) + hoff + (size_t)qi * D;
+  if (qi < N) {
+    __bf16* dQ = reinterpret_cast<__bf16*>(a.dq) + hoff + (size_t)qi * rs;
 #pragma unroll
     for (int md = 0; md < MD; ++md)
 #pragma unroll
@@ -700,7 +721,7 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dq_kernel(BwdArgs a) {
 }  // namespace
 
 hipError_t launch_bwd(const BwdArgs& a, int d, hipStream_t stream, const KernelTimer& tm) {
-  const size_t rows = (size_t)a.B * a.H * a.N;
+  const size_t rows = a.cu ? (size_t)a.total * a.H : (size_t)a.B * a.H * a.N;
   const size_t pre_threads = rows * (size_t)(d / 8);
   const dim3 block(kThreads);
   const dim3 gpre((unsigned)((pre_threads + kThreads - 1) / kThreads));

@@ -149,6 +149,23 @@ __device__ __forceinline__ float other_half(float x) {
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
+// The (b, h) slice of a call: its row count, the element offset of its first row and the
+// offset of its lse / D rows. Dense [B, H, N, d]: every slice has N rows of stride d.
+// Packed sequences [total, H, d] (a.cu != nullptr): sequence b owns tokens cu[b] ..
+// cu[b+1] - 1 (clamped into [0, total], so no boundary array can send an access outside
+// the tensors), rows are a.rs = H d apart, lse / D are [H, total].
+struct HeadSlice {
+  int N;
+  size_t hoff, loff;
+};
+template <int D, class Args>
+__device__ __forceinline__ HeadSlice head_slice(const Args& a, int bh) {
+  if (!a.cu) return HeadSlice{a.N, (size_t)bh * a.N * D, (size_t)bh * a.N};
+  const int b = bh / a.H, hh = bh % a.H;
+  const int c0 = min(max(a.cu[b], 0), a.total), c1 = min(max(a.cu[b + 1], c0), a.total);
+  return HeadSlice{c1 - c0, (size_t)c0 * a.rs + (size_t)hh * D, (size_t)hh * a.total + c0};
+}
+
 // 16-byte global load/store helpers (addresses 16-byte aligned).
 __device__ __forceinline__ u32x4 gload16(const void* p) { return *reinterpret_cast<const u32x4*>(p); }
 __device__ __forceinline__ void lds_store16(FA_LDS char* p, u32x4 v) { *reinterpret_cast<FA_LDS u32x4*>(p) = v; }

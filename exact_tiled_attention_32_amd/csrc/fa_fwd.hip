@@ -94,32 +94,38 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_bf16_kernel(FwdArgs a) {
   const int q0 = qt * kBR;
   const int tid = threadIdx.x, w = wave_id(), l = tid & 63, h = l >> 5, ql = l & 31;
   const int qi = q0 + 32 * w + ql;
-  const size_t hoff = (size_t)bh * a.N * D;
+  const HeadSlice sl = head_slice<D>(a, bh);
+  const int N = sl.N;
+  const size_t hoff = sl.hoff, loff = sl.loff;
+  if (q0 >= N) return;  // a query tile past the end of a shorter sequence (uniform)
+  const size_t rs = (size_t)a.rs;
   const __bf16* __restrict__ Q = reinterpret_cast<const __bf16*>(a.q) + hoff;
   const __bf16* __restrict__ K = reinterpret_cast<const __bf16*>(a.k) + hoff;
   const __bf16* __restrict__ V = reinterpret_cast<const __bf16*>(a.v) + hoff;
 
-  int kv_end = a.N;
-  if (a.kv_len) kv_end = min(max(a.kv_len[b], 0), a.N);
+  int kv_end = N;
+  if (a.kv_len) kv_end = min(max(a.kv_len[b], 0), N);
+  // Key range of the workgroup's rows under the window: [lo, hi).
   int hi = kv_end;
-  if (a.causal) hi = min(hi, q0 + kBR);
+  if (a.wr >= 0) hi = min(hi, q0 + kBR + a.wr);
+  const int t0 = a.wl >= 0 ? max(q0 - a.wl, 0) / kBC : 0;
   const int ntk = (hi + kBC - 1) / kBC;
-  int ntiles = ntk;
+  int ntiles = max(ntk - t0, 0);
   if (a.mask)
     ntiles = __builtin_amdgcn_readfirstlane(build_tile_list(tlist, wcount, a.mask, q0 / a.mb, a.nb, a.mb, ntk, kBC));
   // Key tile of step t, clamped so that the look-ahead of the last steps stays valid.
   auto tile_at = [&](int t) {
     const int tc = min(t, max(ntiles - 1, 0));
-    return a.mask ? __builtin_amdgcn_readfirstlane((int)tlist[tc]) : tc;
+    return a.mask ? __builtin_amdgcn_readfirstlane((int)tlist[tc]) : t0 + tc;
   };
 
   // Q fragments: B operand of S^T = K Q^T, lane holds Q[qi][16 ks + 8h .. +7].
   bf16x8 qf[KS];
   {
-    const __bf16* qrow = Q + (size_t)min(qi, a.N - 1) * D + 8 * h;
+    const __bf16* qrow = Q + (size_t)min(qi, N - 1) * rs + 8 * h;
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) qf[ks] = __builtin_bit_cast(bf16x8, gload16(qrow + 16 * ks));
-    const float qm = qi < a.N ? a.qmul : 0.f;
+    const float qm = qi < N ? a.qmul : 0.f;
     if (qm != 1.0f) {
 #pragma unroll
       for (int ks = 0; ks < KS; ++ks)
@@ -141,12 +147,13 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_bf16_kernel(FwdArgs a) {
   // Tile staging by direct buffer -> LDS loads bounded at row N (rows past the end arrive
   // as zeros): instruction c of wave w fills 1 KB block 4c + w of a tile, lane l the 16
   // bytes at 16 l: tile row (4c + w) RPB + l / CH, physical chunk l % CH, which holds the
-  // logical chunk (l % CH) ^ swz(row); the row step 4 RPB keeps swz unchanged.
+  // logical chunk (l % CH) ^ swz(row); the row step 4 RPB keeps swz unchanged. Global rows
+  // are rs elements apart (d for [B, H, N, d], H d for packed tokens).
   const int dma_row0 = w * RPB + l / CH;
   const int dma_col = ((l % CH) ^ swz<D>(dma_row0)) * 8;
   int dma_off[NDMA];
 #pragma unroll
-  for (int c = 0; c < NDMA; ++c) dma_off[c] = ((dma_row0 + 4 * RPB * c) * D + dma_col) * 2;
+  for (int c = 0; c < NDMA; ++c) dma_off[c] = ((dma_row0 + 4 * RPB * c) * a.rs + dma_col) * 2;
 
   f32x16 o[MD];
 #pragma unroll
@@ -156,7 +163,7 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_bf16_kernel(FwdArgs a) {
 
   auto stage = [&](const __bf16* base, int jt, FA_LDS char* buf) {
     const int key0 = jt * kBC;
-    const auto r = make_rsrc(base + (size_t)key0 * D, (uint32_t)max(a.N - key0, 0) * (uint32_t)(D * 2));
+    const auto r = make_rsrc(base + (size_t)key0 * rs, (uint32_t)max(N - key0, 0) * (uint32_t)(a.rs * 2));
 #pragma unroll
     for (int c = 0; c < NDMA; ++c) {
       // (an array element passed straight to the builtin makes the host pass silently drop
@@ -182,13 +189,16 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_bf16_kernel(FwdArgs a) {
   // Masking of an edge tile, its row maximum and the lazy rescale (a wave-uniform branch).
   auto rowmax_update = [&](int jt, f32x16 (&s)[KB]) {
     const int key0 = jt * kBC;
-    if ((key0 + kBC > kv_end) || (a.causal && key0 + kBC - 1 > q0 + 32 * w)) {
+    const int qw = q0 + 32 * w;  // the wave's first row
+    if ((key0 + kBC > kv_end) || (a.wr >= 0 && key0 + kBC - 1 > qw + a.wr) ||
+        (a.wl >= 0 && key0 < qw + 31 - a.wl)) {
 #pragma unroll
       for (int kbk = 0; kbk < KB; ++kbk)
 #pragma unroll
         for (int i = 0; i < 16; ++i) {
           const int key = key0 + 32 * kbk + 8 * (i >> 2) + 4 * h + (i & 3);
-          if (key >= kv_end || (a.causal && key > qi)) s[kbk][i] = kNegInf;
+          if (key >= kv_end || (a.wr >= 0 && key > qi + a.wr) || (a.wl >= 0 && key < qi - a.wl))
+            s[kbk][i] = kNegInf;
         }
     }
     float tmax = kNegInf;
@@ -277,9 +287,9 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_bf16_kernel(FwdArgs a) {
   }
 
   const float l_tot = l_run + other_half(l_run);
-  if (qi < a.N) {
+  if (qi < N) {
     const float inv = l_tot > 0.f ? 1.0f / l_tot : 0.f;
-    __bf16* O = reinterpret_cast<__bf16*>(a.o) + hoff + (size_t)qi * D;
+    __bf16* O = reinterpret_cast<__bf16*>(a.o) + hoff + (size_t)qi * rs;
 #pragma unroll
     for (int md = 0; md < MD; ++md)
 #pragma unroll
@@ -289,7 +299,7 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_bf16_kernel(FwdArgs a) {
         for (int e = 0; e < 4; ++e) ov[e] = (__bf16)(o[md][4 * g + e] * inv);
         *reinterpret_cast<bf16x4*>(O + 32 * md + 8 * g + 4 * h) = ov;
       }
-    if (h == 0) a.lse[(size_t)bh * a.N + qi] = l_tot > 0.f ? m_run * a.sc_abs + logf(l_tot) : kNegInf;
+    if (h == 0) a.lse[loff + qi] = l_tot > 0.f ? m_run * a.sc_abs + logf(l_tot) : kNegInf;
   }
 }
 

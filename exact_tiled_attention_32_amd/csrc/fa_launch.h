@@ -25,6 +25,15 @@ struct FwdArgs {
   float c2;               // |scale| * log2(e), or log2(e) when scale == 0 (exp2 domain)
   float sc_abs;           // |scale|: lse = m * |scale| + ln l
   float qmul;             // +1, -1 (negative scale) or 0 (zero scale), applied to Q exactly
+  // Sliding window: key j allowed for query i iff i - wl <= j <= i + wr; a negative extent
+  // is unbounded. The host sets wr = 0 for causal attention.
+  int wl, wr;
+  // Packed variable-length sequences (cu != nullptr): B counts sequences, tensors are
+  // [total, H, d] (row stride rs = H d), sequence s owns tokens cu[s] .. cu[s+1] - 1, lse
+  // is [H, total]; N is then the longest sequence. Dense: cu == nullptr, rs == d.
+  const int32_t* cu;
+  int rs;
+  int total;
 };
 
 // Backward arguments, already validated by the host layer.
@@ -46,6 +55,10 @@ struct BwdArgs {
   int causal;
   float scale;            // signed softmax scale
   float c2s;              // scale * log2(e)
+  int wl, wr;             // sliding window, as in FwdArgs
+  const int32_t* cu;      // packed sequences, as in FwdArgs (dsum then [H, total] too)
+  int rs;
+  int total;
 };
 
 // Key/value-cache forward arguments, already validated by the host layer.

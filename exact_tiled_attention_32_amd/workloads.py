@@ -12,7 +12,8 @@ dataset or trained weight is involved.
 
 Generation order per workload: Q, K, V, dO, then the key-padding lengths. Decode
 workloads (a few queries against a key/value cache): Q [B, H, Nq, d], then the cache's
-K and V [B, H, Nk, d], then the cache lengths.
+K and V [B, H, Nk, d], then the cache lengths. Packed variable-length workloads: the
+sequence lengths first (when drawn), then Q, K, V, dO as [total, H, d].
 """
 from __future__ import annotations
 
@@ -22,7 +23,8 @@ from dataclasses import dataclass, field
 import torch
 
 __all__ = ["Workload", "WORKLOADS", "generate", "sparse_block_rule", "make_case",
-           "DecodeWorkload", "DECODE_WORKLOADS", "generate_decode", "make_decode_case"]
+           "DecodeWorkload", "DECODE_WORKLOADS", "generate_decode", "make_decode_case",
+           "VarlenWorkload", "VARLEN_WORKLOADS", "generate_varlen", "make_varlen_case"]
 
 
 @dataclass(frozen=True)
@@ -175,3 +177,69 @@ def make_decode_case(B: int, H: int, Nq: int, Nk: int, d: int, *, seed: int = 0,
     v = torch.randn((B, H, Nk, d), generator=gen).to(torch.bfloat16)
     kl = None if kv_len is None else torch.tensor(kv_len, dtype=torch.int32)
     return {"q": q, "k": k, "v": v, "kv_len": kl, "scale": 1.0 / math.sqrt(d), "causal": causal}
+
+
+@dataclass(frozen=True)
+class VarlenWorkload:
+    """Sequences packed along one token axis ([total, H, d]), optional sliding window."""
+    name: str
+    H: int
+    d: int
+    seed: int
+    lengths: tuple = ()       # fixed lengths, or () to draw n_seq lengths U{lo .. hi}
+    n_seq: int = 0
+    lo: int = 0
+    hi: int = 0
+    causal: bool = False
+    window_left: int = -1
+    window_right: int = -1
+    description: str = field(default="", compare=False)
+
+    @property
+    def scale(self) -> float:
+        return 1.0 / math.sqrt(self.d)
+
+
+VARLEN_WORKLOADS = {
+    "varlen_packed_causal": VarlenWorkload(
+        "varlen_packed_causal", 12, 64, 1201, n_seq=16, lo=128, hi=2048, causal=True,
+        description="16 causal sequences of lengths uniform in [128, 2048] packed into one "
+                    "token axis, GPT-2-shaped heads (H=12, d=64), bf16 fwd+bwd"),
+    "sliding_window_16k": VarlenWorkload(
+        "sliding_window_16k", 16, 128, 1202, lengths=(16384,), causal=True, window_left=4095,
+        description="one causal sequence of 16384 tokens with a 4096-key sliding window "
+                    "(each query sees itself and the 4095 keys before it), H=16, d=128, bf16 fwd+bwd"),
+}
+
+
+def _varlen_tensors(gen, lengths, H, d, q_magnitude=1.0):
+    total = int(sum(lengths))
+    q = (torch.randn((total, H, d), generator=gen) * q_magnitude).to(torch.bfloat16)
+    k, v, do = (torch.randn((total, H, d), generator=gen).to(torch.bfloat16) for _ in range(3))
+    cu = torch.zeros(len(lengths) + 1, dtype=torch.int32)
+    cu[1:] = torch.cumsum(torch.tensor(lengths, dtype=torch.int64), 0).to(torch.int32)
+    return q, k, v, do, cu
+
+
+def generate_varlen(w: VarlenWorkload) -> dict:
+    """CPU tensors q, k, v, do [total, H, d] (bf16), cu_seqlens (int32 [nseq + 1]) and the
+    scalar arguments of a packed workload."""
+    gen = torch.Generator("cpu").manual_seed(w.seed)
+    if w.lengths:
+        lengths = [int(x) for x in w.lengths]
+    else:
+        lengths = torch.randint(w.lo, w.hi + 1, (w.n_seq,), generator=gen, dtype=torch.int64).tolist()
+    q, k, v, do, cu = _varlen_tensors(gen, lengths, w.H, w.d)
+    return {"q": q, "k": k, "v": v, "do": do, "cu_seqlens": cu, "max_seqlen": max(lengths),
+            "scale": w.scale, "causal": w.causal, "window_left": w.window_left,
+            "window_right": w.window_right}
+
+
+def make_varlen_case(lengths, H: int, d: int, *, seed: int = 0, causal: bool = False,
+                     window_left: int = -1, window_right: int = -1, q_magnitude: float = 1.0) -> dict:
+    """A small seeded packed case with the given sequence lengths."""
+    gen = torch.Generator("cpu").manual_seed(seed)
+    q, k, v, do, cu = _varlen_tensors(gen, list(lengths), H, d, q_magnitude)
+    return {"q": q, "k": k, "v": v, "do": do, "cu_seqlens": cu, "max_seqlen": max(list(lengths) + [0]),
+            "scale": 1.0 / math.sqrt(d), "causal": causal, "window_left": window_left,
+            "window_right": window_right}

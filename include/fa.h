@@ -37,7 +37,8 @@
  *     thread-safe. Faults during execution surface at the caller's stream synchronisation.
  *   - bf16 (FA_BF16): d in {64, 128}, forward and backward. fp32 (FA_F32): d in {64, 128},
  *     forward only. The key/value-cache forward takes its own query and key counts
- *     (Nq, Nk) in place of N; its tensors follow the same layout.
+ *     (Nq, Nk) in place of N; its tensors follow the same layout. The packed
+ *     variable-length calls use [total, H, d] tensors and [H, total] lse instead.
  */
 #ifndef EXACT_TILED_ATTENTION_FA_H
 #define EXACT_TILED_ATTENTION_FA_H
@@ -132,6 +133,56 @@ fa_status fa_bwd(fa_dtype dt, int B, int H, int N, int d,
                  hipStream_t stream);
 
 /*
+ * Packed variable-length sequences with an optional sliding window (bf16, d in {64, 128}).
+ * aiwiki "FlashAttention", section "Software integration and limitations", lists
+ * variable-length sequences and sliding-window masks among the interfaces; the cochat.ai
+ * audit's citation check of the Longformer reference describes sliding-window attention as
+ * each query attending a fixed window of keys.
+ *   nseq, H, d     sequences, heads, head dimension
+ *   total          tokens over all sequences (0 is allowed: nothing is launched)
+ *   max_seqlen     an upper bound of every sequence length (sizes the grid; a longer
+ *                  sequence leaves its rows past max_seqlen unwritten)
+ *   cu_seqlens     device int32 [nseq + 1]: sequence s owns tokens cu[s] .. cu[s+1] - 1;
+ *                  cu[0] = 0, nondecreasing, cu[nseq] = total (values are clamped into
+ *                  [0, total], so no boundary array makes the kernels access memory
+ *                  outside the tensors)
+ *   q, k, v, o     [total, H, d] row-major (tokens of all sequences, one after another)
+ *   lse            [H, total] fp32, natural log
+ *   causal         nonzero: key j allowed only for j <= i (positions inside the sequence)
+ *   window_left    >= 0: key j allowed only for j >= i - window_left; -1: unbounded
+ *   window_right   >= 0: key j allowed only for j <= i + window_right; -1: unbounded
+ *                  (ignored when causal, which already bounds j <= i)
+ * Attention never crosses a sequence boundary. A row with no allowed key yields O = 0,
+ * lse = -inf and a zero dQ row. The kernels are those of fa_fwd / fa_bwd; key tiles that
+ * lie wholly outside a query tile's window are not read.
+ */
+fa_status fa_fwd_varlen(fa_dtype dt, int nseq, int H, int total, int max_seqlen, int d,
+                        const int32_t* cu_seqlens,
+                        const void* q, const void* k, const void* v,
+                        void* o, float* lse,
+                        float scale, int causal, int window_left, int window_right,
+                        hipStream_t stream);
+
+/* Bytes of device workspace fa_bwd_varlen needs: D = rowsum(dO * O), fp32 [H, total],
+ * rounded up to 256 bytes. Returns 0 for non-positive H or d, negative total or overflow. */
+size_t fa_bwd_varlen_workspace_bytes(int H, int total, int d);
+
+/*
+ * Backward of fa_fwd_varlen (same arguments; o and lse from the forward call): dq, dk, dv
+ * [total, H, d]. workspace: device memory of at least fa_bwd_varlen_workspace_bytes(H,
+ * total, d) bytes, 256-byte aligned, owned by the caller, overwritten. Deterministic (no
+ * atomics), as fa_bwd.
+ */
+fa_status fa_bwd_varlen(fa_dtype dt, int nseq, int H, int total, int max_seqlen, int d,
+                        const int32_t* cu_seqlens,
+                        const void* q, const void* k, const void* v,
+                        const void* o, const void* dout, const float* lse,
+                        void* dq, void* dk, void* dv,
+                        float scale, int causal, int window_left, int window_right,
+                        void* workspace, size_t workspace_bytes,
+                        hipStream_t stream);
+
+/*
  * Bytes of device workspace fa_fwd_kvcache needs for the partial results of its key split:
  * B*H*units*Nq*(4d + 8) bytes (three regions, each rounded up to 256 bytes), where units
  * is the number of key ranges each (b, h) is split into, chosen from B, H and Nk (about
@@ -170,11 +221,11 @@ fa_status fa_fwd_kvcache(fa_dtype dt, int B, int H, int Nq, int Nk, int d,
 
 /*
  * Measurement hook. When both events are non-NULL, the next fa_fwd, fa_fwd_blocksparse,
- * fa_fwd_kvcache or fa_bwd call on the calling thread that passes validation records
- * `start` on its stream immediately before launching its dominant kernel (the forward
- * kernel, the key-split kernel of the cache forward, or the backward main kernel) and
- * `stop` immediately after it, then forgets both events. Passing NULL clears a pending
- * request. The events are owned by the caller.
+ * fa_fwd_varlen, fa_fwd_kvcache, fa_bwd or fa_bwd_varlen call on the calling thread that
+ * passes validation records `start` on its stream immediately before launching its
+ * dominant kernel (the forward kernel, the key-split kernel of the cache forward, or the
+ * backward main kernel) and `stop` immediately after it, then forgets both events.
+ * Passing NULL clears a pending request. The events are owned by the caller.
  */
 void fa_time_next_kernel(hipEvent_t start, hipEvent_t stop);
 

@@ -191,3 +191,57 @@ def kvc(lib, dt=fa.FA_BF16, B=1, H=1, Nq=1, Nk=256, d=64, q=P, k=P, v=P, o=P, ls
 def test_kvcache_rejects(lib, kwargs, status):
     assert kvc(lib, **kwargs) == status
     assert lib.fa_last_error().decode()
+
+
+def test_varlen_workspace_bytes(lib):
+    al = lambda x: (x + 255) // 256 * 256
+    for H, total, d in [(1, 1, 64), (12, 19432, 64), (16, 16384, 128), (2, 0, 64)]:
+        assert fa.fa_bwd_varlen_workspace_bytes(H, total, d) == al(H * total * 4)
+    assert fa.fa_bwd_varlen_workspace_bytes(0, 5, 64) == 0
+    assert fa.fa_bwd_varlen_workspace_bytes(2, -1, 64) == 0
+
+
+def fvar(lib, dt=fa.FA_BF16, nseq=2, H=2, total=300, max_seqlen=200, d=64, cu=P, q=P, o=P, lse=P,
+         scale=0.125, causal=1, wl=-1, wr=-1):
+    c = ctypes.c_void_p
+    return lib.fa_fwd_varlen(dt, nseq, H, total, max_seqlen, d, None if cu is None else c(cu), c(q), c(P),
+                             c(P), c(o), c(lse), scale, causal, wl, wr, None)
+
+
+@pytest.mark.parametrize("kwargs, status", [
+    (dict(cu=None), fa.FA_ERR_INVALID),
+    (dict(cu=P + 2), fa.FA_ERR_INVALID),
+    (dict(q=0), fa.FA_ERR_INVALID),
+    (dict(o=P + 8), fa.FA_ERR_INVALID),
+    (dict(lse=P + 1), fa.FA_ERR_INVALID),
+    (dict(nseq=0), fa.FA_ERR_INVALID),
+    (dict(H=0), fa.FA_ERR_INVALID),
+    (dict(total=-1), fa.FA_ERR_INVALID),
+    (dict(max_seqlen=-1), fa.FA_ERR_INVALID),
+    (dict(max_seqlen=1 << 30, H=64, nseq=1 << 12), fa.FA_ERR_INVALID),  # grid size overflow
+    (dict(wl=-2), fa.FA_ERR_INVALID),
+    (dict(wr=-5), fa.FA_ERR_INVALID),
+    (dict(scale=float("nan")), fa.FA_ERR_INVALID),
+    (dict(dt=fa.FA_F32), fa.FA_ERR_UNSUPPORTED),
+    (dict(d=32), fa.FA_ERR_UNSUPPORTED),
+])
+def test_varlen_rejects(lib, kwargs, status):
+    assert fvar(lib, **kwargs) == status
+    assert lib.fa_last_error().decode()
+
+
+def test_varlen_no_tokens_launches_nothing(lib):
+    # zero tokens: valid, returns before touching any tensor pointer (even NULL ones)
+    assert fvar(lib, total=0, max_seqlen=0, q=0, o=0, lse=0) == fa.FA_OK
+
+
+def test_varlen_bwd_rejects(lib):
+    c = ctypes.c_void_p
+    need = fa.fa_bwd_varlen_workspace_bytes(2, 300, 64)
+    call = lambda ws, nbytes, dq=P: lib.fa_bwd_varlen(fa.FA_BF16, 2, 2, 300, 200, 64, c(P), c(P), c(P), c(P), c(P),
+                                                      c(P), c(P), c(dq), c(P), c(P), 0.125, 1, -1, -1,
+                                                      None if ws is None else c(ws), nbytes, None)
+    assert call(None, need) == fa.FA_ERR_INVALID
+    assert call(P + 16, need) == fa.FA_ERR_INVALID
+    assert call(P, need - 1) == fa.FA_ERR_INVALID
+    assert call(P, need, dq=0) == fa.FA_ERR_INVALID
