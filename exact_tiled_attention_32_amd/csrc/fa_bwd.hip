@@ -727,7 +727,8 @@ hipError_t launch_bwd(const BwdArgs& a, int d, hipStream_t stream, const KernelT
   const dim3 gpre((unsigned)((pre_threads + kThreads - 1) / kThreads));
   const dim3 gdkdv((unsigned)(((a.N + kBK - 1) / kBK) * a.B * a.H)), bdkdv(kMainThreads);
   const dim3 gdq((unsigned)(((a.N + kDqRows - 1) / kDqRows) * a.B * a.H));
-  if (d == 64) hipLaunchKernelGGL(bwd_pre_kernel<64>, gpre, block, 0, stream, a);
+  if (d == 32) hipLaunchKernelGGL(bwd_pre_kernel<32>, gpre, block, 0, stream, a);
+  else if (d == 64) hipLaunchKernelGGL(bwd_pre_kernel<64>, gpre, block, 0, stream, a);
   else hipLaunchKernelGGL(bwd_pre_kernel<128>, gpre, block, 0, stream, a);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
@@ -738,12 +739,14 @@ hipError_t launch_bwd(const BwdArgs& a, int d, hipStream_t stream, const KernelT
     if (e != hipSuccess) return e;
   }
   if (tm.start) (void)hipEventRecord(tm.start, stream);
-  if (d == 64) hipLaunchKernelGGL(bwd_dkdv_kernel<64>, gdkdv, bdkdv, 0, stream, a);
+  if (d == 32) hipLaunchKernelGGL(bwd_dkdv_kernel<32>, gdkdv, bdkdv, 0, stream, a);
+  else if (d == 64) hipLaunchKernelGGL(bwd_dkdv_kernel<64>, gdkdv, bdkdv, 0, stream, a);
   else hipLaunchKernelGGL(bwd_dkdv_kernel<128>, gdkdv, bdkdv, 0, stream, a);
   e = hipGetLastError();
   if (tm.stop) (void)hipEventRecord(tm.stop, stream);
   if (e != hipSuccess) return e;
-  if (d == 64) hipLaunchKernelGGL(bwd_dq_kernel<64>, gdq, block, 0, stream, a);
+  if (d == 32) hipLaunchKernelGGL(bwd_dq_kernel<32>, gdq, block, 0, stream, a);
+  else if (d == 64) hipLaunchKernelGGL(bwd_dq_kernel<64>, gdq, block, 0, stream, a);
   else hipLaunchKernelGGL(bwd_dq_kernel<128>, gdq, block, 0, stream, a);
   return hipGetLastError();
 }

@@ -43,6 +43,7 @@ constexpr int kNonTemporal = 2;
 // kernel. A stage holds one K tile and one V tile (2 x 32 x D bf16) in LDS; a wave keeps
 // S - 1 tiles in flight while it computes one, so LDS bounds the bytes in flight.
 template <int D> struct SplitShape;
+template <> struct SplitShape<32> { static constexpr int W = 4, S = 4; };
 template <> struct SplitShape<64> { static constexpr int W = 4, S = 4; };
 template <> struct SplitShape<128> { static constexpr int W = 3, S = 3; };
 
@@ -310,7 +311,7 @@ __global__ __launch_bounds__(kThreads) void kvc_merge_kernel(DecArgs a) {
 void kvcache_split_plan(int B, int H, int Nk, int d, int* chunk, int* units) {
   // about kTargetUnits units in all, each a multiple of the tile; the units of a (b, h)
   // rounded up to whole workgroups
-  const int W = d == 64 ? SplitShape<64>::W : SplitShape<128>::W;
+  const int W = kvcache_split_waves(d);
   const long long total = (long long)B * H * Nk;
   long long c = (total + kTargetUnits - 1) / kTargetUnits;
   c = (c + kKT - 1) / kKT * kKT;
@@ -320,18 +321,22 @@ void kvcache_split_plan(int B, int H, int Nk, int d, int* chunk, int* units) {
   *units = (int)((u + W - 1) / W * W);
 }
 
-int kvcache_split_waves(int d) { return d == 64 ? SplitShape<64>::W : SplitShape<128>::W; }
+int kvcache_split_waves(int d) {
+  return d == 32 ? SplitShape<32>::W : d == 64 ? SplitShape<64>::W : SplitShape<128>::W;
+}
 
 hipError_t launch_kvcache(const DecArgs& a, int d, hipStream_t stream, const KernelTimer& tm) {
   const int W = kvcache_split_waves(d);
   const dim3 gsplit((unsigned)(a.units / W * a.B * a.H)), gmerge((unsigned)(a.B * a.H * a.Nq));
   if (tm.start) (void)hipEventRecord(tm.start, stream);
-  if (d == 64) hipLaunchKernelGGL(kvc_split_kernel<64>, gsplit, dim3(64 * W), 0, stream, a);
+  if (d == 32) hipLaunchKernelGGL(kvc_split_kernel<32>, gsplit, dim3(64 * W), 0, stream, a);
+  else if (d == 64) hipLaunchKernelGGL(kvc_split_kernel<64>, gsplit, dim3(64 * W), 0, stream, a);
   else hipLaunchKernelGGL(kvc_split_kernel<128>, gsplit, dim3(64 * W), 0, stream, a);
   hipError_t e = hipGetLastError();
   if (tm.stop) (void)hipEventRecord(tm.stop, stream);
   if (e != hipSuccess) return e;
-  if (d == 64) hipLaunchKernelGGL(kvc_merge_kernel<64>, gmerge, dim3(kThreads), 0, stream, a);
+  if (d == 32) hipLaunchKernelGGL(kvc_merge_kernel<32>, gmerge, dim3(kThreads), 0, stream, a);
+  else if (d == 64) hipLaunchKernelGGL(kvc_merge_kernel<64>, gmerge, dim3(kThreads), 0, stream, a);
   else hipLaunchKernelGGL(kvc_merge_kernel<128>, gmerge, dim3(kThreads), 0, stream, a);
   return hipGetLastError();
 }

@@ -414,10 +414,12 @@ hipError_t launch_fwd(const FwdArgs& a, fa_dtype dt, int d, hipStream_t stream, 
   const dim3 grid((unsigned)(a.ntq * a.B * a.H)), block(kThreads);
   if (tm.start) (void)hipEventRecord(tm.start, stream);
   if (dt == FA_BF16) {
-    if (d == 64) hipLaunchKernelGGL(fwd_bf16_kernel<64>, grid, block, 0, stream, a);
+    if (d == 32) hipLaunchKernelGGL(fwd_bf16_kernel<32>, grid, block, 0, stream, a);
+    else if (d == 64) hipLaunchKernelGGL(fwd_bf16_kernel<64>, grid, block, 0, stream, a);
     else hipLaunchKernelGGL(fwd_bf16_kernel<128>, grid, block, 0, stream, a);
   } else {
-    if (d == 64) hipLaunchKernelGGL(fwd_f32_kernel<64>, grid, block, 0, stream, a);
+    if (d == 32) hipLaunchKernelGGL(fwd_f32_kernel<32>, grid, block, 0, stream, a);
+    else if (d == 64) hipLaunchKernelGGL(fwd_f32_kernel<64>, grid, block, 0, stream, a);
     else hipLaunchKernelGGL(fwd_f32_kernel<128>, grid, block, 0, stream, a);
   }
   hipError_t e = hipGetLastError();

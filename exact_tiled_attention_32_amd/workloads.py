@@ -65,6 +65,10 @@ WORKLOADS = {
     "long_causal_d128": Workload(
         "long_causal_d128", 1, 16, 16384, 128, "bf16", 1014, causal=True,
         description="long-sequence causal attention, bf16 fwd+bwd, B=1 H=16 N=16384 d=128"),
+    "long_causal_d32": Workload(
+        "long_causal_d32", 1, 16, 16384, 32, "bf16", 1024, causal=True,
+        description="long-sequence causal attention at the smallest built head dimension, bf16 "
+                    "fwd+bwd, B=1 H=16 N=16384 d=32"),
     "block_sparse_64k": Workload(
         "block_sparse_64k", 1, 8, 65536, 64, "bf16", 1005, sparse=True,
         description="block-sparse attention, bf16 fwd+bwd, B=1 H=8 N=65536 d=64, 128x128 blocks, "

@@ -81,7 +81,7 @@ SWEEP_N = [1, 17, 64, 127, 128, 129, 300]
 
 def _sweep_cases():
     cases = []
-    for d in (64, 128):
+    for d in (32, 64, 128):
         for N in SWEEP_N:
             cases.append((f"dense-N{N}-d{d}", dict(B=2, H=3, N=N, d=d)))
             cases.append((f"causal-N{N}-d{d}", dict(B=2, H=3, N=N, d=d, causal=True)))
@@ -119,6 +119,7 @@ SPARSE = [
     ("sparse-N640-d128-causal", 640, 128, True, None),
     ("sparse-N700-d64-padded", 700, 64, False, [700, 333]),
     ("sparse-N896-d64-mb256", 896, 64, False, None),
+    ("sparse-N640-d32-causal", 640, 32, True, None),
 ]
 
 
@@ -140,7 +141,7 @@ def test_sparse_rule_medium_heavy_columns(gpu_lib):
     full_check(gpu_lib, case, "bf16", label="sparse-rule-N4096")
 
 
-@pytest.mark.parametrize("N,d", [(1, 64), (77, 64), (128, 64), (300, 128), (129, 128)])
+@pytest.mark.parametrize("N,d", [(1, 64), (77, 64), (128, 64), (300, 128), (129, 128), (77, 32), (300, 32)])
 def test_sweep_f32_forward(gpu_lib, N, d):
     case = workloads.make_case(2, 2, N, d, dtype="f32", seed=N + d, causal=(N % 2 == 1))
     full_check(gpu_lib, case, "f32", backward=False, label=f"f32-N{N}-d{d}")
@@ -271,7 +272,7 @@ def _sampled_check(fa, w, rows, key_rows, key_sel, label):
     parity.check_grad(got["dv"][:, :, key_sel], dv[:, :, key_sel], f"{label} dV[sampled]")
 
 
-@pytest.mark.parametrize("name", ["long_causal_d64", "long_causal_d128"])
+@pytest.mark.parametrize("name", ["long_causal_d64", "long_causal_d128", "long_causal_d32"])
 def test_workload_long_causal_sampled(gpu_lib, name):
     w = workloads.WORKLOADS[name]
     rng = np.random.default_rng(1)
