@@ -552,6 +552,8 @@ def main():
                          "twice over; prints no metric line")
     ap.add_argument("--summarize-counters", nargs=4, metavar=("SQ_CSV", "FETCH_CSV", "WRITE_CSV", "TRACE_CSV"),
                     help="print the per-kernel counter table of a --counter-pass and exit")
+    ap.add_argument("--step-only", action="store_true",
+                    help="time the step alone (no decode or packed workloads), e.g. under a kernel trace")
     ap.add_argument("--decode-only", action="store_true",
                     help="time only the key/value-cache forward on the decode workloads and print them")
     ap.add_argument("--pmc-pass", action="store_true",
@@ -622,17 +624,18 @@ def main():
             "frac_of_peak": round(value / PEAK_BF16_TFLOPS, 4), "per_head_dim": per, "roofline": roofline}
     # the key/value-cache forward (HBM-bound) on its decode workloads, outside the step
     dec = {}
-    for name, w in workloads.DECODE_WORKLOADS.items():
+    for name, w in ({} if args.step_only else workloads.DECODE_WORKLOADS).items():
         r = report_decode(fa, w, dev, 20, 5)
         dec[name] = {"ms": round(r["ms"], 4), "split_kernel_ms": round(r["split_kernel_ms"], 4),
                      "gbs": round(r["gbs"], 1), "frac_of_hbm_peak": round(r["frac_of_hbm_peak"], 4),
                      "algorithmic_mb": round(r["algorithmic_bytes"] / 1e6, 1)}
         del r
         torch.cuda.empty_cache()
-    line["kvcache_decode"] = dec
-    # packed variable-length sequences and the sliding window, outside the step
-    line["varlen"] = {name: report_varlen(fa, w, dev, 10, 3) for name, w in workloads.VARLEN_WORKLOADS.items()}
-    torch.cuda.empty_cache()
+    if not args.step_only:
+        line["kvcache_decode"] = dec
+        # packed variable-length sequences and the sliding window, outside the step
+        line["varlen"] = {name: report_varlen(fa, w, dev, 10, 3) for name, w in workloads.VARLEN_WORKLOADS.items()}
+        torch.cuda.empty_cache()
     if args.report:
         report_all(fa, dev, args.report)
     if not args.no_cpu_baseline:
