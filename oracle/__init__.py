@@ -8,8 +8,10 @@ from .attention import (  # noqa: F401
     allowed_pairs,
     attention_backward,
     attention_forward,
+    dropout_keep,
     forward_rows,
     kvcache_forward,
+    philox4x32_10,
     varlen_backward,
     varlen_forward,
 )

@@ -54,15 +54,26 @@ What it computes, and where the pages define it
   included); query i sits at position L_b - Nq + i and, when causal, attends
   key j iff j <= L_b - Nq + i; always j < L_b. With Nq = Nk = L_b this is the
   square causal mask above.
+* Dropout — the cochat.ai audit of "FlashAttention: Fast and Memory-Efficient
+  Exact Attention with IO-Awareness" quotes the fused kernel applying dropout to
+  the attention probabilities and the backward regenerating the same mask from
+  the generator state instead of storing it. The pages give no generator, so
+  the oracle fixes one: Philox4x32-10 (Salmon, Moraes, Dror, Shaw, "Parallel
+  random numbers: as easy as 1, 2, 3", SC 2011), a counter-based generator
+  written here from its published definition (``philox4x32_10``). Key j of
+  query i in batch b, head h is kept iff word (j mod 4) of
+  Philox((j // 4, i, h, b), (seed mod 2^32, seed // 2^32)) is >= floor(p 2^32);
+  kept probabilities are scaled by 1 / (1 - p). lse stays that of the
+  undropped softmax: O = (P o M) V with M = keep / (1 - p).
 * Backward — the pages say only that the backward is simplified analytically
   and recomputes the attention matrix from the saved statistics
   (cochat.ai audit of "FlashAttention: Fast and Memory-Efficient Exact
   Attention with IO-Awareness", quoted App. B.2/B.4 and Theorem 5 proof). The
   oracle is the chain rule of the definition, written out with the softmax
   Jacobian (no rowsum(dO*O) shortcut):
-      dV = P^T dO
+      dV = (P o M)^T dO                    (M = 1 without dropout)
       dP = dO V^T
-      dS_ij = P_ij (dP_ij - sum_k P_ik dP_ik)
+      dS_ij = P_ij (M_ij dP_ij - sum_k P_ik M_ik dP_ik)
       dQ = scale * dS K
       dK = scale * dS^T Q
 
@@ -84,6 +95,8 @@ __all__ = [
     "kvcache_forward",
     "varlen_forward",
     "varlen_backward",
+    "philox4x32_10",
+    "dropout_keep",
 ]
 
 _ROW_CHUNK = 256
@@ -94,6 +107,48 @@ def _as_f64(x) -> np.ndarray:
     if hasattr(x, "detach"):  # a torch tensor: go through float32, exact for bf16/fp32
         x = x.detach().to("cpu").float().numpy()
     return np.asarray(x, dtype=np.float64)
+
+
+_PHILOX_M = (0xD2511F53, 0xCD9E8D57)   # round multipliers (Salmon et al., SC 2011)
+_PHILOX_W = (0x9E3779B9, 0xBB67AE85)   # key schedule increments (same source)
+_U32 = np.uint64(0xFFFFFFFF)
+
+
+def philox4x32_10(c0, c1, c2, c3, k0: int, k1: int):
+    """Philox4x32 with 10 rounds on arrays of 32-bit counter words (broadcast together).
+
+    One round: the products M0 x0 and M1 x2 (64-bit) split into high and low words;
+    the new state is (hi(M1 x2) ^ x1 ^ k0, lo(M1 x2), hi(M0 x0) ^ x3 ^ k1, lo(M0 x0)),
+    then the key is bumped by the two Weyl constants. Returns the four output words.
+    """
+    x = [np.asarray(v, dtype=np.uint64) & _U32 for v in (c0, c1, c2, c3)]
+    x = list(np.broadcast_arrays(*x))
+    k0, k1 = np.uint64(k0 & 0xFFFFFFFF), np.uint64(k1 & 0xFFFFFFFF)
+    m0, m1 = np.uint64(_PHILOX_M[0]), np.uint64(_PHILOX_M[1])
+    for _ in range(10):
+        p0, p1 = m0 * x[0], m1 * x[2]                     # exact: both factors < 2^32
+        x = [((p1 >> np.uint64(32)) ^ x[1] ^ k0) & _U32, p1 & _U32,
+             ((p0 >> np.uint64(32)) ^ x[3] ^ k1) & _U32, p0 & _U32]
+        k0 = (k0 + np.uint64(_PHILOX_W[0])) & _U32
+        k1 = (k1 + np.uint64(_PHILOX_W[1])) & _U32
+    return x
+
+
+def dropout_keep(b: int, h: int, rows, cols, seed: int, p: float) -> np.ndarray:
+    """Boolean [len(rows), len(cols)]: is key j of query i kept (module docstring)."""
+    rows = np.asarray(rows, dtype=np.int64)[:, None]
+    cols = np.asarray(cols, dtype=np.int64)[None, :]
+    words = philox4x32_10(cols >> 2, rows, h, b, seed & 0xFFFFFFFF, (seed >> 32) & 0xFFFFFFFF)
+    w = np.choose(np.broadcast_to(cols & 3, words[0].shape), words)
+    threshold = min(int(np.floor(p * 2.0 ** 32)), 2 ** 32 - 1)
+    return w >= np.uint64(threshold)
+
+
+def _dropout_scale(b, h, rows, cols, dropout_p, dropout_seed):
+    """M = keep / (1 - p) on the given rows and key columns, or None without dropout."""
+    if dropout_p == 0.0:
+        return None
+    return dropout_keep(b, h, rows, cols, dropout_seed, dropout_p) / (1.0 - dropout_p)
 
 
 def allowed_pairs(rows: np.ndarray, n_keys: int, *, causal: bool, kv_len_b,
@@ -124,12 +179,13 @@ def allowed_pairs(rows: np.ndarray, n_keys: int, *, causal: bool, kv_len_b,
 
 
 def forward_rows(q_rows: np.ndarray, k: np.ndarray, v: np.ndarray, scale: float,
-                 allow: np.ndarray):
+                 allow: np.ndarray, drop: np.ndarray | None = None):
     """Exact attention for a set of query rows of one (batch, head).
 
     q_rows [R, d], k [Nk, d], v [Nk, dv], allow [R, Nk] -> (O [R, dv], lse [R]).
     Two-pass softmax of the materialised score rows (aiwiki "FlashAttention",
-    section "Attention and the memory bottleneck").
+    section "Attention and the memory bottleneck"). ``drop``: optional [R, Nk]
+    dropout multipliers M (keep / (1 - p)) applied to P before it meets V.
     """
     cols = np.nonzero(allow.any(axis=0))[0]
     R = q_rows.shape[0]
@@ -146,6 +202,8 @@ def forward_rows(q_rows: np.ndarray, k: np.ndarray, v: np.ndarray, scale: float,
     e = np.exp(s - m_safe[:, None])                  # exp(-inf) = 0 for masked pairs
     l = e.sum(axis=1)                                # pass 2: row sum
     p = np.where(live[:, None], e / np.where(live, l, 1.0)[:, None], 0.0)
+    if drop is not None:
+        p = p * drop[:, cols]
     out[:] = p @ v[cols]
     lse[live] = m[live] + np.log(l[live])
     return out, lse
@@ -153,12 +211,14 @@ def forward_rows(q_rows: np.ndarray, k: np.ndarray, v: np.ndarray, scale: float,
 
 def attention_forward(q, k, v, scale: float, *, causal: bool = False, kv_len=None,
                       block_mask=None, mask_block: int = 128, window_left: int = -1,
-                      window_right: int = -1, row_chunk: int = _ROW_CHUNK):
+                      window_right: int = -1, dropout_p: float = 0.0, dropout_seed: int = 0,
+                      row_chunk: int = _ROW_CHUNK):
     """O, lse for q/k/v of shape [B, H, N, d] (any float dtype, widened to fp64).
 
     kv_len: None or length-B integers (key padding). block_mask: None or a 2-D
     array [ceil(N/mb), ceil(N/mb)] shared by every (b, h), nonzero = keep.
     window_left / window_right: sliding-window extents (negative = unbounded).
+    dropout_p / dropout_seed: dropout on the probabilities (module docstring).
     Returns O [B, H, N, d] fp64 and lse [B, H, N] fp64 (natural log).
     """
     q, k, v = _as_f64(q), _as_f64(k), _as_f64(v)
@@ -174,7 +234,8 @@ def attention_forward(q, k, v, scale: float, *, causal: bool = False, kv_len=Non
                                   block_mask=block_mask, mask_block=mask_block,
                                   window_left=window_left, window_right=window_right)
             for h in range(H):
-                o_r, l_r = forward_rows(q[b, h, rows], k[b, h], v[b, h], scale, allow)
+                drop = _dropout_scale(b, h, rows, np.arange(k.shape[2]), dropout_p, dropout_seed)
+                o_r, l_r = forward_rows(q[b, h, rows], k[b, h], v[b, h], scale, allow, drop)
                 out[b, h, rows] = o_r
                 lse[b, h, rows] = l_r
     return out, lse
@@ -182,8 +243,8 @@ def attention_forward(q, k, v, scale: float, *, causal: bool = False, kv_len=Non
 
 def attention_backward(q, k, v, dout, scale: float, *, causal: bool = False, kv_len=None,
                        block_mask=None, mask_block: int = 128, window_left: int = -1,
-                       window_right: int = -1, heads=None, rows=None,
-                       row_chunk: int = _ROW_CHUNK):
+                       window_right: int = -1, dropout_p: float = 0.0, dropout_seed: int = 0,
+                       heads=None, rows=None, row_chunk: int = _ROW_CHUNK):
     """dQ, dK, dV of L = sum(O * dO) for the forward above, all fp64.
 
     The probabilities are recomputed from the definition (two-pass softmax);
@@ -220,8 +281,10 @@ def attention_backward(q, k, v, dout, scale: float, *, causal: bool = False, kv_
             e = np.exp(s - np.where(live, m, 0.0)[:, None])
             l = e.sum(axis=1)
             p = np.where(live[:, None], e / np.where(live, l, 1.0)[:, None], 0.0)
-            dv[b, h, cols] += p.T @ dor                        # dV = P^T dO
-            dp = dor @ vc.T                                    # dP = dO V^T
+            mm = _dropout_scale(b, h, rows, cols, dropout_p, dropout_seed)
+            mm = np.ones_like(p) if mm is None else mm         # dropout multipliers M
+            dv[b, h, cols] += (p * mm).T @ dor                 # dV = (P o M)^T dO
+            dp = (dor @ vc.T) * mm                             # dP = dO V^T, through M
             ds = p * (dp - (p * dp).sum(axis=1, keepdims=True))  # softmax Jacobian
             dq[b, h, rows] = scale * (ds @ kc)                 # dQ = scale dS K
             dk[b, h, cols] += scale * (ds.T @ qr)              # dK = scale dS^T Q

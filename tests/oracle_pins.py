@@ -547,6 +547,119 @@ def pin_varlen_isolation(orc):
     assert not np.allclose(a[0][5:12], b[0][5:12])
 
 
+# ----------------------------------------------------------------------------------
+# dropout: the counter-based generator and the mask it defines
+# ----------------------------------------------------------------------------------
+def _philox_scalar(c, k):
+    """Philox4x32-10 on Python integers, one block at a time (a second implementation of
+    the published definition, written independently of the oracle's array version)."""
+    mask = 0xFFFFFFFF
+    x0, x1, x2, x3 = (int(v) & mask for v in c)
+    k0, k1 = int(k[0]) & mask, int(k[1]) & mask
+    for _ in range(10):
+        prod0 = 0xD2511F53 * x0
+        prod1 = 0xCD9E8D57 * x2
+        x0, x1, x2, x3 = ((prod1 >> 32) ^ x1 ^ k0) & mask, prod1 & mask, ((prod0 >> 32) ^ x3 ^ k1) & mask, prod0 & mask
+        k0 = (k0 + 0x9E3779B9) & mask
+        k1 = (k1 + 0xBB67AE85) & mask
+    return [x0, x1, x2, x3]
+
+
+def pin_philox_known_answers(orc):
+    """The generator reproduces the known-answer vectors published with it
+    (tests/golden/philox4x32_10_kat.json), and so does the scalar re-implementation."""
+    import json
+    import os
+    path = os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden", "philox4x32_10_kat.json")
+    for vec in json.load(open(path))["vectors"]:
+        c = [int(x, 16) for x in vec["counter"]]
+        k = [int(x, 16) for x in vec["key"]]
+        want = [int(x, 16) for x in vec["output"]]
+        got = [int(w) for w in orc.philox4x32_10(*c, *k)]
+        assert got == want, (vec, [hex(g) for g in got])
+        assert _philox_scalar(c, k) == want
+
+
+def _keep_scalar(b, h, i, j, seed, p):
+    words = _philox_scalar((j // 4, i, h, b), (seed & 0xFFFFFFFF, seed >> 32))
+    return words[j % 4] >= min(math.floor(p * 2 ** 32), 2 ** 32 - 1)
+
+
+def pin_dropout_mask_rule(orc):
+    """dropout_keep follows the stated rule element by element (scalar generator calls)."""
+    for b, h, seed, p in ((0, 0, 1, 0.5), (3, 5, 0x1234567890ABCDEF, 0.1), (1, 2, 77, 0.9)):
+        rows, cols = [0, 1, 5, 130], list(range(0, 23)) + [64, 127, 1000]
+        keep = orc.dropout_keep(b, h, rows, cols, seed, p)
+        for a, i in enumerate(rows):
+            for c, j in enumerate(cols):
+                assert bool(keep[a, c]) == _keep_scalar(b, h, i, j, seed, p), (b, h, seed, p, i, j)
+
+
+def pin_dropout_keep_rate(orc):
+    """Over 512 x 512 elements the kept fraction is 1 - p within 6 binomial standard
+    deviations, and different heads and seeds give different masks."""
+    n = 512 * 512
+    for p in (0.1, 0.5, 0.9):
+        keep = orc.dropout_keep(0, 1, np.arange(512), np.arange(512), 2024, p)
+        sd = math.sqrt(n * p * (1 - p))
+        assert abs(keep.sum() - n * (1 - p)) < 6 * sd, (p, keep.mean())
+    a = orc.dropout_keep(0, 0, np.arange(64), np.arange(64), 5, 0.5)
+    assert not np.array_equal(a, orc.dropout_keep(0, 1, np.arange(64), np.arange(64), 5, 0.5))
+    assert not np.array_equal(a, orc.dropout_keep(1, 0, np.arange(64), np.arange(64), 5, 0.5))
+    assert not np.array_equal(a, orc.dropout_keep(0, 0, np.arange(64), np.arange(64), 6, 0.5))
+    assert orc.dropout_keep(0, 0, np.arange(64), np.arange(64), 5, 0.0).all()
+
+
+def pin_dropout_identity_values(orc):
+    """V = I exposes P o M: O_ij = P_ij keep_ij / (1 - p), P from a scalar softmax loop and
+    keep from the scalar generator; lse is that of the undropped softmax."""
+    rng = RNG(50)
+    N, d, scale, p, seed = 12, 3, 0.8, 0.4, 99
+    q, k = rng.standard_normal((2, 1, N, d)), rng.standard_normal((2, 1, N, d))
+    v = np.broadcast_to(np.eye(N), (2, 1, N, N)).copy()
+    for causal in (False, True):
+        o, lse = orc.attention_forward(q, k, v, scale, causal=causal, dropout_p=p, dropout_seed=seed)
+        for b in range(2):
+            for i in range(N):
+                js = list(range(i + 1)) if causal else list(range(N))
+                ss = [scale * math.fsum(float(x) * float(y) for x, y in zip(q[b, 0, i], k[b, 0, j])) for j in js]
+                mx = max(ss)
+                den = math.fsum(math.exp(x - mx) for x in ss)
+                for j in range(N):
+                    want = 0.0
+                    if j in js and _keep_scalar(b, 0, i, j, seed, p):
+                        want = math.exp(ss[js.index(j)] - mx) / den / (1 - p)
+                    assert abs(o[b, 0, i, j] - want) < 1e-12, (causal, b, i, j)
+                assert abs(lse[b, 0, i] - (mx + math.log(den))) < 1e-12
+
+
+def pin_dropout_finite_differences(orc):
+    """The mask does not depend on the inputs: central differences of L = sum(O * dO)
+    against dQ, dK, dV with dropout, causal and padded."""
+    rng = RNG(51)
+    B, N, d, scale, p, seed = 2, 7, 3, 0.7, 0.3, 4242
+    q, k, v, do = (rng.standard_normal((B, 1, N, d)) for _ in range(4))
+    kw = dict(causal=True, kv_len=[7, 5], dropout_p=p, dropout_seed=seed)
+    grads = orc.attention_backward(q, k, v, do, scale, **kw)
+
+    def loss(qq, kk, vv):
+        return float(np.sum(orc.attention_forward(qq, kk, vv, scale, **kw)[0] * do))
+
+    for which, g in enumerate(grads):
+        base = [q, k, v]
+        num = np.zeros_like(g)
+        it = np.nditer(base[which], flags=["multi_index"])
+        for _ in it:
+            idx = it.multi_index
+            pp = [x.copy() for x in base]
+            mm = [x.copy() for x in base]
+            pp[which][idx] += 1e-6
+            mm[which][idx] -= 1e-6
+            num[idx] = (loss(*pp) - loss(*mm)) / 2e-6
+        err = np.max(np.abs(num - g)) / max(1.0, np.max(np.abs(g)))
+        assert err < 1e-7, ("qkv"[which], err)
+
+
 ALL_PINS = [
     pin_zero_query,
     pin_one_hot_keys,
@@ -568,4 +681,9 @@ ALL_PINS = [
     pin_window_self_only,
     pin_varlen_library_sdpa,
     pin_varlen_isolation,
+    pin_philox_known_answers,
+    pin_dropout_mask_rule,
+    pin_dropout_keep_rate,
+    pin_dropout_identity_values,
+    pin_dropout_finite_differences,
 ]

@@ -25,14 +25,14 @@ MUTANTS = {
     "lse_log2": ("lse[live] = m[live] + np.log(l[live])", "lse[live] = m[live] + np.log2(l[live])"),
     "lse_missing_max": ("lse[live] = m[live] + np.log(l[live])", "lse[live] = np.log(l[live])"),
     "no_max_subtraction": ("e = np.exp(s - m_safe[:, None])", "e = np.exp(s)"),
-    "normaliser_dropped": ("p = np.where(live[:, None], e / np.where(live, l, 1.0)[:, None], 0.0)\n    out",
-                           "p = np.where(live[:, None], e, 0.0)\n    out"),
+    "normaliser_dropped": ("p = np.where(live[:, None], e / np.where(live, l, 1.0)[:, None], 0.0)\n    if drop",
+                           "p = np.where(live[:, None], e, 0.0)\n    if drop"),
     "bwd_jacobian_sign": ("ds = p * (dp - (p * dp)", "ds = p * (dp + (p * dp)"),
     "bwd_jacobian_term_dropped": ("ds = p * (dp - (p * dp).sum(axis=1, keepdims=True))", "ds = p * dp"),
     "bwd_dk_scale_dropped": ("dk[b, h, cols] += scale * (ds.T @ qr)", "dk[b, h, cols] += (ds.T @ qr)"),
     "bwd_dq_scale_dropped": ("dq[b, h, rows] = scale * (ds @ kc)", "dq[b, h, rows] = (ds @ kc)"),
-    "bwd_dv_wrong_operand": ("dv[b, h, cols] += p.T @ dor", "dv[b, h, cols] += p.T @ qr"),
-    "bwd_dp_wrong_operand": ("dp = dor @ vc.T", "dp = dor @ kc.T"),
+    "bwd_dv_wrong_operand": ("dv[b, h, cols] += (p * mm).T @ dor", "dv[b, h, cols] += (p * mm).T @ qr"),
+    "bwd_dp_wrong_operand": ("dp = (dor @ vc.T) * mm", "dp = (dor @ kc.T) * mm"),
     "bwd_dk_wrong_operand": ("dk[b, h, cols] += scale * (ds.T @ qr)", "dk[b, h, cols] += scale * (ds.T @ dor)"),
     "bwd_scale_dropped_in_recompute": ("s = np.where(a, scale * (qr @ kc.T), -np.inf)",
                                        "s = np.where(a, (qr @ kc.T), -np.inf)"),
@@ -66,6 +66,18 @@ MUTANTS = {
                             "seq = [x[c0:c1].transpose(1, 0, 2)[None] for x in (q,)] + "
                             "[np.roll(x, 1, axis=0)[c0:c1].transpose(1, 0, 2)[None] for x in (k, v)]"),
     "varlen_lse_misplaced": ("lse[:, c0:c1] = l_s[0]", "lse[:, c0:c1] = l_s[0][:, ::-1]"),
+    "dropout_scale_missing": ("return dropout_keep(b, h, rows, cols, dropout_seed, dropout_p) / (1.0 - dropout_p)",
+                              "return dropout_keep(b, h, rows, cols, dropout_seed, dropout_p) * 1.0"),
+    "dropout_word_shifted": ("np.broadcast_to(cols & 3,", "np.broadcast_to((cols + 1) & 3,"),
+    "dropout_counter_transposed": ("philox4x32_10(cols >> 2, rows, h, b,", "philox4x32_10(rows >> 2, cols, h, b,"),
+    "dropout_threshold_flipped": ("return w >= np.uint64(threshold)", "return w < np.uint64(threshold)"),
+    "dropout_heads_swapped": ("philox4x32_10(cols >> 2, rows, h, b,", "philox4x32_10(cols >> 2, rows, b, h,"),
+    "philox_weyl_constant": ("_PHILOX_W = (0x9E3779B9, 0xBB67AE85)", "_PHILOX_W = (0x9E3779B9, 0xBB67AE86)"),
+    "philox_output_order": ("x = [((p1 >> np.uint64(32)) ^ x[1] ^ k0) & _U32, p1 & _U32,",
+                            "x = [((p1 >> np.uint64(32)) ^ x[3] ^ k0) & _U32, p1 & _U32,"),
+    "fwd_dropout_ignored": ("p = p * drop[:, cols]", "p = p * 1.0"),
+    "bwd_dropout_dv_unmasked": ("dv[b, h, cols] += (p * mm).T @ dor", "dv[b, h, cols] += p.T @ dor"),
+    "bwd_dropout_dp_unmasked": ("dp = (dor @ vc.T) * mm", "dp = (dor @ vc.T)"),
     "varlen_bwd_dk_dv_swapped": ("for dst, src in zip((dq, dk, dv), g):", "for dst, src in zip((dq, dv, dk), g):"),
 }
 
