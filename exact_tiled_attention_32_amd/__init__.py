@@ -10,6 +10,10 @@ Entry points (same names as the C ABI):
     fa_fwd(q, k, v, scale, causal=False, kv_len=None, o=None, lse=None) -> (o, lse)
     fa_fwd_blocksparse(q, k, v, scale, block_mask, mask_block=128, causal=False,
                        kv_len=None, o=None, lse=None) -> (o, lse)
+    fa_fwd_dropout(q, k, v, scale, dropout_p, seed, causal=False, kv_len=None, o=None,
+                   lse=None) -> (o, lse)
+    fa_bwd_dropout(q, k, v, o, dout, lse, scale, dropout_p, seed, causal=False, kv_len=None,
+                   dq=None, dk=None, dv=None, workspace=None) -> (dq, dk, dv)
     fa_fwd_varlen(q, k, v, cu_seqlens, max_seqlen, scale, causal=False, window_left=-1,
                   window_right=-1, o=None, lse=None) -> (o, lse)
     fa_bwd_varlen_workspace_bytes(H, total, d) -> int
@@ -34,7 +38,7 @@ import torch
 __all__ = [
     "FA_F32", "FA_BF16", "FA_OK", "FA_ERR_INVALID", "FA_ERR_UNSUPPORTED", "FA_ERR_HIP",
     "FAError", "lib_path", "load", "fa_fwd", "fa_fwd_blocksparse", "fa_bwd",
-    "fa_bwd_workspace_bytes", "fa_fwd_varlen", "fa_bwd_varlen", "fa_bwd_varlen_workspace_bytes", "fa_fwd_kvcache", "fa_fwd_kvcache_workspace_bytes", "fa_time_next_kernel", "fa_status_string", "EXPORTED_SYMBOLS",
+    "fa_bwd_workspace_bytes", "fa_fwd_dropout", "fa_bwd_dropout", "fa_fwd_varlen", "fa_bwd_varlen", "fa_bwd_varlen_workspace_bytes", "fa_fwd_kvcache", "fa_fwd_kvcache_workspace_bytes", "fa_time_next_kernel", "fa_status_string", "EXPORTED_SYMBOLS",
 ]
 
 FA_F32, FA_BF16 = 0, 1
@@ -43,6 +47,7 @@ FA_OK, FA_ERR_INVALID, FA_ERR_UNSUPPORTED, FA_ERR_HIP = 0, 1, 2, 3
 EXPORTED_SYMBOLS = ("fa_fwd", "fa_fwd_blocksparse", "fa_bwd_workspace_bytes", "fa_bwd",
                     "fa_fwd_kvcache_workspace_bytes", "fa_fwd_kvcache",
                     "fa_fwd_varlen", "fa_bwd_varlen_workspace_bytes", "fa_bwd_varlen",
+                    "fa_fwd_dropout", "fa_bwd_dropout",
                     "fa_time_next_kernel", "fa_status_string", "fa_last_error")
 
 _LIB = None
@@ -76,6 +81,11 @@ def load() -> ctypes.CDLL:
     lib.fa_bwd_workspace_bytes.restype = S
     lib.fa_bwd.argtypes = [I, I, I, I, I, P, P, P, P, P, P, P, P, P, F, I, P, P, I, P, S, P]
     lib.fa_bwd.restype = I
+    U64 = ctypes.c_uint64
+    lib.fa_fwd_dropout.argtypes = [I, I, I, I, I, P, P, P, P, P, F, I, P, F, U64, P]
+    lib.fa_fwd_dropout.restype = I
+    lib.fa_bwd_dropout.argtypes = [I, I, I, I, I, P, P, P, P, P, P, P, P, P, F, I, P, F, U64, P, S, P]
+    lib.fa_bwd_dropout.restype = I
     lib.fa_fwd_varlen.argtypes = [I, I, I, I, I, I, P, P, P, P, P, P, F, I, I, I, P]
     lib.fa_fwd_varlen.restype = I
     lib.fa_bwd_varlen_workspace_bytes.argtypes = [I, I, I]
@@ -326,4 +336,40 @@ def fa_bwd_varlen(q, k, v, o, dout, lse, cu_seqlens, max_seqlen: int, scale: flo
                              _ptr(k), _ptr(v), _ptr(o), _ptr(dout), _ptr(lse), _ptr(dq), _ptr(dk), _ptr(dv),
                              float(scale), int(bool(causal)), int(window_left), int(window_right),
                              _ptr(workspace), int(workspace.numel()), _stream(q.device)))
+    return dq, dk, dv
+
+
+def fa_fwd_dropout(q, k, v, scale: float, dropout_p: float, seed: int, causal: bool = False, kv_len=None,
+                   o=None, lse=None):
+    """Forward with dropout on the probabilities; see ``fa_fwd_dropout`` in include/fa.h."""
+    lib = load()
+    q, o, lse = _fwd_common(q, k, v, o, lse)
+    kv = _kv_len(kv_len, q)
+    B, H, N, d = q.shape
+    _check(lib.fa_fwd_dropout(_dtype_code(q), B, H, N, d, _ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse),
+                              float(scale), int(bool(causal)), _ptr(kv), float(dropout_p),
+                              int(seed) & 0xFFFFFFFFFFFFFFFF, _stream(q.device)))
+    return o, lse
+
+
+def fa_bwd_dropout(q, k, v, o, dout, lse, scale: float, dropout_p: float, seed: int, causal: bool = False,
+                   kv_len=None, dq=None, dk=None, dv=None, workspace=None):
+    """Backward of ``fa_fwd_dropout`` (same dropout_p and seed); see include/fa.h."""
+    lib = load()
+    q = _dev_tensor(q, "q")
+    for name, t in (("k", k), ("v", v), ("o", o), ("dout", dout)):
+        _dev_tensor(t, name, q)
+    B, H, N, d = q.shape
+    if lse.shape != (B, H, N) or lse.dtype != torch.float32 or not lse.is_contiguous():
+        raise ValueError("lse must be a contiguous float32 tensor [B, H, N]")
+    dq = torch.empty_like(q) if dq is None else _dev_tensor(dq, "dq", q)
+    dk = torch.empty_like(q) if dk is None else _dev_tensor(dk, "dk", q)
+    dv = torch.empty_like(q) if dv is None else _dev_tensor(dv, "dv", q)
+    kv = _kv_len(kv_len, q)
+    if workspace is None:
+        workspace = torch.empty(fa_bwd_workspace_bytes(B, H, N, d), dtype=torch.uint8, device=q.device)
+    _check(lib.fa_bwd_dropout(_dtype_code(q), B, H, N, d, _ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(dout),
+                              _ptr(lse), _ptr(dq), _ptr(dk), _ptr(dv), float(scale), int(bool(causal)), _ptr(kv),
+                              float(dropout_p), int(seed) & 0xFFFFFFFFFFFFFFFF, _ptr(workspace),
+                              int(workspace.numel()), _stream(q.device)))
     return dq, dk, dv

@@ -1,6 +1,7 @@
 // C-ABI layer: argument validation, workspace sizing and dispatch to the kernels.
 // Declared in include/fa.h. Every check happens on the host before any HIP call, so an
 // invalid request launches nothing and writes nothing.
+#include <algorithm>
 #include <cmath>
 #include <cstdarg>
 #include <cstdio>
@@ -70,10 +71,29 @@ fa_status check_mask(const uint8_t* mask, int mask_block, int N, int tile_keys) 
   return FA_OK;
 }
 
+// Dropout parameters: threshold floor(p 2^32) on the generator word, scale 1 / (1 - p).
+struct DropoutParams {
+  bool on = false;
+  uint32_t thr = 0, seed_lo = 0, seed_hi = 0;
+  float scale = 1.0f;
+};
+
+fa_status make_dropout(float p, uint64_t seed, DropoutParams* out) {
+  if (!(p >= 0.0f && p < 1.0f)) return fail(FA_ERR_INVALID, "dropout_p must be in [0, 1) (got %g)", (double)p);
+  DropoutParams d;
+  d.on = p > 0.0f;
+  d.thr = (uint32_t)std::min(std::floor((double)p * 4294967296.0), 4294967295.0);
+  d.seed_lo = (uint32_t)(seed & 0xFFFFFFFFu);
+  d.seed_hi = (uint32_t)(seed >> 32);
+  d.scale = (float)(1.0 / (1.0 - (double)p));
+  *out = d;
+  return FA_OK;
+}
+
 fa_status fwd_impl(fa_dtype dt, int B, int H, int N, int d, const void* q, const void* k,
                    const void* v, void* o, float* lse, float scale, int causal,
                    const int32_t* kv_len, const uint8_t* mask, int mask_block, bool sparse,
-                   hipStream_t stream) {
+                   hipStream_t stream, const DropoutParams& drop = DropoutParams{}) {
   FA_TRY(check_common(dt, B, H, N, d, scale));
   FA_TRY(check_tensor(q, "q", 16));
   FA_TRY(check_tensor(k, "k", 16));
@@ -111,7 +131,11 @@ fa_status fwd_impl(fa_dtype dt, int B, int H, int N, int d, const void* q, const
   a.cu = nullptr;
   a.rs = d;
   a.total = 0;
-  hipError_t e = fa::launch_fwd(a, dt, d, stream, take_timer());
+  a.drop_thr = drop.thr;
+  a.seed_lo = drop.seed_lo;
+  a.seed_hi = drop.seed_hi;
+  a.drop_scale = drop.scale;
+  hipError_t e = fa::launch_fwd(a, dt, d, stream, take_timer(), drop.on);
   if (e != hipSuccess) return fail(FA_ERR_HIP, "forward launch failed: %s", hipGetErrorString(e));
   return FA_OK;
 }
@@ -176,11 +200,15 @@ size_t fa_bwd_workspace_bytes(int B, int H, int N, int d) {
   return align256((size_t)B * H * N * sizeof(float)) + fa::kMaxKeyTiles * sizeof(uint32_t);
 }
 
-fa_status fa_bwd(fa_dtype dt, int B, int H, int N, int d, const void* q, const void* k,
-                 const void* v, const void* o, const void* dout, const float* lse, void* dq,
-                 void* dk, void* dv, float scale, int causal, const int32_t* kv_len,
-                 const uint8_t* block_mask, int mask_block, void* workspace,
-                 size_t workspace_bytes, hipStream_t stream) {
+}  // extern "C"
+
+namespace {
+
+fa_status bwd_impl(fa_dtype dt, int B, int H, int N, int d, const void* q, const void* k,
+                   const void* v, const void* o, const void* dout, const float* lse, void* dq,
+                   void* dk, void* dv, float scale, int causal, const int32_t* kv_len,
+                   const uint8_t* block_mask, int mask_block, void* workspace,
+                   size_t workspace_bytes, hipStream_t stream, const DropoutParams& drop) {
   FA_TRY(check_common(dt, B, H, N, d, scale));
   if (dt != FA_BF16) return fail(FA_ERR_UNSUPPORTED, "backward is built for bf16 only");
   FA_TRY(check_tensor(q, "q", 16));
@@ -229,9 +257,47 @@ fa_status fa_bwd(fa_dtype dt, int B, int H, int N, int d, const void* q, const v
   a.cu = nullptr;
   a.rs = d;
   a.total = 0;
+  a.drop_thr = drop.thr;
+  a.seed_lo = drop.seed_lo;
+  a.seed_hi = drop.seed_hi;
+  a.drop_scale = drop.scale;
+  a.dropout = drop.on ? 1 : 0;
   hipError_t e = fa::launch_bwd(a, d, stream, take_timer());
   if (e != hipSuccess) return fail(FA_ERR_HIP, "backward launch failed: %s", hipGetErrorString(e));
   return FA_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+fa_status fa_bwd(fa_dtype dt, int B, int H, int N, int d, const void* q, const void* k,
+                 const void* v, const void* o, const void* dout, const float* lse, void* dq,
+                 void* dk, void* dv, float scale, int causal, const int32_t* kv_len,
+                 const uint8_t* block_mask, int mask_block, void* workspace,
+                 size_t workspace_bytes, hipStream_t stream) {
+  return bwd_impl(dt, B, H, N, d, q, k, v, o, dout, lse, dq, dk, dv, scale, causal, kv_len, block_mask,
+                  mask_block, workspace, workspace_bytes, stream, DropoutParams{});
+}
+
+fa_status fa_fwd_dropout(fa_dtype dt, int B, int H, int N, int d, const void* q, const void* k,
+                         const void* v, void* o, float* lse, float scale, int causal,
+                         const int32_t* kv_len, float dropout_p, uint64_t seed, hipStream_t stream) {
+  DropoutParams drop;
+  FA_TRY(make_dropout(dropout_p, seed, &drop));
+  if (drop.on && dt != FA_BF16) return fail(FA_ERR_UNSUPPORTED, "dropout is built for bf16 only");
+  return fwd_impl(dt, B, H, N, d, q, k, v, o, lse, scale, causal, kv_len, nullptr, 0, false, stream, drop);
+}
+
+fa_status fa_bwd_dropout(fa_dtype dt, int B, int H, int N, int d, const void* q, const void* k,
+                         const void* v, const void* o, const void* dout, const float* lse, void* dq,
+                         void* dk, void* dv, float scale, int causal, const int32_t* kv_len,
+                         float dropout_p, uint64_t seed, void* workspace, size_t workspace_bytes,
+                         hipStream_t stream) {
+  DropoutParams drop;
+  FA_TRY(make_dropout(dropout_p, seed, &drop));
+  return bwd_impl(dt, B, H, N, d, q, k, v, o, dout, lse, dq, dk, dv, scale, causal, kv_len, nullptr, 0,
+                  workspace, workspace_bytes, stream, drop);
 }
 
 size_t fa_fwd_kvcache_workspace_bytes(int B, int H, int Nq, int Nk, int d) {
@@ -381,6 +447,7 @@ fa_status fa_bwd_varlen(fa_dtype dt, int nseq, int H, int total, int max_seqlen,
   a.cu = cu_seqlens;
   a.rs = H * d;
   a.total = total;
+  a.dropout = 0;
   hipError_t e = fa::launch_bwd(a, d, stream, take_timer());
   if (e != hipSuccess) return fail(FA_ERR_HIP, "backward launch failed: %s", hipGetErrorString(e));
   return FA_OK;

@@ -161,7 +161,7 @@ __device__ int build_qtile_list512(uint16_t* list, int* wcount, const uint8_t* m
   return count;
 }
 
-template <int D>
+template <int D, bool DROP>
 __global__ __launch_bounds__(kMainThreads, 1) void bwd_dkdv_kernel(BwdArgs a) {
   constexpr int BQ = main_query_step<D>();
   constexpr int QBW = BQ / 64;         // 32-query blocks per wave per step
@@ -363,7 +363,8 @@ __global__ __launch_bounds__(kMainThreads, 1) void bwd_dkdv_kernel(BwdArgs a) {
         dp[b2] = mfma32(o.d[b2], o.v, dp[b2]);
       }
     }
-    // P = exp2(S * scale * log2e - lse * log2e), dS = P (dP - D).
+    // P = exp2(S * scale * log2e - lse * log2e), dS = P (dP - D); with dropout the value
+    // products see P o Z and dS = P (Z dP / (1 - p) - D), Z the keep mask of the pair.
 #pragma unroll
     for (int b2 = 0; b2 < QBW; ++b2)
 #pragma unroll
@@ -371,12 +372,31 @@ __global__ __launch_bounds__(kMainThreads, 1) void bwd_dkdv_kernel(BwdArgs a) {
         const int qr0 = qw0 + 32 * b2 + 8 * g + 4 * h;
         const f32x4 l2 = *reinterpret_cast<const f32x4*>(&stats[BUF][0][qr0]);
         const f32x4 dd = *reinterpret_cast<const f32x4*>(&stats[BUF][1][qr0]);
+        uint32_t keep = 0xFu;
+        if constexpr (DROP) {
+          // this lane's key against the group's four queries: one generator call per query,
+          // of which the lane uses word key % 4
+          keep = 0;
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            const u32x4 wv = philox4x32_10((uint32_t)key >> 2, (uint32_t)(q0 + qr0 + e), (uint32_t)(bh % a.H),
+                                           (uint32_t)b, a.seed_lo, a.seed_hi);
+            const uint32_t wsel = (kl & 3) == 0 ? wv[0] : (kl & 3) == 1 ? wv[1] : (kl & 3) == 2 ? wv[2] : wv[3];
+            keep |= (uint32_t)(wsel >= a.drop_thr) << e;
+          }
+        }
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
           const int i = 4 * g + e;
           const float p = fast_exp2(__builtin_fmaf(s[b2][i], a.c2s, -l2[e]));
-          s[b2][i] = p;
-          dp[b2][i] = p * (dp[b2][i] - dd[e]);
+          if constexpr (DROP) {
+            const bool kept = (keep >> e) & 1u;
+            s[b2][i] = kept ? p : 0.f;
+            dp[b2][i] = p * ((kept ? dp[b2][i] * a.drop_scale : 0.f) - dd[e]);
+          } else {
+            s[b2][i] = p;
+            dp[b2][i] = p * (dp[b2][i] - dd[e]);
+          }
         }
       }
     // Tiles that cross the causal diagonal or the key padding (a wave-uniform test): the
@@ -464,7 +484,7 @@ __global__ __launch_bounds__(kMainThreads, 1) void bwd_dkdv_kernel(BwdArgs a) {
         for (int e = 0; e < 4; ++e) {
           const int i = 4 * g + e;
           kv4[e] = (__bf16)((dkt[md][i] + kred[(md * 16 + i) * 64]) * a.scale);
-          vv4[e] = (__bf16)(dvt[md][i] + vred[(md * 16 + i) * 64]);
+          vv4[e] = (__bf16)((dvt[md][i] + vred[(md * 16 + i) * 64]) * (DROP ? a.drop_scale : 1.0f));
         }
         *reinterpret_cast<bf16x4*>(dK + 32 * md + 8 * g + 4 * h) = kv4;
         *reinterpret_cast<bf16x4*>(dV + 32 * md + 8 * g + 4 * h) = vv4;
@@ -488,7 +508,7 @@ __global__ __launch_bounds__(kMainThreads, 1) void bwd_dkdv_kernel(BwdArgs a) {
 constexpr int kDqRows = 128;  // query rows per workgroup
 constexpr int kDqKeys = 64;   // keys per tile
 
-template <int D>
+template <int D, bool DROP>
 __global__ __launch_bounds__(kThreads, 2) void bwd_dq_kernel(BwdArgs a) {
   constexpr int CH = D / 8;                         // 16-byte chunks per row
   constexpr int TILE = kDqKeys * D * 2;             // bytes of one K or V tile
@@ -654,12 +674,23 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dq_kernel(BwdArgs a) {
         s[kbk] = mfma32(so[it & 1].k, qf[ks], s[kbk]);
         dp[kbk] = mfma32(so[it & 1].v, df[ks], dp[kbk]);
       }
+      // with dropout, dS = P (Z dP / (1 - p) - D): one generator call covers four
+      // consecutive keys of the lane's query, as in the forward
 #pragma unroll
       for (int kbk = 0; kbk < KB; ++kbk)
 #pragma unroll
-        for (int i = 0; i < 16; ++i) {
-          const float p = fast_exp2(__builtin_fmaf(s[kbk][i], a.c2s, -lse2));
-          dp[kbk][i] = p * (dp[kbk][i] - dval);
+        for (int g = 0; g < 4; ++g) {
+          u32x4 wv = u32x4{};
+          if constexpr (DROP)
+            wv = philox4x32_10((uint32_t)(key0 + 32 * kbk + 8 * g + 4 * h) >> 2, (uint32_t)qi, (uint32_t)(bh % a.H),
+                               (uint32_t)b, a.seed_lo, a.seed_hi);
+#pragma unroll
+          for (int r = 0; r < 4; ++r) {
+            const int i = 4 * g + r;
+            const float p = fast_exp2(__builtin_fmaf(s[kbk][i], a.c2s, -lse2));
+            if constexpr (DROP) dp[kbk][i] = p * ((wv[r] >= a.drop_thr ? dp[kbk][i] * a.drop_scale : 0.f) - dval);
+            else dp[kbk][i] = p * (dp[kbk][i] - dval);
+          }
         }
       // Tiles that cross the causal diagonal or the key padding (a wave-uniform test):
       // masked pairs get dS = 0 by selection.
@@ -739,15 +770,27 @@ hipError_t launch_bwd(const BwdArgs& a, int d, hipStream_t stream, const KernelT
     if (e != hipSuccess) return e;
   }
   if (tm.start) (void)hipEventRecord(tm.start, stream);
-  if (d == 32) hipLaunchKernelGGL(bwd_dkdv_kernel<32>, gdkdv, bdkdv, 0, stream, a);
-  else if (d == 64) hipLaunchKernelGGL(bwd_dkdv_kernel<64>, gdkdv, bdkdv, 0, stream, a);
-  else hipLaunchKernelGGL(bwd_dkdv_kernel<128>, gdkdv, bdkdv, 0, stream, a);
+  if (a.dropout) {
+    if (d == 32) hipLaunchKernelGGL((bwd_dkdv_kernel<32, true>), gdkdv, bdkdv, 0, stream, a);
+    else if (d == 64) hipLaunchKernelGGL((bwd_dkdv_kernel<64, true>), gdkdv, bdkdv, 0, stream, a);
+    else hipLaunchKernelGGL((bwd_dkdv_kernel<128, true>), gdkdv, bdkdv, 0, stream, a);
+  } else {
+    if (d == 32) hipLaunchKernelGGL((bwd_dkdv_kernel<32, false>), gdkdv, bdkdv, 0, stream, a);
+    else if (d == 64) hipLaunchKernelGGL((bwd_dkdv_kernel<64, false>), gdkdv, bdkdv, 0, stream, a);
+    else hipLaunchKernelGGL((bwd_dkdv_kernel<128, false>), gdkdv, bdkdv, 0, stream, a);
+  }
   e = hipGetLastError();
   if (tm.stop) (void)hipEventRecord(tm.stop, stream);
   if (e != hipSuccess) return e;
-  if (d == 32) hipLaunchKernelGGL(bwd_dq_kernel<32>, gdq, block, 0, stream, a);
-  else if (d == 64) hipLaunchKernelGGL(bwd_dq_kernel<64>, gdq, block, 0, stream, a);
-  else hipLaunchKernelGGL(bwd_dq_kernel<128>, gdq, block, 0, stream, a);
+  if (a.dropout) {
+    if (d == 32) hipLaunchKernelGGL((bwd_dq_kernel<32, true>), gdq, block, 0, stream, a);
+    else if (d == 64) hipLaunchKernelGGL((bwd_dq_kernel<64, true>), gdq, block, 0, stream, a);
+    else hipLaunchKernelGGL((bwd_dq_kernel<128, true>), gdq, block, 0, stream, a);
+  } else {
+    if (d == 32) hipLaunchKernelGGL((bwd_dq_kernel<32, false>), gdq, block, 0, stream, a);
+    else if (d == 64) hipLaunchKernelGGL((bwd_dq_kernel<64, false>), gdq, block, 0, stream, a);
+    else hipLaunchKernelGGL((bwd_dq_kernel<128, false>), gdq, block, 0, stream, a);
+  }
   return hipGetLastError();
 }
 

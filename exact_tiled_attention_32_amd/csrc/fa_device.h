@@ -166,6 +166,38 @@ __device__ __forceinline__ HeadSlice head_slice(const Args& a, int bh) {
   return HeadSlice{c1 - c0, (size_t)c0 * a.rs + (size_t)hh * D, (size_t)hh * a.total + c0};
 }
 
+// Philox4x32 with 10 rounds (Salmon, Moraes, Dror, Shaw, "Parallel random numbers: as
+// easy as 1, 2, 3", SC 2011): per round the 64-bit products M0 x0 and M1 x2 give the new
+// state (hi(M1 x2) ^ x1 ^ k0, lo(M1 x2), hi(M0 x0) ^ x3 ^ k1, lo(M0 x0)); the key then
+// advances by two Weyl increments. It generates the dropout mask from (position, head,
+// batch, seed) alone, so the backward regenerates the forward's mask without storing it.
+__device__ __forceinline__ u32x4 philox4x32_10(uint32_t x0, uint32_t x1, uint32_t x2, uint32_t x3, uint32_t k0,
+                                               uint32_t k1) {
+#pragma unroll
+  for (int r = 0; r < 10; ++r) {
+    const uint64_t p0 = (uint64_t)0xD2511F53u * x0;
+    const uint64_t p1 = (uint64_t)0xCD9E8D57u * x2;
+    const uint32_t n0 = (uint32_t)(p1 >> 32) ^ x1 ^ k0;
+    const uint32_t n2 = (uint32_t)(p0 >> 32) ^ x3 ^ k1;
+    x1 = (uint32_t)p1;
+    x3 = (uint32_t)p0;
+    x0 = n0;
+    x2 = n2;
+    k0 += 0x9E3779B9u;
+    k1 += 0xBB67AE85u;
+  }
+  return u32x4{x0, x1, x2, x3};
+}
+
+// Dropout parameters of a call: key j of query i in (b, h) is kept iff word j % 4 of
+// philox4x32_10(j / 4, i, h, b, seed_lo, seed_hi) >= thr; kept probabilities are scaled
+// by `scale` = 1 / (1 - p).
+struct Dropout {
+  uint32_t thr;
+  uint32_t seed_lo, seed_hi;
+  float scale;
+};
+
 // 16-byte global load/store helpers (addresses 16-byte aligned).
 __device__ __forceinline__ u32x4 gload16(const void* p) { return *reinterpret_cast<const u32x4*>(p); }
 __device__ __forceinline__ void lds_store16(FA_LDS char* p, u32x4 v) { *reinterpret_cast<FA_LDS u32x4*>(p) = v; }

@@ -66,7 +66,7 @@ constexpr int kSchedDsRead = 0x100;
 // s_waitcnt immediate for vmcnt(0), expcnt and lgkmcnt left free (gfx9 encoding).
 constexpr int kWaitVmcnt0 = 0x0F70;
 
-template <int D>
+template <int D, bool DROP>
 __global__ __launch_bounds__(kThreads, 2) void fwd_bf16_kernel(FwdArgs a) {
   constexpr int CH = D / 8;                    // 16-byte chunks per row
   constexpr int TILE = kBC * D * 2;            // bytes of one K or V tile
@@ -244,6 +244,22 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_bf16_kernel(FwdArgs a) {
     stage(V, tile_at(t + 1), BUF ? vbuf0 : vbuf1);
     // -- region A: score MFMAs of the next tile, exp/sum/pack of this tile
     scores(kb, nxt);
+    // Dropout: bit 16 kbk + i of `keep` says whether this lane's element (kbk, i) of tile t
+    // is kept; one generator call covers four consecutive keys of the lane's query.
+    uint32_t keep = 0xFFFFFFFFu;
+    if constexpr (DROP) {
+      const int key0 = tile_at(t) * kBC;
+      keep = 0;
+#pragma unroll
+      for (int kbk = 0; kbk < KB; ++kbk)
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+          const u32x4 wv = philox4x32_10((uint32_t)(key0 + 32 * kbk + 8 * g + 4 * h) >> 2, (uint32_t)qi,
+                                         (uint32_t)(bh % a.H), (uint32_t)b, a.seed_lo, a.seed_hi);
+#pragma unroll
+          for (int r = 0; r < 4; ++r) keep |= (uint32_t)(wv[r] >= a.drop_thr) << (16 * kbk + 4 * g + r);
+        }
+    }
     bf16x8 pb[PS];
     float lsum = 0.f;
 #pragma unroll
@@ -251,8 +267,9 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_bf16_kernel(FwdArgs a) {
 #pragma unroll
       for (int i = 0; i < 16; ++i) {
         const float p = fast_exp2(__builtin_fmaf(cur[kbk][i], c2, -moff));
-        lsum += p;
-        pb[2 * kbk + (i >> 3)][i & 7] = (__bf16)p;
+        lsum += p;  // the softmax normaliser counts every probability, dropped or not
+        if constexpr (DROP) pb[2 * kbk + (i >> 3)][i & 7] = (__bf16)(((keep >> (16 * kbk + i)) & 1u) ? p : 0.f);
+        else pb[2 * kbk + (i >> 3)][i & 7] = (__bf16)p;
       }
     __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 4, 0);
 #pragma unroll
@@ -288,7 +305,8 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_bf16_kernel(FwdArgs a) {
 
   const float l_tot = l_run + other_half(l_run);
   if (qi < N) {
-    const float inv = l_tot > 0.f ? 1.0f / l_tot : 0.f;
+    float inv = l_tot > 0.f ? 1.0f / l_tot : 0.f;
+    if constexpr (DROP) inv *= a.drop_scale;  // kept probabilities count 1 / (1 - p)
     __bf16* O = reinterpret_cast<__bf16*>(a.o) + hoff + (size_t)qi * rs;
 #pragma unroll
     for (int md = 0; md < MD; ++md)
@@ -410,13 +428,18 @@ __global__ __launch_bounds__(kThreads) void fwd_f32_kernel(FwdArgs a) {
 
 }  // namespace
 
-hipError_t launch_fwd(const FwdArgs& a, fa_dtype dt, int d, hipStream_t stream, const KernelTimer& tm) {
+hipError_t launch_fwd(const FwdArgs& a, fa_dtype dt, int d, hipStream_t stream, const KernelTimer& tm,
+                      bool dropout) {
   const dim3 grid((unsigned)(a.ntq * a.B * a.H)), block(kThreads);
   if (tm.start) (void)hipEventRecord(tm.start, stream);
-  if (dt == FA_BF16) {
-    if (d == 32) hipLaunchKernelGGL(fwd_bf16_kernel<32>, grid, block, 0, stream, a);
-    else if (d == 64) hipLaunchKernelGGL(fwd_bf16_kernel<64>, grid, block, 0, stream, a);
-    else hipLaunchKernelGGL(fwd_bf16_kernel<128>, grid, block, 0, stream, a);
+  if (dt == FA_BF16 && dropout) {
+    if (d == 32) hipLaunchKernelGGL((fwd_bf16_kernel<32, true>), grid, block, 0, stream, a);
+    else if (d == 64) hipLaunchKernelGGL((fwd_bf16_kernel<64, true>), grid, block, 0, stream, a);
+    else hipLaunchKernelGGL((fwd_bf16_kernel<128, true>), grid, block, 0, stream, a);
+  } else if (dt == FA_BF16) {
+    if (d == 32) hipLaunchKernelGGL((fwd_bf16_kernel<32, false>), grid, block, 0, stream, a);
+    else if (d == 64) hipLaunchKernelGGL((fwd_bf16_kernel<64, false>), grid, block, 0, stream, a);
+    else hipLaunchKernelGGL((fwd_bf16_kernel<128, false>), grid, block, 0, stream, a);
   } else {
     if (d == 32) hipLaunchKernelGGL(fwd_f32_kernel<32>, grid, block, 0, stream, a);
     else if (d == 64) hipLaunchKernelGGL(fwd_f32_kernel<64>, grid, block, 0, stream, a);

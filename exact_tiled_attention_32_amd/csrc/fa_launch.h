@@ -34,6 +34,9 @@ struct FwdArgs {
   const int32_t* cu;
   int rs;
   int total;
+  // Dropout on the probabilities (used by the dropout instantiations only).
+  uint32_t drop_thr, seed_lo, seed_hi;
+  float drop_scale;
 };
 
 // Backward arguments, already validated by the host layer.
@@ -59,6 +62,9 @@ struct BwdArgs {
   const int32_t* cu;      // packed sequences, as in FwdArgs (dsum then [H, total] too)
   int rs;
   int total;
+  uint32_t drop_thr, seed_lo, seed_hi;  // dropout, as in FwdArgs
+  float drop_scale;
+  int dropout;            // nonzero: launch the dropout instantiations
 };
 
 // Key/value-cache forward arguments, already validated by the host layer.
@@ -105,7 +111,8 @@ struct KernelTimer {
   hipEvent_t stop = nullptr;
 };
 
-hipError_t launch_fwd(const FwdArgs& a, fa_dtype dt, int d, hipStream_t stream, const KernelTimer& tm);
+hipError_t launch_fwd(const FwdArgs& a, fa_dtype dt, int d, hipStream_t stream, const KernelTimer& tm,
+                      bool dropout = false);
 hipError_t launch_bwd(const BwdArgs& a, int d, hipStream_t stream, const KernelTimer& tm);
 hipError_t launch_kvcache(const DecArgs& a, int d, hipStream_t stream, const KernelTimer& tm);
 

@@ -133,6 +133,36 @@ fa_status fa_bwd(fa_dtype dt, int B, int H, int N, int d,
                  hipStream_t stream);
 
 /*
+ * Forward and backward with dropout on the attention probabilities (bf16). The cochat.ai
+ * audit of "FlashAttention: Fast and Memory-Efficient Exact Attention with IO-Awareness"
+ * quotes the fused kernel applying dropout to the probabilities and the backward
+ * regenerating the mask instead of storing it. The generator is Philox4x32-10 (Salmon,
+ * Moraes, Dror, Shaw, "Parallel random numbers: as easy as 1, 2, 3", SC 2011): key j of
+ * query i in (b, h) is kept iff word j % 4 of Philox(counter (j / 4, i, h, b), key
+ * (seed mod 2^32, seed / 2^32)) >= floor(dropout_p * 2^32); kept probabilities are
+ * scaled by 1 / (1 - dropout_p). lse is that of the undropped softmax, as fa_fwd's, and
+ * fa_bwd_dropout must get the forward's dropout_p and seed to regenerate the same mask.
+ *   dropout_p  in [0, 1); 0 gives exactly fa_fwd / fa_bwd (same kernels)
+ *   seed       64-bit generator key; a new seed draws a new mask
+ * Other arguments as fa_fwd / fa_bwd (no block mask).
+ */
+fa_status fa_fwd_dropout(fa_dtype dt, int B, int H, int N, int d,
+                         const void* q, const void* k, const void* v,
+                         void* o, float* lse,
+                         float scale, int causal, const int32_t* kv_len,
+                         float dropout_p, uint64_t seed,
+                         hipStream_t stream);
+
+fa_status fa_bwd_dropout(fa_dtype dt, int B, int H, int N, int d,
+                         const void* q, const void* k, const void* v,
+                         const void* o, const void* dout, const float* lse,
+                         void* dq, void* dk, void* dv,
+                         float scale, int causal, const int32_t* kv_len,
+                         float dropout_p, uint64_t seed,
+                         void* workspace, size_t workspace_bytes,
+                         hipStream_t stream);
+
+/*
  * Packed variable-length sequences with an optional sliding window (bf16, d in {32, 64,
  * 128}).
  * aiwiki "FlashAttention", section "Software integration and limitations", lists
@@ -222,8 +252,8 @@ fa_status fa_fwd_kvcache(fa_dtype dt, int B, int H, int Nq, int Nk, int d,
 
 /*
  * Measurement hook. When both events are non-NULL, the next fa_fwd, fa_fwd_blocksparse,
- * fa_fwd_varlen, fa_fwd_kvcache, fa_bwd or fa_bwd_varlen call on the calling thread that
- * passes validation records `start` on its stream immediately before launching its
+ * fa_fwd_dropout, fa_fwd_varlen, fa_fwd_kvcache, fa_bwd, fa_bwd_dropout or fa_bwd_varlen
+ * call on the calling thread that passes validation records `start` on its stream immediately before launching its
  * dominant kernel (the forward kernel, the key-split kernel of the cache forward, or the
  * backward main kernel) and `stop` immediately after it, then forgets both events.
  * Passing NULL clears a pending request. The events are owned by the caller.

@@ -245,3 +245,30 @@ def test_varlen_bwd_rejects(lib):
     assert call(P + 16, need) == fa.FA_ERR_INVALID
     assert call(P, need - 1) == fa.FA_ERR_INVALID
     assert call(P, need, dq=0) == fa.FA_ERR_INVALID
+
+
+def fdrop(lib, dt=fa.FA_BF16, p=0.1, seed=1, q=P):
+    c = ctypes.c_void_p
+    return lib.fa_fwd_dropout(dt, 1, 1, 128, 64, c(q), c(P), c(P), c(P), c(P), 0.125, 1, None, p, seed, None)
+
+
+@pytest.mark.parametrize("kwargs, status", [
+    (dict(p=-0.1), fa.FA_ERR_INVALID),
+    (dict(p=1.0), fa.FA_ERR_INVALID),
+    (dict(p=float("nan")), fa.FA_ERR_INVALID),
+    (dict(dt=fa.FA_F32), fa.FA_ERR_UNSUPPORTED),
+    (dict(q=0), fa.FA_ERR_INVALID),
+])
+def test_dropout_rejects(lib, kwargs, status):
+    assert fdrop(lib, **kwargs) == status
+    assert lib.fa_last_error().decode()
+
+
+def test_dropout_bwd_rejects(lib):
+    c = ctypes.c_void_p
+    need = fa.fa_bwd_workspace_bytes(1, 1, 128, 64)
+    call = lambda p, ws: lib.fa_bwd_dropout(fa.FA_BF16, 1, 1, 128, 64, c(P), c(P), c(P), c(P), c(P), c(P), c(P),
+                                            c(P), c(P), 0.125, 1, None, p, 5, None if ws is None else c(ws), need,
+                                            None)
+    assert call(1.5, P) == fa.FA_ERR_INVALID
+    assert call(0.2, None) == fa.FA_ERR_INVALID
