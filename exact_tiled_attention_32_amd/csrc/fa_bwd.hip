@@ -374,16 +374,29 @@ __global__ __launch_bounds__(kMainThreads, 1) void bwd_dkdv_kernel(BwdArgs a) {
         const f32x4 dd = *reinterpret_cast<const f32x4*>(&stats[BUF][1][qr0]);
         uint32_t keep = 0xFu;
         if constexpr (DROP) {
-          // this lane's key against the group's four queries: one generator call per query,
-          // of which the lane uses word key % 4
-          keep = 0;
-#pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            const u32x4 wv = philox4x32_10((uint32_t)key >> 2, (uint32_t)(q0 + qr0 + e), (uint32_t)(bh % a.H),
-                                           (uint32_t)b, a.seed_lo, a.seed_hi);
-            const uint32_t wsel = (kl & 3) == 0 ? wv[0] : (kl & 3) == 1 ? wv[1] : (kl & 3) == 2 ? wv[2] : wv[3];
-            keep |= (uint32_t)(wsel >= a.drop_thr) << e;
+          // The four lanes of a quad hold keys 4m .. 4m + 3 (one generator counter) and need
+          // them against the group's four queries. Lane `own` makes the call for query
+          // `own` of the group; word own ^ s of it goes to lane own ^ s (a quad permutation),
+          // which receives its own key's word of query own ^ s.
+          const uint32_t own = (uint32_t)(kl & 3);
+          const u32x4 wv = philox4x32_10((uint32_t)key >> 2, (uint32_t)(q0 + qr0 + own), (uint32_t)(bh % a.H),
+                                         (uint32_t)b, a.seed_lo, a.seed_hi);
+          // order the words as w[own ^ s] for s = 0 .. 3
+          uint32_t w0 = wv[0], w1 = wv[1], w2 = wv[2], w3 = wv[3];
+          if (own & 1u) {
+            const uint32_t t0 = w0, t2 = w2;
+            w0 = w1; w1 = t0; w2 = w3; w3 = t2;
           }
+          if (own & 2u) {
+            const uint32_t t0 = w0, t1 = w1;
+            w0 = w2; w1 = w3; w2 = t0; w3 = t1;
+          }
+          // quad_perm lane patterns: xor 1 = [1,0,3,2], xor 2 = [2,3,0,1], xor 3 = [3,2,1,0]
+          const uint32_t r1 = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)w1, 0xB1, 0xF, 0xF, false);
+          const uint32_t r2 = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)w2, 0x4E, 0xF, 0xF, false);
+          const uint32_t r3 = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)w3, 0x1B, 0xF, 0xF, false);
+          keep = ((uint32_t)(w0 >= a.drop_thr) << own) | ((uint32_t)(r1 >= a.drop_thr) << (own ^ 1u)) |
+                 ((uint32_t)(r2 >= a.drop_thr) << (own ^ 2u)) | ((uint32_t)(r3 >= a.drop_thr) << (own ^ 3u));
         }
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
