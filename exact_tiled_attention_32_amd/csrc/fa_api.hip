@@ -44,8 +44,8 @@ fa_status check_common(fa_dtype dt, int B, int H, int N, int d, float scale) {
   const long long wgs = (long long)B * H * ((N + fa::kFwdRowsPerWG - 1) / fa::kFwdRowsPerWG);
   if (wgs > 0x7fffffffLL) return fail(FA_ERR_INVALID, "grid too large (B*H*ceil(N/128) > 2^31-1)");
   if (!std::isfinite(scale)) return fail(FA_ERR_INVALID, "scale must be finite");
-  if (d != 32 && d != 64 && d != 128)
-    return fail(FA_ERR_UNSUPPORTED, "head dimension %d not built (32, 64, 128)", d);
+  if (d != 16 && d != 32 && d != 64 && d != 128)
+    return fail(FA_ERR_UNSUPPORTED, "head dimension %d not built (16, 32, 64, 128)", d);
   return FA_OK;
 }
 
@@ -95,6 +95,7 @@ fa_status fwd_impl(fa_dtype dt, int B, int H, int N, int d, const void* q, const
                    const int32_t* kv_len, const uint8_t* mask, int mask_block, bool sparse,
                    hipStream_t stream, const DropoutParams& drop = DropoutParams{}) {
   FA_TRY(check_common(dt, B, H, N, d, scale));
+  if (dt == FA_F32 && d == 16) return fail(FA_ERR_UNSUPPORTED, "fp32 forward is built for d in {32, 64, 128}");
   FA_TRY(check_tensor(q, "q", 16));
   FA_TRY(check_tensor(k, "k", 16));
   FA_TRY(check_tensor(v, "v", 16));
@@ -156,8 +157,8 @@ fa_status check_varlen(fa_dtype dt, int nseq, int H, int total, int max_seqlen, 
   if (window_left < -1 || window_right < -1)
     return fail(FA_ERR_INVALID, "window extents must be >= 0, or -1 for unbounded");
   if (dt != FA_BF16) return fail(FA_ERR_UNSUPPORTED, "packed sequences are built for bf16 only");
-  if (d != 32 && d != 64 && d != 128)
-    return fail(FA_ERR_UNSUPPORTED, "head dimension %d not built (32, 64, 128)", d);
+  if (d != 16 && d != 32 && d != 64 && d != 128)
+    return fail(FA_ERR_UNSUPPORTED, "head dimension %d not built (16, 32, 64, 128)", d);
   return FA_OK;
 }
 
@@ -316,8 +317,8 @@ fa_status fa_fwd_kvcache(fa_dtype dt, int B, int H, int Nq, int Nk, int d, const
   const size_t need = kvcache_ws(B, H, Nq, Nk, d, &off_m, &off_l);
   if (need == 0) return fail(FA_ERR_INVALID, "tensor size overflows");
   if (dt != FA_BF16) return fail(FA_ERR_UNSUPPORTED, "key/value-cache forward is built for bf16 only");
-  if (d != 32 && d != 64 && d != 128)
-    return fail(FA_ERR_UNSUPPORTED, "head dimension %d not built (32, 64, 128)", d);
+  if (d != 16 && d != 32 && d != 64 && d != 128)
+    return fail(FA_ERR_UNSUPPORTED, "head dimension %d not built (16, 32, 64, 128)", d);
   if (Nq > fa::kDecMaxQueries)
     return fail(FA_ERR_UNSUPPORTED, "at most %d queries per (b, h) (got Nq=%d)", fa::kDecMaxQueries, Nq);
   FA_TRY(check_tensor(q, "q", 16));

@@ -31,6 +31,10 @@ namespace {
 constexpr int kThreads = 256;
 constexpr int kBK = kBwdKeyTile;  // keys per dK/dV workgroup (32 per wave)
 
+// Sixteen zero bytes in device memory: the source of the staging lanes that fill the
+// unused upper half of 32-wide tiles when the head dimension is 16 (never written).
+__device__ __attribute__((aligned(16))) uint32_t g_zero16[4];
+
 // ---------------------------------------------------------------------------------------
 // 1. D = rowsum(dO o O). Each thread owns 8 columns of one row.
 // ---------------------------------------------------------------------------------------
@@ -161,11 +165,13 @@ __device__ int build_qtile_list512(uint16_t* list, int* wcount, const uint8_t* m
   return count;
 }
 
-template <int D, bool DROP>
+// DG: head dimension in memory; D: tile width (16 runs on 32-wide tiles, upper half zero).
+template <int D, bool DROP, int DG = D>
 __global__ __launch_bounds__(kMainThreads, 1) void bwd_dkdv_kernel(BwdArgs a) {
+  static_assert(DG == D || (D == 32 && DG == 16), "narrow heads run on 32-wide tiles");
+  constexpr int KSG = (DG + 15) / 16;  // k-steps that carry data
   constexpr int BQ = main_query_step<D>();
   constexpr int QBW = BQ / 64;         // 32-query blocks per wave per step
-  constexpr int KS = D / 16;           // k-steps over d
   constexpr int MD = D / 32;           // 32-row blocks of dK^T / dV^T
   constexpr int QT = BQ * D * 2;       // bytes of a Q or dO tile
   constexpr int KT = kBK * D * 2;      // bytes of the K or V tile
@@ -199,7 +205,7 @@ __global__ __launch_bounds__(kMainThreads, 1) void bwd_dkdv_kernel(BwdArgs a) {
   const int kg = w & 3, qh = w >> 2;
   const int key = k0 + 32 * kg + kl;    // the key this lane's accumulator columns refer to
   const int qw0 = 32 * QBW * qh;        // the wave's first query row inside a step
-  const HeadSlice sl = head_slice<D>(a, bh);
+  const HeadSlice sl = head_slice<DG>(a, bh);
   const int N = sl.N;
   if (k0 >= N) return;  // a key tile past the end of a shorter sequence (uniform)
   const size_t hoff = sl.hoff, rs = (size_t)a.rs;
@@ -227,9 +233,10 @@ __global__ __launch_bounds__(kMainThreads, 1) void bwd_dkdv_kernel(BwdArgs a) {
     const int id = tid + kMainThreads * c;
     const int row = id / (D / 8), col = (id % (D / 8)) * 8;
     const int kk = min(k0 + row, N - 1);
-    const bool ok = k0 + row < N;
-    const u32x4 kv = gload16(K + (size_t)kk * rs + col);
-    const u32x4 vv = gload16(V + (size_t)kk * rs + col);
+    const bool ok = k0 + row < N && col < DG;
+    const int cc = col < DG ? col : 0;  // (a column in range; the value is dropped)
+    const u32x4 kv = gload16(K + (size_t)kk * rs + cc);
+    const u32x4 vv = gload16(V + (size_t)kk * rs + cc);
     lds_store16(kt + tile_off<D>(row, col), ok ? kv : u32x4{});
     lds_store16(vt + tile_off<D>(row, col), ok ? vv : u32x4{});
   }
@@ -277,8 +284,10 @@ __global__ __launch_bounds__(kMainThreads, 1) void bwd_dkdv_kernel(BwdArgs a) {
       FA_LDS char* blk = qb + (c * 8 + w) * 1024;
       // (the builtin takes a non-const pointer; without the cast the host pass silently
       // drops the kernel's launch stub)
-      __builtin_amdgcn_global_load_lds((void*)(Q + row), (FA_LDS void*)blk, 16, 0, 0);
-      __builtin_amdgcn_global_load_lds((void*)(dO + row), (FA_LDS void*)(blk + QT), 16, 0, 0);
+      const bool live = DG == D || dma_col < DG;
+      __builtin_amdgcn_global_load_lds(live ? (void*)(Q + row) : (void*)g_zero16, (FA_LDS void*)blk, 16, 0, 0);
+      __builtin_amdgcn_global_load_lds(live ? (void*)(dO + row) : (void*)g_zero16, (FA_LDS void*)(blk + QT), 16,
+                                       0, 0);
     }
     // threads [0, BQ) stage lse, threads [BQ, 2 BQ) stage D
     const int qq = q0 + (tid % BQ);
@@ -353,8 +362,8 @@ __global__ __launch_bounds__(kMainThreads, 1) void bwd_dkdv_kernel(BwdArgs a) {
     SOps so[2];
     load_s(0, so[0]);
 #pragma unroll
-    for (int ks = 0; ks < KS; ++ks) {
-      if (ks + 1 < KS) load_s(ks + 1, so[(ks + 1) & 1]);
+    for (int ks = 0; ks < KSG; ++ks) {
+      if (ks + 1 < KSG) load_s(ks + 1, so[(ks + 1) & 1]);
       __builtin_amdgcn_sched_barrier(0);
       const SOps& o = so[ks & 1];
 #pragma unroll
@@ -499,8 +508,10 @@ __global__ __launch_bounds__(kMainThreads, 1) void bwd_dkdv_kernel(BwdArgs a) {
           kv4[e] = (__bf16)((dkt[md][i] + kred[(md * 16 + i) * 64]) * a.scale);
           vv4[e] = (__bf16)((dvt[md][i] + vred[(md * 16 + i) * 64]) * (DROP ? a.drop_scale : 1.0f));
         }
-        *reinterpret_cast<bf16x4*>(dK + 32 * md + 8 * g + 4 * h) = kv4;
-        *reinterpret_cast<bf16x4*>(dV + 32 * md + 8 * g + 4 * h) = vv4;
+        if (32 * md + 8 * g < DG) {
+          *reinterpret_cast<bf16x4*>(dK + 32 * md + 8 * g + 4 * h) = kv4;
+          *reinterpret_cast<bf16x4*>(dV + 32 * md + 8 * g + 4 * h) = vv4;
+        }
       }
   }
 }
@@ -521,8 +532,10 @@ __global__ __launch_bounds__(kMainThreads, 1) void bwd_dkdv_kernel(BwdArgs a) {
 constexpr int kDqRows = 128;  // query rows per workgroup
 constexpr int kDqKeys = 64;   // keys per tile
 
-template <int D, bool DROP>
+template <int D, bool DROP, int DG = D>
 __global__ __launch_bounds__(kThreads, 2) void bwd_dq_kernel(BwdArgs a) {
+  static_assert(DG == D || (D == 32 && DG == 16), "narrow heads run on 32-wide tiles");
+  constexpr int KSG = (DG + 15) / 16;               // k-steps that carry data
   constexpr int CH = D / 8;                         // 16-byte chunks per row
   constexpr int TILE = kDqKeys * D * 2;             // bytes of one K or V tile
   constexpr int KS = D / 16;                        // k-steps over d
@@ -547,7 +560,7 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dq_kernel(BwdArgs a) {
   const int q0 = qt * kDqRows;
   const int tid = threadIdx.x, w = wave_id(), l = tid & 63, h = l >> 5, ql = l & 31;
   const int qi = q0 + 32 * w + ql;
-  const HeadSlice sl = head_slice<D>(a, bh);
+  const HeadSlice sl = head_slice<DG>(a, bh);
   const int N = sl.N;
   if (q0 >= N) return;  // a query tile past the end of a shorter sequence (uniform)
   const size_t hoff = sl.hoff, rs = (size_t)a.rs;
@@ -589,10 +602,12 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dq_kernel(BwdArgs a) {
   {
     const size_t row = (size_t)min(qi, N - 1) * rs + 8 * h;
 #pragma unroll
-    for (int ks = 0; ks < KS; ++ks) {
+    for (int ks = 0; ks < KSG; ++ks) {
       qf[ks] = __builtin_bit_cast(bf16x8, gload16(Q + row + 16 * ks));
       df[ks] = __builtin_bit_cast(bf16x8, gload16(dO + row + 16 * ks));
     }
+#pragma unroll
+    for (int ks = KSG; ks < KS; ++ks) qf[ks] = df[ks] = bf16x8{};
   }
   const float lse_v = a.lse[sl.loff + min(qi, N - 1)];
   // an empty row (lse = -inf) and a row past N get lse2 = +inf, so P = 0 there
@@ -614,6 +629,10 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dq_kernel(BwdArgs a) {
   int dma_off[NDMA];
 #pragma unroll
   for (int c = 0; c < NDMA; ++c) dma_off[c] = ((dma_row0 + 4 * RPB * c) * a.rs + dma_col) * 2;
+  if (DG < D && dma_col >= DG) {
+#pragma unroll
+    for (int c = 0; c < NDMA; ++c) dma_off[c] = (int)0xFFFFFFF0u;  // past any range: reads zero
+  }
 
   f32x16 dq[MD];
 #pragma unroll
@@ -625,7 +644,7 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dq_kernel(BwdArgs a) {
   };
   auto stage = [&](int jt, auto bufc) {
     const int key0 = jt * kDqKeys;
-    const uint32_t bytes = (uint32_t)max(N - key0, 0) * (uint32_t)(a.rs * 2);
+    const uint32_t bytes = (uint32_t)min(max(N - key0, 0), kDqKeys) * (uint32_t)(a.rs * 2);
     const auto rk = make_rsrc(K + (size_t)key0 * rs, bytes);
     const auto rv = make_rsrc(V + (size_t)key0 * rs, bytes);
     FA_LDS char* base = (FA_LDS char*)(decltype(bufc)::value ? kv1 : kv0);
@@ -667,7 +686,7 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dq_kernel(BwdArgs a) {
         s[kbk] = f32x16{};
         dp[kbk] = f32x16{};
       }
-      constexpr int NI = KS * KB;
+      constexpr int NI = KSG * KB;
       struct SOps {
         bf16x8 k, v;
       };
@@ -757,7 +776,7 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dq_kernel(BwdArgs a) {
         bf16x4 v4;
 #pragma unroll
         for (int e = 0; e < 4; ++e) v4[e] = (__bf16)(dq[md][4 * g + e] * a.scale);
-        *reinterpret_cast<bf16x4*>(dQ + 32 * md + 8 * g + 4 * h) = v4;
+        if (32 * md + 8 * g < DG) *reinterpret_cast<bf16x4*>(dQ + 32 * md + 8 * g + 4 * h) = v4;
       }
   }
 }
@@ -771,7 +790,8 @@ hipError_t launch_bwd(const BwdArgs& a, int d, hipStream_t stream, const KernelT
   const dim3 gpre((unsigned)((pre_threads + kThreads - 1) / kThreads));
   const dim3 gdkdv((unsigned)(((a.N + kBK - 1) / kBK) * a.B * a.H)), bdkdv(kMainThreads);
   const dim3 gdq((unsigned)(((a.N + kDqRows - 1) / kDqRows) * a.B * a.H));
-  if (d == 32) hipLaunchKernelGGL(bwd_pre_kernel<32>, gpre, block, 0, stream, a);
+  if (d == 16) hipLaunchKernelGGL(bwd_pre_kernel<16>, gpre, block, 0, stream, a);
+  else if (d == 32) hipLaunchKernelGGL(bwd_pre_kernel<32>, gpre, block, 0, stream, a);
   else if (d == 64) hipLaunchKernelGGL(bwd_pre_kernel<64>, gpre, block, 0, stream, a);
   else hipLaunchKernelGGL(bwd_pre_kernel<128>, gpre, block, 0, stream, a);
   hipError_t e = hipGetLastError();
@@ -784,11 +804,13 @@ hipError_t launch_bwd(const BwdArgs& a, int d, hipStream_t stream, const KernelT
   }
   if (tm.start) (void)hipEventRecord(tm.start, stream);
   if (a.dropout) {
-    if (d == 32) hipLaunchKernelGGL((bwd_dkdv_kernel<32, true>), gdkdv, bdkdv, 0, stream, a);
+    if (d == 16) hipLaunchKernelGGL((bwd_dkdv_kernel<32, true, 16>), gdkdv, bdkdv, 0, stream, a);
+    else if (d == 32) hipLaunchKernelGGL((bwd_dkdv_kernel<32, true>), gdkdv, bdkdv, 0, stream, a);
     else if (d == 64) hipLaunchKernelGGL((bwd_dkdv_kernel<64, true>), gdkdv, bdkdv, 0, stream, a);
     else hipLaunchKernelGGL((bwd_dkdv_kernel<128, true>), gdkdv, bdkdv, 0, stream, a);
   } else {
-    if (d == 32) hipLaunchKernelGGL((bwd_dkdv_kernel<32, false>), gdkdv, bdkdv, 0, stream, a);
+    if (d == 16) hipLaunchKernelGGL((bwd_dkdv_kernel<32, false, 16>), gdkdv, bdkdv, 0, stream, a);
+    else if (d == 32) hipLaunchKernelGGL((bwd_dkdv_kernel<32, false>), gdkdv, bdkdv, 0, stream, a);
     else if (d == 64) hipLaunchKernelGGL((bwd_dkdv_kernel<64, false>), gdkdv, bdkdv, 0, stream, a);
     else hipLaunchKernelGGL((bwd_dkdv_kernel<128, false>), gdkdv, bdkdv, 0, stream, a);
   }
@@ -796,11 +818,13 @@ hipError_t launch_bwd(const BwdArgs& a, int d, hipStream_t stream, const KernelT
   if (tm.stop) (void)hipEventRecord(tm.stop, stream);
   if (e != hipSuccess) return e;
   if (a.dropout) {
-    if (d == 32) hipLaunchKernelGGL((bwd_dq_kernel<32, true>), gdq, block, 0, stream, a);
+    if (d == 16) hipLaunchKernelGGL((bwd_dq_kernel<32, true, 16>), gdq, block, 0, stream, a);
+    else if (d == 32) hipLaunchKernelGGL((bwd_dq_kernel<32, true>), gdq, block, 0, stream, a);
     else if (d == 64) hipLaunchKernelGGL((bwd_dq_kernel<64, true>), gdq, block, 0, stream, a);
     else hipLaunchKernelGGL((bwd_dq_kernel<128, true>), gdq, block, 0, stream, a);
   } else {
-    if (d == 32) hipLaunchKernelGGL((bwd_dq_kernel<32, false>), gdq, block, 0, stream, a);
+    if (d == 16) hipLaunchKernelGGL((bwd_dq_kernel<32, false, 16>), gdq, block, 0, stream, a);
+    else if (d == 32) hipLaunchKernelGGL((bwd_dq_kernel<32, false>), gdq, block, 0, stream, a);
     else if (d == 64) hipLaunchKernelGGL((bwd_dq_kernel<64, false>), gdq, block, 0, stream, a);
     else hipLaunchKernelGGL((bwd_dq_kernel<128, false>), gdq, block, 0, stream, a);
   }

@@ -54,8 +54,11 @@ struct StageLds {
   static constexpr int BYTES = USED ? 2 * kKT * D * 2 : 16;
 };
 
-template <int D>
+// DG: head dimension in memory; D: tile width (16 runs on 32-wide tiles, upper half zero).
+template <int D, int DG = D>
 __global__ __launch_bounds__(SplitShape<D>::W * 64, 1) void kvc_split_kernel(DecArgs a) {
+  static_assert(DG == D || (D == 32 && DG == 16), "narrow heads run on 32-wide tiles");
+  constexpr int KSG = (DG + 15) / 16;           // k-steps that carry data
   constexpr int W = SplitShape<D>::W;
   constexpr int S = SplitShape<D>::S;
   static_assert(S >= 2 && S <= 4, "pipeline depth");
@@ -84,18 +87,20 @@ __global__ __launch_bounds__(SplitShape<D>::W * 64, 1) void kvc_split_kernel(Dec
   const int ke = min(kb + a.chunk, L);
   const int ntiles = ke > kb ? (ke - kb + kKT - 1) / kKT : 0;
 
-  const __bf16* __restrict__ Q = reinterpret_cast<const __bf16*>(a.q) + (size_t)bh * a.Nq * D;
-  const __bf16* __restrict__ K = reinterpret_cast<const __bf16*>(a.k) + (size_t)bh * a.Nk * D;
-  const __bf16* __restrict__ V = reinterpret_cast<const __bf16*>(a.v) + (size_t)bh * a.Nk * D;
+  const __bf16* __restrict__ Q = reinterpret_cast<const __bf16*>(a.q) + (size_t)bh * a.Nq * DG;
+  const __bf16* __restrict__ K = reinterpret_cast<const __bf16*>(a.k) + (size_t)bh * a.Nk * DG;
+  const __bf16* __restrict__ V = reinterpret_cast<const __bf16*>(a.v) + (size_t)bh * a.Nk * DG;
 
   // Q fragments (B operand of S^T = K Q^T): lane holds query ql, columns 16 ks + 8 h .. + 7;
   // query rows past Nq are zero (their results are never written). The loads are waited
   // for after the first tiles' loads have been issued.
   u32x4 qraw[KS];
   {
-    const __bf16* qrow = Q + (size_t)min(ql, a.Nq - 1) * D + 8 * h;
+    const __bf16* qrow = Q + (size_t)min(ql, a.Nq - 1) * DG + 8 * h;
 #pragma unroll
-    for (int ks = 0; ks < KS; ++ks) qraw[ks] = gload16(qrow + 16 * ks);
+    for (int ks = 0; ks < KSG; ++ks) qraw[ks] = gload16(qrow + 16 * ks);
+#pragma unroll
+    for (int ks = KSG; ks < KS; ++ks) qraw[ks] = u32x4{};
   }
   bf16x8 qf[KS];
 
@@ -113,7 +118,9 @@ __global__ __launch_bounds__(SplitShape<D>::W * 64, 1) void kvc_split_kernel(Dec
 #pragma unroll
   for (int c = 0; c < NB; ++c) {
     const int row = c * RPB + l / CH;
-    st_off[c] = (row * D + ((l % CH) ^ swz<D>(row)) * 8) * 2;
+    const int chunk = (l % CH) ^ swz<D>(row);
+    // a chunk past the head dimension reads zero (offset past any buffer range)
+    st_off[c] = 8 * chunk < DG ? (row * DG + chunk * 8) * 2 : (int)0xFFFFFFF0u;
   }
   auto stage = [&](auto si) -> FA_LDS char* {
     if constexpr (decltype(si)::value == 0) return (FA_LDS char*)st0[w];
@@ -129,8 +136,8 @@ __global__ __launch_bounds__(SplitShape<D>::W * 64, 1) void kvc_split_kernel(Dec
   auto load = [&](int t, FA_LDS char* dst) {
     __builtin_amdgcn_s_waitcnt(kWaitLgkm0);
     const int t0 = kb + t * kKT;
-    const uint32_t bytes = t < ntiles ? (uint32_t)(L - t0) * (uint32_t)(D * 2) : 0u;
-    const size_t base = t < ntiles ? (size_t)t0 * D : 0;
+    const uint32_t bytes = t < ntiles ? (uint32_t)min(L - t0, kKT) * (uint32_t)(DG * 2) : 0u;
+    const size_t base = t < ntiles ? (size_t)t0 * DG : 0;
     const auto rv = make_rsrc(V + base, bytes);
     const auto rk = make_rsrc(K + base, bytes);
 #pragma unroll
@@ -152,7 +159,7 @@ __global__ __launch_bounds__(SplitShape<D>::W * 64, 1) void kvc_split_kernel(Dec
   auto tile = [&](const FA_LDS char* vt, int t0) {
     f32x16 s = f32x16{};
 #pragma unroll
-    for (int ks = 0; ks < KS; ++ks) s = mfma32(lds_ld8(vt + k_off[ks]), qf[ks], s);
+    for (int ks = 0; ks < KSG; ++ks) s = mfma32(lds_ld8(vt + k_off[ks]), qf[ks], s);
     // keys past the valid range, or (causal) past a query's position
     if (t0 + kKT > L || (a.causal && t0 + kKT - 1 > last)) {
 #pragma unroll
@@ -231,7 +238,7 @@ __global__ __launch_bounds__(SplitShape<D>::W * 64, 1) void kvc_split_kernel(Dec
   const float l_tot = l_run + other_half(l_run);
   if (ql < a.Nq) {
     const size_t pu = ((size_t)bh * a.units + unit) * a.Nq + ql;
-    float* U = a.part_u + pu * D;
+    float* U = a.part_u + pu * DG;
 #pragma unroll
     for (int md = 0; md < MD; ++md)
 #pragma unroll
@@ -239,7 +246,7 @@ __global__ __launch_bounds__(SplitShape<D>::W * 64, 1) void kvc_split_kernel(Dec
         f32x4 v4;
 #pragma unroll
         for (int e = 0; e < 4; ++e) v4[e] = o[md][4 * g + e];
-        *reinterpret_cast<f32x4*>(U + 32 * md + 8 * g + 4 * h) = v4;
+        if (32 * md + 8 * g < DG) *reinterpret_cast<f32x4*>(U + 32 * md + 8 * g + 4 * h) = v4;
       }
     if (h == 0) {
       a.part_m[pu] = m_run;
@@ -322,20 +329,22 @@ void kvcache_split_plan(int B, int H, int Nk, int d, int* chunk, int* units) {
 }
 
 int kvcache_split_waves(int d) {
-  return d == 32 ? SplitShape<32>::W : d == 64 ? SplitShape<64>::W : SplitShape<128>::W;
+  return d <= 32 ? SplitShape<32>::W : d == 64 ? SplitShape<64>::W : SplitShape<128>::W;
 }
 
 hipError_t launch_kvcache(const DecArgs& a, int d, hipStream_t stream, const KernelTimer& tm) {
   const int W = kvcache_split_waves(d);
   const dim3 gsplit((unsigned)(a.units / W * a.B * a.H)), gmerge((unsigned)(a.B * a.H * a.Nq));
   if (tm.start) (void)hipEventRecord(tm.start, stream);
-  if (d == 32) hipLaunchKernelGGL(kvc_split_kernel<32>, gsplit, dim3(64 * W), 0, stream, a);
+  if (d == 16) hipLaunchKernelGGL((kvc_split_kernel<32, 16>), gsplit, dim3(64 * W), 0, stream, a);
+  else if (d == 32) hipLaunchKernelGGL(kvc_split_kernel<32>, gsplit, dim3(64 * W), 0, stream, a);
   else if (d == 64) hipLaunchKernelGGL(kvc_split_kernel<64>, gsplit, dim3(64 * W), 0, stream, a);
   else hipLaunchKernelGGL(kvc_split_kernel<128>, gsplit, dim3(64 * W), 0, stream, a);
   hipError_t e = hipGetLastError();
   if (tm.stop) (void)hipEventRecord(tm.stop, stream);
   if (e != hipSuccess) return e;
-  if (d == 32) hipLaunchKernelGGL(kvc_merge_kernel<32>, gmerge, dim3(kThreads), 0, stream, a);
+  if (d == 16) hipLaunchKernelGGL(kvc_merge_kernel<16>, gmerge, dim3(kThreads), 0, stream, a);
+  else if (d == 32) hipLaunchKernelGGL(kvc_merge_kernel<32>, gmerge, dim3(kThreads), 0, stream, a);
   else if (d == 64) hipLaunchKernelGGL(kvc_merge_kernel<64>, gmerge, dim3(kThreads), 0, stream, a);
   else hipLaunchKernelGGL(kvc_merge_kernel<128>, gmerge, dim3(kThreads), 0, stream, a);
   return hipGetLastError();

@@ -66,8 +66,13 @@ constexpr int kSchedDsRead = 0x100;
 // s_waitcnt immediate for vmcnt(0), expcnt and lgkmcnt left free (gfx9 encoding).
 constexpr int kWaitVmcnt0 = 0x0F70;
 
-template <int D, bool DROP>
+// DG is the head dimension in memory; D the width of the LDS tiles and MFMA operands. A
+// head dimension of 16 runs on 32-wide tiles whose upper half is zero (staged as zeros,
+// never stored).
+template <int D, bool DROP, int DG = D>
 __global__ __launch_bounds__(kThreads, 2) void fwd_bf16_kernel(FwdArgs a) {
+  static_assert(DG == D || (D == 32 && DG == 16), "narrow heads run on 32-wide tiles");
+  constexpr int KSG = (DG + 15) / 16;          // k-steps that carry data
   constexpr int CH = D / 8;                    // 16-byte chunks per row
   constexpr int TILE = kBC * D * 2;            // bytes of one K or V tile
   constexpr int KS = D / 16;                   // k-steps of the score product
@@ -94,7 +99,7 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_bf16_kernel(FwdArgs a) {
   const int q0 = qt * kBR;
   const int tid = threadIdx.x, w = wave_id(), l = tid & 63, h = l >> 5, ql = l & 31;
   const int qi = q0 + 32 * w + ql;
-  const HeadSlice sl = head_slice<D>(a, bh);
+  const HeadSlice sl = head_slice<DG>(a, bh);
   const int N = sl.N;
   const size_t hoff = sl.hoff, loff = sl.loff;
   if (q0 >= N) return;  // a query tile past the end of a shorter sequence (uniform)
@@ -124,7 +129,9 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_bf16_kernel(FwdArgs a) {
   {
     const __bf16* qrow = Q + (size_t)min(qi, N - 1) * rs + 8 * h;
 #pragma unroll
-    for (int ks = 0; ks < KS; ++ks) qf[ks] = __builtin_bit_cast(bf16x8, gload16(qrow + 16 * ks));
+    for (int ks = 0; ks < KSG; ++ks) qf[ks] = __builtin_bit_cast(bf16x8, gload16(qrow + 16 * ks));
+#pragma unroll
+    for (int ks = KSG; ks < KS; ++ks) qf[ks] = bf16x8{};
     const float qm = qi < N ? a.qmul : 0.f;
     if (qm != 1.0f) {
 #pragma unroll
@@ -154,6 +161,10 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_bf16_kernel(FwdArgs a) {
   int dma_off[NDMA];
 #pragma unroll
   for (int c = 0; c < NDMA; ++c) dma_off[c] = ((dma_row0 + 4 * RPB * c) * a.rs + dma_col) * 2;
+  if (DG < D && dma_col >= DG) {
+#pragma unroll
+    for (int c = 0; c < NDMA; ++c) dma_off[c] = (int)0xFFFFFFF0u;  // past any range: reads zero
+  }
 
   f32x16 o[MD];
 #pragma unroll
@@ -163,7 +174,7 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_bf16_kernel(FwdArgs a) {
 
   auto stage = [&](const __bf16* base, int jt, FA_LDS char* buf) {
     const int key0 = jt * kBC;
-    const auto r = make_rsrc(base + (size_t)key0 * rs, (uint32_t)max(N - key0, 0) * (uint32_t)(a.rs * 2));
+    const auto r = make_rsrc(base + (size_t)key0 * rs, (uint32_t)min(max(N - key0, 0), kBC) * (uint32_t)(a.rs * 2));
 #pragma unroll
     for (int c = 0; c < NDMA; ++c) {
       // (an array element passed straight to the builtin makes the host pass silently drop
@@ -183,7 +194,7 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_bf16_kernel(FwdArgs a) {
     for (int kbk = 0; kbk < KB; ++kbk) {
       s[kbk] = f32x16{};
 #pragma unroll
-      for (int ks = 0; ks < KS; ++ks) s[kbk] = mfma32(lds_ld8(kb + k_off[ks] + kbk * 32 * 2 * D), qf[ks], s[kbk]);
+      for (int ks = 0; ks < KSG; ++ks) s[kbk] = mfma32(lds_ld8(kb + k_off[ks] + kbk * 32 * 2 * D), qf[ks], s[kbk]);
     }
   };
   // Masking of an edge tile, its row maximum and the lazy rescale (a wave-uniform branch).
@@ -315,7 +326,7 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_bf16_kernel(FwdArgs a) {
         bf16x4 ov;
 #pragma unroll
         for (int e = 0; e < 4; ++e) ov[e] = (__bf16)(o[md][4 * g + e] * inv);
-        *reinterpret_cast<bf16x4*>(O + 32 * md + 8 * g + 4 * h) = ov;
+        if (32 * md + 8 * g < DG) *reinterpret_cast<bf16x4*>(O + 32 * md + 8 * g + 4 * h) = ov;
       }
     if (h == 0) a.lse[loff + qi] = l_tot > 0.f ? m_run * a.sc_abs + logf(l_tot) : kNegInf;
   }
@@ -433,11 +444,13 @@ hipError_t launch_fwd(const FwdArgs& a, fa_dtype dt, int d, hipStream_t stream, 
   const dim3 grid((unsigned)(a.ntq * a.B * a.H)), block(kThreads);
   if (tm.start) (void)hipEventRecord(tm.start, stream);
   if (dt == FA_BF16 && dropout) {
-    if (d == 32) hipLaunchKernelGGL((fwd_bf16_kernel<32, true>), grid, block, 0, stream, a);
+    if (d == 16) hipLaunchKernelGGL((fwd_bf16_kernel<32, true, 16>), grid, block, 0, stream, a);
+    else if (d == 32) hipLaunchKernelGGL((fwd_bf16_kernel<32, true>), grid, block, 0, stream, a);
     else if (d == 64) hipLaunchKernelGGL((fwd_bf16_kernel<64, true>), grid, block, 0, stream, a);
     else hipLaunchKernelGGL((fwd_bf16_kernel<128, true>), grid, block, 0, stream, a);
   } else if (dt == FA_BF16) {
-    if (d == 32) hipLaunchKernelGGL((fwd_bf16_kernel<32, false>), grid, block, 0, stream, a);
+    if (d == 16) hipLaunchKernelGGL((fwd_bf16_kernel<32, false, 16>), grid, block, 0, stream, a);
+    else if (d == 32) hipLaunchKernelGGL((fwd_bf16_kernel<32, false>), grid, block, 0, stream, a);
     else if (d == 64) hipLaunchKernelGGL((fwd_bf16_kernel<64, false>), grid, block, 0, stream, a);
     else hipLaunchKernelGGL((fwd_bf16_kernel<128, false>), grid, block, 0, stream, a);
   } else {

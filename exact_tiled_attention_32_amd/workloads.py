@@ -69,6 +69,10 @@ WORKLOADS = {
         "long_causal_d32", 1, 16, 16384, 32, "bf16", 1024, causal=True,
         description="long-sequence causal attention at the smallest built head dimension, bf16 "
                     "fwd+bwd, B=1 H=16 N=16384 d=32"),
+    "long_causal_d16": Workload(
+        "long_causal_d16", 1, 16, 16384, 16, "bf16", 1025, causal=True,
+        description="long-sequence causal attention at head dimension 16 (32-wide tiles, upper "
+                    "half zero), bf16 fwd+bwd, B=1 H=16 N=16384 d=16"),
     "block_sparse_64k": Workload(
         "block_sparse_64k", 1, 8, 65536, 64, "bf16", 1005, sparse=True,
         description="block-sparse attention, bf16 fwd+bwd, B=1 H=8 N=65536 d=64, 128x128 blocks, "

@@ -94,7 +94,8 @@ def bwd(lib, dt=fa.FA_BF16, N=128, d=64, ws=P, ws_bytes=None, mask=None, mb=128,
     (dict(scale=float("inf")), fa.FA_ERR_INVALID),
     (dict(dt=7), fa.FA_ERR_INVALID),
     (dict(d=96), fa.FA_ERR_UNSUPPORTED),
-    (dict(d=16), fa.FA_ERR_UNSUPPORTED),
+    (dict(d=8), fa.FA_ERR_UNSUPPORTED),
+    (dict(dt=fa.FA_F32, d=16), fa.FA_ERR_UNSUPPORTED),
     (dict(dt=fa.FA_F32, d=80), fa.FA_ERR_UNSUPPORTED),
 ])
 def test_fwd_rejects(lib, kwargs, status):
@@ -223,7 +224,7 @@ def fvar(lib, dt=fa.FA_BF16, nseq=2, H=2, total=300, max_seqlen=200, d=64, cu=P,
     (dict(wr=-5), fa.FA_ERR_INVALID),
     (dict(scale=float("nan")), fa.FA_ERR_INVALID),
     (dict(dt=fa.FA_F32), fa.FA_ERR_UNSUPPORTED),
-    (dict(d=16), fa.FA_ERR_UNSUPPORTED),
+    (dict(d=48), fa.FA_ERR_UNSUPPORTED),
 ])
 def test_varlen_rejects(lib, kwargs, status):
     assert fvar(lib, **kwargs) == status

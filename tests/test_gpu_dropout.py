@@ -72,7 +72,7 @@ def zero_ref_bound(case, got):
 
 
 SWEEP = []
-for d in (32, 64, 128):
+for d in (16, 32, 64, 128):
     for N in (1, 77, 128, 300):
         for causal in (False, True):
             for p in (0.1, 0.5):

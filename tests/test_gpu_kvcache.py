@@ -50,7 +50,7 @@ def check(fa, case, label):
 
 
 SWEEP = []
-for d in (32, 64, 128):
+for d in (16, 32, 64, 128):
     for Nq in (1, 4, 16, 32):
         for Nk, kv in ((1, None), (31, None), (100, [100, 0]), (777, [3, 777]), (2500, [2500, 1234])):
             for causal in (False, True):

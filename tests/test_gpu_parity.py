@@ -81,7 +81,7 @@ SWEEP_N = [1, 17, 64, 127, 128, 129, 300]
 
 def _sweep_cases():
     cases = []
-    for d in (32, 64, 128):
+    for d in (16, 32, 64, 128):
         for N in SWEEP_N:
             cases.append((f"dense-N{N}-d{d}", dict(B=2, H=3, N=N, d=d)))
             cases.append((f"causal-N{N}-d{d}", dict(B=2, H=3, N=N, d=d, causal=True)))
@@ -272,7 +272,7 @@ def _sampled_check(fa, w, rows, key_rows, key_sel, label):
     parity.check_grad(got["dv"][:, :, key_sel], dv[:, :, key_sel], f"{label} dV[sampled]")
 
 
-@pytest.mark.parametrize("name", ["long_causal_d64", "long_causal_d128", "long_causal_d32"])
+@pytest.mark.parametrize("name", ["long_causal_d64", "long_causal_d128", "long_causal_d32", "long_causal_d16"])
 def test_workload_long_causal_sampled(gpu_lib, name):
     w = workloads.WORKLOADS[name]
     rng = np.random.default_rng(1)

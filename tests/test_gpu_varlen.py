@@ -76,7 +76,7 @@ MODES = [  # (name, causal, window_left, window_right)
     ("right_only_20", False, -1, 20),
 ]
 LENGTHS = [[1, 0, 130, 257, 64], [300], [129, 128, 127]]
-SWEEP = [(f"d{d}_{m[0]}_L{i}", d, m, L) for d in (32, 64, 128) for m in MODES for i, L in enumerate(LENGTHS)]
+SWEEP = [(f"d{d}_{m[0]}_L{i}", d, m, L) for d in (16, 32, 64, 128) for m in MODES for i, L in enumerate(LENGTHS)]
 
 
 @pytest.mark.parametrize("name,d,mode,lengths", SWEEP, ids=[c[0] for c in SWEEP])
