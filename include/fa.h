@@ -35,7 +35,7 @@
  *   - Work is enqueued asynchronously on `stream` (NULL = the default stream). The library
  *     allocates no device memory and keeps no per-call state: calls are re-entrant and
  *     thread-safe. Faults during execution surface at the caller's stream synchronisation.
- *   - bf16 (FA_BF16): d in {32, 64, 128}, forward and backward. fp32 (FA_F32): d in
+ *   - bf16 (FA_BF16): d in {16, 32, 64, 128}, forward and backward. fp32 (FA_F32): d in
  *     {32, 64, 128}, forward only. The key/value-cache forward takes its own query and
  *     key counts (Nq, Nk) in place of N; its tensors follow the same layout. The packed
  *     variable-length calls use [total, H, d] tensors and [H, total] lse instead.
@@ -163,8 +163,8 @@ fa_status fa_bwd_dropout(fa_dtype dt, int B, int H, int N, int d,
                          hipStream_t stream);
 
 /*
- * Packed variable-length sequences with an optional sliding window (bf16, d in {32, 64,
- * 128}).
+ * Packed variable-length sequences with an optional sliding window (bf16, d in {16, 32,
+ * 64, 128}).
  * aiwiki "FlashAttention", section "Software integration and limitations", lists
  * variable-length sequences and sliding-window masks among the interfaces; the cochat.ai
  * audit's citation check of the Longformer reference describes sliding-window attention as
@@ -225,7 +225,7 @@ size_t fa_fwd_kvcache_workspace_bytes(int B, int H, int Nq, int Nk, int d);
 /*
  * Forward of a few new queries against a key/value cache (inference decoding; aiwiki
  * "FlashAttention", section "Software integration and limitations", lists cached keys and
- * values among the supported interfaces). bf16 only, d in {32, 64, 128}, 1 <= Nq <= 32.
+ * values among the supported interfaces). bf16 only, d in {16, 32, 64, 128}, 1 <= Nq <= 32.
  *   q                 [B,H,Nq,d]: the queries of the last Nq positions of each sequence
  *   k_cache, v_cache  [B,H,Nk,d]: cached keys and values; positions >= the valid length
  *                     are never read into the result (their contents do not matter)
