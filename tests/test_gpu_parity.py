@@ -120,6 +120,7 @@ SPARSE = [
     ("sparse-N700-d64-padded", 700, 64, False, [700, 333]),
     ("sparse-N896-d64-mb256", 896, 64, False, None),
     ("sparse-N640-d32-causal", 640, 32, True, None),
+    ("sparse-N384-d16-padded", 384, 16, False, [384, 200]),
 ]
 
 
