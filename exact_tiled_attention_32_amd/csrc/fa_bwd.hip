@@ -644,7 +644,9 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dq_kernel(BwdArgs a) {
   };
   auto stage = [&](int jt, auto bufc) {
     const int key0 = jt * kDqKeys;
-    const uint32_t bytes = (uint32_t)min(max(N - key0, 0), kDqKeys) * (uint32_t)(a.rs * 2);
+    // rows of the tile inside the slice (kept scalar, like the buffer descriptor)
+    const int rows = __builtin_amdgcn_readfirstlane(min(max(N - key0, 0), kDqKeys));
+    const uint32_t bytes = (uint32_t)rows * (uint32_t)(a.rs * 2);
     const auto rk = make_rsrc(K + (size_t)key0 * rs, bytes);
     const auto rv = make_rsrc(V + (size_t)key0 * rs, bytes);
     FA_LDS char* base = (FA_LDS char*)(decltype(bufc)::value ? kv1 : kv0);

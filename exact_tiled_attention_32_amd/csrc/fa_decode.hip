@@ -136,7 +136,8 @@ __global__ __launch_bounds__(SplitShape<D>::W * 64, 1) void kvc_split_kernel(Dec
   auto load = [&](int t, FA_LDS char* dst) {
     __builtin_amdgcn_s_waitcnt(kWaitLgkm0);
     const int t0 = kb + t * kKT;
-    const uint32_t bytes = t < ntiles ? (uint32_t)min(L - t0, kKT) * (uint32_t)(DG * 2) : 0u;
+    const int rows = __builtin_amdgcn_readfirstlane(t < ntiles ? min(L - t0, kKT) : 0);  // scalar
+    const uint32_t bytes = (uint32_t)rows * (uint32_t)(DG * 2);
     const size_t base = t < ntiles ? (size_t)t0 * DG : 0;
     const auto rv = make_rsrc(V + base, bytes);
     const auto rk = make_rsrc(K + base, bytes);

@@ -174,7 +174,10 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_bf16_kernel(FwdArgs a) {
 
   auto stage = [&](const __bf16* base, int jt, FA_LDS char* buf) {
     const int key0 = jt * kBC;
-    const auto r = make_rsrc(base + (size_t)key0 * rs, (uint32_t)min(max(N - key0, 0), kBC) * (uint32_t)(a.rs * 2));
+    // rows of the tile inside the slice (uniform: kept scalar so that the buffer
+    // descriptor stays in scalar registers)
+    const int rows = __builtin_amdgcn_readfirstlane(min(max(N - key0, 0), kBC));
+    const auto r = make_rsrc(base + (size_t)key0 * rs, (uint32_t)rows * (uint32_t)(a.rs * 2));
 #pragma unroll
     for (int c = 0; c < NDMA; ++c) {
       // (an array element passed straight to the builtin makes the host pass silently drop
