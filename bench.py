@@ -308,10 +308,16 @@ def summarize_counters(sq_csv, fetch_csv, write_csv, trace_csv) -> str:
 
 
 def kernel_source_digest() -> str:
+    """Digest of the step kernels' code: comments and whitespace are left out, so that
+    only a change of the code itself invalidates counter data taken on it."""
+    import re
     h = hashlib.sha256()
-    for f in ("fa_device.h", "fa_bwd.hip", "fa_fwd.hip"):
-        with open(os.path.join(ROOT, "exact_tiled_attention_32_amd", "csrc", f), "rb") as fh:
-            h.update(fh.read())
+    for f in ("fa_device.h", "fa_bwd.hip", "fa_fwd.hip", "fa_launch.h"):
+        with open(os.path.join(ROOT, "exact_tiled_attention_32_amd", "csrc", f)) as fh:
+            code = fh.read()
+        code = re.sub(r"/\*.*?\*/", " ", code, flags=re.S)
+        code = re.sub(r"//[^\n]*", " ", code)
+        h.update(" ".join(code.split()).encode())
     return h.hexdigest()[:16]
 
 

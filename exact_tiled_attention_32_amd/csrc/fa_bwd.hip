@@ -15,10 +15,14 @@
 // bounded the whole backward. dQ is therefore computed by its own query-major kernel that
 // recomputes the score tile (two more products per tile, no atomics).
 //
-// Three launches on the caller's stream:
+// Three launches on the caller's stream (four with a block mask):
 //   1. bwd_pre:   D = rowsum(dO o O) in fp32
+//   (1b. bwd_order: block-sparse only, the order of the dK/dV key tiles)
 //   2. bwd_dkdv:  one workgroup per (b, h, 128-key tile); 8 waves (two per SIMD)
 //   3. bwd_dq:    one workgroup per (b, h, 128-query tile); 4 waves, one query per lane
+// As in the forward, packed sequences, causal and windowed masks, dropout (the mask
+// regenerated from the same Philox4x32-10 counters) and a head dimension of 16 are
+// variants of the same kernels.
 #include <type_traits>
 
 #include "fa_device.h"

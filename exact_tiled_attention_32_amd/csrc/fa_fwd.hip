@@ -22,6 +22,12 @@
 //     row's maximum grew by more than 2^8 in the exp2 domain, which keeps every
 //     probability below 256 and leaves the result exact up to rounding (u and l always
 //     share the same reference maximum).
+//
+// The same kernel serves every mask and layout: the (b, h) slice (dense [B, H, N, d] or
+// packed [total, H, d] sequences) comes from head_slice(); the causal mask and sliding
+// windows set the range of key tiles and the edge masking; block-sparse masks a list of
+// key tiles. Template flags add dropout on the probabilities (a Philox4x32-10 mask) and
+// run a head dimension of 16 on 32-wide tiles.
 #include <type_traits>
 
 #include "fa_device.h"
