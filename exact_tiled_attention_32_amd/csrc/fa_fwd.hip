@@ -16,11 +16,8 @@
 //   * The unnormalised output is accumulated transposed too, O^T += V^T P^T: the
 //     probabilities are used straight from the score accumulator as the B operand, and
 //     V^T comes from the row-major V tile through ds_read_b64_tr_b16 transpose reads.
-//   * K and V tiles (64 keys) are double-buffered in LDS; the next tiles' global loads are
-//     in flight while the current step computes.
-//   * The value product lags the scores by a tile: a step issues the score MFMAs of tile
-//     t+1 and the value MFMAs of tile t-1 while the vector ALU computes the exponentials
-//     of tile t between them, so neither unit waits for the other within the step.
+//   * K and V tiles (64 keys) are double-buffered in LDS; the next tile's global loads are
+//     in flight while the current tile is computed.
 //   * The running maximum is refreshed lazily: the accumulator is rescaled only when some
 //     row's maximum grew by more than 2^8 in the exp2 domain, which keeps every
 //     probability below 256 and leaves the result exact up to rounding (u and l always
@@ -210,11 +207,7 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_bf16_kernel(FwdArgs a) {
     }
   };
   // Masking of an edge tile, its row maximum and the lazy rescale (a wave-uniform branch).
-  // l is rescaled at once; the factor for u is returned in `alpha_p` (with true when some
-  // row changed its reference) and applied one step later, once the value product of the
-  // previous tile, made with the old reference, has been added.
-  float alpha_p = 1.0f;
-  auto rowmax_update = [&](int jt, f32x16 (&s)[KB]) -> bool {
+  auto rowmax_update = [&](int jt, f32x16 (&s)[KB]) {
     const int key0 = jt * kBC;
     const int qw = q0 + 32 * w;  // the wave's first row
     if ((key0 + kBC > kv_end) || (a.wr >= 0 && key0 + kBC - 1 > qw + a.wr) ||
@@ -236,51 +229,41 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_bf16_kernel(FwdArgs a) {
     tmax = fmaxf(tmax, other_half(tmax));
     const float mcand = fmaxf(m_run, tmax);
     const bool need = (mcand - m_run) * c2 > kRescaleLog2;
-    const bool any = __ballot(need) != 0;
-    if (any) {
-      alpha_p = need ? fast_exp2((m_run - mcand) * c2) : 1.0f;
+    if (__ballot(need)) {
+      const float alpha = need ? fast_exp2((m_run - mcand) * c2) : 1.0f;
       if (need) m_run = mcand;
-      l_run *= alpha_p;
+      l_run *= alpha;
+#pragma unroll
+      for (int md = 0; md < MD; ++md) o[md] *= alpha;
     }
     moff = (m_run == kNegInf) ? 0.f : m_run * c2;
-    return any;
   };
 
-  // O^T += V^T P^T for one tile: items (st, md), V^T fragments by transpose reads.
-  constexpr int NJ = PS * MD;
-  auto load_v = [&](const FA_LDS char* vb, int j) {
-    const int st = j / MD, md = j % MD;
-    return lds_tr8(vb + v_lo[md] + st * 16 * 2 * D, vb + v_hi[md] + st * 16 * 2 * D);
-  };
-
-  // Software pipeline over key tiles. Step t runs, independently of each other,
-  //   * the score MFMAs of tile t+1 (K buffer (t+1) & 1),
-  //   * the value MFMAs of tile t-1 (V buffer (t-1) & 1, probabilities from step t-1),
-  //   * the exponentials of tile t (vector ALU, probabilities kept for step t+1),
-  // so that the matrix units and the vector ALU work side by side through the whole step;
-  // then the row maximum of tile t+1. Meanwhile K(t+2) and V(t) stream into the buffers
-  // read in step t-1. A last step adds the value product of the final tile.
   f32x16 sa[KB], sb[KB];
-  bf16x8 pa[PS], pb[PS];
-  bool pend = false;  // a rescale of u is due after this step's value product
   if (ntiles > 0) {
     stage(K, tile_at(0), kbuf0);
+    stage(V, tile_at(0), vbuf0);
     stage(K, tile_at(1), kbuf1);
     __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
     __syncthreads();
     scores(kbuf0, sa);
-    pend = rowmax_update(tile_at(0), sa);
+    rowmax_update(tile_at(0), sa);
     __syncthreads();  // step 0 overwrites K buffer 0
   }
 
-  auto step = [&](auto bufc, auto pvc, f32x16 (&cur)[KB], f32x16 (&nxt)[KB], bf16x8 (&pc)[PS],
-                  const bf16x8 (&pp)[PS], int t) {
+  // Step t: S(t+1) from K buffer (t+1)&1 interleaved with the probabilities of tile t;
+  // then O^T += V^T P^T from V buffer t&1; then stage K(t+2), V(t+1) and find the
+  // maximum of tile t+1.
+  auto step = [&](auto bufc, f32x16 (&cur)[KB], f32x16 (&nxt)[KB], int t) {
     constexpr int BUF = decltype(bufc)::value;
-    constexpr bool PV = decltype(pvc)::value;
-    const FA_LDS char* kb = BUF ? kbuf0 : kbuf1;  // K(t+1)
-    const FA_LDS char* vb = BUF ? vbuf0 : vbuf1;  // V(t-1)
+    const FA_LDS char* kb = BUF ? kbuf0 : kbuf1;
+    const FA_LDS char* vb = BUF ? vbuf1 : vbuf0;
+    // K buffer BUF held tile t (read in step t - 1), V buffer BUF ^ 1 tile t - 1 (read in
+    // step t - 1): stream K(t+2) and V(t+1) into them; they land by the end of the step.
     stage(K, tile_at(t + 2), BUF ? kbuf1 : kbuf0);
-    stage(V, tile_at(t), BUF ? vbuf1 : vbuf0);
+    stage(V, tile_at(t + 1), BUF ? vbuf0 : vbuf1);
+    // -- region A: score MFMAs of the next tile, exp/sum/pack of this tile
+    scores(kb, nxt);
     // Dropout: bit 16 kbk + i of `keep` says whether this lane's element (kbk, i) of tile t
     // is kept; one generator call covers four consecutive keys of the lane's query.
     uint32_t keep = 0xFFFFFFFFu;
@@ -297,82 +280,47 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_bf16_kernel(FwdArgs a) {
           for (int r = 0; r < 4; ++r) keep |= (uint32_t)(wv[r] >= a.drop_thr) << (16 * kbk + 4 * g + r);
         }
     }
-    // probabilities of tile t
-    float ls0 = 0.f, ls1 = 0.f;
+    bf16x8 pb[PS];
+    float lsum = 0.f;
 #pragma unroll
     for (int kbk = 0; kbk < KB; ++kbk)
 #pragma unroll
       for (int i = 0; i < 16; ++i) {
         const float p = fast_exp2(__builtin_fmaf(cur[kbk][i], c2, -moff));
-        if (i & 1) ls1 += p;  // the softmax normaliser counts every probability, dropped or not
-        else ls0 += p;
-        if constexpr (DROP) pc[2 * kbk + (i >> 3)][i & 7] = (__bf16)(((keep >> (16 * kbk + i)) & 1u) ? p : 0.f);
-        else pc[2 * kbk + (i >> 3)][i & 7] = (__bf16)p;
+        lsum += p;  // the softmax normaliser counts every probability, dropped or not
+        if constexpr (DROP) pb[2 * kbk + (i >> 3)][i & 7] = (__bf16)(((keep >> (16 * kbk + i)) & 1u) ? p : 0.f);
+        else pb[2 * kbk + (i >> 3)][i & 7] = (__bf16)p;
       }
-    // scores of tile t+1, the two 32-key blocks interleaved
-#pragma unroll
-    for (int kbk = 0; kbk < KB; ++kbk) nxt[kbk] = f32x16{};
-#pragma unroll
-    for (int ks = 0; ks < KSG; ++ks)
-#pragma unroll
-      for (int kbk = 0; kbk < KB; ++kbk) nxt[kbk] = mfma32(lds_ld8(kb + k_off[ks] + kbk * 32 * 2 * D), qf[ks], nxt[kbk]);
-    // value product of tile t-1
-    if constexpr (PV) {
-#pragma unroll
-      for (int j = 0; j < NJ; ++j) o[j % MD] = mfma32(load_v(vb, j), pp[j / MD], o[j % MD]);
-    }
-    // Interleave: each MFMA with its operand reads a few MFMAs ahead and an even share of
-    // the vector work.
-    constexpr int NS = KB * KSG, NP = PV ? NJ : 0;
-    constexpr int NV = ((DROP ? 600 : 120) + NS + NP - 1) / (NS + NP);
     __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 4, 0);
 #pragma unroll
-    for (int k = 0; k < NS; ++k) {
+    for (int k = 0; k < KB * KS; ++k) {
       __builtin_amdgcn_sched_group_barrier(kSchedMfma, 1, 0);
-      if (PV && k >= NS - 2) __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 2, 0);
-      else __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 1, 0);
-      __builtin_amdgcn_sched_group_barrier(kSchedValu, NV, 0);
+      if (k + 4 < KB * KS) __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(kSchedValu, 7, 0);
     }
+    l_run += lsum;
+    // -- region B: O^T += V^T P^T, items (st, md), transpose reads one item ahead
+    constexpr int NJ = PS * MD;
+    bf16x8 vt8[2];
+    auto load_v = [&](int j) {
+      const int st = j / MD, md = j % MD;
+      return lds_tr8(vb + v_lo[md] + st * 16 * 2 * D, vb + v_hi[md] + st * 16 * 2 * D);
+    };
+    vt8[0] = load_v(0);
 #pragma unroll
-    for (int j = 0; j < NP; ++j) {
-      __builtin_amdgcn_sched_group_barrier(kSchedMfma, 1, 0);
-      __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 2, 0);
-      __builtin_amdgcn_sched_group_barrier(kSchedValu, NV, 0);
+    for (int j = 0; j < NJ; ++j) {
+      if (j + 1 < NJ) vt8[(j + 1) & 1] = load_v(j + 1);
+      __builtin_amdgcn_sched_barrier(0);
+      o[j % MD] = mfma32(vt8[j & 1], pb[j / MD], o[j % MD]);
     }
-    l_run += ls0 + ls1;
-    // Keep the probabilities in this block: without a use here the compiler moves them
-    // below the rescale branch, out of reach of the interleave.
-    asm volatile("" ::"v"(pc[0]), "v"(pc[1]), "v"(pc[2]), "v"(pc[3]), "v"(l_run));
-    // u now holds tiles up to t-1 at the reference of tile t-1: bring it to tile t's
-    if (pend) {
-#pragma unroll
-      for (int md = 0; md < MD; ++md) o[md] *= alpha_p;
-    }
-    pend = false;
-    if (t + 1 < ntiles) pend = rowmax_update(tile_at(t + 1), nxt);
-    // the staged tiles must have landed before the barrier
+    // -- prepare tile t+1; the staged tiles must have landed before the barrier
+    if (t + 1 < ntiles) rowmax_update(tile_at(t + 1), nxt);
     __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
     __syncthreads();
   };
-  using I0 = std::integral_constant<int, 0>;
-  using I1 = std::integral_constant<int, 1>;
-  using PV0 = std::integral_constant<bool, false>;
-  using PV1 = std::integral_constant<bool, true>;
-  if (ntiles > 0) {
-    step(I0{}, PV0{}, sa, sb, pa, pb, 0);
-    for (int t = 1; t < ntiles; t += 2) {
-      step(I1{}, PV1{}, sb, sa, pb, pa, t);
-      if (t + 1 < ntiles) step(I0{}, PV1{}, sa, sb, pa, pb, t + 1);
-    }
-    // value product of the last tile (its probabilities were made with the final reference)
-    const FA_LDS char* vb = ((ntiles - 1) & 1) ? vbuf1 : vbuf0;
-    if ((ntiles - 1) & 1) {
-#pragma unroll
-      for (int j = 0; j < NJ; ++j) o[j % MD] = mfma32(load_v(vb, j), pb[j / MD], o[j % MD]);
-    } else {
-#pragma unroll
-      for (int j = 0; j < NJ; ++j) o[j % MD] = mfma32(load_v(vb, j), pa[j / MD], o[j % MD]);
-    }
+  for (int t = 0; t < ntiles; t += 2) {
+    step(std::integral_constant<int, 0>{}, sa, sb, t);
+    if (t + 1 < ntiles) step(std::integral_constant<int, 1>{}, sb, sa, t + 1);
   }
 
   const float l_tot = l_run + other_half(l_run);
