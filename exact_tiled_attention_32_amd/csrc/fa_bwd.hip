@@ -18,7 +18,7 @@
 // Three launches on the caller's stream (four with a block mask):
 //   1. bwd_pre:   D = rowsum(dO o O) in fp32
 //   (1b. bwd_order: block-sparse only, the order of the dK/dV key tiles)
-//   2. bwd_dkdv:  one workgroup per (b, h, 128-key tile); 8 waves (two per SIMD)
+//   2. bwd_dkdv:  one workgroup per (b, h, 128-key tile); 4 waves, two workgroups per CU
 //   3. bwd_dq:    one workgroup per (b, h, 128-query tile); 4 waves, one query per lane
 // As in the forward, packed sequences, causal and windowed masks, dropout (the mask
 // regenerated from the same Philox4x32-10 counters) and a head dimension of 16 are
@@ -128,29 +128,41 @@ __global__ __launch_bounds__(kThreads) void bwd_order_kernel(const uint8_t* __re
 }
 
 // ---------------------------------------------------------------------------------------
-// 2. dK / dV kernel: one workgroup per (b, h, 128-key tile), 8 waves (two per SIMD).
-//    Wave w owns key group kg = w % 4 (keys 32 kg .. 32 kg + 31 of the tile) and query half
-//    qh = w / 4 of each query step (QBW 32-row blocks: the step is 64 rows at d = 128 and
-//    128 rows at d = 64). Orientation (v_mfma_f32_32x32x16_bf16):
+// 2. dK / dV kernel: one workgroup per (b, h, 128-key tile). Wave w owns key group
+//    kg = w % 4 (keys 32 kg .. 32 kg + 31 of the tile) and takes QBW 32-row query blocks
+//    per step (1 at d = 128, 2 below). Normally the workgroup is those 4 waves and two
+//    workgroups share a CU (two waves per SIMD from different workgroups); the dropout
+//    variant at d = 128 has 8 waves, the second four taking the other half (qh = w / 4) of
+//    each 64-row query step, one workgroup per CU. Orientation (v_mfma_f32_32x32x16_bf16):
 //   S, dP   = Q K^T, dO V^T   (M = the wave's queries, N = its 32 keys): Q/dO rows and K/V
-//             rows are 16-byte LDS reads.
+//             rows are 16-byte LDS reads (K fragments held in registers at d = 128).
 //   dV^T   += dO^T P          (M = d, N = keys): dO^T from transpose reads, P straight
 //   dK^T   += Q^T dS           from the accumulator (same layout trick as the forward).
-//   At the end the two query halves' dK^T, dV^T partials are summed through LDS.
+//   With two query halves, their dK^T, dV^T partials are summed through LDS at the end.
 // ---------------------------------------------------------------------------------------
-constexpr int kMainThreads = 512;
 // s_waitcnt immediate for vmcnt(0), expcnt and lgkmcnt left free (gfx9 encoding).
 constexpr int kWaitVmcnt0 = 0x0F70;
 
+// Waves of a key group (32 keys) that split each query step between them. With one, a
+// workgroup is 4 waves and two workgroups share a CU, so the two waves of a SIMD belong
+// to different workgroups and drift apart instead of meeting at every barrier. The
+// dropout variant at d = 128 cannot hold K in registers next to its generator state, needs
+// K in LDS and so keeps one 8-wave workgroup per CU (two query halves).
+template <int D, bool DROP>
+constexpr int dkdv_halves() { return D == 128 && DROP ? 2 : 1; }
+template <int D, bool DROP>
+constexpr int dkdv_threads() { return 256 * dkdv_halves<D, DROP>(); }
+// 32-query blocks per wave and step
 template <int D>
-constexpr int main_query_step() { return D == 128 ? 64 : 128; }
+constexpr int dkdv_query_blocks() { return D == 128 ? 1 : 2; }
 
 // Query tiles [i0, ntq) whose mask block in column `cb` is nonzero (block-sparse path).
-__device__ int build_qtile_list512(uint16_t* list, int* wcount, const uint8_t* mask, int cb, int nb,
-                                   int mb, int i0, int ntq, int bq) {
+template <int NT>
+__device__ int build_qtile_list(uint16_t* list, int* wcount, const uint8_t* mask, int cb, int nb, int mb, int i0,
+                                int ntq, int bq) {
   const int tid = threadIdx.x, w = tid >> 6, l = tid & 63;
   int count = 0;
-  for (int base = i0; base < ntq; base += kMainThreads) {
+  for (int base = i0; base < ntq; base += NT) {
     const int i = base + tid;
     const bool keep = i < ntq && mask[(size_t)((i * bq) / mb) * nb + cb] != 0;
     const uint64_t bal = __ballot(keep);
@@ -158,7 +170,7 @@ __device__ int build_qtile_list512(uint16_t* list, int* wcount, const uint8_t* m
     if (l == 0) wcount[w] = __popcll(bal);
     __syncthreads();
     int off = count, tot = 0;
-    for (int k = 0; k < 8; ++k) {
+    for (int k = 0; k < NT / 64; ++k) {
       off += k < w ? wcount[k] : 0;
       tot += wcount[k];
     }
@@ -171,14 +183,23 @@ __device__ int build_qtile_list512(uint16_t* list, int* wcount, const uint8_t* m
 
 // DG: head dimension in memory; D: tile width (16 runs on 32-wide tiles, upper half zero).
 template <int D, bool DROP, int DG = D>
-__global__ __launch_bounds__(kMainThreads, 1) void bwd_dkdv_kernel(BwdArgs a) {
+__global__ __launch_bounds__((dkdv_threads<D, DROP>()), (dkdv_halves<D, DROP>() == 1 ? 2 : 1)) void bwd_dkdv_kernel(
+    BwdArgs a) {
   static_assert(DG == D || (D == 32 && DG == 16), "narrow heads run on 32-wide tiles");
+  constexpr int kMainThreads = dkdv_threads<D, DROP>();
+  constexpr int QH = dkdv_halves<D, DROP>();  // query halves (waves per key group)
+  constexpr int NW = 4 * QH;                  // waves per workgroup
   constexpr int KSG = (DG + 15) / 16;  // k-steps that carry data
-  constexpr int BQ = main_query_step<D>();
-  constexpr int QBW = BQ / 64;         // 32-query blocks per wave per step
+  constexpr int QBW = dkdv_query_blocks<D>();  // 32-query blocks per wave per step
+  constexpr int BQ = 32 * QBW * QH;            // query rows per step
+  // At d = 128 without dropout the wave's K fragments (the A operand of S, the same in
+  // every step) are loaded once into registers and K is not kept in LDS.
+  constexpr bool KREG = D == 128 && !DROP;
+  static_assert(!KREG || QH == 1, "K in registers goes with the 4-wave layout");
   constexpr int MD = D / 32;           // 32-row blocks of dK^T / dV^T
   constexpr int QT = BQ * D * 2;       // bytes of a Q or dO tile
   constexpr int KT = kBK * D * 2;      // bytes of the K or V tile
+  constexpr int KVT = KREG ? KT : 2 * KT;  // the K | V tile in LDS (V alone when K is in registers)
   constexpr int NDMA = QT / (kMainThreads * 16);     // DMA instructions per wave per Q/dO tile
   constexpr int RPB = 1024 / (2 * D);                 // rows per 1 KB DMA block
   constexpr int KCH = kBK * (D / 8) / kMainThreads;  // 16-byte chunks per thread per K/V tile
@@ -187,16 +208,16 @@ __global__ __launch_bounds__(kMainThreads, 1) void bwd_dkdv_kernel(BwdArgs a) {
   // touch the other, and does not wait for them before reading it.
   __shared__ __attribute__((aligned(16))) char qd0[2 * QT];
   __shared__ __attribute__((aligned(16))) char qd1[2 * QT];
-  __shared__ __attribute__((aligned(16))) char kvt[2 * KT];
+  __shared__ __attribute__((aligned(16))) char kvt[KVT];
   __shared__ __attribute__((aligned(16))) float stats[2][2][BQ];  // [buf][lse2 | D][row]
   __shared__ uint16_t qlist[kMaxTileList];
   __shared__ int wcount[8];
-  FA_LDS char* const kt = (FA_LDS char*)kvt;
-  FA_LDS char* const vt = kt + KT;
+  FA_LDS char* const kt = (FA_LDS char*)kvt;  // (unused when K is in registers)
+  FA_LDS char* const vt = KREG ? kt : kt + KT;
   // After the loop the upper query half hands its partials over through LDS: dK^T of key
   // group kg in kvt, dV^T in the Q | dO buffer kg / 2.
   constexpr int RED = MD * 16 * 64;  // floats per key group and tensor
-  static_assert(4 * RED * 4 <= 2 * KT && 2 * RED * 4 <= 2 * QT, "dK/dV reduction fits in LDS");
+  static_assert(QH == 1 || (4 * RED * 4 <= KVT && 2 * RED * 4 <= 2 * QT), "dK/dV reduction fits in LDS");
 
   const int BH = a.B * a.H;
   const int bh = blockIdx.x % BH;
@@ -229,7 +250,8 @@ __global__ __launch_bounds__(kMainThreads, 1) void bwd_dkdv_kernel(BwdArgs a) {
   const int i1 = a.wl >= 0 ? min((min(k0 + kBK - 1 + a.wl, N - 1)) / BQ + 1, ntq) : ntq;
   int nq = k0 < kv_end ? max(i1 - i0, 0) : 0;  // key tile entirely padded: zero dK/dV
   if (a.mask && nq > 0)
-    nq = __builtin_amdgcn_readfirstlane(build_qtile_list512(qlist, wcount, a.mask, k0 / a.mb, a.nb, a.mb, i0, ntq, BQ));
+    nq = __builtin_amdgcn_readfirstlane(
+        build_qtile_list<kMainThreads>(qlist, wcount, a.mask, k0 / a.mb, a.nb, a.mb, i0, ntq, BQ));
 
   // K and V tiles stay in LDS for the whole kernel (rows past N are zero).
 #pragma unroll
@@ -239,9 +261,11 @@ __global__ __launch_bounds__(kMainThreads, 1) void bwd_dkdv_kernel(BwdArgs a) {
     const int kk = min(k0 + row, N - 1);
     const bool ok = k0 + row < N && col < DG;
     const int cc = col < DG ? col : 0;  // (a column in range; the value is dropped)
-    const u32x4 kv = gload16(K + (size_t)kk * rs + cc);
+    if constexpr (!KREG) {
+      const u32x4 kv = gload16(K + (size_t)kk * rs + cc);
+      lds_store16(kt + tile_off<D>(row, col), ok ? kv : u32x4{});
+    }
     const u32x4 vv = gload16(V + (size_t)kk * rs + cc);
-    lds_store16(kt + tile_off<D>(row, col), ok ? kv : u32x4{});
     lds_store16(vt + tile_off<D>(row, col), ok ? vv : u32x4{});
   }
 
@@ -264,11 +288,12 @@ __global__ __launch_bounds__(kMainThreads, 1) void bwd_dkdv_kernel(BwdArgs a) {
   // i the 16 bytes at offset 16 i, so lane i fetches the chunk whose swizzled slot that
   // is. Rows past N (last query tile only) read row N-1; they get P = 0 through the
   // staged lse (+inf), so their values never reach a result.
-  // Lane l of DMA block c covers row (8c + w) RPB + l / (D/8); the block rows are a
+  // Lane l of DMA block c covers row (NW c + w) RPB + l / (D/8); the block rows are a
   // multiple of 16 apart, so the swizzled column is the same for every block.
   const int dma_row0 = w * RPB + l / (D / 8);
   const int dma_col = ((l % (D / 8)) ^ swz<D>(dma_row0)) * 8;
-  static_assert((8 * RPB) % 16 == 0, "DMA block step must keep the swizzle");
+  static_assert((NW * RPB) % 16 == 0, "DMA block step must keep the swizzle");
+  static_assert(NDMA >= 1 && NDMA * kMainThreads * 16 == QT, "Q / dO tile staging covers the tile");
 
   f32x16 dkt[MD], dvt[MD];
 #pragma unroll
@@ -284,8 +309,8 @@ __global__ __launch_bounds__(kMainThreads, 1) void bwd_dkdv_kernel(BwdArgs a) {
     FA_LDS char* qb = (FA_LDS char*)(decltype(bufc)::value ? qd1 : qd0);
 #pragma unroll
     for (int c = 0; c < NDMA; ++c) {
-      const size_t row = (size_t)min(q0 + dma_row0 + c * 8 * RPB, N - 1) * rs + dma_col;
-      FA_LDS char* blk = qb + (c * 8 + w) * 1024;
+      const size_t row = (size_t)min(q0 + dma_row0 + c * NW * RPB, N - 1) * rs + dma_col;
+      FA_LDS char* blk = qb + (c * NW + w) * 1024;
       // (the builtin takes a non-const pointer; without the cast the host pass silently
       // drops the kernel's launch stub)
       const bool live = DG == D || dma_col < DG;
@@ -313,25 +338,24 @@ __global__ __launch_bounds__(kMainThreads, 1) void bwd_dkdv_kernel(BwdArgs a) {
   };
   // Wait for this wave's staging loads before the barrier that publishes the staged tile.
   auto wait_loads = [&]() { __builtin_amdgcn_s_waitcnt(kWaitVmcnt0); };
-  // Query tiles are visited last-first, so the workgroups of one head that run together
-  // add into the same dQ tile at about the same time.
+  // Query tiles are visited last-first.
   auto tile_at = [&](int t) {
     return a.mask ? __builtin_amdgcn_readfirstlane((int)qlist[nq - 1 - t]) : i0 + nq - 1 - t;
   };
 
+  // K fragments in registers: lane (kl, h) holds K[key][16 ks + 8 h .. + 7] (zero past N)
+  bf16x8 kf[KREG ? KSG : 1];
+  if constexpr (KREG) {
+    const __bf16* krow = K + (size_t)min(key, N - 1) * rs + 8 * h;
+#pragma unroll
+    for (int ks = 0; ks < KSG; ++ks)
+      kf[ks] = key < N ? __builtin_bit_cast(bf16x8, gload16(krow + 16 * ks)) : bf16x8{};
+  }
   stage_q(nq > 0 ? tile_at(0) : 0, std::integral_constant<int, 0>{});
   wait_loads();
   store_stats(0);
   __syncthreads();
   asm volatile("" ::: "memory");
-  // At d = 128 the wave's K fragments (the A operand of S, the same in every step) are
-  // held in registers, which saves a quarter of the step's row reads from LDS.
-  constexpr bool KREG = D == 128 && !DROP;
-  bf16x8 kf[KREG ? KSG : 1];
-  if constexpr (KREG) {
-#pragma unroll
-    for (int ks = 0; ks < KSG; ++ks) kf[ks] = lds_ld8(kt + (kv_off0 ^ (32 * ks)));
-  }
 
   auto step = [&](auto bufc, int t) {
     constexpr int BUF = decltype(bufc)::value;
@@ -490,22 +514,33 @@ __global__ __launch_bounds__(kMainThreads, 1) void bwd_dkdv_kernel(BwdArgs a) {
   }
 
   wait_loads();  // the last step's look-ahead staging must land before LDS is reused
-  __syncthreads();
-  // Sum the two query halves' partials through LDS (all tiles are free now): the upper
-  // half stores dK^T, dV^T in fp32 in its accumulator layout, the lower half adds them.
-  // [MD][16 regs][64 lanes] per key group
-  float* const kred = reinterpret_cast<float*>(kvt) + kg * RED + l;
-  float* const vred = reinterpret_cast<float*>(kg < 2 ? qd0 : qd1) + (kg & 1) * RED + l;
-  if (qh == 1) {
+  if constexpr (QH == 2) {
+    __syncthreads();
+    // Sum the two query halves' partials through LDS (all tiles are free now): the upper
+    // half stores dK^T, dV^T in fp32 in its accumulator layout, the lower half adds them.
+    // [MD][16 regs][64 lanes] per key group
+    float* const kred = reinterpret_cast<float*>(kvt) + kg * RED + l;
+    float* const vred = reinterpret_cast<float*>(kg < 2 ? qd0 : qd1) + (kg & 1) * RED + l;
+    if (qh == 1) {
 #pragma unroll
-    for (int md = 0; md < MD; ++md)
+      for (int md = 0; md < MD; ++md)
 #pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        kred[(md * 16 + i) * 64] = dkt[md][i];
-        vred[(md * 16 + i) * 64] = dvt[md][i];
-      }
+        for (int i = 0; i < 16; ++i) {
+          kred[(md * 16 + i) * 64] = dkt[md][i];
+          vred[(md * 16 + i) * 64] = dvt[md][i];
+        }
+    }
+    __syncthreads();
+    if (qh == 0) {
+#pragma unroll
+      for (int md = 0; md < MD; ++md)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+          dkt[md][i] += kred[(md * 16 + i) * 64];
+          dvt[md][i] += vred[(md * 16 + i) * 64];
+        }
+    }
   }
-  __syncthreads();
   if (qh == 0 && key < N) {
     __bf16* dK = reinterpret_cast<__bf16*>(a.dk) + hoff + (size_t)key * rs;
     __bf16* dV = reinterpret_cast<__bf16*>(a.dv) + hoff + (size_t)key * rs;
@@ -517,8 +552,8 @@ __global__ __launch_bounds__(kMainThreads, 1) void bwd_dkdv_kernel(BwdArgs a) {
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
           const int i = 4 * g + e;
-          kv4[e] = (__bf16)((dkt[md][i] + kred[(md * 16 + i) * 64]) * a.scale);
-          vv4[e] = (__bf16)((dvt[md][i] + vred[(md * 16 + i) * 64]) * (DROP ? a.drop_scale : 1.0f));
+          kv4[e] = (__bf16)(dkt[md][i] * a.scale);
+          vv4[e] = (__bf16)(dvt[md][i] * (DROP ? a.drop_scale : 1.0f));
         }
         if (32 * md + 8 * g < DG) {
           *reinterpret_cast<bf16x4*>(dK + 32 * md + 8 * g + 4 * h) = kv4;
@@ -802,7 +837,7 @@ hipError_t launch_bwd(const BwdArgs& a, int d, hipStream_t stream, const KernelT
   const size_t pre_threads = rows * (size_t)(d / 8);
   const dim3 block(kThreads);
   const dim3 gpre((unsigned)((pre_threads + kThreads - 1) / kThreads));
-  const dim3 gdkdv((unsigned)(((a.N + kBK - 1) / kBK) * a.B * a.H)), bdkdv(kMainThreads);
+  const dim3 gdkdv((unsigned)(((a.N + kBK - 1) / kBK) * a.B * a.H));
   const dim3 gdq((unsigned)(((a.N + kDqRows - 1) / kDqRows) * a.B * a.H));
   if (d == 16) hipLaunchKernelGGL(bwd_pre_kernel<16>, gpre, block, 0, stream, a);
   else if (d == 32) hipLaunchKernelGGL(bwd_pre_kernel<32>, gpre, block, 0, stream, a);
@@ -817,16 +852,17 @@ hipError_t launch_bwd(const BwdArgs& a, int d, hipStream_t stream, const KernelT
     if (e != hipSuccess) return e;
   }
   if (tm.start) (void)hipEventRecord(tm.start, stream);
+  auto dkdv = [&](auto kernel, int threads) { hipLaunchKernelGGL(kernel, gdkdv, dim3(threads), 0, stream, a); };
   if (a.dropout) {
-    if (d == 16) hipLaunchKernelGGL((bwd_dkdv_kernel<32, true, 16>), gdkdv, bdkdv, 0, stream, a);
-    else if (d == 32) hipLaunchKernelGGL((bwd_dkdv_kernel<32, true>), gdkdv, bdkdv, 0, stream, a);
-    else if (d == 64) hipLaunchKernelGGL((bwd_dkdv_kernel<64, true>), gdkdv, bdkdv, 0, stream, a);
-    else hipLaunchKernelGGL((bwd_dkdv_kernel<128, true>), gdkdv, bdkdv, 0, stream, a);
+    if (d == 16) dkdv(bwd_dkdv_kernel<32, true, 16>, dkdv_threads<32, true>());
+    else if (d == 32) dkdv(bwd_dkdv_kernel<32, true>, dkdv_threads<32, true>());
+    else if (d == 64) dkdv(bwd_dkdv_kernel<64, true>, dkdv_threads<64, true>());
+    else dkdv(bwd_dkdv_kernel<128, true>, dkdv_threads<128, true>());
   } else {
-    if (d == 16) hipLaunchKernelGGL((bwd_dkdv_kernel<32, false, 16>), gdkdv, bdkdv, 0, stream, a);
-    else if (d == 32) hipLaunchKernelGGL((bwd_dkdv_kernel<32, false>), gdkdv, bdkdv, 0, stream, a);
-    else if (d == 64) hipLaunchKernelGGL((bwd_dkdv_kernel<64, false>), gdkdv, bdkdv, 0, stream, a);
-    else hipLaunchKernelGGL((bwd_dkdv_kernel<128, false>), gdkdv, bdkdv, 0, stream, a);
+    if (d == 16) dkdv(bwd_dkdv_kernel<32, false, 16>, dkdv_threads<32, false>());
+    else if (d == 32) dkdv(bwd_dkdv_kernel<32, false>, dkdv_threads<32, false>());
+    else if (d == 64) dkdv(bwd_dkdv_kernel<64, false>, dkdv_threads<64, false>());
+    else dkdv(bwd_dkdv_kernel<128, false>, dkdv_threads<128, false>());
   }
   e = hipGetLastError();
   if (tm.stop) (void)hipEventRecord(tm.stop, stream);

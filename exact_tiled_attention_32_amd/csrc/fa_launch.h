@@ -98,9 +98,9 @@ constexpr int kFwdRowsPerWGBF16 = 128;   // bf16 forward: 4 waves x 32 query row
 constexpr int fwd_tile_keys_bf16(int) { return 64; }
 constexpr int kFwdTileKeysF32 = 32;
 constexpr int kMaxTileList = 4096;
-// Smallest tile of the backward kernels (64 keys per dQ-kernel tile, 64 or 128 query
-// rows per dK/dV step); their block-sparse tile lists hold at most N / 64 entries.
-constexpr int kBwdMinTile = 64;
+// Smallest tile of the backward kernels (32 query rows per dK/dV step at d = 128); their
+// block-sparse tile lists hold at most N / 32 entries.
+constexpr int kBwdMinTile = 32;
 // Keys per dK/dV workgroup, and the capacity of the block-sparse key-tile order.
 constexpr int kBwdKeyTile = 128;
 constexpr int kMaxKeyTiles = kMaxTileList * kBwdMinTile / kBwdKeyTile;

@@ -102,7 +102,7 @@ fa_status fa_fwd_blocksparse(fa_dtype dt, int B, int H, int N, int d,
 
 /*
  * Bytes of device workspace fa_bwd needs: the per-row D = rowsum(dO * O) (fp32 [B,H,N],
- * rounded up to 256 bytes), then 8 KB for the block-sparse order of the key tiles. Linear in N (the backward keeps O(N) extra memory; cochat.ai
+ * rounded up to 256 bytes), then 4 KB for the block-sparse order of the key tiles. Linear in N (the backward keeps O(N) extra memory; cochat.ai
  * audit of "FlashAttention: Fast and Memory-Efficient Exact Attention with IO-Awareness",
  * quoted backward-pass memory claim). Returns 0 for non-positive or overflowing sizes.
  */
@@ -114,7 +114,8 @@ size_t fa_bwd_workspace_bytes(int B, int H, int N, int d);
  *                     arguments); o and lse are read, not recomputed
  *   dout              upstream gradient [B,H,N,d]
  *   dq, dk, dv        outputs [B,H,N,d]
- *   block_mask        NULL (dense) or as in fa_fwd_blocksparse; mask_block ignored if NULL
+ *   block_mask        NULL (dense) or as in fa_fwd_blocksparse; mask_block ignored if NULL;
+ *                     with a mask N is at most 131072 (FA_ERR_UNSUPPORTED beyond)
  *   workspace         device memory of at least fa_bwd_workspace_bytes(B,H,N,d) bytes,
  *                     256-byte aligned, owned by the caller; its contents on entry do not
  *                     matter and are overwritten

@@ -38,14 +38,14 @@ def test_exports_every_declared_symbol(lib):
 
 
 def test_workspace_bytes_linear_in_n(lib):
-    # exact formula: align256(rows * 4) + 8 KiB: the fp32 D = rowsum(dO * O) of every row,
-    # then the block-sparse key-tile order (2048 entries)
+    # exact formula: align256(rows * 4) + 4 KiB: the fp32 D = rowsum(dO * O) of every row,
+    # then the block-sparse key-tile order (1024 entries)
     for B, H, N, d in [(1, 1, 1, 64), (8, 16, 512, 64), (1, 16, 16384, 128), (1, 8, 65536, 64)]:
         rows = B * H * N
         al = lambda x: (x + 255) // 256 * 256
-        assert fa.fa_bwd_workspace_bytes(B, H, N, d) == al(rows * 4) + 8192
+        assert fa.fa_bwd_workspace_bytes(B, H, N, d) == al(rows * 4) + 4096
     # O(N): doubling N doubles the workspace (no N^2 term)
-    ws = lambda n: fa.fa_bwd_workspace_bytes(1, 1, n, 64) - 8192
+    ws = lambda n: fa.fa_bwd_workspace_bytes(1, 1, n, 64) - 4096
     assert ws(32768) == 2 * ws(16384)
     assert fa.fa_bwd_workspace_bytes(0, 1, 1, 64) == 0
     assert fa.fa_bwd_workspace_bytes(1, 1, -5, 64) == 0
