@@ -121,6 +121,7 @@ def test_fwd_blocksparse_rejects(lib, kwargs, status):
     (dict(ws_bytes=100), fa.FA_ERR_INVALID),     # D for N=128 needs 512 bytes
     (dict(dq=0), fa.FA_ERR_INVALID),
     (dict(mask=P, mb=96), fa.FA_ERR_INVALID),
+    (dict(mask=P, N=131072 + 1), fa.FA_ERR_UNSUPPORTED),  # query-tile list capacity (32-row steps)
     (dict(scale=float("nan")), fa.FA_ERR_INVALID),
     (dict(d=256), fa.FA_ERR_UNSUPPORTED),
 ])
