@@ -111,9 +111,10 @@ class KernelClock:
 
 
 KERNEL_NAMES = {  # demangled kernel -> short name used by the bench and the traffic file
-    # (template arguments: tile width, dropout flag, head dimension in memory)
+    # (template arguments: tile width, dropout flag, head dimension in memory; for dK/dV
+    # also the query halves, 1 for the dense 4-wave layout)
     "fwd_bf16_kernel<64, false, 64>": "fwd_d64", "fwd_bf16_kernel<128, false, 128>": "fwd_d128",
-    "bwd_dkdv_kernel<64, false, 64>": "bwd_dkdv_d64", "bwd_dkdv_kernel<128, false, 128>": "bwd_dkdv_d128",
+    "bwd_dkdv_kernel<64, false, 64, 1>": "bwd_dkdv_d64", "bwd_dkdv_kernel<128, false, 128, 1>": "bwd_dkdv_d128",
     "bwd_dq_kernel<64, false, 64>": "bwd_dq_d64", "bwd_dq_kernel<128, false, 128>": "bwd_dq_d128",
     "bwd_pre_kernel<64>": "bwd_pre_d64", "bwd_pre_kernel<128>": "bwd_pre_d128",
     "kvc_split_kernel<64>": "kvc_split_d64", "kvc_split_kernel<128>": "kvc_split_d128",

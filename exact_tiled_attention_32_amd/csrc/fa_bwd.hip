@@ -143,15 +143,17 @@ __global__ __launch_bounds__(kThreads) void bwd_order_kernel(const uint8_t* __re
 // s_waitcnt immediate for vmcnt(0), expcnt and lgkmcnt left free (gfx9 encoding).
 constexpr int kWaitVmcnt0 = 0x0F70;
 
-// Waves of a key group (32 keys) that split each query step between them. With one, a
-// workgroup is 4 waves and two workgroups share a CU, so the two waves of a SIMD belong
-// to different workgroups and drift apart instead of meeting at every barrier. The
-// dropout variant at d = 128 cannot hold K in registers next to its generator state, needs
-// K in LDS and so keeps one 8-wave workgroup per CU (two query halves).
+// Waves of a key group (32 keys) that split each query step between them (QH). With one,
+// a workgroup is 4 waves and two workgroups share a CU, so the two waves of a SIMD belong
+// to different workgroups and drift apart instead of meeting at every barrier. With two,
+// a workgroup is 8 waves, one per CU, and a key tile's query steps are shared by twice
+// as many waves: the block-sparse path uses it, where the kept blocks of a few "global"
+// key columns make some key tiles far longer than the rest and their duration sets the
+// end of the launch; so does the dropout variant at d = 128, which cannot hold K in
+// registers next to its generator state and so needs K in LDS.
 template <int D, bool DROP>
 constexpr int dkdv_halves() { return D == 128 && DROP ? 2 : 1; }
-template <int D, bool DROP>
-constexpr int dkdv_threads() { return 256 * dkdv_halves<D, DROP>(); }
+constexpr int dkdv_threads(int qh) { return 256 * qh; }
 // 32-query blocks per wave and step
 template <int D>
 constexpr int dkdv_query_blocks() { return D == 128 ? 1 : 2; }
@@ -182,20 +184,19 @@ __device__ int build_qtile_list(uint16_t* list, int* wcount, const uint8_t* mask
 }
 
 // DG: head dimension in memory; D: tile width (16 runs on 32-wide tiles, upper half zero).
-template <int D, bool DROP, int DG = D>
-__global__ __launch_bounds__((dkdv_threads<D, DROP>()), (dkdv_halves<D, DROP>() == 1 ? 2 : 1)) void bwd_dkdv_kernel(
-    BwdArgs a) {
+template <int D, bool DROP, int DG = D, int QH = dkdv_halves<D, DROP>()>
+__global__ __launch_bounds__(dkdv_threads(QH), QH == 1 ? 2 : 1) void bwd_dkdv_kernel(BwdArgs a) {
   static_assert(DG == D || (D == 32 && DG == 16), "narrow heads run on 32-wide tiles");
-  constexpr int kMainThreads = dkdv_threads<D, DROP>();
-  constexpr int QH = dkdv_halves<D, DROP>();  // query halves (waves per key group)
+  static_assert(QH == 1 || QH == 2, "one or two query halves");
+  static_assert(QH == 2 || dkdv_halves<D, DROP>() == 1, "this variant needs the 8-wave layout");
+  constexpr int kMainThreads = dkdv_threads(QH);
   constexpr int NW = 4 * QH;                  // waves per workgroup
   constexpr int KSG = (DG + 15) / 16;  // k-steps that carry data
   constexpr int QBW = dkdv_query_blocks<D>();  // 32-query blocks per wave per step
   constexpr int BQ = 32 * QBW * QH;            // query rows per step
   // At d = 128 without dropout the wave's K fragments (the A operand of S, the same in
   // every step) are loaded once into registers and K is not kept in LDS.
-  constexpr bool KREG = D == 128 && !DROP;
-  static_assert(!KREG || QH == 1, "K in registers goes with the 4-wave layout");
+  constexpr bool KREG = D == 128 && !DROP && QH == 1;
   constexpr int MD = D / 32;           // 32-row blocks of dK^T / dV^T
   constexpr int QT = BQ * D * 2;       // bytes of a Q or dO tile
   constexpr int KT = kBK * D * 2;      // bytes of the K or V tile
@@ -852,17 +853,21 @@ hipError_t launch_bwd(const BwdArgs& a, int d, hipStream_t stream, const KernelT
     if (e != hipSuccess) return e;
   }
   if (tm.start) (void)hipEventRecord(tm.start, stream);
-  auto dkdv = [&](auto kernel, int threads) { hipLaunchKernelGGL(kernel, gdkdv, dim3(threads), 0, stream, a); };
+  // the block-sparse path takes the 8-wave layout (see dkdv_halves)
+  auto dkdv = [&](auto k1, auto k2, int qh1) {
+    if (a.mask) hipLaunchKernelGGL(k2, gdkdv, dim3(dkdv_threads(2)), 0, stream, a);
+    else hipLaunchKernelGGL(k1, gdkdv, dim3(dkdv_threads(qh1)), 0, stream, a);
+  };
   if (a.dropout) {
-    if (d == 16) dkdv(bwd_dkdv_kernel<32, true, 16>, dkdv_threads<32, true>());
-    else if (d == 32) dkdv(bwd_dkdv_kernel<32, true>, dkdv_threads<32, true>());
-    else if (d == 64) dkdv(bwd_dkdv_kernel<64, true>, dkdv_threads<64, true>());
-    else dkdv(bwd_dkdv_kernel<128, true>, dkdv_threads<128, true>());
+    if (d == 16) dkdv(bwd_dkdv_kernel<32, true, 16>, bwd_dkdv_kernel<32, true, 16, 2>, dkdv_halves<32, true>());
+    else if (d == 32) dkdv(bwd_dkdv_kernel<32, true>, bwd_dkdv_kernel<32, true, 32, 2>, dkdv_halves<32, true>());
+    else if (d == 64) dkdv(bwd_dkdv_kernel<64, true>, bwd_dkdv_kernel<64, true, 64, 2>, dkdv_halves<64, true>());
+    else dkdv(bwd_dkdv_kernel<128, true>, bwd_dkdv_kernel<128, true, 128, 2>, dkdv_halves<128, true>());
   } else {
-    if (d == 16) dkdv(bwd_dkdv_kernel<32, false, 16>, dkdv_threads<32, false>());
-    else if (d == 32) dkdv(bwd_dkdv_kernel<32, false>, dkdv_threads<32, false>());
-    else if (d == 64) dkdv(bwd_dkdv_kernel<64, false>, dkdv_threads<64, false>());
-    else dkdv(bwd_dkdv_kernel<128, false>, dkdv_threads<128, false>());
+    if (d == 16) dkdv(bwd_dkdv_kernel<32, false, 16>, bwd_dkdv_kernel<32, false, 16, 2>, dkdv_halves<32, false>());
+    else if (d == 32) dkdv(bwd_dkdv_kernel<32, false>, bwd_dkdv_kernel<32, false, 32, 2>, dkdv_halves<32, false>());
+    else if (d == 64) dkdv(bwd_dkdv_kernel<64, false>, bwd_dkdv_kernel<64, false, 64, 2>, dkdv_halves<64, false>());
+    else dkdv(bwd_dkdv_kernel<128, false>, bwd_dkdv_kernel<128, false, 128, 2>, dkdv_halves<128, false>());
   }
   e = hipGetLastError();
   if (tm.stop) (void)hipEventRecord(tm.stop, stream);
