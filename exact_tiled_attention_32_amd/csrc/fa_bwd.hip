@@ -215,8 +215,8 @@ __global__ __launch_bounds__(dkdv_threads(QH), QH == 1 ? 2 : 1) void bwd_dkdv_ke
   __shared__ int wcount[8];
   FA_LDS char* const kt = (FA_LDS char*)kvt;  // (unused when K is in registers)
   FA_LDS char* const vt = KREG ? kt : kt + KT;
-  // After the loop the upper query half hands its partials over through LDS: dK^T of key
-  // group kg in kvt, dV^T in the Q | dO buffer kg / 2.
+  // With two query halves, after the loop the upper half hands its partials over through
+  // LDS: dK^T of key group kg in kvt, dV^T in the Q | dO buffer kg / 2.
   constexpr int RED = MD * 16 * 64;  // floats per key group and tensor
   static_assert(QH == 1 || (4 * RED * 4 <= KVT && 2 * RED * 4 <= 2 * QT), "dK/dV reduction fits in LDS");
 
@@ -254,7 +254,8 @@ __global__ __launch_bounds__(dkdv_threads(QH), QH == 1 ? 2 : 1) void bwd_dkdv_ke
     nq = __builtin_amdgcn_readfirstlane(
         build_qtile_list<kMainThreads>(qlist, wcount, a.mask, k0 / a.mb, a.nb, a.mb, i0, ntq, BQ));
 
-  // K and V tiles stay in LDS for the whole kernel (rows past N are zero).
+  // The V tile, and the K tile unless K is held in registers, stay in LDS for the whole
+  // kernel (rows past N are zero).
 #pragma unroll
   for (int c = 0; c < KCH; ++c) {
     const int id = tid + kMainThreads * c;
