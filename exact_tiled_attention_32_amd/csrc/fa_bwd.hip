@@ -854,21 +854,22 @@ hipError_t launch_bwd(const BwdArgs& a, int d, hipStream_t stream, const KernelT
     if (e != hipSuccess) return e;
   }
   if (tm.start) (void)hipEventRecord(tm.start, stream);
-  // the block-sparse path takes the 8-wave layout (see dkdv_halves)
-  auto dkdv = [&](auto k1, auto k2, int qh1) {
-    if (a.mask) hipLaunchKernelGGL(k2, gdkdv, dim3(dkdv_threads(2)), 0, stream, a);
-    else hipLaunchKernelGGL(k1, gdkdv, dim3(dkdv_threads(qh1)), 0, stream, a);
-  };
-  if (a.dropout) {
-    if (d == 16) dkdv(bwd_dkdv_kernel<32, true, 16>, bwd_dkdv_kernel<32, true, 16, 2>, dkdv_halves<32, true>());
-    else if (d == 32) dkdv(bwd_dkdv_kernel<32, true>, bwd_dkdv_kernel<32, true, 32, 2>, dkdv_halves<32, true>());
-    else if (d == 64) dkdv(bwd_dkdv_kernel<64, true>, bwd_dkdv_kernel<64, true, 64, 2>, dkdv_halves<64, true>());
-    else dkdv(bwd_dkdv_kernel<128, true>, bwd_dkdv_kernel<128, true, 128, 2>, dkdv_halves<128, true>());
+  auto dkdv = [&](auto kernel, int qh) { hipLaunchKernelGGL(kernel, gdkdv, dim3(dkdv_threads(qh)), 0, stream, a); };
+  if (a.dropout) {  // (the dropout calls take no block mask)
+    if (d == 16) dkdv(bwd_dkdv_kernel<32, true, 16>, dkdv_halves<32, true>());
+    else if (d == 32) dkdv(bwd_dkdv_kernel<32, true>, dkdv_halves<32, true>());
+    else if (d == 64) dkdv(bwd_dkdv_kernel<64, true>, dkdv_halves<64, true>());
+    else dkdv(bwd_dkdv_kernel<128, true>, dkdv_halves<128, true>());
+  } else if (a.mask) {  // block-sparse: the 8-wave layout (see dkdv_halves)
+    if (d == 16) dkdv(bwd_dkdv_kernel<32, false, 16, 2>, 2);
+    else if (d == 32) dkdv(bwd_dkdv_kernel<32, false, 32, 2>, 2);
+    else if (d == 64) dkdv(bwd_dkdv_kernel<64, false, 64, 2>, 2);
+    else dkdv(bwd_dkdv_kernel<128, false, 128, 2>, 2);
   } else {
-    if (d == 16) dkdv(bwd_dkdv_kernel<32, false, 16>, bwd_dkdv_kernel<32, false, 16, 2>, dkdv_halves<32, false>());
-    else if (d == 32) dkdv(bwd_dkdv_kernel<32, false>, bwd_dkdv_kernel<32, false, 32, 2>, dkdv_halves<32, false>());
-    else if (d == 64) dkdv(bwd_dkdv_kernel<64, false>, bwd_dkdv_kernel<64, false, 64, 2>, dkdv_halves<64, false>());
-    else dkdv(bwd_dkdv_kernel<128, false>, bwd_dkdv_kernel<128, false, 128, 2>, dkdv_halves<128, false>());
+    if (d == 16) dkdv(bwd_dkdv_kernel<32, false, 16>, dkdv_halves<32, false>());
+    else if (d == 32) dkdv(bwd_dkdv_kernel<32, false>, dkdv_halves<32, false>());
+    else if (d == 64) dkdv(bwd_dkdv_kernel<64, false>, dkdv_halves<64, false>());
+    else dkdv(bwd_dkdv_kernel<128, false>, dkdv_halves<128, false>());
   }
   e = hipGetLastError();
   if (tm.stop) (void)hipEventRecord(tm.stop, stream);
