@@ -142,6 +142,34 @@ def test_sparse_rule_medium_heavy_columns(gpu_lib):
     full_check(gpu_lib, case, "bf16", label="sparse-rule-N4096")
 
 
+@pytest.mark.parametrize("d", [16, 128])
+def test_blocksparse_largest_n(gpu_lib, d):
+    """Block-sparse forward and backward at the largest N the backward's tile lists take
+    (131072: 4096 query steps of 32 rows, 1024 key tiles in the order table), banded mask
+    |i - j| <= 1. A key block's dK, dV depend only on the query blocks next to it, so sampled
+    blocks (first, second, middle, last) are compared with the oracle exactly."""
+    N, mb = 131072, 128
+    nb = N // mb
+    i = np.arange(nb)
+    mask = (np.abs(i[:, None] - i[None, :]) <= 1).astype(np.uint8)
+    case = workloads.make_case(1, 1, N, d, seed=41 + d, block_mask=mask, mask_block=mb)
+    note(f"[parity] sparse largest N={N} d={d}")
+    got = gpu_run(gpu_lib, case)
+    q64, k64, v64 = (parity.to64(case[n])[0, 0] for n in ("q", "k", "v"))
+    for r in (0, 1, nb // 2, nb - 1):
+        rows = np.arange(r * mb, (r + 1) * mb)
+        allow = oracle.allowed_pairs(rows, N, causal=False, kv_len_b=None, block_mask=mask, mask_block=mb)
+        ref_o, ref_lse = oracle.forward_rows(q64[rows], k64, v64, case["scale"], allow)
+        parity.check_o(got["o"][0, 0, rows], ref_o, "bf16", f"block {r} O")
+        parity.check_lse(got["lse"][0, 0, rows], ref_lse, f"block {r} lse")
+        near = np.arange(max(r - 1, 0) * mb, min(r + 2, nb) * mb)  # query blocks that see key block r
+        dq, dk, dv = oracle.attention_backward(case["q"], case["k"], case["v"], case["do"], case["scale"],
+                                               block_mask=mask, mask_block=mb, rows=near)
+        parity.check_grad(got["dk"][0, 0, rows], dk[0, 0, rows], f"block {r} dK")
+        parity.check_grad(got["dv"][0, 0, rows], dv[0, 0, rows], f"block {r} dV")
+        parity.check_grad(got["dq"][0, 0, near], dq[0, 0, near], f"blocks near {r} dQ")
+
+
 @pytest.mark.parametrize("N,d", [(1, 64), (77, 64), (128, 64), (300, 128), (129, 128), (77, 32), (300, 32)])
 def test_sweep_f32_forward(gpu_lib, N, d):
     case = workloads.make_case(2, 2, N, d, dtype="f32", seed=N + d, causal=(N % 2 == 1))
