@@ -14,6 +14,9 @@ Packed variable-length sequences and the sliding-window mask are timed outside t
 on their own workloads and reported under "varlen" (FLOP counted exactly over the allowed
 query-key pairs: 4 d per pair forward, 2.5x that backward).
 
+Dropout (p = 0.1) on the step's workloads is timed outside the step and reported under
+"dropout", by the same FLOP convention (the generator's work is not counted).
+
 The key/value-cache forward (a few queries against a long cache, HBM-bound) is timed
 outside the step on its decode workloads and reported under "kvcache_decode": algorithmic
 bytes = every valid cached key and value read once plus Q and O, divided by the time of the
@@ -37,6 +40,7 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 PEAK_BF16_TFLOPS = 2500.0  # MI355X dense bf16 MFMA
+DROPOUT_P, DROPOUT_SEED = 0.1, 1234  # the dropout report's probability and seed
 PEAK_HBM_GBS = 8000.0
 METRIC = "attention fwd+bwd TFLOP/s (bf16, causal) and % of MI355X bf16 MFMA peak"
 STEP_WORKLOADS = ("long_causal_d64", "long_causal_d128")
@@ -197,6 +201,10 @@ def counter_sequence(workloads):
         for name, w in workloads.VARLEN_WORKLOADS.items():
             seq += [(name, f"fwd_bf16_kernel<{w.d}>"), (name, f"bwd_pre_kernel<{w.d}>"),
                     (name, f"bwd_dkdv_kernel<{w.d}>"), (name, f"bwd_dq_kernel<{w.d}>")]
+        for name in STEP_WORKLOADS:
+            d = workloads.WORKLOADS[name].d
+            seq += [(name + "_dropout", f"fwd_bf16_kernel<{d}>"), (name + "_dropout", f"bwd_pre_kernel<{d}>"),
+                    (name + "_dropout", f"bwd_dkdv_kernel<{d}>"), (name + "_dropout", f"bwd_dq_kernel<{d}>")]
         for name, w in workloads.DECODE_WORKLOADS.items():
             seq += [(name, f"kvc_split_kernel<{w.d}>"), (name, f"kvc_merge_kernel<{w.d}>")]
     return seq
@@ -238,6 +246,11 @@ def counter_pass(fa, dev):
             fa.fa_bwd_varlen(t["q"], t["k"], t["v"], o, t["do"], lse, t["cu_seqlens"], x["max_seqlen"], x["scale"],
                              **kw)
             torch.cuda.synchronize()
+        for r in runners:
+            if r.w.name in STEP_WORKLOADS:
+                o, lse = fa.fa_fwd_dropout(r.q, r.k, r.v, r.scale, DROPOUT_P, DROPOUT_SEED, True)
+                fa.fa_bwd_dropout(r.q, r.k, r.v, o, r.do, lse, r.scale, DROPOUT_P, DROPOUT_SEED, True)
+                torch.cuda.synchronize()
         for w, q, k, v, kv, scale, ws in dec:
             fa.fa_fwd_kvcache(q, k, v, scale, w.causal, kv, workspace=ws)
             torch.cuda.synchronize()
@@ -502,6 +515,45 @@ def report_varlen(fa, w, dev, steps, warmup) -> dict:
     return res
 
 
+def report_dropout(fa, w, dev, steps, warmup) -> dict:
+    """Forward and backward with dropout (p = DROPOUT_P) on one of the step's workloads,
+    whole calls timed with events, plus the dominant kernel of each (forward kernel; dK/dV
+    kernel) through the library's event hook. FLOP as in the step; the generator's work is
+    not counted."""
+    import torch
+    from exact_tiled_attention_32_amd import workloads
+    x = workloads.generate(w)
+    q, k, v, do = (x[n].to(dev) for n in ("q", "k", "v", "do"))
+    o = torch.empty_like(q)
+    lse = torch.empty(q.shape[:3], dtype=torch.float32, device=dev)
+    dq, dk, dv = (torch.empty_like(q) for _ in range(3))
+    ws = torch.empty(fa.fa_bwd_workspace_bytes(w.B, w.H, w.N, w.d), dtype=torch.uint8, device=dev)
+    fns = {
+        "fwd": lambda: fa.fa_fwd_dropout(q, k, v, x["scale"], DROPOUT_P, DROPOUT_SEED, w.causal, o=o, lse=lse),
+        "bwd": lambda: fa.fa_bwd_dropout(q, k, v, o, do, lse, x["scale"], DROPOUT_P, DROPOUT_SEED, w.causal,
+                                         dq=dq, dk=dk, dv=dv, workspace=ws),
+    }
+    res = {"p": DROPOUT_P, "d": w.d}
+    for phase, fn in fns.items():
+        for _ in range(warmup):
+            fn()
+        torch.cuda.synchronize()
+        clock = KernelClock()
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record()
+        for _ in range(steps):
+            clock.arm(fa, phase)
+            fn()
+        b.record()
+        torch.cuda.synchronize()
+        ms = a.elapsed_time(b) / steps
+        flop = attn_flops(w) * (2.5 if phase == "bwd" else 1.0)
+        res[phase] = {"ms": round(ms, 4), "tflops": round(flop / ms / 1e9, 1),
+                      "frac_of_peak": round(flop / ms / 1e9 / PEAK_BF16_TFLOPS, 4),
+                      ("fwd_kernel_ms" if phase == "fwd" else "dkdv_kernel_ms"): round(clock.mean_ms(phase), 4)}
+    return res
+
+
 def report_all(fa, dev, path, steps=10, warmup=3):
     """Per-workload fwd / bwd timing (not the metric line)."""
     import torch
@@ -648,6 +700,9 @@ def main():
         line["kvcache_decode"] = dec
         # packed variable-length sequences and the sliding window, outside the step
         line["varlen"] = {name: report_varlen(fa, w, dev, 10, 3) for name, w in workloads.VARLEN_WORKLOADS.items()}
+        torch.cuda.empty_cache()
+        # dropout on the step's workloads, outside the step
+        line["dropout"] = {name: report_dropout(fa, workloads.WORKLOADS[name], dev, 10, 3) for name in STEP_WORKLOADS}
         torch.cuda.empty_cache()
     if args.report:
         report_all(fa, dev, args.report)
