@@ -1,0 +1,99 @@
+"""Host-side logic of bench.py (no GPU): the FLOP and byte conventions behind the metric
+line, the digest that gates the committed traffic figures, the dispatch sequence the
+counter summary expects, and the refusal of more than one GPU."""
+import json
+import os
+import shutil
+import subprocess
+import sys
+
+import pytest
+import torch
+
+import bench
+from exact_tiled_attention_32_amd import workloads
+
+
+def test_attn_flops_convention():
+    # 4 B H N^2 d for the forward, halved for causal attention
+    assert bench.attn_flops(workloads.WORKLOADS["long_causal_d128"]) == 4.0 * 16 * 16384 ** 2 * 128 / 2
+    assert bench.attn_flops(workloads.WORKLOADS["bert_padded"]) == 4.0 * 8 * 16 * 512 ** 2 * 64
+    w = workloads.WORKLOADS["block_sparse_64k"]
+    assert bench.attn_flops(w, 0.068) == pytest.approx(4.0 * 8 * 65536 ** 2 * 64 * 0.068)
+
+
+@pytest.mark.parametrize("n", [0, 1, 2, 7, 33])
+@pytest.mark.parametrize("causal,wl,wr", [(False, -1, -1), (True, -1, -1), (True, 3, -1), (False, 2, 5),
+                                           (False, 0, 0), (False, -1, 4), (True, 0, -1), (True, 2, 9)])
+def test_allowed_pair_count_brute_force(n, causal, wl, wr):
+    # key j is allowed for query i iff i - wl <= j <= i + wr (each side unbounded when -1);
+    # causal attention is wr = 0, whatever wr says
+    count = 0
+    for i in range(n):
+        for j in range(n):
+            if causal and j > i:
+                continue
+            if wl >= 0 and j < i - wl:
+                continue
+            if not causal and wr >= 0 and j > i + wr:
+                continue
+            count += 1
+    assert bench.allowed_pair_count(n, causal, wl, wr) == count
+
+
+def test_decode_bytes():
+    w = workloads.DecodeWorkload("tiny", B=2, H=3, Nq=4, Nk=100, d=64, seed=0)
+    q_and_o = 2 * 2 * (2 * 3 * 4 * 64)  # bf16 queries read, outputs written
+    kv = lambda keys: 2 * 2 * 3 * 64 * keys  # bf16 keys and values of every valid position
+    assert bench.decode_bytes(w, torch.tensor([100, 37])) == kv(137) + q_and_o
+    assert bench.decode_bytes(w, None) == kv(200) + q_and_o
+    assert bench.decode_bytes(w, torch.tensor([500, -3])) == kv(100) + q_and_o  # clamped to [0, Nk]
+
+
+def test_traffic_gated_by_source_digest(monkeypatch):
+    with open(os.path.join(bench.ROOT, "profiles", "hbm_traffic.json")) as f:
+        entry = json.load(f)["kernels"]["bwd_dkdv_d128"]
+    monkeypatch.setattr(bench, "kernel_source_digest", lambda: entry["source_digest"])
+    assert bench.load_traffic("bwd_dkdv_d128") == entry["bytes_per_launch"]
+    assert bench.load_traffic("no_such_kernel") is None
+    monkeypatch.setattr(bench, "kernel_source_digest", lambda: "0" * 16)
+    assert bench.load_traffic("bwd_dkdv_d128") is None
+
+
+def test_digest_ignores_comments_only(tmp_path, monkeypatch):
+    src = os.path.join(bench.ROOT, "exact_tiled_attention_32_amd", "csrc")
+    dst = tmp_path / "exact_tiled_attention_32_amd" / "csrc"
+    dst.mkdir(parents=True)
+    for f in ("fa_device.h", "fa_bwd.hip", "fa_fwd.hip", "fa_launch.h"):
+        shutil.copy(os.path.join(src, f), dst / f)
+    monkeypatch.setattr(bench, "ROOT", str(tmp_path))
+    base = bench.kernel_source_digest()
+    path = dst / "fa_fwd.hip"
+    code = path.read_text()
+    path.write_text("// a new comment\n/* and a block\n   comment */\n" + code.replace("\n", "\n\n", 3))
+    assert bench.kernel_source_digest() == base
+    path.write_text(code.replace("kRescaleLog2 = 8.0f", "kRescaleLog2 = 4.0f"))
+    assert bench.kernel_source_digest() != base
+
+
+def test_counter_sequence():
+    seq = bench.counter_sequence(workloads)
+    half = len(seq) // 2
+    assert seq[:half] == seq[half:]  # two identical rounds, the second is summarised
+    names = {w for w, _ in seq}
+    assert set(workloads.WORKLOADS) | set(workloads.VARLEN_WORKLOADS) | set(workloads.DECODE_WORKLOADS) <= names
+    assert {n + "_dropout" for n in bench.STEP_WORKLOADS} <= names
+    kernels = {}
+    for w, k in seq[:half]:
+        kernels.setdefault(w, []).append(k.split("<")[0])
+    assert kernels["block_sparse_64k"] == ["fwd_bf16_kernel", "bwd_pre_kernel", "bwd_order_kernel",
+                                           "bwd_dkdv_kernel", "bwd_dq_kernel"]
+    assert kernels["single_head_f32"] == ["fwd_f32_kernel"]
+    assert kernels["decode_q1_d128"] == ["kvc_split_kernel", "kvc_merge_kernel"]
+
+
+def test_more_than_one_gpu_refused():
+    r = subprocess.run([sys.executable, "bench.py", "--gpus", "2"], cwd=bench.ROOT, capture_output=True, text=True,
+                       timeout=300)
+    assert r.returncode == 2
+    assert "one GPU" in r.stderr
