@@ -99,13 +99,21 @@ class KernelClock:
     def __init__(self):
         self.pairs = {}
 
-    def arm(self, fa, name):
+    @staticmethod
+    def new_pair():
         import torch
         s, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         # torch creates the HIP event at its first record; the library then re-records it
         # around the kernel launch on the same stream
         s.record()
         e.record()
+        return s, e
+
+    def arm(self, fa, name, pair=None):
+        """Has the library time the dominant kernel of its next call. `pair` is an event pair
+        made beforehand by new_pair(), so that no extra event is recorded on the stream in a
+        timed region; without one a pair is made here."""
+        s, e = pair if pair is not None else self.new_pair()
         self.pairs.setdefault(name, []).append((s, e))
         fa.fa_time_next_kernel(s, e)
 
@@ -404,15 +412,17 @@ def time_step(fa, runners, steps, warmup):
             r.bwd()
     torch.cuda.synchronize()
     clock = KernelClock()
+    # the kernel clock's event pairs are made before the timed region
+    pairs = [[(KernelClock.new_pair(), KernelClock.new_pair()) for _ in runners] for _ in range(steps)]
     t0 = torch.cuda.Event(enable_timing=True)
     t1 = torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     t0.record()
-    for _ in range(steps):
-        for r in runners:
-            clock.arm(fa, f"fwd_d{r.w.d}")
+    for i in range(steps):
+        for r, (pf, pb) in zip(runners, pairs[i]):
+            clock.arm(fa, f"fwd_d{r.w.d}", pf)
             r.fwd()
-            clock.arm(fa, f"bwd_dkdv_d{r.w.d}")
+            clock.arm(fa, f"bwd_dkdv_d{r.w.d}", pb)
             r.bwd()
     t1.record()
     torch.cuda.synchronize()
@@ -539,10 +549,11 @@ def report_dropout(fa, w, dev, steps, warmup) -> dict:
             fn()
         torch.cuda.synchronize()
         clock = KernelClock()
+        pairs = [KernelClock.new_pair() for _ in range(steps)]
         a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         a.record()
-        for _ in range(steps):
-            clock.arm(fa, phase)
+        for pair in pairs:
+            clock.arm(fa, phase, pair)
             fn()
         b.record()
         torch.cuda.synchronize()
@@ -573,10 +584,11 @@ def report_all(fa, dev, path, steps=10, warmup=3):
                 fn()
             torch.cuda.synchronize()
             clock = KernelClock()
+            pairs = [KernelClock.new_pair() for _ in range(steps)]
             a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
             a.record()
-            for _ in range(steps):
-                clock.arm(fa, phase)
+            for pair in pairs:
+                clock.arm(fa, phase, pair)
                 fn()
             b.record()
             torch.cuda.synchronize()
