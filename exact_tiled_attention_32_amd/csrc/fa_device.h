@@ -177,8 +177,9 @@ __device__ __forceinline__ u32x4 philox4x32_10(uint32_t x0, uint32_t x1, uint32_
   for (int r = 0; r < 10; ++r) {
     const uint64_t p0 = (uint64_t)0xD2511F53u * x0;
     const uint64_t p1 = (uint64_t)0xCD9E8D57u * x2;
-    const uint32_t n0 = (uint32_t)(p1 >> 32) ^ x1 ^ k0;
-    const uint32_t n2 = (uint32_t)(p0 >> 32) ^ x3 ^ k1;
+    // three-input XORs as one v_bitop3_b32 each (truth table 0x96 = a ^ b ^ c)
+    const uint32_t n0 = __builtin_amdgcn_bitop3_b32((uint32_t)(p1 >> 32), x1, k0, 0x96);
+    const uint32_t n2 = __builtin_amdgcn_bitop3_b32((uint32_t)(p0 >> 32), x3, k1, 0x96);
     x1 = (uint32_t)p1;
     x3 = (uint32_t)p0;
     x0 = n0;
