@@ -49,6 +49,25 @@ KERNEL_FLOP_FACTOR = {"fwd": 1.0, "bwd_dkdv": 2.0}
 CALIBRATION_BYTES = 256 << 20
 
 
+# Minimum GPU time of every warm-up: the engine clock falls while the GPU idles (for instance
+# while the next workload's inputs are generated on the host) and takes milliseconds to climb
+# back, so a fixed few warm-up calls can leave the first timed calls at a low clock.
+MIN_WARMUP_S = 0.2
+
+
+def warm_up(fn, calls: int, min_s: float = MIN_WARMUP_S) -> None:
+    """Runs `fn` at least `calls` times and until `min_s` seconds have passed, then syncs."""
+    import torch
+    t_end = time.perf_counter() + min_s
+    n = 0
+    while n < calls or time.perf_counter() < t_end:
+        fn()
+        n += 1
+        if n >= calls:
+            torch.cuda.synchronize()
+    torch.cuda.synchronize()
+
+
 def attn_flops(w, kept_fraction=None) -> float:
     """Forward FLOP of a workload under the convention above."""
     f = 4.0 * w.B * w.H * w.N * w.N * w.d
@@ -406,6 +425,8 @@ def cpu_baseline(target_s: float = 15.0) -> dict:
 
 def time_step(fa, runners, steps, warmup):
     import torch
+    # exactly `warmup` untimed steps (the metric line's contract); at ~7 ms a step, the
+    # default 10 also bring the engine clock up
     for _ in range(warmup):
         for r in runners:
             r.fwd()
@@ -450,9 +471,7 @@ def report_decode(fa, w, dev, steps, warmup) -> dict:
     def call():
         fa.fa_fwd_kvcache(q, k, v, x["scale"], w.causal, kv, o=o, lse=lse, workspace=ws)
 
-    for _ in range(warmup):
-        call()
-    torch.cuda.synchronize()
+    warm_up(call, warmup)
     a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     a.record()
     for _ in range(steps):
@@ -509,9 +528,7 @@ def report_varlen(fa, w, dev, steps, warmup) -> dict:
     res = {"sequences": len(lens), "tokens": int(q.shape[0]), "H": w.H, "d": w.d, "causal": w.causal,
            "window_left": w.window_left, "window_right": w.window_right, "allowed_pairs_per_head": pairs}
     for phase, fn in fns.items():
-        for _ in range(warmup):
-            fn()
-        torch.cuda.synchronize()
+        warm_up(fn, warmup)
         a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         a.record()
         for _ in range(steps):
@@ -545,9 +562,7 @@ def report_dropout(fa, w, dev, steps, warmup) -> dict:
     }
     res = {"p": DROPOUT_P, "d": w.d}
     for phase, fn in fns.items():
-        for _ in range(warmup):
-            fn()
-        torch.cuda.synchronize()
+        warm_up(fn, warmup)
         clock = KernelClock()
         pairs = [KernelClock.new_pair() for _ in range(steps)]
         a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
@@ -580,9 +595,7 @@ def report_all(fa, dev, path, steps=10, warmup=3):
             res["kept_block_fraction"] = kept
         for phase in ("fwd", "bwd") if w.backward else ("fwd",):
             fn = r.fwd if phase == "fwd" else r.bwd
-            for _ in range(warmup):
-                fn()
-            torch.cuda.synchronize()
+            warm_up(fn, warmup)
             clock = KernelClock()
             pairs = [KernelClock.new_pair() for _ in range(steps)]
             a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
