@@ -97,3 +97,19 @@ def test_more_than_one_gpu_refused():
                        timeout=300)
     assert r.returncode == 2
     assert "one GPU" in r.stderr
+
+
+def test_warm_up_runs_the_minimum_calls_and_time(monkeypatch):
+    # at least `calls` calls and at least `min_s` seconds, with the device synchronised
+    # after each call past the minimum count (so the time counted is device time)
+    import time
+    syncs = []
+    monkeypatch.setattr(torch.cuda, "synchronize", lambda *a, **k: syncs.append(1))
+    calls = []
+    t0 = time.perf_counter()
+    bench.warm_up(lambda: calls.append(1), 5, 0.05)
+    assert len(calls) >= 5 and time.perf_counter() - t0 >= 0.05
+    assert len(syncs) >= len(calls) - 4
+    calls.clear()
+    bench.warm_up(lambda: calls.append(1), 3, 0.0)
+    assert len(calls) == 3
