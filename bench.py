@@ -17,6 +17,10 @@ query-key pairs: 4 d per pair forward, 2.5x that backward).
 Dropout (p = 0.1) on the step's workloads is timed outside the step and reported under
 "dropout", by the same FLOP convention (the generator's work is not counted).
 
+The short-sequence workloads (BERT-shaped N=512 with key padding, GPT-2-shaped N=1024
+causal) are timed outside the step as forward + backward pairs, eagerly and as a replayed
+HIP graph, under "short_n".
+
 The key/value-cache forward (a few queries against a long cache, HBM-bound) is timed
 outside the step on its decode workloads and reported under "kvcache_decode": algorithmic
 bytes = every valid cached key and value read once plus Q and O, divided by the time of the
@@ -44,6 +48,7 @@ DROPOUT_P, DROPOUT_SEED = 0.1, 1234  # the dropout report's probability and seed
 PEAK_HBM_GBS = 8000.0
 METRIC = "attention fwd+bwd TFLOP/s (bf16, causal) and % of MI355X bf16 MFMA peak"
 STEP_WORKLOADS = ("long_causal_d64", "long_causal_d128")
+SHORT_WORKLOADS = ("bert_padded", "gpt2_causal")
 # Algorithmic FLOP of each timed kernel, as a multiple of the forward FLOP.
 KERNEL_FLOP_FACTOR = {"fwd": 1.0, "bwd_dkdv": 2.0}
 CALIBRATION_BYTES = 256 << 20
@@ -580,6 +585,47 @@ def report_dropout(fa, w, dev, steps, warmup) -> dict:
     return res
 
 
+def report_graph(fa, w, dev, steps, warmup) -> dict:
+    """Forward + backward of a short-sequence workload: eager calls against the same two
+    calls captured once in a HIP graph (torch.cuda.CUDAGraph) and replayed. At these sizes
+    the kernels last tens of microseconds, so launch overheads and the gaps between
+    launches are a visible part of a call."""
+    import torch
+    r = Runner(fa, w, dev)
+
+    def step():
+        r.fwd()
+        r.bwd()
+    warm_up(step, warmup)
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        step()
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        step()
+    torch.cuda.synchronize()
+
+    def timed(fn):
+        warm_up(fn, warmup)
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record()
+        for _ in range(steps):
+            fn()
+        b.record()
+        torch.cuda.synchronize()
+        return a.elapsed_time(b) / steps
+
+    eager_ms, graph_ms = timed(step), timed(g.replay)
+    flop = 3.5 * attn_flops(w)
+    del g, r
+    return {"shape": [w.B, w.H, w.N, w.d], "causal": w.causal, "padding": w.padding,
+            "eager_ms": round(eager_ms, 4), "graph_ms": round(graph_ms, 4),
+            "eager_tflops": round(flop / eager_ms / 1e9, 1), "graph_tflops": round(flop / graph_ms / 1e9, 1)}
+
+
 def report_all(fa, dev, path, steps=10, warmup=3):
     """Per-workload fwd / bwd timing (not the metric line)."""
     import torch
@@ -728,6 +774,11 @@ def main():
         torch.cuda.empty_cache()
         # dropout on the step's workloads, outside the step
         line["dropout"] = {name: report_dropout(fa, workloads.WORKLOADS[name], dev, 10, 3) for name in STEP_WORKLOADS}
+        torch.cuda.empty_cache()
+        # the short-sequence workloads (BERT- and GPT-2-shaped), fwd + bwd, eager and as a
+        # replayed HIP graph (TFLOP/s by the step's convention, dense N^2 for key padding)
+        line["short_n"] = {name: report_graph(fa, workloads.WORKLOADS[name], dev, 50, 10)
+                           for name in SHORT_WORKLOADS}
         torch.cuda.empty_cache()
     if args.report:
         report_all(fa, dev, args.report)
