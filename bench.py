@@ -777,8 +777,15 @@ def main():
         torch.cuda.empty_cache()
         # the short-sequence workloads (BERT- and GPT-2-shaped), fwd + bwd, eager and as a
         # replayed HIP graph (TFLOP/s by the step's convention, dense N^2 for key padding)
-        line["short_n"] = {name: report_graph(fa, workloads.WORKLOADS[name], dev, 50, 10)
-                           for name in SHORT_WORKLOADS}
+        # (a failed capture is recorded, not raised: it must not cost the metric line)
+        short = {}
+        for name in SHORT_WORKLOADS:
+            try:
+                short[name] = report_graph(fa, workloads.WORKLOADS[name], dev, 50, 10)
+            except RuntimeError as e:
+                torch.cuda.synchronize()
+                short[name] = {"error": str(e)[:200]}
+        line["short_n"] = short
         torch.cuda.empty_cache()
     if args.report:
         report_all(fa, dev, args.report)
