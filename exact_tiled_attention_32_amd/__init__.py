@@ -144,6 +144,27 @@ def _dev_tensor(t: torch.Tensor, name: str, like: torch.Tensor | None = None) ->
     return t
 
 
+def _f32_out(t, name: str, shape, q: torch.Tensor) -> torch.Tensor:
+    """A caller-supplied fp32 output (lse): device tensor on q's device, given shape."""
+    if not isinstance(t, torch.Tensor) or not t.is_cuda or t.device != q.device:
+        raise ValueError(f"{name} must be a device tensor on {q.device}")
+    if tuple(t.shape) != tuple(shape) or t.dtype != torch.float32 or not t.is_contiguous():
+        raise ValueError(f"{name} must be a contiguous float32 tensor {list(shape)}")
+    return t
+
+
+def _workspace(ws, need: int, q: torch.Tensor) -> torch.Tensor:
+    """The caller's workspace, or a new one of `need` bytes: a uint8 device tensor on q's
+    device (its size is checked by the library)."""
+    if ws is None:
+        return torch.empty(max(int(need), 1), dtype=torch.uint8, device=q.device)
+    if not isinstance(ws, torch.Tensor) or not ws.is_cuda or ws.device != q.device:
+        raise ValueError(f"workspace must be a device tensor on {q.device}")
+    if ws.dtype != torch.uint8 or not ws.is_contiguous():
+        raise ValueError("workspace must be a contiguous uint8 tensor")
+    return ws
+
+
 def _ptr(t):
     return None if t is None else ctypes.c_void_p(t.data_ptr())
 
@@ -181,8 +202,8 @@ def _fwd_common(q, k, v, o, lse):
     o = torch.empty_like(q) if o is None else _dev_tensor(o, "o", q)
     if lse is None:
         lse = torch.empty((B, H, N), dtype=torch.float32, device=q.device)
-    elif lse.shape != (B, H, N) or lse.dtype != torch.float32 or not lse.is_contiguous():
-        raise ValueError("lse must be a contiguous float32 tensor [B, H, N]")
+    else:
+        _f32_out(lse, "lse", (B, H, N), q)
     return q, o, lse
 
 
@@ -225,16 +246,13 @@ def fa_bwd(q, k, v, o, dout, lse, scale: float, causal: bool = False, kv_len=Non
     for name, t in (("k", k), ("v", v), ("o", o), ("dout", dout)):
         _dev_tensor(t, name, q)
     B, H, N, d = q.shape
-    if lse.shape != (B, H, N) or lse.dtype != torch.float32 or not lse.is_contiguous():
-        raise ValueError("lse must be a contiguous float32 tensor [B, H, N]")
+    _f32_out(lse, "lse", (B, H, N), q)
     dq = torch.empty_like(q) if dq is None else _dev_tensor(dq, "dq", q)
     dk = torch.empty_like(q) if dk is None else _dev_tensor(dk, "dk", q)
     dv = torch.empty_like(q) if dv is None else _dev_tensor(dv, "dv", q)
     kv = _kv_len(kv_len, q)
     m = _mask(block_mask, q, mask_block)
-    need = fa_bwd_workspace_bytes(B, H, N, d)
-    if workspace is None:
-        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+    workspace = _workspace(workspace, fa_bwd_workspace_bytes(B, H, N, d), q)
     _check(lib.fa_bwd(_dtype_code(q), B, H, N, d, _ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(dout),
                       _ptr(lse), _ptr(dq), _ptr(dk), _ptr(dv), float(scale), int(bool(causal)), _ptr(kv),
                       _ptr(m), int(mask_block), _ptr(workspace), int(workspace.numel()),
@@ -264,12 +282,10 @@ def fa_fwd_kvcache(q, k_cache, v_cache, scale: float, causal: bool = False, kv_l
     o = torch.empty_like(q) if o is None else _dev_tensor(o, "o", q)
     if lse is None:
         lse = torch.empty((B, H, Nq), dtype=torch.float32, device=q.device)
-    elif lse.shape != (B, H, Nq) or lse.dtype != torch.float32 or not lse.is_contiguous():
-        raise ValueError("lse must be a contiguous float32 tensor [B, H, Nq]")
+    else:
+        _f32_out(lse, "lse", (B, H, Nq), q)
     kv = _kv_len(kv_len, q)
-    if workspace is None:
-        need = fa_fwd_kvcache_workspace_bytes(B, H, Nq, Nk, d)
-        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=q.device)
+    workspace = _workspace(workspace, fa_fwd_kvcache_workspace_bytes(B, H, Nq, Nk, d), q)
     _check(lib.fa_fwd_kvcache(_dtype_code(q), B, H, Nq, Nk, d, _ptr(q), _ptr(k_cache), _ptr(v_cache),
                               _ptr(o), _ptr(lse), float(scale), int(bool(causal)), _ptr(kv),
                               _ptr(workspace), int(workspace.numel()), _stream(q.device)))
@@ -303,8 +319,8 @@ def fa_fwd_varlen(q, k, v, cu_seqlens, max_seqlen: int, scale: float, causal: bo
     o = torch.empty_like(q) if o is None else _dev_tensor(o, "o", q)
     if lse is None:
         lse = torch.empty((H, total), dtype=torch.float32, device=q.device)
-    elif lse.shape != (H, total) or lse.dtype != torch.float32 or not lse.is_contiguous():
-        raise ValueError("lse must be a contiguous float32 tensor [H, total]")
+    else:
+        _f32_out(lse, "lse", (H, total), q)
     _check(lib.fa_fwd_varlen(_dtype_code(q), cu.numel() - 1, H, total, int(max_seqlen), d, _ptr(cu), _ptr(q),
                              _ptr(k), _ptr(v), _ptr(o), _ptr(lse), float(scale), int(bool(causal)),
                              int(window_left), int(window_right), _stream(q.device)))
@@ -324,14 +340,11 @@ def fa_bwd_varlen(q, k, v, o, dout, lse, cu_seqlens, max_seqlen: int, scale: flo
         _dev_tensor(t, name, q)
     cu = _cu_seqlens(cu_seqlens, q)
     total, H, d = q.shape
-    if lse.shape != (H, total) or lse.dtype != torch.float32 or not lse.is_contiguous():
-        raise ValueError("lse must be a contiguous float32 tensor [H, total]")
+    _f32_out(lse, "lse", (H, total), q)
     dq = torch.empty_like(q) if dq is None else _dev_tensor(dq, "dq", q)
     dk = torch.empty_like(q) if dk is None else _dev_tensor(dk, "dk", q)
     dv = torch.empty_like(q) if dv is None else _dev_tensor(dv, "dv", q)
-    if workspace is None:
-        workspace = torch.empty(max(fa_bwd_varlen_workspace_bytes(H, total, d), 1), dtype=torch.uint8,
-                                device=q.device)
+    workspace = _workspace(workspace, fa_bwd_varlen_workspace_bytes(H, total, d), q)
     _check(lib.fa_bwd_varlen(_dtype_code(q), cu.numel() - 1, H, total, int(max_seqlen), d, _ptr(cu), _ptr(q),
                              _ptr(k), _ptr(v), _ptr(o), _ptr(dout), _ptr(lse), _ptr(dq), _ptr(dk), _ptr(dv),
                              float(scale), int(bool(causal)), int(window_left), int(window_right),
@@ -360,14 +373,12 @@ def fa_bwd_dropout(q, k, v, o, dout, lse, scale: float, dropout_p: float, seed: 
     for name, t in (("k", k), ("v", v), ("o", o), ("dout", dout)):
         _dev_tensor(t, name, q)
     B, H, N, d = q.shape
-    if lse.shape != (B, H, N) or lse.dtype != torch.float32 or not lse.is_contiguous():
-        raise ValueError("lse must be a contiguous float32 tensor [B, H, N]")
+    _f32_out(lse, "lse", (B, H, N), q)
     dq = torch.empty_like(q) if dq is None else _dev_tensor(dq, "dq", q)
     dk = torch.empty_like(q) if dk is None else _dev_tensor(dk, "dk", q)
     dv = torch.empty_like(q) if dv is None else _dev_tensor(dv, "dv", q)
     kv = _kv_len(kv_len, q)
-    if workspace is None:
-        workspace = torch.empty(fa_bwd_workspace_bytes(B, H, N, d), dtype=torch.uint8, device=q.device)
+    workspace = _workspace(workspace, fa_bwd_workspace_bytes(B, H, N, d), q)
     _check(lib.fa_bwd_dropout(_dtype_code(q), B, H, N, d, _ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(dout),
                               _ptr(lse), _ptr(dq), _ptr(dk), _ptr(dv), float(scale), int(bool(causal)), _ptr(kv),
                               float(dropout_p), int(seed) & 0xFFFFFFFFFFFFFFFF, _ptr(workspace),

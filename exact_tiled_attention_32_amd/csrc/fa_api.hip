@@ -43,6 +43,7 @@ fa_status check_common(fa_dtype dt, int B, int H, int N, int d, float scale) {
   if (elems * 4 > (long double)(1ull << 62)) return fail(FA_ERR_INVALID, "tensor size overflows");
   const long long wgs = (long long)B * H * ((N + fa::kFwdRowsPerWG - 1) / fa::kFwdRowsPerWG);
   if (wgs > 0x7fffffffLL) return fail(FA_ERR_INVALID, "grid too large (B*H*ceil(N/128) > 2^31-1)");
+  if (N > fa::kMaxSeqLen) return fail(FA_ERR_UNSUPPORTED, "N=%d beyond the supported %d", N, fa::kMaxSeqLen);
   if (!std::isfinite(scale)) return fail(FA_ERR_INVALID, "scale must be finite");
   if (d != 16 && d != 32 && d != 64 && d != 128)
     return fail(FA_ERR_UNSUPPORTED, "head dimension %d not built (16, 32, 64, 128)", d);
@@ -141,6 +142,11 @@ fa_status fwd_impl(fa_dtype dt, int B, int H, int N, int d, const void* q, const
   return FA_OK;
 }
 
+// A window extent that reaches past every position of a sequence of at most max_seqlen
+// tokens (i - j and j - i never exceed max_seqlen - 1) allows every key: it is replaced by
+// -1 (unbounded), so the kernels never add an extent near INT_MAX to a row index.
+int clamp_window(int extent, int max_seqlen) { return extent >= max_seqlen ? -1 : extent; }
+
 // Shared validation of the packed variable-length calls.
 fa_status check_varlen(fa_dtype dt, int nseq, int H, int total, int max_seqlen, int d, float scale,
                        const int32_t* cu, int window_left, int window_right) {
@@ -151,6 +157,8 @@ fa_status check_varlen(fa_dtype dt, int nseq, int H, int total, int max_seqlen, 
   if ((long double)total * H * d * 4 > (long double)(1ull << 62)) return fail(FA_ERR_INVALID, "tensor size overflows");
   const long long wgs = (long long)nseq * H * ((max_seqlen + fa::kFwdRowsPerWG - 1) / fa::kFwdRowsPerWG);
   if (wgs > 0x7fffffffLL) return fail(FA_ERR_INVALID, "grid too large (nseq*H*ceil(max_seqlen/128) > 2^31-1)");
+  if (max_seqlen > fa::kMaxSeqLen)
+    return fail(FA_ERR_UNSUPPORTED, "max_seqlen %d beyond the supported %d", max_seqlen, fa::kMaxSeqLen);
   if (!std::isfinite(scale)) return fail(FA_ERR_INVALID, "scale must be finite");
   if (cu == nullptr) return fail(FA_ERR_INVALID, "cu_seqlens is NULL");
   if (!aligned(cu, 4)) return fail(FA_ERR_INVALID, "cu_seqlens is not 4-byte aligned");
@@ -386,8 +394,8 @@ fa_status fa_fwd_varlen(fa_dtype dt, int nseq, int H, int total, int max_seqlen,
   a.qmul = scale > 0.f ? 1.f : (scale < 0.f ? -1.f : 0.f);
   a.c2 = scale != 0.f ? sabs * 1.4426950408889634f : 1.4426950408889634f;
   a.sc_abs = sabs;
-  a.wl = window_left;
-  a.wr = causal ? 0 : window_right;
+  a.wl = clamp_window(window_left, max_seqlen);
+  a.wr = causal ? 0 : clamp_window(window_right, max_seqlen);
   a.cu = cu_seqlens;
   a.rs = H * d;
   a.total = total;
@@ -443,8 +451,8 @@ fa_status fa_bwd_varlen(fa_dtype dt, int nseq, int H, int total, int max_seqlen,
   a.causal = causal ? 1 : 0;
   a.scale = scale;
   a.c2s = scale * 1.4426950408889634f;
-  a.wl = window_left;
-  a.wr = causal ? 0 : window_right;
+  a.wl = clamp_window(window_left, max_seqlen);
+  a.wr = causal ? 0 : clamp_window(window_right, max_seqlen);
   a.cu = cu_seqlens;
   a.rs = H * d;
   a.total = total;

@@ -87,6 +87,10 @@ struct DecArgs {
 
 constexpr int kDecMaxQueries = 32;
 
+// Longest sequence the kernels take (dense N, packed max_seqlen): row indices plus a tile
+// or a window extent below it stay far from the int range.
+constexpr int kMaxSeqLen = 1 << 30;
+
 // Split of the cached keys into units: chunk keys each, units per (b, h).
 void kvcache_split_plan(int B, int H, int Nk, int d, int* chunk, int* units);
 // Waves (units) per workgroup of the key-split kernel for head dimension d.

@@ -35,6 +35,7 @@
  *   - Work is enqueued asynchronously on `stream` (NULL = the default stream). The library
  *     allocates no device memory and keeps no per-call state: calls are re-entrant and
  *     thread-safe. Faults during execution surface at the caller's stream synchronisation.
+ *   - N (and max_seqlen of the packed calls) is at most 2^30 (FA_ERR_UNSUPPORTED beyond).
  *   - bf16 (FA_BF16): d in {16, 32, 64, 128}, forward and backward. fp32 (FA_F32): d in
  *     {32, 64, 128}, forward only. The key/value-cache forward takes its own query and
  *     key counts (Nq, Nk) in place of N; its tensors follow the same layout. The packed
@@ -184,6 +185,9 @@ fa_status fa_bwd_dropout(fa_dtype dt, int B, int H, int N, int d,
  *   window_left    >= 0: key j allowed only for j >= i - window_left; -1: unbounded
  *   window_right   >= 0: key j allowed only for j <= i + window_right; -1: unbounded
  *                  (ignored when causal, which already bounds j <= i)
+ *                  An extent >= max_seqlen bounds nothing inside a sequence of at most
+ *                  max_seqlen tokens and is taken as -1 (so any int is valid, INT_MAX too).
+ *   max_seqlen beyond 2^30 is FA_ERR_UNSUPPORTED.
  * Attention never crosses a sequence boundary. A row with no allowed key yields O = 0,
  * lse = -inf and a zero dQ row. The kernels are those of fa_fwd / fa_bwd; key tiles that
  * lie wholly outside a query tile's window are not read.

@@ -321,6 +321,51 @@ def pin_library_sdpa(orc, magnitude=1.0):
             assert np.allclose(dv[b], rdv, atol=tol, rtol=1e-9), name
 
 
+def pin_restricted_backward(orc):
+    """The sampling mode of the backward (``heads=``, ``rows=``), which the large-workload
+    GPU checks rely on. Restricting the loss to rows R of the listed (b, h) is the same as
+    L = sum over those rows of O * dO, i.e. dO zeroed everywhere else; torch's SDPA with
+    autograd on that dO gives the expected dQ (rows R), dK and dV (every key: the
+    contributions of rows R alone). Everything outside the restriction must be exactly 0.
+    Masks: causal, key padding, block mask (every row keeps key block 0) and a sliding
+    window; a row chunk of 2 puts chunk boundaries inside R."""
+    B, H, N, d, mb = 2, 3, 11, 4, 4
+    bm = [[1, 0, 1], [1, 1, 0], [1, 0, 1]]
+    cases = [
+        dict(causal=True, kv_len=[9, 11], block_mask=bm, wl=-1),
+        dict(causal=False, kv_len=None, block_mask=None, wl=3),
+    ]
+    rows = np.array([0, 3, 4, 7, 10])
+    heads = [(1, 2), (0, 0), (1, 0)]
+    rng = RNG(24)
+    for c in cases:
+        q, k, v, do = (rng.standard_normal((B, H, N, d)) for _ in range(4))
+        scale = 0.6
+        dq, dk, dv = orc.attention_backward(
+            q, k, v, do, scale, causal=c["causal"], kv_len=c["kv_len"],
+            block_mask=None if c["block_mask"] is None else np.array(c["block_mask"]), mask_block=mb,
+            window_left=c["wl"], heads=heads, rows=rows, row_chunk=2)
+        for b in range(B):
+            lists = allowed_lists(N, c["causal"], None if c["kv_len"] is None else c["kv_len"][b],
+                                  c["block_mask"], mb if c["block_mask"] is not None else 1)
+            allow = dense_bool(lists, N)
+            if c["wl"] >= 0:
+                allow &= dense_bool(window_lists(N, False, c["wl"], -1), N)
+            assert allow.any(axis=1).all()
+            for h in range(H):
+                if (b, h) not in heads:
+                    assert not dq[b, h].any() and not dk[b, h].any() and not dv[b, h].any(), (b, h)
+                    continue
+                do_r = np.zeros_like(do[b, h])
+                do_r[rows] = do[b, h, rows]
+                _, rdq, rdk, rdv = _sdpa(q[b, h], k[b, h], v[b, h], do_r, scale, allow)
+                assert np.allclose(dq[b, h, rows], rdq[rows], atol=1e-12, rtol=1e-9), (b, h)
+                other = np.setdiff1d(np.arange(N), rows)
+                assert not dq[b, h, other].any(), (b, h)
+                assert np.allclose(dk[b, h], rdk, atol=1e-12, rtol=1e-9), (b, h)
+                assert np.allclose(dv[b, h], rdv, atol=1e-12, rtol=1e-9), (b, h)
+
+
 def pin_large_magnitude(orc):
     """Inputs x30 (scores in the hundreds): still finite and equal to the library routine."""
     pin_library_sdpa(orc, magnitude=30.0)
@@ -672,6 +717,7 @@ ALL_PINS = [
     pin_finite_differences,
     pin_lse_gradient,
     pin_library_sdpa,
+    pin_restricted_backward,
     pin_large_magnitude,
     pin_block_rule_medium,
     pin_kvcache_zero_query,

@@ -97,6 +97,7 @@ def bwd(lib, dt=fa.FA_BF16, N=128, d=64, ws=P, ws_bytes=None, mask=None, mb=128,
     (dict(d=8), fa.FA_ERR_UNSUPPORTED),
     (dict(dt=fa.FA_F32, d=16), fa.FA_ERR_UNSUPPORTED),
     (dict(dt=fa.FA_F32, d=80), fa.FA_ERR_UNSUPPORTED),
+    (dict(N=(1 << 30) + 128), fa.FA_ERR_UNSUPPORTED),  # beyond the longest supported sequence
 ])
 def test_fwd_rejects(lib, kwargs, status):
     assert fwd(lib, **kwargs) == status
@@ -226,6 +227,7 @@ def fvar(lib, dt=fa.FA_BF16, nseq=2, H=2, total=300, max_seqlen=200, d=64, cu=P,
     (dict(scale=float("nan")), fa.FA_ERR_INVALID),
     (dict(dt=fa.FA_F32), fa.FA_ERR_UNSUPPORTED),
     (dict(d=48), fa.FA_ERR_UNSUPPORTED),
+    (dict(max_seqlen=(1 << 30) + 1), fa.FA_ERR_UNSUPPORTED),
 ])
 def test_varlen_rejects(lib, kwargs, status):
     assert fvar(lib, **kwargs) == status

@@ -54,12 +54,13 @@ def oracle_args(case):
     return dict(causal=case["causal"], kv_len=kv, block_mask=bm, mask_block=case["mask_block"])
 
 
-def full_check(fa, case, dtype, backward=True, label=""):
+def full_check(fa, case, dtype, backward=True, label="", sparse=None):
     note(f"[parity] {label}")
-    got = gpu_run(fa, case, backward=backward)
+    got = gpu_run(fa, case, backward=backward, sparse=sparse)
     ref_o, ref_lse = oracle.attention_forward(case["q"], case["k"], case["v"], case["scale"], **oracle_args(case))
-    parity.check_o(got["o"], ref_o, dtype, f"{label} O")
-    parity.check_lse(got["lse"], ref_lse, f"{label} lse")
+    raw = parity.check_o(got["o"], ref_o, dtype, f"{label} O")
+    lse_err = parity.check_lse(got["lse"], ref_lse, f"{label} lse")
+    note(f"[parity] {label}: O max-abs {raw:.3e}, lse max-abs {lse_err:.3e}")
     if backward:
         grads = oracle.attention_backward(case["q"], case["k"], case["v"], case["do"], case["scale"],
                                           **oracle_args(case))
@@ -178,6 +179,44 @@ def test_sweep_f32_forward(gpu_lib, N, d):
     full_check(gpu_lib, case, "f32", backward=False, label=f"f32-padded-N{N}-d{d}")
 
 
+F32_SPARSE = [
+    ("f32-sparse-N129-d64", 129, 64, False, None),
+    ("f32-sparse-N640-d32-causal", 640, 32, True, None),
+    ("f32-sparse-N700-d128-padded", 700, 128, False, [700, 333]),
+    ("f32-sparse-N896-d64-mb256-causal", 896, 64, True, None),
+]
+
+
+@pytest.mark.parametrize("name,N,d,causal,kv", F32_SPARSE, ids=[c[0] for c in F32_SPARSE])
+def test_sweep_f32_blocksparse_forward(gpu_lib, name, N, d, causal, kv):
+    """The fp32 forward's key-tile list (fa_fwd_blocksparse with FA_F32), ragged N, a key block
+    no query block keeps and a query block with no kept key block (O = 0, lse = -inf)."""
+    mb = 256 if "mb256" in name else 128
+    nb = -(-N // mb)
+    B = 1 if kv is None else len(kv)
+    case = workloads.make_case(B, 2, N, d, dtype="f32", seed=zlib.crc32(name.encode()) % 10000, causal=causal,
+                               kv_len=kv, block_mask=_synthetic_mask(nb, nb + 1), mask_block=mb)
+    full_check(gpu_lib, case, "f32", backward=False, label=name)
+
+
+BF16_SPARSE_FWD = [
+    ("bf16-sparse-fwd-N1-d64", 1, 64, False),
+    ("bf16-sparse-fwd-N1000-d128-causal", 1000, 128, True),
+    ("bf16-sparse-fwd-N2049-d16", 2049, 16, False),
+]
+
+
+@pytest.mark.parametrize("name,N,d,causal", BF16_SPARSE_FWD, ids=[c[0] for c in BF16_SPARSE_FWD])
+def test_sweep_bf16_blocksparse_forward(gpu_lib, name, N, d, causal):
+    """fa_fwd_blocksparse alone (bf16): a single token, a causal ragged tail, and a sequence
+    one token past a whole number of mask blocks."""
+    mb = 128
+    nb = -(-N // mb)
+    case = workloads.make_case(1, 3, N, d, seed=zlib.crc32(name.encode()) % 10000, causal=causal,
+                               block_mask=_synthetic_mask(nb, nb + 2), mask_block=mb)
+    full_check(gpu_lib, case, "bf16", backward=False, label=name)
+
+
 @pytest.mark.parametrize("N", [300, 1000])
 def test_large_score_magnitude(gpu_lib, N):
     """Q x30: scores with a standard deviation of ~30 make the running maximum jump by
@@ -291,8 +330,9 @@ def _sampled_check(fa, w, rows, key_rows, key_sel, label):
                                      block_mask=bm, mask_block=w.mask_block)
         for h in range(H):
             ref_o[b, h], ref_l[b, h] = oracle.forward_rows(q64[b, h, rows], k64[b, h], v64[b, h], w.scale, allow)
-    parity.check_o(got["o"][:, :, rows], ref_o, "bf16", f"{label} O[sampled]")
-    parity.check_lse(got["lse"][:, :, rows], ref_l, f"{label} lse[sampled]")
+    raw = parity.check_o(got["o"][:, :, rows], ref_o, "bf16", f"{label} O[sampled]")
+    lse_err = parity.check_lse(got["lse"][:, :, rows], ref_l, f"{label} lse[sampled]")
+    note(f"[parity] {label}: O max-abs {raw:.3e}, lse max-abs {lse_err:.3e} on {rows.size} rows")
     dq, _, _ = oracle.attention_backward(q64, k64, v64, do64, w.scale, rows=rows, **args)
     parity.check_grad(got["dq"][:, :, rows], dq[:, :, rows], f"{label} dQ[sampled]")
     note(f"[parity] {label}: oracle dK/dV on {key_sel.size} keys from {key_rows.size} rows")
@@ -319,3 +359,70 @@ def test_workload_block_sparse_sampled(gpu_lib):
     key_sel = np.concatenate([np.arange(5 * mb, 6 * mb), np.arange(301 * mb, 302 * mb)])
     key_rows = np.concatenate([np.arange(4 * mb, 7 * mb), np.arange(300 * mb, 303 * mb)])
     _sampled_check(gpu_lib, w, rows, key_rows, key_sel, w.name)
+
+
+# ------------------------------------------------------------------------------------------
+# the longest accumulations at full length: key tiles that every query tile reaches
+# ------------------------------------------------------------------------------------------
+def _heavy_keys_check(fa, w, keys, label):
+    """dK, dV of `keys` in head (0, 0), from the oracle's backward over ALL query rows of that
+    head (every row that may attend to them), and dQ of the same head in full."""
+    note(f"[parity] {label}: generating inputs")
+    case = workloads.generate(w)
+    note(f"[parity] {label}: GPU forward + backward")
+    got = gpu_run(fa, case)
+    note(f"[parity] {label}: oracle backward of head (0, 0), all {w.N} rows")
+    dq, dk, dv = oracle.attention_backward(case["q"], case["k"], case["v"], case["do"], w.scale,
+                                           heads=[(0, 0)], **oracle_args(case))
+    e_k = parity.check_grad(got["dk"][0, 0, keys], dk[0, 0, keys], f"{label} dK[heavy keys]")
+    e_v = parity.check_grad(got["dv"][0, 0, keys], dv[0, 0, keys], f"{label} dV[heavy keys]")
+    e_q = parity.check_grad(got["dq"][0, 0], dq[0, 0], f"{label} dQ[head 0]")
+    e_k_all = parity.check_grad(got["dk"][0, 0], dk[0, 0], f"{label} dK[head 0]")
+    e_v_all = parity.check_grad(got["dv"][0, 0], dv[0, 0], f"{label} dV[head 0]")
+    note(f"[parity] {label}: rel-L2 heavy dK {e_k:.2e} dV {e_v:.2e}; head 0 dQ {e_q:.2e} dK {e_k_all:.2e} "
+         f"dV {e_v_all:.2e}")
+
+
+@pytest.mark.timeout(600)
+@pytest.mark.parametrize("name", ["long_causal_d64", "long_causal_d128"])
+def test_workload_long_causal_heavy_keys(gpu_lib, name):
+    """Causal N = 16384: keys 0..127 are attended by all 16384 rows, so their dK/dV workgroup
+    accumulates over every query step (at d = 128 the path with K held in registers)."""
+    w = workloads.WORKLOADS[name]
+    _heavy_keys_check(gpu_lib, w, np.arange(0, 128), name)
+
+
+@pytest.mark.timeout(900)
+def test_workload_block_sparse_global_column(gpu_lib):
+    """N = 65536 block-sparse: key block 16 (j mod 16 == 0) is kept by all 512 query blocks,
+    the longest dK/dV accumulation of the launch (the 8-wave layout's two-half reduction)."""
+    w = workloads.WORKLOADS["block_sparse_64k"]
+    mb = w.mask_block
+    _heavy_keys_check(gpu_lib, w, np.arange(16 * mb, 17 * mb), w.name)
+
+
+def test_binding_rejects_host_buffers(gpu_lib):
+    """A host (CPU) lse or workspace, or one on the wrong dtype, is refused by the binding with
+    ValueError before any call into the library, so no host pointer reaches a kernel."""
+    fa = gpu_lib
+    case = workloads.make_case(1, 2, 64, 64, seed=1, causal=True)
+    q, k, v, do = (case[n].to(DEV) for n in ("q", "k", "v", "do"))
+    lse_host = torch.empty((1, 2, 64), dtype=torch.float32)
+    with pytest.raises(ValueError):
+        fa.fa_fwd(q, k, v, case["scale"], causal=True, lse=lse_host)
+    with pytest.raises(ValueError):
+        fa.fa_fwd_blocksparse(q, k, v, case["scale"], torch.ones((1, 1), dtype=torch.uint8, device=DEV),
+                              lse=lse_host)
+    o, lse = fa.fa_fwd(q, k, v, case["scale"], causal=True)
+    with pytest.raises(ValueError):
+        fa.fa_bwd(q, k, v, o, do, lse_host, case["scale"], causal=True)
+    need = fa.fa_bwd_workspace_bytes(1, 2, 64, 64)
+    for bad in (torch.empty(need, dtype=torch.uint8),                       # host memory
+                torch.empty(need // 4, dtype=torch.float32, device=DEV)):   # wrong dtype
+        with pytest.raises(ValueError):
+            fa.fa_bwd(q, k, v, o, do, lse, case["scale"], causal=True, workspace=bad)
+        with pytest.raises(ValueError):
+            fa.fa_bwd_dropout(q, k, v, o, do, lse, case["scale"], 0.1, 7, causal=True, workspace=bad)
+    with pytest.raises(ValueError):
+        fa.fa_fwd_kvcache(q, k, v, case["scale"], workspace=torch.empty(1 << 20, dtype=torch.uint8))
+    torch.cuda.synchronize()

@@ -94,6 +94,31 @@ def test_max_seqlen_above_longest(gpu_lib):
     full_check(gpu_lib, case, "max_seqlen_700")
 
 
+INT_MAX = 2**31 - 1
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_window_extent_int_max(gpu_lib, causal):
+    """Window extents of 2^31 - 1 (far beyond any sequence) are the same as unbounded: the
+    result must match the oracle without a window, with no overflow in the tile ranges."""
+    lengths = [1, 130, 257]
+    case = workloads.make_varlen_case(lengths, 2, 64, seed=31 + causal, causal=causal,
+                                      window_left=INT_MAX, window_right=INT_MAX)
+    note(f"[varlen] window INT_MAX causal={causal}")
+    got = gpu_varlen(gpu_lib, case)
+    cu = case["cu_seqlens"].tolist()
+    ref_o, ref_lse = oracle.varlen_forward(case["q"], case["k"], case["v"], cu, case["scale"], causal=causal)
+    parity.check_o(got["o"], ref_o, "bf16", "INT_MAX window O")
+    parity.check_lse(got["lse"], ref_lse, "INT_MAX window lse")
+    grads = oracle.varlen_backward(case["q"], case["k"], case["v"], case["do"], cu, case["scale"], causal=causal)
+    check_grads(got, grads, "INT_MAX window")
+    # and bitwise the same as the call with unbounded extents
+    unb = dict(case, window_left=-1, window_right=-1)
+    ref = gpu_varlen(gpu_lib, unb)
+    for n in got:
+        assert torch.equal(got[n], ref[n]), n
+
+
 def test_no_tokens(gpu_lib):
     fa = gpu_lib
     q = torch.zeros((0, 2, 64), dtype=torch.bfloat16, device=DEV)

@@ -78,6 +78,12 @@ MUTANTS = {
     "fwd_dropout_ignored": ("p = p * drop[:, cols]", "p = p * 1.0"),
     "bwd_dropout_dv_unmasked": ("dv[b, h, cols] += (p * mm).T @ dor", "dv[b, h, cols] += p.T @ dor"),
     "bwd_dropout_dp_unmasked": ("dp = (dor @ vc.T) * mm", "dp = (dor @ vc.T)"),
+    "bwd_rows_ignored": ("all_rows = np.arange(N) if rows is None else np.asarray(rows, dtype=np.int64)",
+                         "all_rows = np.arange(N)"),
+    "bwd_heads_truncated": ("for b in range(B) for h in range(H)] if heads is None else list(heads)",
+                            "for b in range(B) for h in range(H)] if heads is None else list(heads)[:1]"),
+    "bwd_last_row_chunk_dropped": ("for r0 in range(0, all_rows.size, row_chunk):",
+                                   "for r0 in range(0, all_rows.size - 1, row_chunk):"),
     "varlen_bwd_dk_dv_swapped": ("for dst, src in zip((dq, dk, dv), g):", "for dst, src in zip((dq, dv, dk), g):"),
 }
 
