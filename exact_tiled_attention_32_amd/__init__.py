@@ -23,6 +23,8 @@ Entry points (same names as the C ABI):
     fa_fwd_kvcache_workspace_bytes(B, H, Nq, Nk, d) -> int
     fa_fwd_kvcache(q, k_cache, v_cache, scale, causal=False, kv_len=None, o=None, lse=None,
                    workspace=None) -> (o, lse)
+    fa_fwd_kvcache_noalloc(q, k_cache, v_cache, scale, o, lse, causal=False, kv_len=None)
+        -> (o, lse)   (partial results in the library's static scratch; o, lse required)
     fa_bwd_workspace_bytes(B, H, N, d) -> int
     fa_bwd(q, k, v, o, dout, lse, scale, causal=False, kv_len=None, block_mask=None,
            mask_block=128, dq=None, dk=None, dv=None, workspace=None) -> (dq, dk, dv)
@@ -38,19 +40,20 @@ import torch
 __all__ = [
     "FA_F32", "FA_BF16", "FA_OK", "FA_ERR_INVALID", "FA_ERR_UNSUPPORTED", "FA_ERR_HIP",
     "FAError", "lib_path", "load", "fa_fwd", "fa_fwd_blocksparse", "fa_bwd",
-    "fa_bwd_workspace_bytes", "fa_fwd_dropout", "fa_bwd_dropout", "fa_fwd_varlen", "fa_bwd_varlen", "fa_bwd_varlen_workspace_bytes", "fa_fwd_kvcache", "fa_fwd_kvcache_workspace_bytes", "fa_time_next_kernel", "fa_status_string", "EXPORTED_SYMBOLS",
+    "fa_bwd_workspace_bytes", "fa_fwd_dropout", "fa_bwd_dropout", "fa_fwd_varlen", "fa_bwd_varlen", "fa_bwd_varlen_workspace_bytes", "fa_fwd_kvcache", "fa_fwd_kvcache_workspace_bytes", "fa_fwd_kvcache_noalloc", "NOALLOC_SCRATCH_BYTES", "fa_time_next_kernel", "fa_status_string", "EXPORTED_SYMBOLS",
 ]
 
 FA_F32, FA_BF16 = 0, 1
 FA_OK, FA_ERR_INVALID, FA_ERR_UNSUPPORTED, FA_ERR_HIP = 0, 1, 2, 3
 
 EXPORTED_SYMBOLS = ("fa_fwd", "fa_fwd_blocksparse", "fa_bwd_workspace_bytes", "fa_bwd",
-                    "fa_fwd_kvcache_workspace_bytes", "fa_fwd_kvcache",
+                    "fa_fwd_kvcache_workspace_bytes", "fa_fwd_kvcache", "fa_fwd_kvcache_noalloc",
                     "fa_fwd_varlen", "fa_bwd_varlen_workspace_bytes", "fa_bwd_varlen",
                     "fa_fwd_dropout", "fa_bwd_dropout",
                     "fa_time_next_kernel", "fa_status_string", "fa_last_error")
 
 _LIB = None
+NOALLOC_SCRATCH_BYTES = 64 << 20  # FA_NOALLOC_SCRATCH_BYTES of include/fa.h
 
 
 class FAError(RuntimeError):
@@ -96,6 +99,8 @@ def load() -> ctypes.CDLL:
     lib.fa_fwd_kvcache_workspace_bytes.restype = S
     lib.fa_fwd_kvcache.argtypes = [I, I, I, I, I, I, P, P, P, P, P, F, I, P, P, S, P]
     lib.fa_fwd_kvcache.restype = I
+    lib.fa_fwd_kvcache_noalloc.argtypes = [I, I, I, I, I, I, P, P, P, P, P, F, I, P, P]
+    lib.fa_fwd_kvcache_noalloc.restype = I
     lib.fa_status_string.argtypes = [I]
     lib.fa_status_string.restype = ctypes.c_char_p
     lib.fa_time_next_kernel.argtypes = [P, P]
@@ -289,6 +294,32 @@ def fa_fwd_kvcache(q, k_cache, v_cache, scale: float, causal: bool = False, kv_l
     _check(lib.fa_fwd_kvcache(_dtype_code(q), B, H, Nq, Nk, d, _ptr(q), _ptr(k_cache), _ptr(v_cache),
                               _ptr(o), _ptr(lse), float(scale), int(bool(causal)), _ptr(kv),
                               _ptr(workspace), int(workspace.numel()), _stream(q.device)))
+    return o, lse
+
+
+def fa_fwd_kvcache_noalloc(q, k_cache, v_cache, scale: float, o, lse, causal: bool = False, kv_len=None):
+    """The cache forward without a workspace: its partial results live in the library's
+    static device scratch (see ``fa_fwd_kvcache_noalloc`` in include/fa.h). The outputs o
+    [B, H, Nq, d] and lse [B, H, Nq] are the caller's; nothing is allocated here either."""
+    lib = load()
+    q = _dev_tensor(q, "q")
+    if q.dim() != 4:
+        raise ValueError("q must be [B, H, Nq, d]")
+    k_cache = _dev_tensor(k_cache, "k_cache")
+    _dev_tensor(v_cache, "v_cache", k_cache)
+    B, H, Nq, d = q.shape
+    Nk = k_cache.shape[2]
+    if (k_cache.dim() != 4 or k_cache.shape[0] != B or k_cache.shape[1] != H or k_cache.shape[3] != d
+            or k_cache.dtype != q.dtype or k_cache.device != q.device):
+        raise ValueError("k_cache and v_cache must be [B, H, Nk, d] of q's dtype and device")
+    if o is None or lse is None:
+        raise ValueError("o and lse are required (this call allocates nothing)")
+    _dev_tensor(o, "o", q)
+    _f32_out(lse, "lse", (B, H, Nq), q)
+    kv = _kv_len(kv_len, q)
+    _check(lib.fa_fwd_kvcache_noalloc(_dtype_code(q), B, H, Nq, Nk, d, _ptr(q), _ptr(k_cache), _ptr(v_cache),
+                                      _ptr(o), _ptr(lse), float(scale), int(bool(causal)), _ptr(kv),
+                                      _stream(q.device)))
     return o, lse
 
 

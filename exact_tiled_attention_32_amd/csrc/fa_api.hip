@@ -6,6 +6,7 @@
 #include <cstdarg>
 #include <cstdio>
 #include <cstring>
+#include <mutex>
 
 #include "fa.h"
 #include "fa_launch.h"
@@ -313,10 +314,51 @@ size_t fa_fwd_kvcache_workspace_bytes(int B, int H, int Nq, int Nk, int d) {
   return kvcache_ws(B, H, Nq, Nk, d, nullptr, nullptr);
 }
 
-fa_status fa_fwd_kvcache(fa_dtype dt, int B, int H, int Nq, int Nk, int d, const void* q,
-                         const void* k_cache, const void* v_cache, void* o, float* lse,
-                         float scale, int causal, const int32_t* kv_len, void* workspace,
-                         size_t workspace_bytes, hipStream_t stream) {
+}  // extern "C"
+
+namespace {
+
+// Device scratch of fa_fwd_kvcache_noalloc: the key split's partial results live here
+// instead of in a caller workspace. Each device that runs the call holds its own copy
+// until the process ends. In host code `scratch` only names the symbol; the device
+// address comes from hipGetSymbolAddress, looked up once per device (scratch_ptr).
+constexpr size_t kNoAllocScratchBytes = FA_NOALLOC_SCRATCH_BYTES;
+__device__ __align__(256) char scratch[kNoAllocScratchBytes];
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+// The current device's copy of `scratch` (nullptr with *status set on failure).
+void* scratch_ptr(fa_status* status) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) {
+    *status = fail(FA_ERR_HIP, "hipGetDevice failed: %s", hipGetErrorString(e));
+    return nullptr;
+  }
+  if (dev < 0 || dev >= kMaxDevices) {
+    *status = fail(FA_ERR_UNSUPPORTED, "device %d beyond the %d devices the scratch table covers", dev, kMaxDevices);
+    return nullptr;
+  }
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (g_scratch_ptr[dev] == nullptr) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess || p == nullptr) {
+      *status = fail(FA_ERR_HIP, "hipGetSymbolAddress(scratch) failed on device %d: %s", dev, hipGetErrorString(e));
+      return nullptr;
+    }
+    g_scratch_ptr[dev] = p;
+  }
+  return g_scratch_ptr[dev];
+}
+
+// Shared body of the two cache-forward calls. With use_scratch the partial results go to
+// the current device's static scratch (workspace and workspace_bytes are ignored).
+fa_status kvcache_impl(fa_dtype dt, int B, int H, int Nq, int Nk, int d, const void* q, const void* k_cache,
+                       const void* v_cache, void* o, float* lse, float scale, int causal, const int32_t* kv_len,
+                       void* workspace, size_t workspace_bytes, bool use_scratch, hipStream_t stream) {
   if (dt != FA_F32 && dt != FA_BF16) return fail(FA_ERR_INVALID, "unknown dtype %d", (int)dt);
   if (B <= 0 || H <= 0 || Nq <= 0 || Nk <= 0 || d <= 0)
     return fail(FA_ERR_INVALID, "sizes must be positive (B=%d H=%d Nq=%d Nk=%d d=%d)", B, H, Nq, Nk, d);
@@ -335,15 +377,26 @@ fa_status fa_fwd_kvcache(fa_dtype dt, int B, int H, int Nq, int Nk, int d, const
   FA_TRY(check_tensor(o, "o", 16));
   FA_TRY(check_tensor(lse, "lse", 4));
   if (kv_len && !aligned(kv_len, 4)) return fail(FA_ERR_INVALID, "kv_len is not 4-byte aligned");
-  if (workspace == nullptr) return fail(FA_ERR_INVALID, "workspace is NULL");
-  if (!aligned(workspace, 256)) return fail(FA_ERR_INVALID, "workspace is not 256-byte aligned");
-  if (workspace_bytes < need)
-    return fail(FA_ERR_INVALID, "workspace too small: %zu bytes given, %zu needed", workspace_bytes, need);
+  if (use_scratch) {
+    if (need > kNoAllocScratchBytes)
+      return fail(FA_ERR_UNSUPPORTED, "partial results need %zu bytes, beyond the %zu-byte static scratch", need,
+                  kNoAllocScratchBytes);
+  } else {
+    if (workspace == nullptr) return fail(FA_ERR_INVALID, "workspace is NULL");
+    if (!aligned(workspace, 256)) return fail(FA_ERR_INVALID, "workspace is not 256-byte aligned");
+    if (workspace_bytes < need)
+      return fail(FA_ERR_INVALID, "workspace too small: %zu bytes given, %zu needed", workspace_bytes, need);
+  }
 
   fa::DecArgs a{};
   fa::kvcache_split_plan(B, H, Nk, d, &a.chunk, &a.units);
   if ((long long)a.units / fa::kvcache_split_waves(d) * B * H > 0x7fffffffLL || (long long)B * H * Nq > 0x7fffffffLL)
     return fail(FA_ERR_INVALID, "grid too large (B*H*units/waves or B*H*Nq > 2^31-1)");
+  if (use_scratch) {
+    fa_status st = FA_OK;
+    workspace = scratch_ptr(&st);
+    if (workspace == nullptr) return st;
+  }
   a.q = q;
   a.k = k_cache;
   a.v = v_cache;
@@ -366,6 +419,25 @@ fa_status fa_fwd_kvcache(fa_dtype dt, int B, int H, int Nq, int Nk, int d, const
   hipError_t e = fa::launch_kvcache(a, d, stream, take_timer());
   if (e != hipSuccess) return fail(FA_ERR_HIP, "key/value-cache forward launch failed: %s", hipGetErrorString(e));
   return FA_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+fa_status fa_fwd_kvcache(fa_dtype dt, int B, int H, int Nq, int Nk, int d, const void* q,
+                         const void* k_cache, const void* v_cache, void* o, float* lse,
+                         float scale, int causal, const int32_t* kv_len, void* workspace,
+                         size_t workspace_bytes, hipStream_t stream) {
+  return kvcache_impl(dt, B, H, Nq, Nk, d, q, k_cache, v_cache, o, lse, scale, causal, kv_len, workspace,
+                      workspace_bytes, false, stream);
+}
+
+fa_status fa_fwd_kvcache_noalloc(fa_dtype dt, int B, int H, int Nq, int Nk, int d, const void* q,
+                                 const void* k_cache, const void* v_cache, void* o, float* lse, float scale,
+                                 int causal, const int32_t* kv_len, hipStream_t stream) {
+  return kvcache_impl(dt, B, H, Nq, Nk, d, q, k_cache, v_cache, o, lse, scale, causal, kv_len, nullptr, 0, true,
+                      stream);
 }
 
 fa_status fa_fwd_varlen(fa_dtype dt, int nseq, int H, int total, int max_seqlen, int d,

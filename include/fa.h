@@ -256,6 +256,30 @@ fa_status fa_fwd_kvcache(fa_dtype dt, int B, int H, int Nq, int Nk, int d,
                          hipStream_t stream);
 
 /*
+ * The cache forward for callers that cannot allocate device memory: code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc. Same arguments, semantics
+ * and kernels as fa_fwd_kvcache, without the workspace: the key split's partial results go
+ * to a static device array of FA_NOALLOC_SCRATCH_BYTES bytes that the library defines.
+ *   - Allocates nothing: no hipMalloc, hipFree or allocating library routine. Each device
+ *     the call runs on holds its own copy of the array, from the first call on that device
+ *     (which looks up its address once) until the process ends.
+ *   - A call whose partial results would need more than FA_NOALLOC_SCRATCH_BYTES bytes
+ *     (fa_fwd_kvcache_workspace_bytes(B,H,Nq,Nk,d)) returns FA_ERR_UNSUPPORTED and launches
+ *     nothing.
+ *   - Every call on one device shares that device's array, which keeps the last call's
+ *     contents (every slot a call reads is written by the same call first, so nothing needs
+ *     clearing). Calls that overlap on one device (different streams or threads, without
+ *     ordering between them) race on the array and must not be issued.
+ */
+#define FA_NOALLOC_SCRATCH_BYTES ((size_t)64 << 20)
+
+fa_status fa_fwd_kvcache_noalloc(fa_dtype dt, int B, int H, int Nq, int Nk, int d,
+                                 const void* q, const void* k_cache, const void* v_cache,
+                                 void* o, float* lse,
+                                 float scale, int causal, const int32_t* kv_len,
+                                 hipStream_t stream);
+
+/*
  * Measurement hook. When both events are non-NULL, the next fa_fwd, fa_fwd_blocksparse,
  * fa_fwd_dropout, fa_fwd_varlen, fa_fwd_kvcache, fa_bwd, fa_bwd_dropout or fa_bwd_varlen
  * call on the calling thread that passes validation records `start` on its stream immediately before launching its

@@ -276,3 +276,23 @@ def test_dropout_bwd_rejects(lib):
                                             None)
     assert call(1.5, P) == fa.FA_ERR_INVALID
     assert call(0.2, None) == fa.FA_ERR_INVALID
+
+
+def kvc_noalloc(lib, dt=fa.FA_BF16, B=1, H=1, Nq=1, Nk=256, d=64, q=P, o=P, lse=P, scale=0.125):
+    c = ctypes.c_void_p
+    return lib.fa_fwd_kvcache_noalloc(dt, B, H, Nq, Nk, d, c(q), c(P), c(P), c(o), c(lse), scale, 1, None, None)
+
+
+@pytest.mark.parametrize("kwargs, status", [
+    (dict(q=0), fa.FA_ERR_INVALID),
+    (dict(lse=P + 2), fa.FA_ERR_INVALID),
+    (dict(Nq=0), fa.FA_ERR_INVALID),
+    (dict(scale=float("nan")), fa.FA_ERR_INVALID),
+    (dict(d=96), fa.FA_ERR_UNSUPPORTED),
+    (dict(Nq=33), fa.FA_ERR_UNSUPPORTED),
+    # partial results beyond the static scratch (204 MB for 12288 units x 32 queries x d=128)
+    (dict(B=64, H=64, Nq=32, Nk=32, d=128), fa.FA_ERR_UNSUPPORTED),
+])
+def test_kvcache_noalloc_rejects(lib, kwargs, status):
+    assert kvc_noalloc(lib, **kwargs) == status
+    assert lib.fa_last_error().decode()
