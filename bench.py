@@ -2,8 +2,10 @@
 
 A step is one pass of the whole hot path over the long-sequence causal workload
 (B=1, H=16, N=16384, bf16, causal, at d=64 and at d=128): for each head dimension
-the forward (O, lse) and the backward (D pre-pass, dK/dV kernel, dQ kernel) through
-the C ABI, on inputs already resident in device memory.
+the forward (O, lse) and the backward (the dQ kernel, whose prologue is the D =
+rowsum(dO o O) pre-pass, then the dK/dV kernel) through the C ABI, on inputs already
+resident in device memory. The library's per-kernel events (fa_time_next_call) give
+each kernel's time inside the timed region.
 
 FLOP convention: forward 4*B*H*N^2*d, halved for causal; backward 2.5x the forward
 (five products per score tile instead of two). value = FLOP per step / time per step.
@@ -25,6 +27,12 @@ The key/value-cache forward (a few queries against a long cache, HBM-bound) is t
 outside the step on its decode workloads and reported under "kvcache_decode": algorithmic
 bytes = every valid cached key and value read once plus Q and O, divided by the time of the
 whole call (key-split kernel and merge).
+
+Every named workload (single-head fp32, BERT-shaped with key padding, GPT-2-shaped causal,
+the long causal pair, block-sparse 64K) is also reported under "configs", forward and
+backward separately: ms, TFLOP/s and fraction of peak by the headline convention (plus the
+allowed-pair convention for key padding; kept blocks for the block mask) and HBM GB/s of
+the compulsory bytes. "clock" samples the engine clock (rocm-smi) while the step runs.
 
 Prints ONE JSON line (the metric line). `--report FILE` additionally times every
 workload (forward and backward separately) and writes a per-workload JSON;
@@ -49,8 +57,12 @@ PEAK_HBM_GBS = 8000.0
 METRIC = "attention fwd+bwd TFLOP/s (bf16, causal) and % of MI355X bf16 MFMA peak"
 STEP_WORKLOADS = ("long_causal_d64", "long_causal_d128")
 SHORT_WORKLOADS = ("bert_padded", "gpt2_causal")
-# Algorithmic FLOP of each timed kernel, as a multiple of the forward FLOP.
-KERNEL_FLOP_FACTOR = {"fwd": 1.0, "bwd_dkdv": 2.0}
+# Algorithmic FLOP of each timed kernel, as a multiple of the forward FLOP: the forward's two
+# products; four of the backward's five (dV, dP, dK and the recomputed S count as S, dP, dV,
+# dK of the convention) in the dK/dV kernel; the fifth (dQ) in the dQ kernel, which also
+# recomputes S and dP (executed: 1.5x) without the convention counting them.
+KERNEL_FLOP_FACTOR = {"fwd": 1.0, "bwd_dkdv": 2.0, "bwd_dq": 0.5}
+KERNEL_EXECUTED_FACTOR = {"fwd": 1.0, "bwd_dkdv": 2.0, "bwd_dq": 1.5}
 CALIBRATION_BYTES = 256 << 20
 
 
@@ -105,6 +117,11 @@ class Runner:
         if self.mask is not None:
             self.kept = float(x["block_mask"].double().mean())
 
+    @property
+    def bwd_kernels(self):
+        """The backward call's kernels in launch order (the timer's event order)."""
+        return (["bwd_order"] if self.mask is not None else []) + ["bwd_dq", "bwd_dkdv"]
+
     def fwd(self):
         if self.mask is not None:
             self.fa.fa_fwd_blocksparse(self.q, self.k, self.v, self.scale, self.mask, self.w.mask_block,
@@ -118,32 +135,37 @@ class Runner:
 
 
 class KernelClock:
-    """HIP events recorded by the library around the dominant kernel of each call."""
+    """HIP events recorded by the library before a call's first kernel and after each of
+    its kernels (fa_time_next_call), on the call's own stream."""
 
     def __init__(self):
-        self.pairs = {}
+        self.samples = {}
 
     @staticmethod
-    def new_pair():
+    def new_events(n):
         import torch
-        s, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        evs = [torch.cuda.Event(enable_timing=True) for _ in range(n)]
         # torch creates the HIP event at its first record; the library then re-records it
-        # around the kernel launch on the same stream
-        s.record()
-        e.record()
-        return s, e
+        # around the kernel launches on the same stream
+        for e in evs:
+            e.record()
+        return evs
 
-    def arm(self, fa, name, pair=None):
-        """Has the library time the dominant kernel of its next call. `pair` is an event pair
-        made beforehand by new_pair(), so that no extra event is recorded on the stream in a
-        timed region; without one a pair is made here."""
-        s, e = pair if pair is not None else self.new_pair()
-        self.pairs.setdefault(name, []).append((s, e))
-        fa.fa_time_next_kernel(s, e)
+    def arm(self, fa, name, events):
+        """Has the library time the kernels of its next call with `events` (made beforehand
+        by new_events, so that no event is created inside a timed region)."""
+        self.samples.setdefault(name, []).append(events)
+        fa.fa_time_next_call(events)
 
-    def mean_ms(self, name):
-        ps = self.pairs.get(name, [])
-        return sum(s.elapsed_time(e) for s, e in ps) / len(ps) if ps else float("nan")
+    def kernel_ms(self, name, i):
+        """Mean duration of the i-th kernel of the calls armed under `name`."""
+        ev = self.samples.get(name, [])
+        return sum(e[i].elapsed_time(e[i + 1]) for e in ev) / len(ev) if ev else float("nan")
+
+    def call_ms(self, name):
+        """Mean time from before the first to after the last bracketed kernel."""
+        ev = self.samples.get(name, [])
+        return sum(e[0].elapsed_time(e[-1]) for e in ev) / len(ev) if ev else float("nan")
 
 
 KERNEL_NAMES = {  # demangled kernel -> short name used by the bench and the traffic file
@@ -152,7 +174,6 @@ KERNEL_NAMES = {  # demangled kernel -> short name used by the bench and the tra
     "fwd_bf16_kernel<64, false, 64>": "fwd_d64", "fwd_bf16_kernel<128, false, 128>": "fwd_d128",
     "bwd_dkdv_kernel<64, false, 64, 1>": "bwd_dkdv_d64", "bwd_dkdv_kernel<128, false, 128, 1>": "bwd_dkdv_d128",
     "bwd_dq_kernel<64, false, 64>": "bwd_dq_d64", "bwd_dq_kernel<128, false, 128>": "bwd_dq_d128",
-    "bwd_pre_kernel<64>": "bwd_pre_d64", "bwd_pre_kernel<128>": "bwd_pre_d128",
     "kvc_split_kernel<64>": "kvc_split_d64", "kvc_split_kernel<128>": "kvc_split_d128",
     "kvc_merge_kernel<64>": "kvc_merge_d64", "kvc_merge_kernel<128>": "kvc_merge_d128",
 }
@@ -214,6 +235,7 @@ def summarize_pmc(fetch_csv: str, write_csv: str, out_path: str) -> dict:
 COUNTER_SETS = {  # one rocprofv3 --pmc pass each (at most 8 SQ, 4 TCC and 2 GRBM counters)
     "sq": "SQ_BUSY_CU_CYCLES SQ_VALU_MFMA_BUSY_CYCLES SQ_INSTS_MFMA SQ_INSTS_LDS SQ_LDS_BANK_CONFLICT "
           "SQ_LDS_IDX_ACTIVE SQ_WAVE_CYCLES GRBM_GUI_ACTIVE",
+    "valu": "SQ_BUSY_CU_CYCLES SQ_ACTIVE_INST_VALU SQ_INSTS_VALU SQ_INSTS_MFMA SQ_INSTS_SALU SQ_ACTIVE_INST_LDS",
     "fetch": "FETCH_SIZE",
     "write": "WRITE_SIZE",
 }
@@ -226,17 +248,16 @@ def counter_sequence(workloads):
         for name, w in workloads.WORKLOADS.items():
             seq.append((name, "fwd_f32_kernel<64>" if w.dtype == "f32" else f"fwd_bf16_kernel<{w.d}>"))
             if w.backward:
-                seq.append((name, f"bwd_pre_kernel<{w.d}>"))
                 if w.sparse:
                     seq.append((name, "bwd_order_kernel"))
-                seq += [(name, f"bwd_dkdv_kernel<{w.d}>"), (name, f"bwd_dq_kernel<{w.d}>")]
+                seq += [(name, f"bwd_dq_kernel<{w.d}>"), (name, f"bwd_dkdv_kernel<{w.d}>")]
         for name, w in workloads.VARLEN_WORKLOADS.items():
-            seq += [(name, f"fwd_bf16_kernel<{w.d}>"), (name, f"bwd_pre_kernel<{w.d}>"),
-                    (name, f"bwd_dkdv_kernel<{w.d}>"), (name, f"bwd_dq_kernel<{w.d}>")]
+            seq += [(name, f"fwd_bf16_kernel<{w.d}>"), (name, f"bwd_dq_kernel<{w.d}>"),
+                    (name, f"bwd_dkdv_kernel<{w.d}>")]
         for name in STEP_WORKLOADS:
             d = workloads.WORKLOADS[name].d
-            seq += [(name + "_dropout", f"fwd_bf16_kernel<{d}>"), (name + "_dropout", f"bwd_pre_kernel<{d}>"),
-                    (name + "_dropout", f"bwd_dkdv_kernel<{d}>"), (name + "_dropout", f"bwd_dq_kernel<{d}>")]
+            seq += [(name + "_dropout", f"fwd_bf16_kernel<{d}>"), (name + "_dropout", f"bwd_dq_kernel<{d}>"),
+                    (name + "_dropout", f"bwd_dkdv_kernel<{d}>")]
         for name, w in workloads.DECODE_WORKLOADS.items():
             seq += [(name, f"kvc_split_kernel<{w.d}>"), (name, f"kvc_merge_kernel<{w.d}>")]
     return seq
@@ -289,10 +310,11 @@ def counter_pass(fa, dev):
     print("counter pass done", flush=True)
 
 
-def summarize_counters(sq_csv, fetch_csv, write_csv, trace_csv) -> str:
+def summarize_counters(sq_csv, fetch_csv, write_csv, trace_csv, valu_csv=None) -> str:
     """Markdown table per (workload, kernel) of the second round of `--counter-pass`:
     duration (kernel trace), HBM bytes and GB/s (FETCH_SIZE, WRITE_SIZE scaled by the
-    calibration copy), MFMA busy and LDS bank conflicts (SQ counters)."""
+    calibration copy), MFMA busy and LDS bank conflicts (SQ counters), and with a VALU
+    counter file the VALU-active cycles and VALU instructions per MFMA."""
     import csv
     from exact_tiled_attention_32_amd import workloads
 
@@ -316,6 +338,7 @@ def summarize_counters(sq_csv, fetch_csv, write_csv, trace_csv) -> str:
         return CALIBRATION_BYTES / (c[-1][counter] * 1024.0)
 
     sq, fe, wr = load(sq_csv), load(fetch_csv), load(write_csv)
+    va = load(valu_csv) if valu_csv else None
     ff, fw = calib(fe, "FETCH_SIZE"), calib(wr, "WRITE_SIZE")
     trace = []
     for row in csv.DictReader(open(trace_csv)):
@@ -326,12 +349,17 @@ def summarize_counters(sq_csv, fetch_csv, write_csv, trace_csv) -> str:
     seq = counter_sequence(workloads)
     strip = lambda rows: [r for r in rows if "copyBuffer" not in r["name"]]
     sq, fe, wr = strip(sq), strip(fe), strip(wr)
-    for what, rows in (("sq", sq), ("fetch", fe), ("write", wr), ("trace", trace)):
+    checks = [("sq", sq), ("fetch", fe), ("write", wr), ("trace", trace)]
+    if va is not None:
+        va = strip(va)
+        checks.append(("valu", va))
+    for what, rows in checks:
         if len(rows) != len(seq):
             raise RuntimeError(f"{what}: {len(rows)} library dispatches, expected {len(seq)}")
     half = len(seq) // 2
-    lines = ["| workload | kernel | µs | FETCH MB | WRITE MB | HBM GB/s | MFMA busy | LDS bank-conflict cycles "
-             "/ LDS active cycles | MFMA insts | LDS insts | active MHz |", "|---|---|---|---|---|---|---|---|---|---|---|"]
+    lines = ["| workload | kernel | µs | FETCH MB | WRITE MB | HBM GB/s | MFMA busy | VALU busy | VALU insts / MFMA "
+             "| LDS bank-conflict cycles / LDS active cycles | MFMA insts | LDS insts |",
+             "|---|---|---|---|---|---|---|---|---|---|---|---|"]
     for i in range(half, len(seq)):
         wname, kname = seq[i]
         name = trace[i][1]
@@ -346,10 +374,17 @@ def summarize_counters(sq_csv, fetch_csv, write_csv, trace_csv) -> str:
         # over the 8 XCDs, per microsecond of the kernel.
         mfma = c["SQ_VALU_MFMA_BUSY_CYCLES"] / max(4.0 * c["SQ_BUSY_CU_CYCLES"], 1.0)
         bank = c["SQ_LDS_BANK_CONFLICT"] / max(c["SQ_LDS_IDX_ACTIVE"], 1.0)
+        if va is not None:
+            v = va[i]
+            # SQ_ACTIVE_INST_VALU: cycles in which the SQ had a VALU instruction of a wave in
+            # issue (MFMA issue included), summed like SQ_BUSY_CU_CYCLES over the CUs; per SIMD
+            valu = f"{100 * v['SQ_ACTIVE_INST_VALU'] / max(4.0 * v['SQ_BUSY_CU_CYCLES'], 1.0):.1f} %"
+            vpm = f"{v['SQ_INSTS_VALU'] / max(v['SQ_INSTS_MFMA'], 1.0):.2f}"
+        else:
+            valu = vpm = "—"
         lines.append(f"| {wname} | {kname} | {us:.1f} | {fb / 1e6:.1f} | {wb / 1e6:.1f} | "
-                     f"{(fb + wb) / us / 1e3:.0f} | {100 * mfma:.1f} % | {100 * bank:.2f} % | "
-                     f"{c['SQ_INSTS_MFMA']:.3g} | {c['SQ_INSTS_LDS']:.3g} | "
-                     f"{c['GRBM_GUI_ACTIVE'] / 8 / us:.0f} |")
+                     f"{(fb + wb) / us / 1e3:.0f} | {100 * mfma:.1f} % | {valu} | {vpm} | {100 * bank:.2f} % | "
+                     f"{c['SQ_INSTS_MFMA']:.3g} | {c['SQ_INSTS_LDS']:.3g} |")
     return "\n".join(lines)
 
 
@@ -381,17 +416,98 @@ def load_traffic(kernel: str):
     return entry.get("bytes_per_launch")
 
 
-def cpu_baseline(target_s: float = 15.0) -> dict:
-    """The fp64 oracle on a bounded sample of the step's workload: head (0, 0), the last R
-    query rows (full causal prefix), forward + backward, for d = 64 and d = 128."""
+def cpu_info() -> dict:
+    """The host the oracle runs on: CPU model, core counts, BLAS library and NumPy version."""
+    import platform
+
+    import numpy as np
+    model = platform.processor() or "unknown"
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    try:
+        affinity = len(os.sched_getaffinity(0))
+    except AttributeError:
+        affinity = os.cpu_count() or 1
+    blas = []
+    try:
+        from threadpoolctl import threadpool_info
+        for i in threadpool_info():
+            if i.get("user_api") == "blas":
+                blas.append({"library": i.get("internal_api"), "version": i.get("version"),
+                             "threads": i.get("num_threads")})
+    except Exception:  # noqa: BLE001
+        pass
+    return {"cpu_model": model, "os_cpu_count": os.cpu_count(), "affinity_cores": affinity, "blas": blas,
+            "numpy": np.__version__}
+
+
+def _oracle_case(w):
+    """fp64 copies of head (0, 0) of a workload's seeded inputs, plus its mask arguments."""
+    import numpy as np
+    from exact_tiled_attention_32_amd import workloads
+    x = workloads.generate(w)
+    head = {n: x[n][0:1, 0:1].float().numpy().astype(np.float64) for n in ("q", "k", "v")}
+    head["do"] = None if x["do"] is None else x["do"][0:1, 0:1].float().numpy().astype(np.float64)
+    kv = None if x["kv_len"] is None else int(x["kv_len"][0])
+    bm = None if x["block_mask"] is None else x["block_mask"].numpy()
+    return head, kv, bm
+
+
+def oracle_config_timings(R_long: int) -> dict:
+    """The fp64 oracle on each named workload: forward and backward timed separately on a
+    bounded sample (head (0, 0); for the long workloads R query rows), with the sample's
+    algorithmic GFLOP (4 d per allowed pair forward, 2.5x that backward)."""
     import numpy as np
     import oracle
     from exact_tiled_attention_32_amd import workloads
-    try:
-        from threadpoolctl import threadpool_info
-        blas_threads = max((i.get("num_threads", 1) for i in threadpool_info()), default=1)
-    except Exception:  # noqa: BLE001
-        blas_threads = os.cpu_count() or 1
+    out = {}
+    for name, w in workloads.WORKLOADS.items():
+        if name in ("long_causal_d32", "long_causal_d16"):
+            continue
+        head, kv, bm = _oracle_case(w)
+        if w.N <= 1024:
+            rows = np.arange(w.N)
+            what = f"head (0,0), all {w.N} rows"
+        elif w.sparse:
+            rows = np.arange(16 * w.mask_block, 17 * w.mask_block)
+            what = f"head (0,0), the {w.mask_block} rows of query block 16 against its kept key blocks"
+        else:
+            rows = np.arange(w.N - R_long, w.N)
+            what = f"head (0,0), the last {R_long} rows with their full causal prefix"
+        allow = oracle.allowed_pairs(rows, w.N, causal=w.causal, kv_len_b=kv, block_mask=bm,
+                                     mask_block=w.mask_block)
+        pairs = float(allow.sum())
+        t0 = time.perf_counter()
+        oracle.forward_rows(head["q"][0, 0, rows], head["k"][0, 0], head["v"][0, 0], w.scale, allow)
+        t_fwd = time.perf_counter() - t0
+        res = {"sample": what, "allowed_pairs": pairs, "fwd_s": round(t_fwd, 4),
+               "fwd_gflops": round(4.0 * w.d * pairs / t_fwd / 1e9, 3)}
+        if w.backward:
+            t0 = time.perf_counter()
+            oracle.attention_backward(head["q"], head["k"], head["v"], head["do"], w.scale, causal=w.causal,
+                                      kv_len=None if kv is None else [kv], block_mask=bm,
+                                      mask_block=w.mask_block, rows=rows)
+            t_bwd = time.perf_counter() - t0
+            res.update(bwd_s=round(t_bwd, 4), bwd_gflops=round(10.0 * w.d * pairs / t_bwd / 1e9, 3))
+        out[name] = res
+    return out
+
+
+def cpu_baseline(target_s: float = 12.0) -> dict:
+    """The fp64 oracle on a bounded sample of the step's workload: head (0, 0), the last R
+    query rows (full causal prefix), forward + backward, for d = 64 and d = 128; then every
+    named workload on a small sample (forward and backward separately)."""
+    import numpy as np
+    import oracle
+    from exact_tiled_attention_32_amd import workloads
+    info = cpu_info()
+    threads = max([b["threads"] or 1 for b in info["blas"]] or [os.cpu_count() or 1])
 
     heads = {}
     for name in STEP_WORKLOADS:
@@ -411,8 +527,12 @@ def cpu_baseline(target_s: float = 15.0) -> dict:
             flop += 3.5 * 4.0 * w.d * pairs
         return flop, time.perf_counter() - t0
 
-    # size R so that the timed run takes about target_s (the work is close to linear in R;
-    # a second correction absorbs the start-up share of the short calibration run)
+    # one warm-up on the single-head workload, then size R so that the timed run takes about
+    # target_s (the work is close to linear in R; a second correction absorbs the start-up
+    # share of the short calibration run)
+    w1 = workloads.WORKLOADS["single_head_f32"]
+    head1, _, _ = _oracle_case(w1)
+    oracle.attention_forward(head1["q"], head1["k"], head1["v"], w1.scale)
     N = workloads.WORKLOADS[STEP_WORKLOADS[0]].N
     R = 512
     flop, dt = run(R)
@@ -422,10 +542,12 @@ def cpu_baseline(target_s: float = 15.0) -> dict:
         flop, dt = run(R)
         if dt >= 0.7 * target_s or R >= N:
             break
-    return {"value": flop / dt / 1e12, "unit": "TFLOP/s", "cores": int(blas_threads), "kind": "oracle",
+    per = oracle_config_timings(max(128, R // 8))
+    return {"value": flop / dt / 1e12, "unit": "TFLOP/s", "cores": int(threads), "kind": "oracle",
             "sample": f"fp64 NumPy oracle, head (b=0,h=0) of the step's workloads (d=64 and d=128), the last {R} "
                       f"query rows of N=16384 with their full causal prefix, forward + backward; "
-                      f"{flop / 1e9:.1f} GFLOP (same FLOP convention) in {dt:.1f} s"}
+                      f"{flop / 1e9:.1f} GFLOP (same FLOP convention) in {dt:.1f} s",
+            "host": info, "per_config": per, "note": "a baseline, not the target"}
 
 
 def time_step(fa, runners, steps, warmup):
@@ -438,21 +560,72 @@ def time_step(fa, runners, steps, warmup):
             r.bwd()
     torch.cuda.synchronize()
     clock = KernelClock()
-    # the kernel clock's event pairs are made before the timed region
-    pairs = [[(KernelClock.new_pair(), KernelClock.new_pair()) for _ in runners] for _ in range(steps)]
+    # the kernel clock's events are made before the timed region
+    evs = [[(KernelClock.new_events(2), KernelClock.new_events(1 + len(r.bwd_kernels))) for r in runners]
+           for _ in range(steps)]
     t0 = torch.cuda.Event(enable_timing=True)
     t1 = torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     t0.record()
     for i in range(steps):
-        for r, (pf, pb) in zip(runners, pairs[i]):
-            clock.arm(fa, f"fwd_d{r.w.d}", pf)
+        for r, (ef, eb) in zip(runners, evs[i]):
+            clock.arm(fa, f"fwd_d{r.w.d}", ef)
             r.fwd()
-            clock.arm(fa, f"bwd_dkdv_d{r.w.d}", pb)
+            clock.arm(fa, f"bwd_d{r.w.d}", eb)
             r.bwd()
     t1.record()
     torch.cuda.synchronize()
     return t0.elapsed_time(t1) / steps, clock
+
+
+def sample_clock(fn, seconds: float = 3.0) -> dict:
+    """Engine clock while `fn` (one step) runs back to back for `seconds`: rocm-smi (or
+    amd-smi) is polled from a second thread; each reading is a child process."""
+    import re
+    import subprocess
+    import threading
+
+    import torch
+    cmds = [["rocm-smi", "--showclocks"], ["amd-smi", "metric", "--clock"]]
+    samples, tool = [], None
+    stop = threading.Event()
+
+    def poll():
+        nonlocal tool
+        while not stop.is_set():
+            for c in cmds:
+                try:
+                    out = subprocess.run(c, capture_output=True, text=True, timeout=10).stdout
+                except (OSError, subprocess.SubprocessError):
+                    continue
+                # rocm-smi: "sclk clock level: N: (1700Mhz)"; amd-smi: a GFX clock block "CLK: 1700 MHz"
+                vals = [int(x) for x in re.findall(r"sclk[^\n]*?\((\d+)\s*mhz\)", out, flags=re.I)]
+                if not vals:
+                    vals = [int(x) for x in re.findall(r"gfx[_\s]*0?[^\n]*\n?[^\n]*?clk[^\d\n]*(\d+)\s*mhz",
+                                                        out, flags=re.I)]
+                if vals:
+                    tool = c[0]
+                    samples.append(vals[0])
+                    break
+            stop.wait(0.2)
+
+    th = threading.Thread(target=poll, daemon=True)
+    th.start()
+    t_end = time.perf_counter() + seconds
+    n = 0
+    while time.perf_counter() < t_end:
+        fn()
+        n += 1
+        if n % 20 == 0:
+            torch.cuda.synchronize()
+    torch.cuda.synchronize()
+    stop.set()
+    th.join(timeout=15)
+    if not samples:
+        return {"source": None, "samples": 0, "note": "no clock reading from rocm-smi or amd-smi"}
+    return {"source": tool, "samples": len(samples), "sclk_mhz_mean": round(sum(samples) / len(samples)),
+            "sclk_mhz_min": min(samples), "sclk_mhz_max": max(samples),
+            "during": f"the step run back to back for {seconds:.0f} s after the timed region"}
 
 
 def decode_bytes(w, kv_len) -> float:
@@ -487,11 +660,12 @@ def report_decode(fa, w, dev, steps, warmup) -> dict:
     # second pass with the library's events around the key-split kernel (their records
     # add gaps between launches, so the whole-call time above is taken without them)
     clock = KernelClock()
-    for _ in range(steps):
-        clock.arm(fa, "split")
+    evs = [KernelClock.new_events(3) for _ in range(steps)]
+    for e in evs:
+        clock.arm(fa, "split", e)
         call()
     torch.cuda.synchronize()
-    split_ms = clock.mean_ms("split")
+    split_ms = clock.kernel_ms("split", 0)
     nbytes = decode_bytes(w, x["kv_len"])
     return {"shape": {"B": w.B, "H": w.H, "Nq": w.Nq, "Nk": w.Nk, "d": w.d}, "causal": w.causal,
             "padding": w.padding, "algorithmic_bytes": nbytes, "ms": ms, "split_kernel_ms": split_ms,
@@ -566,22 +740,24 @@ def report_dropout(fa, w, dev, steps, warmup) -> dict:
                                          dq=dq, dk=dk, dv=dv, workspace=ws),
     }
     res = {"p": DROPOUT_P, "d": w.d}
+    kernels = {"fwd": ["fwd"], "bwd": ["bwd_dq", "bwd_dkdv"]}
     for phase, fn in fns.items():
         warm_up(fn, warmup)
         clock = KernelClock()
-        pairs = [KernelClock.new_pair() for _ in range(steps)]
+        evs = [KernelClock.new_events(1 + len(kernels[phase])) for _ in range(steps)]
         a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         a.record()
-        for pair in pairs:
-            clock.arm(fa, phase, pair)
+        for e in evs:
+            clock.arm(fa, phase, e)
             fn()
         b.record()
         torch.cuda.synchronize()
         ms = a.elapsed_time(b) / steps
         flop = attn_flops(w) * (2.5 if phase == "bwd" else 1.0)
         res[phase] = {"ms": round(ms, 4), "tflops": round(flop / ms / 1e9, 1),
-                      "frac_of_peak": round(flop / ms / 1e9 / PEAK_BF16_TFLOPS, 4),
-                      ("fwd_kernel_ms" if phase == "fwd" else "dkdv_kernel_ms"): round(clock.mean_ms(phase), 4)}
+                      "frac_of_peak": round(flop / ms / 1e9 / PEAK_BF16_TFLOPS, 4)}
+        for i, kname in enumerate(kernels[phase]):
+            res[phase][kname + "_kernel_ms"] = round(clock.kernel_ms(phase, i), 4)
     return res
 
 
@@ -626,41 +802,84 @@ def report_graph(fa, w, dev, steps, warmup) -> dict:
             "eager_tflops": round(flop / eager_ms / 1e9, 1), "graph_tflops": round(flop / graph_ms / 1e9, 1)}
 
 
+def compulsory_bytes(w, phase: str) -> float:
+    """Algorithmic HBM bytes of one call: forward Q, K, V read and O written once plus lse;
+    backward Q, K, V, O, dO read and dQ, dK, dV written once, lse read, D written and read."""
+    el = 4 if w.dtype == "f32" else 2
+    nd = w.B * w.H * w.N * w.d
+    rows = w.B * w.H * w.N
+    return (4 * nd * el + 4 * rows) if phase == "fwd" else (8 * nd * el + 12 * rows)
+
+
+def kept_pair_flops(w, kv_len) -> float:
+    """Forward FLOP over the allowed pairs only (4 d per pair) for key padding: each of the N
+    query rows of batch b attends its L_b valid keys (non-causal)."""
+    return 4.0 * w.H * w.d * w.N * float(sum(min(max(int(x), 0), w.N) for x in kv_len))
+
+
+def phase_figures(ms: float, flop: float, nbytes: float) -> dict:
+    return {"ms": round(ms, 4), "tflops": round(flop / ms / 1e9, 1),
+            "frac_of_peak": round(flop / ms / 1e9 / PEAK_BF16_TFLOPS, 4),
+            "hbm_gbs": round(nbytes / ms / 1e6, 1), "hbm_frac": round(nbytes / ms / 1e6 / PEAK_HBM_GBS, 4)}
+
+
+def report_config(fa, w, dev, steps=20, warmup=3) -> dict:
+    """Forward and backward of one named workload, timed separately (whole calls, HIP events
+    on the launch stream), with each kernel's share from the library's per-kernel events.
+    TFLOP/s by the headline convention (dense N^2, halved for causal; kept blocks for a
+    block mask), and by allowed pairs for key padding; HBM GB/s of the compulsory bytes."""
+    import torch
+    r = Runner(fa, w, dev)
+    ff = attn_flops(w, r.kept)
+    res = {"shape": [w.B, w.H, w.N, w.d], "dtype": w.dtype, "causal": w.causal, "padding": w.padding,
+           "sparse": w.sparse, "fwd_gflop": round(ff / 1e9, 3)}
+    if r.kept is not None:
+        res["kept_block_fraction"] = round(r.kept, 5)
+        res["flop_convention"] = "kept 128x128 blocks only"
+    kept_ff = None
+    if r.kv is not None:
+        kept_ff = kept_pair_flops(w, r.kv.cpu().tolist())
+        res["flop_convention"] = "dense N^2 (tflops); allowed pairs only (tflops_kept_pairs)"
+        res["kept_pair_fraction"] = round(kept_ff / attn_flops(w), 4)
+    kernels = {"fwd": ["fwd"], "bwd": r.bwd_kernels if w.backward else []}
+    for phase in ("fwd", "bwd") if w.backward else ("fwd",):
+        fn = r.fwd if phase == "fwd" else r.bwd
+        warm_up(fn, warmup)
+        clock = KernelClock()
+        evs = [KernelClock.new_events(1 + len(kernels[phase])) for _ in range(steps)]
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record()
+        for e in evs:
+            clock.arm(fa, phase, e)
+            fn()
+        b.record()
+        torch.cuda.synchronize()
+        ms = a.elapsed_time(b) / steps
+        mult = 2.5 if phase == "bwd" else 1.0
+        fig = phase_figures(ms, ff * mult, compulsory_bytes(w, phase))
+        if kept_ff is not None:
+            fig["tflops_kept_pairs"] = round(kept_ff * mult / ms / 1e9, 1)
+            fig["frac_of_peak_kept_pairs"] = round(kept_ff * mult / ms / 1e9 / PEAK_BF16_TFLOPS, 4)
+        if w.dtype == "f32":
+            fig["us"] = round(ms * 1e3, 2)
+        for i, kname in enumerate(kernels[phase]):
+            fig[kname + "_kernel_ms"] = round(clock.kernel_ms(phase, i), 4)
+        res[phase] = fig
+    del r
+    torch.cuda.empty_cache()
+    return res
+
+
 def report_all(fa, dev, path, steps=10, warmup=3):
-    """Per-workload fwd / bwd timing (not the metric line)."""
+    """Every workload (forward and backward separately), packed and decode workloads; written
+    to `path` (not the metric line)."""
     import torch
     from exact_tiled_attention_32_amd import workloads
     out = {}
     for name, w in workloads.WORKLOADS.items():
-        r = Runner(fa, w, dev)
-        kept = r.kept
-        ff = attn_flops(w, kept)
-        res = {"shape": [w.B, w.H, w.N, w.d], "dtype": w.dtype, "causal": w.causal, "padding": w.padding,
-               "sparse": w.sparse, "fwd_gflop": ff / 1e9}
-        if kept is not None:
-            res["kept_block_fraction"] = kept
-        for phase in ("fwd", "bwd") if w.backward else ("fwd",):
-            fn = r.fwd if phase == "fwd" else r.bwd
-            warm_up(fn, warmup)
-            clock = KernelClock()
-            pairs = [KernelClock.new_pair() for _ in range(steps)]
-            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-            a.record()
-            for pair in pairs:
-                clock.arm(fa, phase, pair)
-                fn()
-            b.record()
-            torch.cuda.synchronize()
-            ms = a.elapsed_time(b) / steps
-            flop = ff * (2.5 if phase == "bwd" else 1.0)
-            hbm = 2 * w.B * w.H * w.N * w.d * (4 if phase == "fwd" else 8) * (2 if w.dtype == "bf16" else 4)
-            res[phase] = {"ms": ms, "tflops": flop / ms / 1e9, "frac_of_peak": flop / ms / 1e9 / PEAK_BF16_TFLOPS,
-                          "main_kernel_ms": clock.mean_ms(phase),
-                          "compulsory_hbm_gbs": hbm / 2 / ms / 1e6}
-        out[name] = res
-        print(f"[report] {name}: " + json.dumps({k: v for k, v in res.items() if k in ("fwd", "bwd")}), flush=True)
-        del r
-        torch.cuda.empty_cache()
+        out[name] = report_config(fa, w, dev, steps, warmup)
+        print(f"[report] {name}: " + json.dumps({k: v for k, v in out[name].items() if k in ("fwd", "bwd")}),
+              flush=True)
     for name, w in workloads.VARLEN_WORKLOADS.items():
         out[name] = report_varlen(fa, w, dev, steps, warmup)
         print(f"[report] {name}: " + json.dumps({k: out[name][k] for k in ("fwd", "bwd")}), flush=True)
@@ -686,8 +905,9 @@ def main():
     ap.add_argument("--counter-pass", action="store_true",
                     help="for rocprofv3 --pmc / --kernel-trace: a calibration copy, then every workload once, "
                          "twice over; prints no metric line")
-    ap.add_argument("--summarize-counters", nargs=4, metavar=("SQ_CSV", "FETCH_CSV", "WRITE_CSV", "TRACE_CSV"),
-                    help="print the per-kernel counter table of a --counter-pass and exit")
+    ap.add_argument("--summarize-counters", nargs="+", metavar="CSV",
+                    help="SQ_CSV FETCH_CSV WRITE_CSV TRACE_CSV [VALU_CSV]: print the per-kernel counter table "
+                         "of a --counter-pass and exit")
     ap.add_argument("--step-only", action="store_true",
                     help="time the step alone (no decode or packed workloads), e.g. under a kernel trace")
     ap.add_argument("--decode-only", action="store_true",
@@ -736,28 +956,62 @@ def main():
     step_flop = sum(3.5 * attn_flops(r.w) for r in runners)
     value = step_flop / (ms * 1e-3) / 1e12
 
-    per = {}
+    # per head dimension: the forward and backward phases of the step, and each kernel
+    phases, kern = {}, {}
     for r in runners:
-        f = attn_flops(r.w)
-        per[f"d{r.w.d}"] = {k + "_kernel_ms": round(clock.mean_ms(f"{k}_d{r.w.d}"), 4) for k in KERNEL_FLOP_FACTOR}
-        per[f"d{r.w.d}"].update({k + "_tflops": round(KERNEL_FLOP_FACTOR[k] * f / clock.mean_ms(f"{k}_d{r.w.d}") / 1e9, 1)
-                                 for k in KERNEL_FLOP_FACTOR})
+        d, f = r.w.d, attn_flops(r.w)
+        k_ms = {"fwd": clock.kernel_ms(f"fwd_d{d}", 0)}
+        for i, k in enumerate(r.bwd_kernels):
+            k_ms[k] = clock.kernel_ms(f"bwd_d{d}", i)
+        fwd_ms, bwd_ms = k_ms["fwd"], clock.call_ms(f"bwd_d{d}")
+        phases[f"d{d}"] = {
+            "fwd": phase_figures(fwd_ms, f, compulsory_bytes(r.w, "fwd")),
+            "bwd": phase_figures(bwd_ms, 2.5 * f, compulsory_bytes(r.w, "bwd")),
+            "fwd_bwd_tflops": round(3.5 * f / (fwd_ms + bwd_ms) / 1e9, 1),
+        }
+        for k, kms in k_ms.items():
+            alg = KERNEL_FLOP_FACTOR[k] * f
+            kern[f"{k}_d{d}"] = {"ms": round(kms, 4), "algorithmic_tflop_per_launch": round(alg / 1e12, 4),
+                                 "tflops": round(alg / kms / 1e9, 1),
+                                 "frac": round(alg / kms / 1e9 / PEAK_BF16_TFLOPS, 4),
+                                 "executed_frac": round(KERNEL_EXECUTED_FACTOR[k] * f / kms / 1e9 / PEAK_BF16_TFLOPS,
+                                                        4)}
     # dominant kernel: the one with the largest time per step
-    cands = [(clock.mean_ms(f"{k}_d{r.w.d}"), k, r) for r in runners for k in KERNEL_FLOP_FACTOR]
-    dom_ms, dom_kind, dom_r = max(cands, key=lambda c: c[0])
-    dom_flop = attn_flops(dom_r.w) * KERNEL_FLOP_FACTOR[dom_kind]
-    dom_name = f"{dom_kind}_d{dom_r.w.d}"
-    achieved = dom_flop / dom_ms / 1e9
-    roofline = {"bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
-                "frac": round(achieved / PEAK_BF16_TFLOPS, 4), "traffic": load_traffic(dom_name),
-                "kernel": dom_name, "kernel_ms": round(dom_ms, 4),
-                "algorithmic_tflop_per_launch": round(dom_flop / 1e12, 4)}
+    dom_name = max(kern, key=lambda k: kern[k]["ms"])
+    dom = kern[dom_name]
+    roofline = {"bound": "mfma", "achieved": dom["tflops"], "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                "frac": dom["frac"], "traffic": load_traffic(dom_name), "kernel": dom_name, "kernel_ms": dom["ms"],
+                "algorithmic_tflop_per_launch": dom["algorithmic_tflop_per_launch"],
+                "kernels": {k: v["frac"] for k, v in kern.items()},
+                "bwd_phase": {d: p["bwd"]["frac_of_peak"] for d, p in phases.items()},
+                "fwd_phase": {d: p["fwd"]["frac_of_peak"] for d, p in phases.items()}}
     line = {"metric": METRIC, "value": round(value, 2), "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps,
             "warmup": args.warmup, "ms_per_step": round(ms, 4), "higher_is_better": True, "scaling": "weak",
             "vs_baseline": None, "dtype": "bf16", "data": "synthetic (iid N(0,1), seeded)",
             "config": {"workload": "long-sequence causal attention fwd+bwd, B=1 H=16 N=16384, d=64 and d=128",
                        "B": 1, "H": 16, "N": 16384, "d": [64, 128], "causal": True},
-            "frac_of_peak": round(value / PEAK_BF16_TFLOPS, 4), "per_head_dim": per, "roofline": roofline}
+            "frac_of_peak": round(value / PEAK_BF16_TFLOPS, 4), "phases": phases, "kernels": kern,
+            "roofline": roofline}
+
+    def one_step():
+        for r in runners:
+            r.fwd()
+            r.bwd()
+    line["clock"] = sample_clock(one_step, 3.0)
+    if not args.step_only:
+        # every named workload, forward and backward separately (the step's own two from the
+        # step above)
+        cfgs = {}
+        for name, w in workloads.WORKLOADS.items():
+            if name in STEP_WORKLOADS:
+                p = phases[f"d{w.d}"]
+                cfgs[name] = {"shape": [w.B, w.H, w.N, w.d], "causal": True, "from": "the timed step",
+                              "fwd": p["fwd"], "bwd": p["bwd"]}
+            elif name in ("long_causal_d32", "long_causal_d16"):
+                continue
+            else:
+                cfgs[name] = report_config(fa, w, dev)
+        line["configs"] = cfgs
     # the key/value-cache forward (HBM-bound) on its decode workloads, outside the step
     dec = {}
     for name, w in ({} if args.step_only else workloads.DECODE_WORKLOADS).items():

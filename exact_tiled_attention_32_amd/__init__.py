@@ -40,7 +40,7 @@ import torch
 __all__ = [
     "FA_F32", "FA_BF16", "FA_OK", "FA_ERR_INVALID", "FA_ERR_UNSUPPORTED", "FA_ERR_HIP",
     "FAError", "lib_path", "load", "fa_fwd", "fa_fwd_blocksparse", "fa_bwd",
-    "fa_bwd_workspace_bytes", "fa_fwd_dropout", "fa_bwd_dropout", "fa_fwd_varlen", "fa_bwd_varlen", "fa_bwd_varlen_workspace_bytes", "fa_fwd_kvcache", "fa_fwd_kvcache_workspace_bytes", "fa_fwd_kvcache_noalloc", "NOALLOC_SCRATCH_BYTES", "fa_time_next_kernel", "fa_status_string", "EXPORTED_SYMBOLS",
+    "fa_bwd_workspace_bytes", "fa_fwd_dropout", "fa_bwd_dropout", "fa_fwd_varlen", "fa_bwd_varlen", "fa_bwd_varlen_workspace_bytes", "fa_fwd_kvcache", "fa_fwd_kvcache_workspace_bytes", "fa_fwd_kvcache_noalloc", "NOALLOC_SCRATCH_BYTES", "fa_time_next_call", "fa_status_string", "EXPORTED_SYMBOLS",
 ]
 
 FA_F32, FA_BF16 = 0, 1
@@ -50,7 +50,7 @@ EXPORTED_SYMBOLS = ("fa_fwd", "fa_fwd_blocksparse", "fa_bwd_workspace_bytes", "f
                     "fa_fwd_kvcache_workspace_bytes", "fa_fwd_kvcache", "fa_fwd_kvcache_noalloc",
                     "fa_fwd_varlen", "fa_bwd_varlen_workspace_bytes", "fa_bwd_varlen",
                     "fa_fwd_dropout", "fa_bwd_dropout",
-                    "fa_time_next_kernel", "fa_status_string", "fa_last_error")
+                    "fa_time_next_call", "fa_status_string", "fa_last_error")
 
 _LIB = None
 NOALLOC_SCRATCH_BYTES = 64 << 20  # FA_NOALLOC_SCRATCH_BYTES of include/fa.h
@@ -103,22 +103,25 @@ def load() -> ctypes.CDLL:
     lib.fa_fwd_kvcache_noalloc.restype = I
     lib.fa_status_string.argtypes = [I]
     lib.fa_status_string.restype = ctypes.c_char_p
-    lib.fa_time_next_kernel.argtypes = [P, P]
-    lib.fa_time_next_kernel.restype = None
+    lib.fa_time_next_call.argtypes = [P, I]
+    lib.fa_time_next_call.restype = None
     lib.fa_last_error.argtypes = []
     lib.fa_last_error.restype = ctypes.c_char_p
     _LIB = lib
     return lib
 
 
-def fa_time_next_kernel(start: "torch.cuda.Event", stop: "torch.cuda.Event") -> None:
-    """Measurement hook: the next call on this thread records the two (timing-enabled)
-    events around its dominant kernel on its stream. Pass None, None to clear."""
+def fa_time_next_call(events) -> None:
+    """Measurement hook: the next call on this thread records events[0] on its stream before
+    its first kernel and events[i] after its i-th kernel (timing-enabled torch.cuda.Event
+    objects that have been recorded once, so that their HIP events exist; at most 8). Pass
+    None or [] to clear."""
     lib = load()
-    if start is None or stop is None:
-        lib.fa_time_next_kernel(None, None)
-    else:
-        lib.fa_time_next_kernel(ctypes.c_void_p(start.cuda_event), ctypes.c_void_p(stop.cuda_event))
+    if not events:
+        lib.fa_time_next_call(None, 0)
+        return
+    arr = (ctypes.c_void_p * len(events))(*[ctypes.c_void_p(e.cuda_event) for e in events])
+    lib.fa_time_next_call(arr, len(events))
 
 
 def fa_status_string(status: int) -> str:

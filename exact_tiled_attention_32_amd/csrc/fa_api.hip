@@ -16,7 +16,8 @@ namespace {
 thread_local char g_last_error[256] = "";
 thread_local fa::KernelTimer g_timer;
 
-// Hands out (and clears) the pending measurement events of this thread.
+// Hands out (and clears) the pending measurement events of this thread. The launch code
+// records them as it goes (KernelTimer::mark), so each call gets its own copy.
 fa::KernelTimer take_timer() {
   fa::KernelTimer t = g_timer;
   g_timer = fa::KernelTimer{};
@@ -138,7 +139,8 @@ fa_status fwd_impl(fa_dtype dt, int B, int H, int N, int d, const void* q, const
   a.seed_lo = drop.seed_lo;
   a.seed_hi = drop.seed_hi;
   a.drop_scale = drop.scale;
-  hipError_t e = fa::launch_fwd(a, dt, d, stream, take_timer(), drop.on);
+  fa::KernelTimer tm = take_timer();
+  hipError_t e = fa::launch_fwd(a, dt, d, stream, tm, drop.on);
   if (e != hipSuccess) return fail(FA_ERR_HIP, "forward launch failed: %s", hipGetErrorString(e));
   return FA_OK;
 }
@@ -272,7 +274,8 @@ fa_status bwd_impl(fa_dtype dt, int B, int H, int N, int d, const void* q, const
   a.seed_hi = drop.seed_hi;
   a.drop_scale = drop.scale;
   a.dropout = drop.on ? 1 : 0;
-  hipError_t e = fa::launch_bwd(a, d, stream, take_timer());
+  fa::KernelTimer tm = take_timer();
+  hipError_t e = fa::launch_bwd(a, d, stream, tm);
   if (e != hipSuccess) return fail(FA_ERR_HIP, "backward launch failed: %s", hipGetErrorString(e));
   return FA_OK;
 }
@@ -416,7 +419,8 @@ fa_status kvcache_impl(fa_dtype dt, int B, int H, int Nq, int Nk, int d, const v
   a.qmul = scale > 0.f ? 1.f : (scale < 0.f ? -1.f : 0.f);
   a.c2 = scale != 0.f ? sabs * 1.4426950408889634f : 1.4426950408889634f;
   a.sc_abs = sabs;
-  hipError_t e = fa::launch_kvcache(a, d, stream, take_timer());
+  fa::KernelTimer tm = take_timer();
+  hipError_t e = fa::launch_kvcache(a, d, stream, tm);
   if (e != hipSuccess) return fail(FA_ERR_HIP, "key/value-cache forward launch failed: %s", hipGetErrorString(e));
   return FA_OK;
 }
@@ -471,7 +475,8 @@ fa_status fa_fwd_varlen(fa_dtype dt, int nseq, int H, int total, int max_seqlen,
   a.cu = cu_seqlens;
   a.rs = H * d;
   a.total = total;
-  hipError_t e = fa::launch_fwd(a, dt, d, stream, take_timer());
+  fa::KernelTimer tm = take_timer();
+  hipError_t e = fa::launch_fwd(a, dt, d, stream, tm);
   if (e != hipSuccess) return fail(FA_ERR_HIP, "forward launch failed: %s", hipGetErrorString(e));
   return FA_OK;
 }
@@ -529,13 +534,21 @@ fa_status fa_bwd_varlen(fa_dtype dt, int nseq, int H, int total, int max_seqlen,
   a.rs = H * d;
   a.total = total;
   a.dropout = 0;
-  hipError_t e = fa::launch_bwd(a, d, stream, take_timer());
+  fa::KernelTimer tm = take_timer();
+  hipError_t e = fa::launch_bwd(a, d, stream, tm);
   if (e != hipSuccess) return fail(FA_ERR_HIP, "backward launch failed: %s", hipGetErrorString(e));
   return FA_OK;
 }
 
-void fa_time_next_kernel(hipEvent_t start, hipEvent_t stop) {
-  g_timer = (start && stop) ? fa::KernelTimer{start, stop} : fa::KernelTimer{};
+void fa_time_next_call(const hipEvent_t* events, int n) {
+  g_timer = fa::KernelTimer{};
+  if (events == nullptr || n <= 0) return;
+  const int m = std::min(n, fa::KernelTimer::kMax);
+  for (int i = 0; i < m; ++i) {
+    if (events[i] == nullptr) return;  // an incomplete list clears the request
+    g_timer.ev[i] = events[i];
+  }
+  g_timer.n = m;
 }
 
 const char* fa_status_string(fa_status s) {

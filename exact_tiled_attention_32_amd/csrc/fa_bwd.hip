@@ -15,11 +15,13 @@
 // bounded the whole backward. dQ is therefore computed by its own query-major kernel that
 // recomputes the score tile (two more products per tile, no atomics).
 //
-// Three launches on the caller's stream (four with a block mask):
-//   1. bwd_pre:   D = rowsum(dO o O) in fp32
-//   (1b. bwd_order: block-sparse only, the order of the dK/dV key tiles)
-//   2. bwd_dkdv:  one workgroup per (b, h, 128-key tile); 4 waves, two workgroups per CU
-//   3. bwd_dq:    one workgroup per (b, h, 128-query tile); 4 waves, one query per lane
+// Two launches on the caller's stream (three with a block mask):
+//   (1. bwd_order: block-sparse only, the order of the dK/dV key tiles)
+//   2. bwd_dq:    one workgroup per (b, h, 128-query tile); 4 waves, one query per lane.
+//                 Its prologue is the D pre-pass: each lane forms D = rowsum(dO o O) of its
+//                 query in fp32 from the dO and O rows and writes it to the workspace.
+//   3. bwd_dkdv:  one workgroup per (b, h, 128-key tile); 4 waves, two workgroups per CU;
+//                 reads D (so it runs after the dQ kernel)
 // As in the forward, packed sequences, causal and windowed masks, dropout (the mask
 // regenerated from the same Philox4x32-10 counters) and a head dimension of 16 are
 // variants of the same kernels.
@@ -40,34 +42,7 @@ constexpr int kBK = kBwdKeyTile;  // keys per dK/dV workgroup (32 per wave)
 __device__ __attribute__((aligned(16))) uint32_t g_zero16[4];
 
 // ---------------------------------------------------------------------------------------
-// 1. D = rowsum(dO o O). Each thread owns 8 columns of one row.
-// ---------------------------------------------------------------------------------------
-template <int D>
-__global__ __launch_bounds__(kThreads) void bwd_pre_kernel(BwdArgs a) {
-  constexpr int LPR = D / 8;  // lanes per row
-  // Rows of d elements, contiguous in both layouts: [B, H, N] order, or [total, H] order
-  // for packed sequences (whose D goes to [H, total], like their lse).
-  const size_t rows = a.cu ? (size_t)a.total * a.H : (size_t)a.B * a.H * a.N;
-  const size_t gid = (size_t)blockIdx.x * kThreads + threadIdx.x;
-  const size_t row = gid / LPR;
-  const int c0 = (int)(gid % LPR) * 8;
-  float acc = 0.f;
-  if (row < rows) {
-    const bf16x8 ov = __builtin_bit_cast(bf16x8, gload16(reinterpret_cast<const __bf16*>(a.o) + row * D + c0));
-    const bf16x8 dv = __builtin_bit_cast(bf16x8, gload16(reinterpret_cast<const __bf16*>(a.dout) + row * D + c0));
-#pragma unroll
-    for (int e = 0; e < 8; ++e) acc += (float)ov[e] * (float)dv[e];
-  }
-#pragma unroll
-  for (int off = LPR / 2; off > 0; off >>= 1) acc += __shfl_xor(acc, off);
-  if (row < rows && (gid % LPR) == 0) {
-    const size_t at = a.cu ? (row % a.H) * (size_t)a.total + row / a.H : row;
-    a.dsum[at] = acc;
-  }
-}
-
-// ---------------------------------------------------------------------------------------
-// 1b. Block-sparse only: the order in which the dK/dV workgroups take their key tiles, most
+// 1. Block-sparse only: the order in which the dK/dV workgroups take their key tiles, most
 //     kept mask blocks first. The work of a key tile is proportional to the kept blocks of
 //     its mask column; a column kept for every query block (a "global" column) can take
 //     far longer than the rest, and started last it would set the end of the launch.
@@ -128,7 +103,7 @@ __global__ __launch_bounds__(kThreads) void bwd_order_kernel(const uint8_t* __re
 }
 
 // ---------------------------------------------------------------------------------------
-// 2. dK / dV kernel: one workgroup per (b, h, 128-key tile). Wave w owns key group
+// 3. dK / dV kernel: one workgroup per (b, h, 128-key tile). Wave w owns key group
 //    kg = w % 4 (keys 32 kg .. 32 kg + 31 of the tile) and takes QBW 32-row query blocks
 //    per step (1 at d = 128, 2 below). Normally the workgroup is those 4 waves and two
 //    workgroups share a CU (two waves per SIMD from different workgroups); the dropout
@@ -572,7 +547,7 @@ __global__ __launch_bounds__(dkdv_threads(QH), QH == 1 ? 2 : 1) void bwd_dkdv_ke
 }
 
 // ---------------------------------------------------------------------------------------
-// 3. dQ kernel: one workgroup per (b, h, 128-query tile), 4 waves of 32 queries; key tiles
+// 2. dQ kernel: one workgroup per (b, h, 128-query tile), 4 waves of 32 queries; key tiles
 //    of 64 keys stream through double-buffered LDS. The orientation is the forward's:
 //    scores are formed transposed so each lane owns one query and lse, D are per-lane
 //    scalars.
@@ -653,24 +628,37 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dq_kernel(BwdArgs a) {
   }
 
   // The wave's Q and dO rows (B operands), and its row statistics in the exp2 domain.
+  // Lane (ql, h) holds columns 16 ks + 8 h .. + 7 of its query's row; with the O row in the
+  // same layout it also forms that query's D = rowsum(dO o O) (the two halves of the row
+  // meet across the half-waves) and publishes it for the dK/dV kernel, which runs next.
   bf16x8 qf[KS], df[KS];
+  float dval;
   {
     const size_t row = (size_t)min(qi, N - 1) * rs + 8 * h;
+    const __bf16* __restrict__ O = reinterpret_cast<const __bf16*>(a.o) + hoff;
+    bf16x8 of[KSG];
 #pragma unroll
     for (int ks = 0; ks < KSG; ++ks) {
       qf[ks] = __builtin_bit_cast(bf16x8, gload16(Q + row + 16 * ks));
       df[ks] = __builtin_bit_cast(bf16x8, gload16(dO + row + 16 * ks));
+      of[ks] = __builtin_bit_cast(bf16x8, gload16(O + row + 16 * ks));
     }
 #pragma unroll
     for (int ks = KSG; ks < KS; ++ks) qf[ks] = df[ks] = bf16x8{};
+    // The fragments are read in every step: let them land here, so that no wait for them is
+    // left inside the loop.
+    __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
+    float part = 0.f;
+#pragma unroll
+    for (int ks = 0; ks < KSG; ++ks)
+#pragma unroll
+      for (int e = 0; e < 8; ++e) part = __builtin_fmaf((float)df[ks][e], (float)of[ks][e], part);
+    dval = part + other_half(part);
+    if (h == 0 && qi < N) a.dsum[sl.loff + qi] = dval;
   }
   const float lse_v = a.lse[sl.loff + min(qi, N - 1)];
   // an empty row (lse = -inf) and a row past N get lse2 = +inf, so P = 0 there
   const float lse2 = (qi >= N || lse_v == kNegInf) ? __builtin_inff() : lse_v * kLog2e;
-  const float dval = a.dsum[sl.loff + min(qi, N - 1)];
-  // The fragments are read in every step: let them land here, so that no wait for them is
-  // left inside the loop.
-  __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
 
   // Per-lane LDS byte offsets (XOR-derived per k-step / d-block, see the dK/dV kernel).
   const int k_off0 = tile_off<D>(ql, 8 * h);  // K / V row operand, k-step 0 (+32 kb rows)
@@ -845,26 +833,34 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dq_kernel(BwdArgs a) {
 
 }  // namespace
 
-hipError_t launch_bwd(const BwdArgs& a, int d, hipStream_t stream, const KernelTimer& tm) {
-  const size_t rows = a.cu ? (size_t)a.total * a.H : (size_t)a.B * a.H * a.N;
-  const size_t pre_threads = rows * (size_t)(d / 8);
+hipError_t launch_bwd(const BwdArgs& a, int d, hipStream_t stream, KernelTimer& tm) {
   const dim3 block(kThreads);
-  const dim3 gpre((unsigned)((pre_threads + kThreads - 1) / kThreads));
   const dim3 gdkdv((unsigned)(((a.N + kBK - 1) / kBK) * a.B * a.H));
   const dim3 gdq((unsigned)(((a.N + kDqRows - 1) / kDqRows) * a.B * a.H));
-  if (d == 16) hipLaunchKernelGGL(bwd_pre_kernel<16>, gpre, block, 0, stream, a);
-  else if (d == 32) hipLaunchKernelGGL(bwd_pre_kernel<32>, gpre, block, 0, stream, a);
-  else if (d == 64) hipLaunchKernelGGL(bwd_pre_kernel<64>, gpre, block, 0, stream, a);
-  else hipLaunchKernelGGL(bwd_pre_kernel<128>, gpre, block, 0, stream, a);
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return e;
+  tm.mark(stream);
+  hipError_t e;
   if (a.order) {
     hipLaunchKernelGGL(bwd_order_kernel, dim3(1), block, 0, stream, a.mask, a.nb, a.mb,
                        (a.N + kBK - 1) / kBK, a.order);
     e = hipGetLastError();
     if (e != hipSuccess) return e;
+    tm.mark(stream);
   }
-  if (tm.start) (void)hipEventRecord(tm.start, stream);
+  // dQ first: its prologue writes D, which the dK/dV kernel reads
+  if (a.dropout) {
+    if (d == 16) hipLaunchKernelGGL((bwd_dq_kernel<32, true, 16>), gdq, block, 0, stream, a);
+    else if (d == 32) hipLaunchKernelGGL((bwd_dq_kernel<32, true>), gdq, block, 0, stream, a);
+    else if (d == 64) hipLaunchKernelGGL((bwd_dq_kernel<64, true>), gdq, block, 0, stream, a);
+    else hipLaunchKernelGGL((bwd_dq_kernel<128, true>), gdq, block, 0, stream, a);
+  } else {
+    if (d == 16) hipLaunchKernelGGL((bwd_dq_kernel<32, false, 16>), gdq, block, 0, stream, a);
+    else if (d == 32) hipLaunchKernelGGL((bwd_dq_kernel<32, false>), gdq, block, 0, stream, a);
+    else if (d == 64) hipLaunchKernelGGL((bwd_dq_kernel<64, false>), gdq, block, 0, stream, a);
+    else hipLaunchKernelGGL((bwd_dq_kernel<128, false>), gdq, block, 0, stream, a);
+  }
+  e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  tm.mark(stream);
   auto dkdv = [&](auto kernel, int qh) { hipLaunchKernelGGL(kernel, gdkdv, dim3(dkdv_threads(qh)), 0, stream, a); };
   if (a.dropout) {  // (the dropout calls take no block mask)
     if (d == 16) dkdv(bwd_dkdv_kernel<32, true, 16>, dkdv_halves<32, true>());
@@ -883,20 +879,8 @@ hipError_t launch_bwd(const BwdArgs& a, int d, hipStream_t stream, const KernelT
     else dkdv(bwd_dkdv_kernel<128, false>, dkdv_halves<128, false>());
   }
   e = hipGetLastError();
-  if (tm.stop) (void)hipEventRecord(tm.stop, stream);
-  if (e != hipSuccess) return e;
-  if (a.dropout) {
-    if (d == 16) hipLaunchKernelGGL((bwd_dq_kernel<32, true, 16>), gdq, block, 0, stream, a);
-    else if (d == 32) hipLaunchKernelGGL((bwd_dq_kernel<32, true>), gdq, block, 0, stream, a);
-    else if (d == 64) hipLaunchKernelGGL((bwd_dq_kernel<64, true>), gdq, block, 0, stream, a);
-    else hipLaunchKernelGGL((bwd_dq_kernel<128, true>), gdq, block, 0, stream, a);
-  } else {
-    if (d == 16) hipLaunchKernelGGL((bwd_dq_kernel<32, false, 16>), gdq, block, 0, stream, a);
-    else if (d == 32) hipLaunchKernelGGL((bwd_dq_kernel<32, false>), gdq, block, 0, stream, a);
-    else if (d == 64) hipLaunchKernelGGL((bwd_dq_kernel<64, false>), gdq, block, 0, stream, a);
-    else hipLaunchKernelGGL((bwd_dq_kernel<128, false>), gdq, block, 0, stream, a);
-  }
-  return hipGetLastError();
+  if (e == hipSuccess) tm.mark(stream);
+  return e;
 }
 
 }  // namespace fa

@@ -333,22 +333,24 @@ int kvcache_split_waves(int d) {
   return d <= 32 ? SplitShape<32>::W : d == 64 ? SplitShape<64>::W : SplitShape<128>::W;
 }
 
-hipError_t launch_kvcache(const DecArgs& a, int d, hipStream_t stream, const KernelTimer& tm) {
+hipError_t launch_kvcache(const DecArgs& a, int d, hipStream_t stream, KernelTimer& tm) {
   const int W = kvcache_split_waves(d);
   const dim3 gsplit((unsigned)(a.units / W * a.B * a.H)), gmerge((unsigned)(a.B * a.H * a.Nq));
-  if (tm.start) (void)hipEventRecord(tm.start, stream);
+  tm.mark(stream);
   if (d == 16) hipLaunchKernelGGL((kvc_split_kernel<32, 16>), gsplit, dim3(64 * W), 0, stream, a);
   else if (d == 32) hipLaunchKernelGGL(kvc_split_kernel<32>, gsplit, dim3(64 * W), 0, stream, a);
   else if (d == 64) hipLaunchKernelGGL(kvc_split_kernel<64>, gsplit, dim3(64 * W), 0, stream, a);
   else hipLaunchKernelGGL(kvc_split_kernel<128>, gsplit, dim3(64 * W), 0, stream, a);
   hipError_t e = hipGetLastError();
-  if (tm.stop) (void)hipEventRecord(tm.stop, stream);
   if (e != hipSuccess) return e;
+  tm.mark(stream);
   if (d == 16) hipLaunchKernelGGL(kvc_merge_kernel<16>, gmerge, dim3(kThreads), 0, stream, a);
   else if (d == 32) hipLaunchKernelGGL(kvc_merge_kernel<32>, gmerge, dim3(kThreads), 0, stream, a);
   else if (d == 64) hipLaunchKernelGGL(kvc_merge_kernel<64>, gmerge, dim3(kThreads), 0, stream, a);
   else hipLaunchKernelGGL(kvc_merge_kernel<128>, gmerge, dim3(kThreads), 0, stream, a);
-  return hipGetLastError();
+  e = hipGetLastError();
+  if (e == hipSuccess) tm.mark(stream);
+  return e;
 }
 
 }  // namespace fa

@@ -455,10 +455,10 @@ __global__ __launch_bounds__(kThreads) void fwd_f32_kernel(FwdArgs a) {
 
 }  // namespace
 
-hipError_t launch_fwd(const FwdArgs& a, fa_dtype dt, int d, hipStream_t stream, const KernelTimer& tm,
+hipError_t launch_fwd(const FwdArgs& a, fa_dtype dt, int d, hipStream_t stream, KernelTimer& tm,
                       bool dropout) {
   const dim3 grid((unsigned)(a.ntq * a.B * a.H)), block(kThreads);
-  if (tm.start) (void)hipEventRecord(tm.start, stream);
+  tm.mark(stream);
   if (dt == FA_BF16 && dropout) {
     if (d == 16) hipLaunchKernelGGL((fwd_bf16_kernel<32, true, 16>), grid, block, 0, stream, a);
     else if (d == 32) hipLaunchKernelGGL((fwd_bf16_kernel<32, true>), grid, block, 0, stream, a);
@@ -475,7 +475,7 @@ hipError_t launch_fwd(const FwdArgs& a, fa_dtype dt, int d, hipStream_t stream, 
     else hipLaunchKernelGGL(fwd_f32_kernel<128>, grid, block, 0, stream, a);
   }
   hipError_t e = hipGetLastError();
-  if (tm.stop) (void)hipEventRecord(tm.stop, stream);
+  if (e == hipSuccess) tm.mark(stream);
   return e;
 }
 

@@ -109,15 +109,21 @@ constexpr int kBwdMinTile = 32;
 constexpr int kBwdKeyTile = 128;
 constexpr int kMaxKeyTiles = kMaxTileList * kBwdMinTile / kBwdKeyTile;
 
-// Optional events recorded around the dominant kernel of a call (may be nullptr).
+// Optional measurement events of a call: ev[0] is recorded before its first kernel and
+// ev[i] after its i-th kernel, as far as the caller supplied events (n of them).
 struct KernelTimer {
-  hipEvent_t start = nullptr;
-  hipEvent_t stop = nullptr;
+  static constexpr int kMax = 8;
+  hipEvent_t ev[kMax] = {};
+  int n = 0;
+  int next = 0;
+  void mark(hipStream_t stream) {
+    if (next < n) (void)hipEventRecord(ev[next++], stream);
+  }
 };
 
-hipError_t launch_fwd(const FwdArgs& a, fa_dtype dt, int d, hipStream_t stream, const KernelTimer& tm,
+hipError_t launch_fwd(const FwdArgs& a, fa_dtype dt, int d, hipStream_t stream, KernelTimer& tm,
                       bool dropout = false);
-hipError_t launch_bwd(const BwdArgs& a, int d, hipStream_t stream, const KernelTimer& tm);
-hipError_t launch_kvcache(const DecArgs& a, int d, hipStream_t stream, const KernelTimer& tm);
+hipError_t launch_bwd(const BwdArgs& a, int d, hipStream_t stream, KernelTimer& tm);
+hipError_t launch_kvcache(const DecArgs& a, int d, hipStream_t stream, KernelTimer& tm);
 
 }  // namespace fa

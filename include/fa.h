@@ -280,14 +280,20 @@ fa_status fa_fwd_kvcache_noalloc(fa_dtype dt, int B, int H, int Nq, int Nk, int 
                                  hipStream_t stream);
 
 /*
- * Measurement hook. When both events are non-NULL, the next fa_fwd, fa_fwd_blocksparse,
- * fa_fwd_dropout, fa_fwd_varlen, fa_fwd_kvcache, fa_bwd, fa_bwd_dropout or fa_bwd_varlen
- * call on the calling thread that passes validation records `start` on its stream immediately before launching its
- * dominant kernel (the forward kernel, the key-split kernel of the cache forward, or the
- * backward main kernel) and `stop` immediately after it, then forgets both events.
- * Passing NULL clears a pending request. The events are owned by the caller.
+ * Measurement hook. The next fa_fwd, fa_fwd_blocksparse, fa_fwd_dropout, fa_fwd_varlen,
+ * fa_fwd_kvcache, fa_fwd_kvcache_noalloc, fa_bwd, fa_bwd_dropout or fa_bwd_varlen call on
+ * the calling thread that passes validation records events[0] on its stream immediately
+ * before its first kernel and events[i] immediately after its i-th kernel, for i < n (at
+ * most 8 events; kernels past the supplied events are not bracketed). Kernels in launch
+ * order:
+ *   forward calls:      the forward kernel (events[0], events[1])
+ *   backward calls:     [with a block mask: the key-tile order kernel,] the dQ kernel (whose
+ *                       prologue computes D = rowsum(dO * O)), the dK/dV kernel
+ *   cache forward:      the key-split kernel, the merge kernel
+ * The request is then forgotten. events == NULL, n <= 0 or a NULL entry clears a pending
+ * request. The events are owned by the caller.
  */
-void fa_time_next_kernel(hipEvent_t start, hipEvent_t stop);
+void fa_time_next_call(const hipEvent_t* events, int n);
 
 /* Static English name of a status code. */
 const char* fa_status_string(fa_status s);

@@ -86,8 +86,11 @@ def test_counter_sequence():
     kernels = {}
     for w, k in seq[:half]:
         kernels.setdefault(w, []).append(k.split("<")[0])
-    assert kernels["block_sparse_64k"] == ["fwd_bf16_kernel", "bwd_pre_kernel", "bwd_order_kernel",
-                                           "bwd_dkdv_kernel", "bwd_dq_kernel"]
+    # the backward: (block mask: the key-tile order,) the dQ kernel, whose prologue writes D,
+    # then the dK/dV kernel that reads it
+    assert kernels["block_sparse_64k"] == ["fwd_bf16_kernel", "bwd_order_kernel", "bwd_dq_kernel",
+                                           "bwd_dkdv_kernel"]
+    assert kernels["long_causal_d128"] == ["fwd_bf16_kernel", "bwd_dq_kernel", "bwd_dkdv_kernel"]
     assert kernels["single_head_f32"] == ["fwd_f32_kernel"]
     assert kernels["decode_q1_d128"] == ["kvc_split_kernel", "kvc_merge_kernel"]
 
@@ -113,3 +116,50 @@ def test_warm_up_runs_the_minimum_calls_and_time(monkeypatch):
     calls.clear()
     bench.warm_up(lambda: calls.append(1), 3, 0.0)
     assert len(calls) == 3
+
+
+def test_compulsory_bytes():
+    # forward: Q, K, V read and O written once (bf16) plus lse; backward: Q, K, V, O, dO read,
+    # dQ, dK, dV written, lse read, D written and read
+    w = workloads.WORKLOADS["long_causal_d128"]
+    nd, rows = 16 * 16384 * 128, 16 * 16384
+    assert bench.compulsory_bytes(w, "fwd") == 4 * nd * 2 + 4 * rows
+    assert bench.compulsory_bytes(w, "bwd") == 8 * nd * 2 + 12 * rows
+    w1 = workloads.WORKLOADS["single_head_f32"]
+    assert bench.compulsory_bytes(w1, "fwd") == 4 * 128 * 64 * 4 + 4 * 128
+
+
+def test_kept_pair_flops_brute_force():
+    # key padding, non-causal: every query row of batch b attends its L_b valid keys
+    w = workloads.Workload("tiny", B=3, H=2, N=10, d=8, dtype="bf16", seed=0, padding=True)
+    lens = [10, 4, 0]
+    pairs = sum(1 for b in range(3) for i in range(10) for j in range(10) if j < lens[b])
+    assert bench.kept_pair_flops(w, lens) == 4.0 * 2 * 8 * pairs
+    assert bench.kept_pair_flops(w, [12, -1, 3]) == 4.0 * 2 * 8 * 10 * (10 + 0 + 3)  # clamped to [0, N]
+
+
+class _FakeEvent:
+    def __init__(self, t):
+        self.t = t
+
+    def elapsed_time(self, other):
+        return other.t - self.t
+
+
+def test_kernel_clock_arithmetic(monkeypatch):
+    # events[0] before the first kernel, events[i] after the i-th: kernel i lasts
+    # events[i + 1] - events[i]; the call spans events[0] .. events[-1]
+    class FakeFa:
+        armed = []
+
+        def fa_time_next_call(self, events):
+            self.armed.append(events)
+
+    fa = FakeFa()
+    clock = bench.KernelClock()
+    clock.arm(fa, "bwd", [_FakeEvent(t) for t in (0.0, 1.0, 4.0)])
+    clock.arm(fa, "bwd", [_FakeEvent(t) for t in (10.0, 12.0, 14.0)])
+    assert len(fa.armed) == 2
+    assert clock.kernel_ms("bwd", 0) == pytest.approx(1.5)
+    assert clock.kernel_ms("bwd", 1) == pytest.approx(2.5)
+    assert clock.call_ms("bwd") == pytest.approx(4.0)
