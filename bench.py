@@ -357,7 +357,7 @@ def summarize_counters(sq_csv, fetch_csv, write_csv, trace_csv, valu_csv=None) -
         if len(rows) != len(seq):
             raise RuntimeError(f"{what}: {len(rows)} library dispatches, expected {len(seq)}")
     half = len(seq) // 2
-    lines = ["| workload | kernel | µs | FETCH MB | WRITE MB | HBM GB/s | MFMA busy | VALU busy | VALU insts / MFMA "
+    lines = ["| workload | kernel | µs | FETCH MB | WRITE MB | HBM GB/s | MFMA busy | VALU pipe | VALU insts / MFMA "
              "| LDS bank-conflict cycles / LDS active cycles | MFMA insts | LDS insts |",
              "|---|---|---|---|---|---|---|---|---|---|---|---|"]
     for i in range(half, len(seq)):
@@ -376,10 +376,13 @@ def summarize_counters(sq_csv, fetch_csv, write_csv, trace_csv, valu_csv=None) -
         bank = c["SQ_LDS_BANK_CONFLICT"] / max(c["SQ_LDS_IDX_ACTIVE"], 1.0)
         if va is not None:
             v = va[i]
-            # SQ_ACTIVE_INST_VALU: cycles in which the SQ had a VALU instruction of a wave in
-            # issue (MFMA issue included), summed like SQ_BUSY_CU_CYCLES over the CUs; per SIMD
-            valu = f"{100 * v['SQ_ACTIVE_INST_VALU'] / max(4.0 * v['SQ_BUSY_CU_CYCLES'], 1.0):.1f} %"
-            vpm = f"{v['SQ_INSTS_VALU'] / max(v['SQ_INSTS_MFMA'], 1.0):.2f}"
+            # VALU pipe: non-MFMA VALU instructions (SQ_INSTS_VALU counts MFMAs too) x 4 cycles
+            # each (a wave64 instruction on a 16-lane SIMD) over the SIMD cycles (4 x
+            # SQ_BUSY_CU_CYCLES, as for MFMA busy); transcendentals take longer, so this is a
+            # lower bound of the pipe's occupancy
+            valu = (f"{100 * 4.0 * (v['SQ_INSTS_VALU'] - v['SQ_INSTS_MFMA']) / max(4.0 * v['SQ_BUSY_CU_CYCLES'], 1.0):.1f}"
+                    f" %")
+            vpm = f"{(v['SQ_INSTS_VALU'] - v['SQ_INSTS_MFMA']) / max(v['SQ_INSTS_MFMA'], 1.0):.2f}"
         else:
             valu = vpm = "—"
         lines.append(f"| {wname} | {kname} | {us:.1f} | {fb / 1e6:.1f} | {wb / 1e6:.1f} | "
