@@ -74,7 +74,7 @@ fa_status check_mask(const uint8_t* mask, int mask_block, int N, int tile_keys) 
   return FA_OK;
 }
 
-// Dropout parameters: threshold floor(p 2^32) on the generator word, scale 1 / (1 - p).
+// Dropout parameters: threshold floor(p 2^16) on a 16-bit generator value, scale 1 / (1 - p).
 struct DropoutParams {
   bool on = false;
   uint32_t thr = 0, seed_lo = 0, seed_hi = 0;
@@ -85,7 +85,7 @@ fa_status make_dropout(float p, uint64_t seed, DropoutParams* out) {
   if (!(p >= 0.0f && p < 1.0f)) return fail(FA_ERR_INVALID, "dropout_p must be in [0, 1) (got %g)", (double)p);
   DropoutParams d;
   d.on = p > 0.0f;
-  d.thr = (uint32_t)std::min(std::floor((double)p * 4294967296.0), 4294967295.0);
+  d.thr = (uint32_t)std::min(std::floor((double)p * 65536.0), 65535.0);
   d.seed_lo = (uint32_t)(seed & 0xFFFFFFFFu);
   d.seed_hi = (uint32_t)(seed >> 32);
   d.scale = (float)(1.0 / (1.0 - (double)p));

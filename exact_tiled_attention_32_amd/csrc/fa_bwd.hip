@@ -392,7 +392,22 @@ __global__ __launch_bounds__(dkdv_threads(QH), QH == 1 ? 2 : 1) void bwd_dkdv_ke
     }
     if constexpr (kPrioS) __builtin_amdgcn_s_setprio(0);
     // P = exp2(S * scale * log2e - lse * log2e), dS = P (dP - D); with dropout the value
-    // products see P o Z and dS = P (Z dP / (1 - p) - D), Z the keep mask of the pair.
+    // products see P o Z and dS = P (Z dP / (1 - p) - D), Z the keep mask of the pair: bit
+    // 4 g + e of zbits[b2] for query e of register group g (dropout_bits_klane, one call
+    // per lane per pair of groups).
+    uint32_t zbits[QBW];
+#pragma unroll
+    for (int b2 = 0; b2 < QBW; ++b2) {
+      zbits[b2] = 0xFFFFu;
+      if constexpr (DROP) {
+        zbits[b2] = 0;
+#pragma unroll
+        for (int gp = 0; gp < 2; ++gp)
+          zbits[b2] |= dropout_bits_klane(key, q0 + qw0 + 32 * b2 + 16 * gp + 4 * h, (uint32_t)(bh % a.H),
+                                          (uint32_t)b, a.seed_lo, a.seed_hi, a.drop_thr)
+                       << (8 * gp);
+      }
+    }
 #pragma unroll
     for (int b2 = 0; b2 < QBW; ++b2)
 #pragma unroll
@@ -400,32 +415,7 @@ __global__ __launch_bounds__(dkdv_threads(QH), QH == 1 ? 2 : 1) void bwd_dkdv_ke
         const int qr0 = qw0 + 32 * b2 + 8 * g + 4 * h;
         const f32x4 l2 = *reinterpret_cast<const f32x4*>(&stats[BUF][0][qr0]);
         const f32x4 dd = *reinterpret_cast<const f32x4*>(&stats[BUF][1][qr0]);
-        uint32_t keep = 0xFu;
-        if constexpr (DROP) {
-          // The four lanes of a quad hold keys 4m .. 4m + 3 (one generator counter) and need
-          // them against the group's four queries. Lane `own` makes the call for query
-          // `own` of the group; word own ^ s of it goes to lane own ^ s (a quad permutation),
-          // which receives its own key's word of query own ^ s.
-          const uint32_t own = (uint32_t)(kl & 3);
-          const u32x4 wv = philox4x32_10((uint32_t)key >> 2, (uint32_t)(q0 + qr0 + own), (uint32_t)(bh % a.H),
-                                         (uint32_t)b, a.seed_lo, a.seed_hi);
-          // order the words as w[own ^ s] for s = 0 .. 3
-          uint32_t w0 = wv[0], w1 = wv[1], w2 = wv[2], w3 = wv[3];
-          if (own & 1u) {
-            const uint32_t t0 = w0, t2 = w2;
-            w0 = w1; w1 = t0; w2 = w3; w3 = t2;
-          }
-          if (own & 2u) {
-            const uint32_t t0 = w0, t1 = w1;
-            w0 = w2; w1 = w3; w2 = t0; w3 = t1;
-          }
-          // quad_perm lane patterns: xor 1 = [1,0,3,2], xor 2 = [2,3,0,1], xor 3 = [3,2,1,0]
-          const uint32_t r1 = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)w1, 0xB1, 0xF, 0xF, false);
-          const uint32_t r2 = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)w2, 0x4E, 0xF, 0xF, false);
-          const uint32_t r3 = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)w3, 0x1B, 0xF, 0xF, false);
-          keep = ((uint32_t)(w0 >= a.drop_thr) << own) | ((uint32_t)(r1 >= a.drop_thr) << (own ^ 1u)) |
-                 ((uint32_t)(r2 >= a.drop_thr) << (own ^ 2u)) | ((uint32_t)(r3 >= a.drop_thr) << (own ^ 3u));
-        }
+        const uint32_t keep = (zbits[b2] >> (4 * g)) & 0xFu;
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
           const int i = 4 * g + e;
@@ -751,24 +741,20 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dq_kernel(BwdArgs a) {
         s[kbk] = mfma32(so[it & 1].k, qf[ks], s[kbk]);
         dp[kbk] = mfma32(so[it & 1].v, df[ks], dp[kbk]);
       }
-      // with dropout, dS = P (Z dP / (1 - p) - D): one generator call covers four
-      // consecutive keys of the lane's query, as in the forward
+      // with dropout, dS = P (Z dP / (1 - p) - D), the keep bits Z as in the forward
 #pragma unroll
-      for (int kbk = 0; kbk < KB; ++kbk)
+      for (int kbk = 0; kbk < KB; ++kbk) {
+        uint32_t keep = 0xFFFFu;
+        if constexpr (DROP)
+          keep = dropout_bits_qlane(key0 + 32 * kbk, qi, ql, h, (uint32_t)(bh % a.H), (uint32_t)b, a.seed_lo,
+                                    a.seed_hi, a.drop_thr);
 #pragma unroll
-        for (int g = 0; g < 4; ++g) {
-          u32x4 wv = u32x4{};
-          if constexpr (DROP)
-            wv = philox4x32_10((uint32_t)(key0 + 32 * kbk + 8 * g + 4 * h) >> 2, (uint32_t)qi, (uint32_t)(bh % a.H),
-                               (uint32_t)b, a.seed_lo, a.seed_hi);
-#pragma unroll
-          for (int r = 0; r < 4; ++r) {
-            const int i = 4 * g + r;
-            const float p = fast_exp2(__builtin_fmaf(s[kbk][i], a.c2s, -lse2));
-            if constexpr (DROP) dp[kbk][i] = p * ((wv[r] >= a.drop_thr ? dp[kbk][i] * a.drop_scale : 0.f) - dval);
-            else dp[kbk][i] = p * (dp[kbk][i] - dval);
-          }
+        for (int i = 0; i < 16; ++i) {
+          const float p = fast_exp2(__builtin_fmaf(s[kbk][i], a.c2s, -lse2));
+          if constexpr (DROP) dp[kbk][i] = p * ((((keep >> i) & 1u) ? dp[kbk][i] * a.drop_scale : 0.f) - dval);
+          else dp[kbk][i] = p * (dp[kbk][i] - dval);
         }
+      }
       // Tiles that cross the causal diagonal or the key padding (a wave-uniform test):
       // masked pairs get dS = 0 by selection.
       if ((key0 + kDqKeys > kv_end) || (a.wr >= 0 && key0 + kDqKeys - 1 > qw + a.wr) ||

@@ -190,14 +190,79 @@ __device__ __forceinline__ u32x4 philox4x32_10(uint32_t x0, uint32_t x1, uint32_
   return u32x4{x0, x1, x2, x3};
 }
 
-// Dropout parameters of a call: key j of query i in (b, h) is kept iff word j % 4 of
-// philox4x32_10(j / 4, i, h, b, seed_lo, seed_hi) >= thr; kept probabilities are scaled
-// by `scale` = 1 / (1 - p).
-struct Dropout {
-  uint32_t thr;
-  uint32_t seed_lo, seed_hi;
-  float scale;
-};
+// Dropout keep rule: one generator call per block of 4 keys x 2 queries, counter
+// (key / 4, query / 2, head, batch), key (seed_lo, seed_hi); key j of query i takes word
+// j % 4, 16-bit half i % 2 (0 = low), and is kept iff that value is >= thr (floor(p 2^16));
+// kept probabilities are scaled by 1 / (1 - p). With thr_hi = thr << 16, a high half is
+// >= thr iff its word is >= thr_hi, a low half iff the word shifted left by 16 is.
+
+// Keep bits of two packed words: x01 holds the values of items 0 (low) and 1 (high),
+// x23 those of items 2 and 3. Bit k = item k kept.
+__device__ __forceinline__ uint32_t dropout_keep4(uint32_t x01, uint32_t x23, uint32_t thr_hi) {
+  return (uint32_t)((x01 << 16) >= thr_hi) | ((uint32_t)(x01 >= thr_hi) << 1) |
+         ((uint32_t)((x23 << 16) >= thr_hi) << 2) | ((uint32_t)(x23 >= thr_hi) << 3);
+}
+
+// Query-per-lane layout (forward and dQ kernels): in the 32-key block at kb0, lane (ql, h)
+// holds query qi and keys kb0 + 8 g + 4 h + r (g, r = 0..3). Queries 2m and 2m + 1 sit in
+// lanes ql and ql ^ 1 of one quad and share each key group's call: for the group pairs
+// (0, 1) and (2, 3) the lane makes the call of group 2 gp + (ql & 1), packs the halves of its
+// query (v_perm_b32, two values to a word) and swaps the other halves with its neighbour
+// (one DPP exchange per packed word). Returns the block's keep bits, bit 4 g + r.
+__device__ __forceinline__ uint32_t dropout_bits_qlane(int kb0, int qi, int ql, int h, uint32_t head, uint32_t bat,
+                                                       uint32_t seed_lo, uint32_t seed_hi, uint32_t thr) {
+  const uint32_t odd = (uint32_t)(ql & 1);
+  const uint32_t thr_hi = thr << 16;
+  // byte selectors of v_perm_b32(w_hi, w_lo): low halves of both words, or high halves
+  const uint32_t sel_own = odd ? 0x07060302u : 0x05040100u;
+  const uint32_t sel_other = odd ? 0x05040100u : 0x07060302u;
+  uint32_t bits = 0;
+#pragma unroll
+  for (int gp = 0; gp < 2; ++gp) {
+    const int g = 2 * gp + (int)odd;
+    const u32x4 w = philox4x32_10((uint32_t)(kb0 + 8 * g + 4 * h) >> 2, (uint32_t)qi >> 1, head, bat, seed_lo,
+                                  seed_hi);
+    const uint32_t own01 = __builtin_amdgcn_perm(w[1], w[0], sel_own);
+    const uint32_t own23 = __builtin_amdgcn_perm(w[3], w[2], sel_own);
+    const uint32_t snd01 = __builtin_amdgcn_perm(w[1], w[0], sel_other);
+    const uint32_t snd23 = __builtin_amdgcn_perm(w[3], w[2], sel_other);
+    // quad_perm [1, 0, 3, 2]: the value of lane ql ^ 1
+    const uint32_t rcv01 = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)snd01, 0xB1, 0xF, 0xF, false);
+    const uint32_t rcv23 = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)snd23, 0xB1, 0xF, 0xF, false);
+    bits |= (dropout_keep4(own01, own23, thr_hi) << (4 * g)) |
+            (dropout_keep4(rcv01, rcv23, thr_hi) << (4 * (g ^ 1)));
+  }
+  return bits;
+}
+
+// Key-per-lane layout (dK/dV kernel): lane (kl, h) holds key `key` and, in query group G,
+// queries q_g0 + 8 (G - g0) + e (e = 0..3; q_g0 counts the lane's 4 h offset). The lanes of
+// a quad hold keys 4c .. 4c + 3, the keys of one call. For the group pair (g0, g0 + 1) the
+// quad needs four calls (two query pairs per group): lane q = key % 4 makes the call of group
+// g0 + q / 2, query pair q % 2; a 4 x 4 transpose across the quad (two rounds of DPP
+// exchanges) then leaves in lane q word q of every call, which holds its key's values for
+// that call's two queries. Returns bit 4 (G - g0) + e = query e of group G kept.
+__device__ __forceinline__ uint32_t dropout_bits_klane(int key, int q_g0, uint32_t head, uint32_t bat,
+                                                       uint32_t seed_lo, uint32_t seed_hi, uint32_t thr) {
+  const uint32_t q = (uint32_t)(key & 3);
+  const uint32_t qpair = (uint32_t)(q_g0 + 8 * (int)(q >> 1) + 2 * (int)(q & 1)) >> 1;
+  const u32x4 w = philox4x32_10((uint32_t)key >> 2, qpair, head, bat, seed_lo, seed_hi);
+  // round 1, lanes q and q ^ 1: swap the words whose index differs from q in bit 0
+  const bool o1 = (q & 1u) != 0;
+  const uint32_t s0 = o1 ? w[0] : w[1], s1 = o1 ? w[2] : w[3];
+  const uint32_t r0 = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)s0, 0xB1, 0xF, 0xF, false);
+  const uint32_t r1 = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)s1, 0xB1, 0xF, 0xF, false);
+  const uint32_t a0 = o1 ? r0 : w[0], a1 = o1 ? w[1] : r0, a2 = o1 ? r1 : w[2], a3 = o1 ? w[3] : r1;
+  // round 2, lanes q and q ^ 2 (quad_perm [2, 3, 0, 1]): the same in bit 1
+  const bool o2 = (q & 2u) != 0;
+  const uint32_t t0 = o2 ? a0 : a2, t1 = o2 ? a1 : a3;
+  const uint32_t u0 = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)t0, 0x4E, 0xF, 0xF, false);
+  const uint32_t u1 = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)t1, 0x4E, 0xF, 0xF, false);
+  const uint32_t b0 = o2 ? u0 : a0, b1 = o2 ? u1 : a1, b2 = o2 ? a2 : u0, b3 = o2 ? a3 : u1;
+  // b_j: word q of lane j's call (group g0 + j / 2, query pair j % 2), halves by query parity
+  const uint32_t thr_hi = thr << 16;
+  return dropout_keep4(b0, b1, thr_hi) | (dropout_keep4(b2, b3, thr_hi) << 4);
+}
 
 // 16-byte global load/store helpers (addresses 16-byte aligned).
 __device__ __forceinline__ u32x4 gload16(const void* p) { return *reinterpret_cast<const u32x4*>(p); }

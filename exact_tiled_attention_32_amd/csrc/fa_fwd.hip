@@ -271,20 +271,16 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_bf16_kernel(FwdArgs a) {
     if constexpr (kPrioA) __builtin_amdgcn_s_setprio(1);
     scores(kb, nxt);
     // Dropout: bit 16 kbk + i of `keep` says whether this lane's element (kbk, i) of tile t
-    // is kept; one generator call covers four consecutive keys of the lane's query.
+    // is kept (register i of a block holds key 8 (i / 4) + 4 h + i % 4).
     uint32_t keep = 0xFFFFFFFFu;
     if constexpr (DROP) {
       const int key0 = tile_at(t) * kBC;
       keep = 0;
 #pragma unroll
       for (int kbk = 0; kbk < KB; ++kbk)
-#pragma unroll
-        for (int g = 0; g < 4; ++g) {
-          const u32x4 wv = philox4x32_10((uint32_t)(key0 + 32 * kbk + 8 * g + 4 * h) >> 2, (uint32_t)qi,
-                                         (uint32_t)(bh % a.H), (uint32_t)b, a.seed_lo, a.seed_hi);
-#pragma unroll
-          for (int r = 0; r < 4; ++r) keep |= (uint32_t)(wv[r] >= a.drop_thr) << (16 * kbk + 4 * g + r);
-        }
+        keep |= dropout_bits_qlane(key0 + 32 * kbk, qi, ql, h, (uint32_t)(bh % a.H), (uint32_t)b, a.seed_lo,
+                                   a.seed_hi, a.drop_thr)
+                << (16 * kbk);
     }
     bf16x8 pb[PS];
     float lsum = 0.f;

@@ -139,10 +139,11 @@ fa_status fa_bwd(fa_dtype dt, int B, int H, int N, int d,
  * audit of "FlashAttention: Fast and Memory-Efficient Exact Attention with IO-Awareness"
  * quotes the fused kernel applying dropout to the probabilities and the backward
  * regenerating the mask instead of storing it. The generator is Philox4x32-10 (Salmon,
- * Moraes, Dror, Shaw, "Parallel random numbers: as easy as 1, 2, 3", SC 2011): key j of
- * query i in (b, h) is kept iff word j % 4 of Philox(counter (j / 4, i, h, b), key
- * (seed mod 2^32, seed / 2^32)) >= floor(dropout_p * 2^32); kept probabilities are
- * scaled by 1 / (1 - dropout_p). lse is that of the undropped softmax, as fa_fwd's, and
+ * Moraes, Dror, Shaw, "Parallel random numbers: as easy as 1, 2, 3", SC 2011). One call
+ * covers 4 keys x 2 queries: key j of query i in (b, h) takes 16-bit half i % 2 (0 = low)
+ * of word j % 4 of Philox(counter (j / 4, i / 2, h, b), key (seed mod 2^32, seed / 2^32))
+ * and is kept iff that value is >= min(floor(dropout_p * 2^16), 65535); kept probabilities
+ * are scaled by 1 / (1 - dropout_p). lse is that of the undropped softmax, as fa_fwd's, and
  * fa_bwd_dropout must get the forward's dropout_p and seed to regenerate the same mask.
  *   dropout_p  in [0, 1); 0 gives exactly fa_fwd / fa_bwd (same kernels)
  *   seed       64-bit generator key; a new seed draws a new mask

@@ -60,11 +60,13 @@ What it computes, and where the pages define it
   the generator state instead of storing it. The pages give no generator, so
   the oracle fixes one: Philox4x32-10 (Salmon, Moraes, Dror, Shaw, "Parallel
   random numbers: as easy as 1, 2, 3", SC 2011), a counter-based generator
-  written here from its published definition (``philox4x32_10``). Key j of
-  query i in batch b, head h is kept iff word (j mod 4) of
-  Philox((j // 4, i, h, b), (seed mod 2^32, seed // 2^32)) is >= floor(p 2^32);
-  kept probabilities are scaled by 1 / (1 - p). lse stays that of the
-  undropped softmax: O = (P o M) V with M = keep / (1 - p).
+  written here from its published definition (``philox4x32_10``). One call
+  covers a block of 4 keys x 2 queries: its counter is (j // 4, i // 2, h, b)
+  and its key (seed mod 2^32, seed // 2^32); its four 32-bit words hold eight
+  16-bit values, and key j of query i in batch b, head h takes word (j mod 4),
+  16-bit half (i mod 2) (0 = low). The pair is kept iff that value is
+  >= floor(p 2^16); kept probabilities are scaled by 1 / (1 - p).
+  lse stays that of the undropped softmax: O = (P o M) V with M = keep / (1 - p).
 * Backward — the pages say only that the backward is simplified analytically
   and recomputes the attention matrix from the saved statistics
   (cochat.ai audit of "FlashAttention: Fast and Memory-Efficient Exact
@@ -138,10 +140,11 @@ def dropout_keep(b: int, h: int, rows, cols, seed: int, p: float) -> np.ndarray:
     """Boolean [len(rows), len(cols)]: is key j of query i kept (module docstring)."""
     rows = np.asarray(rows, dtype=np.int64)[:, None]
     cols = np.asarray(cols, dtype=np.int64)[None, :]
-    words = philox4x32_10(cols >> 2, rows, h, b, seed & 0xFFFFFFFF, (seed >> 32) & 0xFFFFFFFF)
-    w = np.choose(np.broadcast_to(cols & 3, words[0].shape), words)
-    threshold = min(int(np.floor(p * 2.0 ** 32)), 2 ** 32 - 1)
-    return w >= np.uint64(threshold)
+    words = philox4x32_10(cols >> 2, rows >> 1, h, b, seed & 0xFFFFFFFF, (seed >> 32) & 0xFFFFFFFF)
+    w = np.choose(np.broadcast_to(cols & 3, words[0].shape), words)        # word j mod 4
+    half = (w >> (np.uint64(16) * (rows & 1).astype(np.uint64))) & np.uint64(0xFFFF)  # half i mod 2
+    threshold = min(int(np.floor(p * 65536.0)), 65535)
+    return half >= np.uint64(threshold)
 
 
 def _dropout_scale(b, h, rows, cols, dropout_p, dropout_seed):

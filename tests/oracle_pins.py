@@ -626,14 +626,18 @@ def pin_philox_known_answers(orc):
 
 
 def _keep_scalar(b, h, i, j, seed, p):
-    words = _philox_scalar((j // 4, i, h, b), (seed & 0xFFFFFFFF, seed >> 32))
-    return words[j % 4] >= min(math.floor(p * 2 ** 32), 2 ** 32 - 1)
+    """The keep rule for one pair, on Python integers: the call for the block of keys
+    4 (j // 4) .. + 3 and queries 2 (i // 2), + 1; of its eight 16-bit values (two per
+    word, low half first) the pair takes value number 2 (j % 4) + i % 2."""
+    words = _philox_scalar((j // 4, i // 2, h, b), (seed & 0xFFFFFFFF, seed >> 32))
+    values = [(wd >> shift) & 0xFFFF for wd in words for shift in (0, 16)]
+    return values[2 * (j % 4) + i % 2] >= min(math.floor(p * 65536), 65535)
 
 
 def pin_dropout_mask_rule(orc):
     """dropout_keep follows the stated rule element by element (scalar generator calls)."""
     for b, h, seed, p in ((0, 0, 1, 0.5), (3, 5, 0x1234567890ABCDEF, 0.1), (1, 2, 77, 0.9)):
-        rows, cols = [0, 1, 5, 130], list(range(0, 23)) + [64, 127, 1000]
+        rows, cols = [0, 1, 2, 5, 130, 131], list(range(0, 23)) + [64, 127, 1000]
         keep = orc.dropout_keep(b, h, rows, cols, seed, p)
         for a, i in enumerate(rows):
             for c, j in enumerate(cols):

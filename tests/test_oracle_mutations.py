@@ -69,9 +69,14 @@ MUTANTS = {
     "dropout_scale_missing": ("return dropout_keep(b, h, rows, cols, dropout_seed, dropout_p) / (1.0 - dropout_p)",
                               "return dropout_keep(b, h, rows, cols, dropout_seed, dropout_p) * 1.0"),
     "dropout_word_shifted": ("np.broadcast_to(cols & 3,", "np.broadcast_to((cols + 1) & 3,"),
-    "dropout_counter_transposed": ("philox4x32_10(cols >> 2, rows, h, b,", "philox4x32_10(rows >> 2, cols, h, b,"),
-    "dropout_threshold_flipped": ("return w >= np.uint64(threshold)", "return w < np.uint64(threshold)"),
-    "dropout_heads_swapped": ("philox4x32_10(cols >> 2, rows, h, b,", "philox4x32_10(cols >> 2, rows, b, h,"),
+    "dropout_half_from_key": ("(np.uint64(16) * (rows & 1).astype(np.uint64))",
+                              "(np.uint64(16) * (cols & 1).astype(np.uint64))"),
+    "dropout_half_swapped": ("(np.uint64(16) * (rows & 1).astype(np.uint64))",
+                             "(np.uint64(16) * ((rows + 1) & 1).astype(np.uint64))"),
+    "dropout_query_pair_ignored": ("philox4x32_10(cols >> 2, rows >> 1, h, b,", "philox4x32_10(cols >> 2, rows, h, b,"),
+    "dropout_counter_transposed": ("philox4x32_10(cols >> 2, rows >> 1, h, b,", "philox4x32_10(rows >> 2, cols >> 1, h, b,"),
+    "dropout_threshold_flipped": ("return half >= np.uint64(threshold)", "return half < np.uint64(threshold)"),
+    "dropout_heads_swapped": ("philox4x32_10(cols >> 2, rows >> 1, h, b,", "philox4x32_10(cols >> 2, rows >> 1, b, h,"),
     "philox_weyl_constant": ("_PHILOX_W = (0x9E3779B9, 0xBB67AE85)", "_PHILOX_W = (0x9E3779B9, 0xBB67AE86)"),
     "philox_output_order": ("x = [((p1 >> np.uint64(32)) ^ x[1] ^ k0) & _U32, p1 & _U32,",
                             "x = [((p1 >> np.uint64(32)) ^ x[3] ^ k0) & _U32, p1 & _U32,"),
