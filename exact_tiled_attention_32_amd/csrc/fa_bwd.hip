@@ -229,23 +229,6 @@ __global__ __launch_bounds__(dkdv_threads(QH), QH == 1 ? 2 : 1) void bwd_dkdv_ke
     nq = __builtin_amdgcn_readfirstlane(
         build_qtile_list<kMainThreads>(qlist, wcount, a.mask, k0 / a.mb, a.nb, a.mb, i0, ntq, BQ));
 
-  // The V tile, and the K tile unless K is held in registers, stay in LDS for the whole
-  // kernel (rows past N are zero).
-#pragma unroll
-  for (int c = 0; c < KCH; ++c) {
-    const int id = tid + kMainThreads * c;
-    const int row = id / (D / 8), col = (id % (D / 8)) * 8;
-    const int kk = min(k0 + row, N - 1);
-    const bool ok = k0 + row < N && col < DG;
-    const int cc = col < DG ? col : 0;  // (a column in range; the value is dropped)
-    if constexpr (!KREG) {
-      const u32x4 kv = gload16(K + (size_t)kk * rs + cc);
-      lds_store16(kt + tile_off<D>(row, col), ok ? kv : u32x4{});
-    }
-    const u32x4 vv = gload16(V + (size_t)kk * rs + cc);
-    lds_store16(vt + tile_off<D>(row, col), ok ? vv : u32x4{});
-  }
-
   // Per-lane LDS byte offsets, fixed for the whole kernel. Within a swizzled row the
   // offsets of chunk c and of chunk c ^ m differ by an XOR with 16 m, so one base register
   // per operand family serves every k-step and d-block (the XOR only touches bits below
@@ -329,6 +312,23 @@ __global__ __launch_bounds__(dkdv_threads(QH), QH == 1 ? 2 : 1) void bwd_dkdv_ke
       kf[ks] = key < N ? __builtin_bit_cast(bf16x8, gload16(krow + 16 * ks)) : bf16x8{};
   }
   stage_q(nq > 0 ? tile_at(0) : 0, std::integral_constant<int, 0>{});
+  // The V tile, and the K tile unless K is held in registers, stay in LDS for the whole
+  // kernel (rows past N are zero). Requested after the first query tile's staging, so that
+  // the prologue waits for one memory latency, not two.
+#pragma unroll
+  for (int c = 0; c < KCH; ++c) {
+    const int id = tid + kMainThreads * c;
+    const int row = id / (D / 8), col = (id % (D / 8)) * 8;
+    const int kk = min(k0 + row, N - 1);
+    const bool ok = k0 + row < N && col < DG;
+    const int cc = col < DG ? col : 0;  // (a column in range; the value is dropped)
+    if constexpr (!KREG) {
+      const u32x4 kv = gload16(K + (size_t)kk * rs + cc);
+      lds_store16(kt + tile_off<D>(row, col), ok ? kv : u32x4{});
+    }
+    const u32x4 vv = gload16(V + (size_t)kk * rs + cc);
+    lds_store16(vt + tile_off<D>(row, col), ok ? vv : u32x4{});
+  }
   wait_loads();
   store_stats(0);
   __syncthreads();
@@ -622,11 +622,12 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dq_kernel(BwdArgs a) {
   // same layout it also forms that query's D = rowsum(dO o O) (the two halves of the row
   // meet across the half-waves) and publishes it for the dK/dV kernel, which runs next.
   bf16x8 qf[KS], df[KS];
-  float dval;
+  // The loads are waited for together with the first tile's staging below (one memory
+  // latency, not two).
+  bf16x8 of[KSG];
   {
     const size_t row = (size_t)min(qi, N - 1) * rs + 8 * h;
     const __bf16* __restrict__ O = reinterpret_cast<const __bf16*>(a.o) + hoff;
-    bf16x8 of[KSG];
 #pragma unroll
     for (int ks = 0; ks < KSG; ++ks) {
       qf[ks] = __builtin_bit_cast(bf16x8, gload16(Q + row + 16 * ks));
@@ -635,20 +636,8 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dq_kernel(BwdArgs a) {
     }
 #pragma unroll
     for (int ks = KSG; ks < KS; ++ks) qf[ks] = df[ks] = bf16x8{};
-    // The fragments are read in every step: let them land here, so that no wait for them is
-    // left inside the loop.
-    __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
-    float part = 0.f;
-#pragma unroll
-    for (int ks = 0; ks < KSG; ++ks)
-#pragma unroll
-      for (int e = 0; e < 8; ++e) part = __builtin_fmaf((float)df[ks][e], (float)of[ks][e], part);
-    dval = part + other_half(part);
-    if (h == 0 && qi < N) a.dsum[sl.loff + qi] = dval;
   }
   const float lse_v = a.lse[sl.loff + min(qi, N - 1)];
-  // an empty row (lse = -inf) and a row past N get lse2 = +inf, so P = 0 there
-  const float lse2 = (qi >= N || lse_v == kNegInf) ? __builtin_inff() : lse_v * kLog2e;
 
   // Per-lane LDS byte offsets (XOR-derived per k-step / d-block, see the dK/dV kernel).
   const int k_off0 = tile_off<D>(ql, 8 * h);  // K / V row operand, k-step 0 (+32 kb rows)
@@ -693,7 +682,21 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dq_kernel(BwdArgs a) {
   };
 
   stage(tile_at(0), std::integral_constant<int, 0>{});
+  // The fragments are read in every step: let them land here, so that no wait for them is
+  // left inside the loop.
   __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
+  float dval;
+  {
+    float part = 0.f;
+#pragma unroll
+    for (int ks = 0; ks < KSG; ++ks)
+#pragma unroll
+      for (int e = 0; e < 8; ++e) part = __builtin_fmaf((float)df[ks][e], (float)of[ks][e], part);
+    dval = part + other_half(part);
+    if (h == 0 && qi < N) a.dsum[sl.loff + qi] = dval;
+  }
+  // an empty row (lse = -inf) and a row past N get lse2 = +inf, so P = 0 there
+  const float lse2 = (qi >= N || lse_v == kNegInf) ? __builtin_inff() : lse_v * kLog2e;
   __syncthreads();
 
   int ko0 = k_off0, tl0 = t_lo0, th0 = t_hi0;

@@ -71,13 +71,22 @@ constexpr int kSchedValu = 0x002;
 constexpr int kSchedDsRead = 0x100;
 // s_waitcnt immediate for vmcnt(0), expcnt and lgkmcnt left free (gfx9 encoding).
 constexpr int kWaitVmcnt0 = 0x0F70;
+// s_waitcnt immediate for vmcnt(n) (n < 64: low four bits at [3:0], high two at [15:14]).
+constexpr int wait_vmcnt(int n) { return kWaitVmcnt0 | (n & 0xF) | ((n >> 4) << 14); }
 
 // DG is the head dimension in memory; D the width of the LDS tiles and MFMA operands. A
 // head dimension of 16 runs on 32-wide tiles whose upper half is zero (staged as zeros,
 // never stored).
-template <int D, bool DROP, int DG = D>
+// NS is the number of K and V tile buffers: the loads of a tile are issued NS - 1 steps
+// before it is read. Two suffice when most tiles come from L2 (long sequences, where the
+// tiles of one head are shared by all its query tiles on an XCD); short sequences read most
+// tiles from HBM, whose latency is several steps there. Workgroups staged more than two
+// deep serve dense launches only and carry no block-sparse tile list.
+template <int D, bool DROP, int DG = D, int NS = 2>
 __global__ __launch_bounds__(kThreads, 2) void fwd_bf16_kernel(FwdArgs a) {
   static_assert(DG == D || (D == 32 && DG == 16), "narrow heads run on 32-wide tiles");
+  static_assert(NS >= 2 && NS <= 4, "two to four tile buffers");
+  constexpr bool LIST = NS == 2;  // block-sparse tile list
   constexpr int KSG = (DG + 15) / 16;          // k-steps that carry data
   constexpr int CH = D / 8;                    // 16-byte chunks per row
   constexpr int TILE = kBC * D * 2;            // bytes of one K or V tile
@@ -88,14 +97,19 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_bf16_kernel(FwdArgs a) {
   constexpr int RPB = 1024 / (2 * D);          // tile rows per 1 KB staging block
   constexpr int NDMA = TILE / (kThreads * 16); // staging instructions per wave per tile
   static_assert((4 * RPB) % 16 == 0, "staging block step must keep the swizzle");
-  // LDS: two K and two V buffers, each its own array so that the staging loads into one
+  // LDS: NS K and NS V buffers, each its own array so that the staging loads into one
   // buffer are known not to touch the others (no wait for them before reading those).
-  // The score product runs one tile ahead of the value product: step t reads K(t+1), V(t).
+  // The score product runs one tile ahead of the value product: step t reads K(t+1), V(t);
+  // tile j lives in buffer j mod NS.
   __shared__ __attribute__((aligned(16))) char kb0[TILE];
   __shared__ __attribute__((aligned(16))) char kb1[TILE];
+  __shared__ __attribute__((aligned(16))) char kb2[NS > 2 ? TILE : 16];
+  __shared__ __attribute__((aligned(16))) char kb3[NS > 3 ? TILE : 16];
   __shared__ __attribute__((aligned(16))) char vb0[TILE];
   __shared__ __attribute__((aligned(16))) char vb1[TILE];
-  __shared__ uint16_t tlist[kMaxTiles];
+  __shared__ __attribute__((aligned(16))) char vb2[NS > 2 ? TILE : 16];
+  __shared__ __attribute__((aligned(16))) char vb3[NS > 3 ? TILE : 16];
+  __shared__ uint16_t tlist[LIST ? kMaxTiles : 1];
   __shared__ int wcount[4];
 
   const int BH = a.B * a.H;
@@ -122,15 +136,19 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_bf16_kernel(FwdArgs a) {
   const int t0 = a.wl >= 0 ? max(q0 - a.wl, 0) / kBC : 0;
   const int ntk = (hi + kBC - 1) / kBC;
   int ntiles = max(ntk - t0, 0);
-  if (a.mask)
-    ntiles = __builtin_amdgcn_readfirstlane(build_tile_list(tlist, wcount, a.mask, q0 / a.mb, a.nb, a.mb, ntk, kBC));
+  if constexpr (LIST) {
+    if (a.mask)
+      ntiles = __builtin_amdgcn_readfirstlane(build_tile_list(tlist, wcount, a.mask, q0 / a.mb, a.nb, a.mb, ntk, kBC));
+  }
   // Key tile of step t, clamped so that the look-ahead of the last steps stays valid.
   auto tile_at = [&](int t) {
     const int tc = min(t, max(ntiles - 1, 0));
-    return a.mask ? __builtin_amdgcn_readfirstlane((int)tlist[tc]) : t0 + tc;
+    if constexpr (LIST) return a.mask ? __builtin_amdgcn_readfirstlane((int)tlist[tc]) : t0 + tc;
+    else return t0 + tc;
   };
 
-  // Q fragments: B operand of S^T = K Q^T, lane holds Q[qi][16 ks + 8h .. +7].
+  // Q fragments: B operand of S^T = K Q^T, lane holds Q[qi][16 ks + 8h .. +7]. The loads
+  // are waited for together with the first tiles' staging (one memory latency, not two).
   bf16x8 qf[KS];
   {
     const __bf16* qrow = Q + (size_t)min(qi, N - 1) * rs + 8 * h;
@@ -138,6 +156,9 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_bf16_kernel(FwdArgs a) {
     for (int ks = 0; ks < KSG; ++ks) qf[ks] = __builtin_bit_cast(bf16x8, gload16(qrow + 16 * ks));
 #pragma unroll
     for (int ks = KSG; ks < KS; ++ks) qf[ks] = bf16x8{};
+  }
+  // Scaling by the sign of the softmax scale (or by 0): applied once the fragments landed.
+  auto scale_q = [&]() {
     const float qm = qi < N ? a.qmul : 0.f;
     if (qm != 1.0f) {
 #pragma unroll
@@ -145,10 +166,7 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_bf16_kernel(FwdArgs a) {
 #pragma unroll
         for (int e = 0; e < 8; ++e) qf[ks][e] = (__bf16)((float)qf[ks][e] * qm);
     }
-    // The fragments are read in every step: let them land here, so that no wait for them
-    // is left inside the loop.
-    __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
-  }
+  };
 
   // Per-lane LDS byte offsets, tile-relative, fixed for the whole kernel.
   int k_off[KS];             // S^T A operand: K row ql, columns 16 ks + 8h (+32 kb rows)
@@ -192,10 +210,26 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_bf16_kernel(FwdArgs a) {
       __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (FA_LDS void*)(buf + (4 * c + w) * 1024), 16, voff, 0, 0, 0);
     }
   };
-  FA_LDS char* const kbuf0 = (FA_LDS char*)kb0;
-  FA_LDS char* const kbuf1 = (FA_LDS char*)kb1;
-  FA_LDS char* const vbuf0 = (FA_LDS char*)vb0;
-  FA_LDS char* const vbuf1 = (FA_LDS char*)vb1;
+  // Buffer of tile j (j mod NS, a compile-time index).
+  auto kbuf = [&](auto jc) {
+    constexpr int J = decltype(jc)::value % NS;
+    if constexpr (J == 0) return (FA_LDS char*)kb0;
+    else if constexpr (J == 1) return (FA_LDS char*)kb1;
+    else if constexpr (J == 2) return (FA_LDS char*)kb2;
+    else return (FA_LDS char*)kb3;
+  };
+  auto vbuf = [&](auto jc) {
+    constexpr int J = decltype(jc)::value % NS;
+    if constexpr (J == 0) return (FA_LDS char*)vb0;
+    else if constexpr (J == 1) return (FA_LDS char*)vb1;
+    else if constexpr (J == 2) return (FA_LDS char*)vb2;
+    else return (FA_LDS char*)vb3;
+  };
+  // vmcnt that leaves the loads of the last NS - 2 steps in flight (each step stages one K
+  // and one V tile, NDMA loads each per wave)
+  constexpr int kWaitAhead = wait_vmcnt(2 * NDMA * (NS - 2));
+  using I0 = std::integral_constant<int, 0>;
+  using I1 = std::integral_constant<int, 1>;
 
   // Score tile S^T = K Q^T of the K tile at `kb` (MFMA phase only).
   auto scores = [&](const FA_LDS char* kb, f32x16 (&s)[KB]) {
@@ -241,27 +275,45 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_bf16_kernel(FwdArgs a) {
 
   f32x16 sa[KB], sb[KB];
   if (ntiles > 0) {
-    stage(K, tile_at(0), kbuf0);
-    stage(V, tile_at(0), vbuf0);
-    stage(K, tile_at(1), kbuf1);
-    __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
+    // K(0), V(0), K(1), then V(j), K(j + 1) up to K(NS - 1); wait for the first three and
+    // the Q fragments, which were requested before them
+    stage(K, tile_at(0), kbuf(I0{}));
+    stage(V, tile_at(0), vbuf(I0{}));
+    stage(K, tile_at(1), kbuf(I1{}));
+    if constexpr (NS > 2) {
+      stage(V, tile_at(1), vbuf(I1{}));
+      stage(K, tile_at(2), kbuf(std::integral_constant<int, 2>{}));
+    }
+    if constexpr (NS > 3) {
+      stage(V, tile_at(2), vbuf(std::integral_constant<int, 2>{}));
+      stage(K, tile_at(3), kbuf(std::integral_constant<int, 3>{}));
+    }
+    __builtin_amdgcn_s_waitcnt(kWaitAhead);
+    scale_q();
     __syncthreads();
-    scores(kbuf0, sa);
+    scores(kbuf(I0{}), sa);
     rowmax_update(tile_at(0), sa);
     __syncthreads();  // step 0 overwrites K buffer 0
+  } else {
+    __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);  // (the unused Q loads)
   }
 
-  // Step t: S(t+1) from K buffer (t+1)&1 interleaved with the probabilities of tile t;
-  // then O^T += V^T P^T from V buffer t&1; then stage K(t+2), V(t+1) and find the
-  // maximum of tile t+1.
-  auto step = [&](auto bufc, f32x16 (&cur)[KB], f32x16 (&nxt)[KB], int t) {
-    constexpr int BUF = decltype(bufc)::value;
-    const FA_LDS char* kb = BUF ? kbuf0 : kbuf1;
-    const FA_LDS char* vb = BUF ? vbuf1 : vbuf0;
-    // K buffer BUF held tile t (read in step t - 1), V buffer BUF ^ 1 tile t - 1 (read in
-    // step t - 1): stream K(t+2) and V(t+1) into them; they land by the end of the step.
-    stage(K, tile_at(t + 2), BUF ? kbuf1 : kbuf0);
-    stage(V, tile_at(t + 1), BUF ? vbuf0 : vbuf1);
+  // Step t: S(t+1) from K(t+1) interleaved with the probabilities of tile t; then
+  // O^T += V^T P^T from V(t); then find the maximum of tile t+1. At its start the step
+  // streams K(t+NS) into the buffer of K(t) and V(t+NS-1) into that of V(t-1), both read
+  // in step t - 1; at its end K(t+2) and V(t+1) have landed.
+  auto step = [&](auto phc, f32x16 (&cur)[KB], f32x16 (&nxt)[KB], int t) {
+    constexpr int P = decltype(phc)::value;  // t mod NS
+    const FA_LDS char* kb = kbuf(std::integral_constant<int, P + 1>{});
+    const FA_LDS char* vb = vbuf(phc);
+    // Deeper staging issues no loads once the last tile is staged (uniform): the step then
+    // waits for all. With two buffers the look-ahead tiles are clamped re-loads of the last
+    // one and every step waits for all anyway.
+    const bool more = NS == 2 || t + NS - 1 < ntiles;
+    if (more) {
+      stage(K, tile_at(t + NS), kbuf(phc));
+      stage(V, tile_at(t + NS - 1), vbuf(std::integral_constant<int, P + NS - 1>{}));
+    }
     // -- region A: score MFMAs of the next tile, exp/sum/pack of this tile. At d = 128 the
     // wave raises its issue priority over the other wave of its SIMD for this region and
     // drops it before the value products: the matrix work interleaved with its softmax then
@@ -318,12 +370,23 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_bf16_kernel(FwdArgs a) {
     }
     // -- prepare tile t+1; the staged tiles must have landed before the barrier
     if (t + 1 < ntiles) rowmax_update(tile_at(t + 1), nxt);
-    __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
+    if (more) __builtin_amdgcn_s_waitcnt(kWaitAhead);
+    else __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
     __syncthreads();
   };
-  for (int t = 0; t < ntiles; t += 2) {
+  // Unrolled over a multiple of NS (buffer phase) and of 2 (score register pair).
+  constexpr int U = NS % 2 == 0 ? NS : 2 * NS;
+  for (int t = 0; t < ntiles; t += U) {
     step(std::integral_constant<int, 0>{}, sa, sb, t);
-    if (t + 1 < ntiles) step(std::integral_constant<int, 1>{}, sb, sa, t + 1);
+    if (t + 1 < ntiles) step(std::integral_constant<int, 1 % NS>{}, sb, sa, t + 1);
+    if constexpr (U > 2) {
+      if (t + 2 < ntiles) step(std::integral_constant<int, 2 % NS>{}, sa, sb, t + 2);
+      if (t + 3 < ntiles) step(std::integral_constant<int, 3 % NS>{}, sb, sa, t + 3);
+    }
+    if constexpr (U > 4) {
+      if (t + 4 < ntiles) step(std::integral_constant<int, 4 % NS>{}, sa, sb, t + 4);
+      if (t + 5 < ntiles) step(std::integral_constant<int, 5 % NS>{}, sb, sa, t + 5);
+    }
   }
 
   const float l_tot = l_run + other_half(l_run);
@@ -451,20 +514,47 @@ __global__ __launch_bounds__(kThreads) void fwd_f32_kernel(FwdArgs a) {
 
 }  // namespace
 
+// Tile buffers of a dense bf16 forward without dropout: deeper staging where the
+// workgroups' key ranges are short (their tiles mostly come from HBM).
+constexpr int kShortStages = 3;
+constexpr int kShortMaxKeys = 4096;  // longest key range (N) that takes it
+constexpr int kShortMaxD = 64;       // d = 128 would lose a workgroup per CU to the LDS
+int fwd_stages(const FwdArgs& a, int d, bool dropout) {
+  return (!a.mask && !dropout && a.N <= kShortMaxKeys && d <= kShortMaxD) ? kShortStages : 2;
+}
+
+template <int D, bool DROP, int DG = D>
+void launch_bf16(const FwdArgs& a, dim3 grid, dim3 block, hipStream_t stream, int ns) {
+  if constexpr (!DROP && D <= kShortMaxD) {
+    if (ns == 3) {
+      hipLaunchKernelGGL((fwd_bf16_kernel<D, false, DG, 3>), grid, block, 0, stream, a);
+      return;
+    }
+    if (ns == 4) {
+      hipLaunchKernelGGL((fwd_bf16_kernel<D, false, DG, 4>), grid, block, 0, stream, a);
+      return;
+    }
+  }
+  hipLaunchKernelGGL((fwd_bf16_kernel<D, DROP, DG, 2>), grid, block, 0, stream, a);
+}
+
 hipError_t launch_fwd(const FwdArgs& a, fa_dtype dt, int d, hipStream_t stream, KernelTimer& tm,
                       bool dropout) {
   const dim3 grid((unsigned)(a.ntq * a.B * a.H)), block(kThreads);
   tm.mark(stream);
-  if (dt == FA_BF16 && dropout) {
-    if (d == 16) hipLaunchKernelGGL((fwd_bf16_kernel<32, true, 16>), grid, block, 0, stream, a);
-    else if (d == 32) hipLaunchKernelGGL((fwd_bf16_kernel<32, true>), grid, block, 0, stream, a);
-    else if (d == 64) hipLaunchKernelGGL((fwd_bf16_kernel<64, true>), grid, block, 0, stream, a);
-    else hipLaunchKernelGGL((fwd_bf16_kernel<128, true>), grid, block, 0, stream, a);
-  } else if (dt == FA_BF16) {
-    if (d == 16) hipLaunchKernelGGL((fwd_bf16_kernel<32, false, 16>), grid, block, 0, stream, a);
-    else if (d == 32) hipLaunchKernelGGL((fwd_bf16_kernel<32, false>), grid, block, 0, stream, a);
-    else if (d == 64) hipLaunchKernelGGL((fwd_bf16_kernel<64, false>), grid, block, 0, stream, a);
-    else hipLaunchKernelGGL((fwd_bf16_kernel<128, false>), grid, block, 0, stream, a);
+  if (dt == FA_BF16) {
+    const int ns = fwd_stages(a, d, dropout);
+    if (dropout) {
+      if (d == 16) launch_bf16<32, true, 16>(a, grid, block, stream, ns);
+      else if (d == 32) launch_bf16<32, true>(a, grid, block, stream, ns);
+      else if (d == 64) launch_bf16<64, true>(a, grid, block, stream, ns);
+      else launch_bf16<128, true>(a, grid, block, stream, ns);
+    } else {
+      if (d == 16) launch_bf16<32, false, 16>(a, grid, block, stream, ns);
+      else if (d == 32) launch_bf16<32, false>(a, grid, block, stream, ns);
+      else if (d == 64) launch_bf16<64, false>(a, grid, block, stream, ns);
+      else launch_bf16<128, false>(a, grid, block, stream, ns);
+    }
   } else {
     if (d == 32) hipLaunchKernelGGL(fwd_f32_kernel<32>, grid, block, 0, stream, a);
     else if (d == 64) hipLaunchKernelGGL(fwd_f32_kernel<64>, grid, block, 0, stream, a);
