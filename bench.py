@@ -41,6 +41,7 @@ workload (forward and backward separately) and writes a per-workload JSON;
 from __future__ import annotations
 
 import argparse
+import csv
 import hashlib
 import json
 import math
@@ -805,6 +806,88 @@ def report_graph(fa, w, dev, steps, warmup) -> dict:
             "eager_tflops": round(flop / eager_ms / 1e9, 1), "graph_tflops": round(flop / graph_ms / 1e9, 1)}
 
 
+GRAPH_PASS_WORKLOADS = ("bert_padded", "gpt2_causal")
+GRAPH_PASS_WARM = 5
+
+
+def graph_pass(fa, dev, steps) -> dict:
+    """Eager steps against replays of the same step captured in a HIP graph, for the short
+    workloads: four blocks per workload (eager, graph, eager, graph) of GRAPH_PASS_WARM
+    untimed and `steps` timed steps; per block the GPU time per step (HIP events) and the
+    host time to issue a step. Under a kernel trace the blocks give the kernel timeline of
+    both modes (summarize_graph_trace)."""
+    import time
+    import torch
+    from exact_tiled_attention_32_amd import workloads
+    out = {}
+    for name in GRAPH_PASS_WORKLOADS:
+        r = Runner(fa, workloads.WORKLOADS[name], dev)
+
+        def step():
+            r.fwd()
+            r.bwd()
+        warm_up(step, GRAPH_PASS_WARM)
+        s = torch.cuda.Stream()
+        s.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(s):
+            step()
+        torch.cuda.current_stream().wait_stream(s)
+        torch.cuda.synchronize()
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            step()
+        torch.cuda.synchronize()
+        blocks = []
+        for mode, fn in (("eager", step), ("graph", g.replay), ("eager", step), ("graph", g.replay)):
+            for _ in range(GRAPH_PASS_WARM):
+                fn()
+            torch.cuda.synchronize()
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a.record()
+            h0 = time.perf_counter()
+            for _ in range(steps):
+                fn()
+            h1 = time.perf_counter()
+            b.record()
+            torch.cuda.synchronize()
+            blocks.append({"mode": mode, "gpu_ms_per_step": round(a.elapsed_time(b) / steps, 4),
+                           "host_ms_per_step": round((h1 - h0) * 1e3 / steps, 4)})
+        out[name] = blocks
+        print(f"[graph-pass] {name}: " + json.dumps(blocks), flush=True)
+        del g, r
+        torch.cuda.empty_cache()
+    return out
+
+
+def summarize_graph_trace(trace_csv: str, steps: int) -> str:
+    """Markdown table of a kernel trace of `--graph-pass`: per workload and block, the median
+    kernel durations, the idle gaps inside a step and between steps, and the step span."""
+    import statistics
+    rows = [r for r in csv.DictReader(open(trace_csv)) if "fa::" in r["Kernel_Name"]]
+    rows.sort(key=lambda r: int(r["Start_Timestamp"]))
+    seq = [(int(r["Start_Timestamp"]), int(r["End_Timestamp"])) for r in rows]
+    trip = [seq[i:i + 3] for i in range(0, len(seq) - 2, 3)]  # forward, dQ, dK/dV
+    per = GRAPH_PASS_WARM + 1 + 4 * (GRAPH_PASS_WARM + steps)  # warm-up, side stream, blocks
+    lines = ["| workload | mode | forward | dQ | dK/dV | idle gap forward→dQ | idle gap between steps | step span |",
+             "|---|---|---|---|---|---|---|---|"]
+    med = lambda xs: round(statistics.median(xs) / 1000, 1)
+    for wi, name in enumerate(GRAPH_PASS_WORKLOADS):
+        st = trip[wi * per:(wi + 1) * per]
+        for blk in range(4):
+            lo = GRAPH_PASS_WARM + 1 + blk * (GRAPH_PASS_WARM + steps) + GRAPH_PASS_WARM
+            seg = st[lo:lo + steps]
+            if len(seg) < 2:
+                continue
+            dur = [[e - s for s, e in t] for t in seg]
+            gap = [max(t[1][0] - t[0][1], 0) for t in seg]
+            inter = [max(seg[i][0][0] - seg[i - 1][2][1], 0) for i in range(1, len(seg))]
+            span = [t[2][1] - t[0][0] for t in seg]
+            lines.append(f"| {name} | {'eager' if blk % 2 == 0 else 'graph'} | " +
+                         " | ".join(str(med(x)) for x in zip(*dur)) +
+                         f" | {med(gap)} | {med(inter)} | {med(span)} |")
+    return "\n".join(lines)
+
+
 def compulsory_bytes(w, phase: str) -> float:
     """Algorithmic HBM bytes of one call: forward Q, K, V read and O written once plus lse;
     backward Q, K, V, O, dO read and dQ, dK, dV written once, lse read, D written and read."""
@@ -915,12 +998,20 @@ def main():
                     help="time the step alone (no decode or packed workloads), e.g. under a kernel trace")
     ap.add_argument("--decode-only", action="store_true",
                     help="time only the key/value-cache forward on the decode workloads and print them")
+    ap.add_argument("--graph-pass", action="store_true",
+                    help="eager steps against replayed HIP-graph steps on the short workloads (four "
+                         "blocks of --steps each); prints per-block times, no metric line")
+    ap.add_argument("--summarize-graph-trace", metavar="TRACE_CSV",
+                    help="print the kernel timeline table of a traced --graph-pass (same --steps) and exit")
     ap.add_argument("--pmc-pass", action="store_true",
                     help="for rocprofv3 --pmc: one 256 MiB device copy (counter calibration), then one "
                          "untimed pass of the step; prints no metric line")
     args = ap.parse_args()
     if args.summarize_counters:
         print(summarize_counters(*args.summarize_counters))
+        return
+    if args.summarize_graph_trace:
+        print(summarize_graph_trace(args.summarize_graph_trace, args.steps))
         return
     if args.summarize_pmc:
         res = summarize_pmc(*args.summarize_pmc, os.path.join(ROOT, "profiles", "hbm_traffic.json"))
@@ -938,6 +1029,9 @@ def main():
     dev = "cuda:0"
     if args.counter_pass:
         counter_pass(fa, dev)
+        return
+    if args.graph_pass:
+        graph_pass(fa, dev, args.steps)
         return
     if args.decode_only:
         for name, w in workloads.DECODE_WORKLOADS.items():

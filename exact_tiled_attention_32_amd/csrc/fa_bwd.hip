@@ -37,10 +37,6 @@ namespace {
 constexpr int kThreads = 256;
 constexpr int kBK = kBwdKeyTile;  // keys per dK/dV workgroup (32 per wave)
 
-// Sixteen zero bytes in device memory: the source of the staging lanes that fill the
-// unused upper half of 32-wide tiles when the head dimension is 16 (never written).
-__device__ __attribute__((aligned(16))) uint32_t g_zero16[4];
-
 // ---------------------------------------------------------------------------------------
 // 1. Block-sparse only: the order in which the dK/dV workgroups take their key tiles, most
 //     kept mask blocks first. The work of a key tile is proportional to the kept blocks of
@@ -244,16 +240,22 @@ __global__ __launch_bounds__(dkdv_threads(QH), QH == 1 ? 2 : 1) void bwd_dkdv_ke
   tr_lo0 += qw0 * 2 * D;
   tr_hi0 += qw0 * 2 * D;
   int ro0 = row_off0, ko0 = kv_off0, tl0 = tr_lo0, th0 = tr_hi0;
-  // Q / dO staging by direct global -> LDS loads: each wave instruction fills 1 KB, lane
-  // i the 16 bytes at offset 16 i, so lane i fetches the chunk whose swizzled slot that
-  // is. Rows past N (last query tile only) read row N-1; they get P = 0 through the
-  // staged lse (+inf), so their values never reach a result.
+  // Q / dO staging by raw buffer -> LDS loads: each wave instruction fills 1 KB, lane i
+  // the 16 bytes at offset 16 i, so lane i fetches the chunk whose swizzled slot that is.
+  // A query tile's buffer range ends at row N, so rows past it (last query tile only)
+  // arrive as zeros; they also get P = 0 through the staged lse (+inf). The per-lane byte
+  // offsets inside a tile are fixed; only the tile's base (scalar) changes per step.
   // Lane l of DMA block c covers row (NW c + w) RPB + l / (D/8); the block rows are a
   // multiple of 16 apart, so the swizzled column is the same for every block.
   const int dma_row0 = w * RPB + l / (D / 8);
   const int dma_col = ((l % (D / 8)) ^ swz<D>(dma_row0)) * 8;
   static_assert((NW * RPB) % 16 == 0, "DMA block step must keep the swizzle");
   static_assert(NDMA >= 1 && NDMA * kMainThreads * 16 == QT, "Q / dO tile staging covers the tile");
+  int qdma_off[NDMA];
+#pragma unroll
+  for (int c = 0; c < NDMA; ++c)
+    qdma_off[c] = (DG == D || dma_col < DG) ? ((dma_row0 + c * NW * RPB) * a.rs + dma_col) * 2
+                                            : (int)0xFFFFFFF0u;  // past any range: reads zero
 
   f32x16 dkt[MD], dvt[MD];
 #pragma unroll
@@ -267,16 +269,17 @@ __global__ __launch_bounds__(dkdv_threads(QH), QH == 1 ? 2 : 1) void bwd_dkdv_ke
   auto stage_q = [&](int it, auto bufc) {
     const int q0 = it * BQ;
     FA_LDS char* qb = (FA_LDS char*)(decltype(bufc)::value ? qd1 : qd0);
+    // rows of the tile inside the slice (uniform: kept scalar, like the descriptors)
+    const int rows = __builtin_amdgcn_readfirstlane(min(max(N - q0, 0), BQ));
+    const uint32_t bytes = (uint32_t)rows * (uint32_t)(a.rs * 2);
+    const auto rq = make_rsrc(Q + (size_t)q0 * rs, bytes);
+    const auto rd = make_rsrc(dO + (size_t)q0 * rs, bytes);
 #pragma unroll
     for (int c = 0; c < NDMA; ++c) {
-      const size_t row = (size_t)min(q0 + dma_row0 + c * NW * RPB, N - 1) * rs + dma_col;
       FA_LDS char* blk = qb + (c * NW + w) * 1024;
-      // (the builtin takes a non-const pointer; without the cast the host pass silently
-      // drops the kernel's launch stub)
-      const bool live = DG == D || dma_col < DG;
-      __builtin_amdgcn_global_load_lds(live ? (void*)(Q + row) : (void*)g_zero16, (FA_LDS void*)blk, 16, 0, 0);
-      __builtin_amdgcn_global_load_lds(live ? (void*)(dO + row) : (void*)g_zero16, (FA_LDS void*)(blk + QT), 16,
-                                       0, 0);
+      const int voff = qdma_off[c];  // (a local copy: see the forward's staging)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rq, (FA_LDS void*)blk, 16, voff, 0, 0, 0);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rd, (FA_LDS void*)(blk + QT), 16, voff, 0, 0, 0);
     }
     // threads [0, BQ) stage lse, threads [BQ, 2 BQ) stage D
     const int qq = q0 + (tid % BQ);

@@ -163,3 +163,42 @@ def test_kernel_clock_arithmetic(monkeypatch):
     assert clock.kernel_ms("bwd", 0) == pytest.approx(1.5)
     assert clock.kernel_ms("bwd", 1) == pytest.approx(2.5)
     assert clock.call_ms("bwd") == pytest.approx(4.0)
+
+
+def test_summarize_graph_trace(tmp_path):
+    """The graph-pass timeline table: per block, median kernel durations and idle gaps, from
+    a synthetic kernel trace laid out as --graph-pass dispatches (warm-up, side-stream step,
+    four blocks of warm-up + timed steps per workload)."""
+    steps, warm = 4, bench.GRAPH_PASS_WARM
+    per = warm + 1 + 4 * (warm + steps)
+    rows, t = [], 0
+    for wi in range(len(bench.GRAPH_PASS_WORKLOADS)):
+        for i in range(per):
+            blk = (i - warm - 1) // (warm + steps) if i >= warm + 1 else -1
+            graph = blk in (1, 3)
+            dur = (10_000 * (wi + 1), 20_000, 30_000)      # ns
+            t += 8_000 if graph else 0                     # idle gap before each graph step
+            for k, name in enumerate(("fa::fwd_bf16_kernel", "fa::bwd_dq_kernel", "fa::bwd_dkdv_kernel")):
+                if k == 1 and not graph:
+                    t += 2_000                             # host gap inside an eager step
+                rows.append((name, t, t + dur[k]))
+                t += dur[k]
+    path = tmp_path / "trace.csv"
+    with open(path, "w") as f:
+        f.write("Kernel_Name,Start_Timestamp,End_Timestamp\n")
+        for n, s, e in rows:
+            f.write(f"{n},{s},{e}\n")
+    table = bench.summarize_graph_trace(str(path), steps).splitlines()
+    body = [ln.split("|")[1:-1] for ln in table[2:]]
+    assert len(body) == 8
+    for cells in body:
+        name, mode = cells[0].strip(), cells[1].strip()
+        vals = [float(c) for c in cells[2:]]
+        wi = bench.GRAPH_PASS_WORKLOADS.index(name)
+        assert vals[:3] == [10.0 * (wi + 1), 20.0, 30.0]
+        if mode == "graph":
+            assert vals[3] == 0.0 and vals[4] == 8.0
+            assert vals[5] == 10.0 * (wi + 1) + 50.0
+        else:
+            assert vals[3] == 2.0 and vals[4] == 0.0
+            assert vals[5] == 10.0 * (wi + 1) + 52.0
