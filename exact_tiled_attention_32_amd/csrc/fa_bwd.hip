@@ -281,11 +281,14 @@ __global__ __launch_bounds__(dkdv_threads(QH), QH == 1 ? 2 : 1) void bwd_dkdv_ke
       __builtin_amdgcn_raw_ptr_buffer_load_lds(rq, (FA_LDS void*)blk, 16, voff, 0, 0, 0);
       __builtin_amdgcn_raw_ptr_buffer_load_lds(rd, (FA_LDS void*)(blk + QT), 16, voff, 0, 0, 0);
     }
-    // threads [0, BQ) stage lse, threads [BQ, 2 BQ) stage D
-    const int qq = q0 + (tid % BQ);
-    svalid = qq < N;
-    const float* src = tid < BQ ? lse : dsum;
-    sr = src[min(qq, N - 1)];
+    // threads [0, BQ) stage lse, threads [BQ, 2 BQ) stage D (whole waves: 2 BQ is a
+    // multiple of 64, so the other waves skip this by a scalar branch)
+    if (w * 64 < 2 * BQ) {
+      const int qq = q0 + (tid % BQ);
+      svalid = qq < N;
+      const float* src = tid < BQ ? lse : dsum;
+      sr = src[min(qq, N - 1)];
+    }
   };
   auto store_stats = [&](int buf) {
     if (tid < 2 * BQ) {
@@ -343,12 +346,8 @@ __global__ __launch_bounds__(dkdv_threads(QH), QH == 1 ? 2 : 1) void bwd_dkdv_ke
     const int q0 = it * BQ;
     // buffer BUF ^ 1 was last read in step t - 1: stream the next query tile into it
     stage_q(tile_at(min(t + 1, nq - 1)), std::integral_constant<int, BUF ^ 1>{});
-    // Opaque copies of the offset bases: keeps the compiler from hoisting every derived
-    // offset out of the loop into its own register.
-    ro0 = row_off0;
-    ko0 = kv_off0;
-    tl0 = tr_lo0;
-    th0 = tr_hi0;
+    // Offset bases made opaque once per step (no copy; the value is unchanged): keeps the
+    // compiler from hoisting every derived offset out of the loop into its own register.
     asm volatile("" : "+v"(ro0), "+v"(ko0), "+v"(tl0), "+v"(th0));
     const FA_LDS char* qb = (const FA_LDS char*)(BUF ? qd1 : qd0);
     const FA_LDS char* db = qb + QT;
@@ -710,10 +709,8 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dq_kernel(BwdArgs a) {
     const int jt = tile_at(t);
     // buffer BUF ^ 1 was last read in step t - 1: stream the next tile into it
     stage(tile_at(t + 1), std::integral_constant<int, BUF ^ 1>{});
-    // opaque offset bases: keep the derived offsets from being hoisted into registers
-    ko0 = k_off0;
-    tl0 = t_lo0;
-    th0 = t_hi0;
+    // offset bases made opaque once per step (no copy): keeps the derived offsets from
+    // being hoisted into registers
     asm volatile("" : "+v"(ko0), "+v"(tl0), "+v"(th0));
     const int key0 = jt * kDqKeys;
     // A wave whose queries all lie outside the tile's window has nothing to do here.

@@ -77,7 +77,7 @@ def full_check(fa, case, dtype, backward=True, label="", sparse=None):
 # ------------------------------------------------------------------------------------------
 # sweep of small and ragged shapes
 # ------------------------------------------------------------------------------------------
-SWEEP_N = [1, 17, 64, 127, 128, 129, 300]
+SWEEP_N = [1, 17, 64, 127, 128, 129, 200, 300, 520]
 
 
 def _sweep_cases():
