@@ -170,9 +170,10 @@ class KernelClock:
 
 
 KERNEL_NAMES = {  # demangled kernel -> short name used by the bench and the traffic file
-    # (template arguments: tile width, dropout flag, head dimension in memory; for dK/dV
-    # also the query halves, 1 for the dense 4-wave layout)
-    "fwd_bf16_kernel<64, false, 64>": "fwd_d64", "fwd_bf16_kernel<128, false, 128>": "fwd_d128",
+    # (template arguments: tile width, dropout flag, head dimension in memory; for the
+    # forward also its K/V buffer count, two on these long workloads; for dK/dV the query
+    # halves, 1 for the dense 4-wave layout)
+    "fwd_bf16_kernel<64, false, 64, 2>": "fwd_d64", "fwd_bf16_kernel<128, false, 128, 2>": "fwd_d128",
     "bwd_dkdv_kernel<64, false, 64, 1>": "bwd_dkdv_d64", "bwd_dkdv_kernel<128, false, 128, 1>": "bwd_dkdv_d128",
     "bwd_dq_kernel<64, false, 64>": "bwd_dq_d64", "bwd_dq_kernel<128, false, 128>": "bwd_dq_d128",
     "kvc_split_kernel<64>": "kvc_split_d64", "kvc_split_kernel<128>": "kvc_split_d128",
@@ -826,7 +827,9 @@ def graph_pass(fa, dev, steps) -> dict:
         def step():
             r.fwd()
             r.bwd()
-        warm_up(step, GRAPH_PASS_WARM)
+        for _ in range(GRAPH_PASS_WARM):  # a fixed count: the trace summary counts dispatches
+            step()
+        torch.cuda.synchronize()
         s = torch.cuda.Stream()
         s.wait_stream(torch.cuda.current_stream())
         with torch.cuda.stream(s):
@@ -868,6 +871,9 @@ def summarize_graph_trace(trace_csv: str, steps: int) -> str:
     seq = [(int(r["Start_Timestamp"]), int(r["End_Timestamp"])) for r in rows]
     trip = [seq[i:i + 3] for i in range(0, len(seq) - 2, 3)]  # forward, dQ, dK/dV
     per = GRAPH_PASS_WARM + 1 + 4 * (GRAPH_PASS_WARM + steps)  # warm-up, side stream, blocks
+    if len(seq) != 3 * per * len(GRAPH_PASS_WORKLOADS):
+        raise ValueError(f"{len(seq)} library dispatches in the trace, expected "
+                         f"{3 * per * len(GRAPH_PASS_WORKLOADS)} for --graph-pass --steps {steps}")
     lines = ["| workload | mode | forward | dQ | dK/dV | idle gap forward→dQ | idle gap between steps | step span |",
              "|---|---|---|---|---|---|---|---|"]
     med = lambda xs: round(statistics.median(xs) / 1000, 1)
