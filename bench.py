@@ -4,8 +4,9 @@ A step is one pass of the whole hot path over the long-sequence causal workload
 (B=1, H=16, N=16384, bf16, causal, at d=64 and at d=128): for each head dimension
 the forward (O, lse) and the backward (the dQ kernel, whose prologue is the D =
 rowsum(dO o O) pre-pass, then the dK/dV kernel) through the C ABI, on inputs already
-resident in device memory. The library's per-kernel events (fa_time_next_call) give
-each kernel's time inside the timed region.
+resident in device memory. The K timed steps run bare (the metric); K more steps with the
+library's per-kernel events armed (fa_time_next_call) give each kernel's and each phase's
+time, and their step time is reported as instrumented_ms_per_step.
 
 FLOP convention: forward 4*B*H*N^2*d, halved for causal; backward 2.5x the forward
 (five products per score tile instead of two). value = FLOP per step / time per step.
@@ -167,6 +168,16 @@ class KernelClock:
         """Mean time from before the first to after the last bracketed kernel."""
         ev = self.samples.get(name, [])
         return sum(e[0].elapsed_time(e[-1]) for e in ev) / len(ev) if ev else float("nan")
+
+    def call_ms_median(self, name):
+        """Median over the calls of the time from before the first to after the last
+        bracketed kernel."""
+        ev = self.samples.get(name, [])
+        if not ev:
+            return float("nan")
+        t = sorted(e[0].elapsed_time(e[-1]) for e in ev)
+        m = len(t) // 2
+        return t[m] if len(t) % 2 else 0.5 * (t[m - 1] + t[m])
 
 
 KERNEL_NAMES = {  # demangled kernel -> short name used by the bench and the traffic file
@@ -556,20 +567,32 @@ def cpu_baseline(target_s: float = 12.0) -> dict:
 
 
 def time_step(fa, runners, steps, warmup):
+    """Exactly `warmup` untimed steps, then exactly `steps` timed steps with nothing but the
+    library calls in them (the metric), then `steps` more with the library's per-kernel
+    event markers armed (the per-kernel and per-phase figures; the markers cost the step
+    about 1 %, so they stay out of the metric). Returns (ms per bare step, ms per
+    instrumented step, the kernel clock)."""
     import torch
-    # exactly `warmup` untimed steps (the metric line's contract); at ~7 ms a step, the
-    # default 10 also bring the engine clock up
+    # at ~7 ms a step, the default 10 warm-up steps also bring the engine clock up
     for _ in range(warmup):
         for r in runners:
             r.fwd()
             r.bwd()
     torch.cuda.synchronize()
-    clock = KernelClock()
-    # the kernel clock's events are made before the timed region
-    evs = [[(KernelClock.new_events(2), KernelClock.new_events(1 + len(r.bwd_kernels))) for r in runners]
-           for _ in range(steps)]
     t0 = torch.cuda.Event(enable_timing=True)
     t1 = torch.cuda.Event(enable_timing=True)
+    t0.record()
+    for _ in range(steps):
+        for r in runners:
+            r.fwd()
+            r.bwd()
+    t1.record()
+    torch.cuda.synchronize()
+    bare_ms = t0.elapsed_time(t1) / steps
+    clock = KernelClock()
+    # the kernel clock's events are made before the instrumented region
+    evs = [[(KernelClock.new_events(2), KernelClock.new_events(1 + len(r.bwd_kernels))) for r in runners]
+           for _ in range(steps)]
     torch.cuda.synchronize()
     t0.record()
     for i in range(steps):
@@ -580,7 +603,7 @@ def time_step(fa, runners, steps, warmup):
             r.bwd()
     t1.record()
     torch.cuda.synchronize()
-    return t0.elapsed_time(t1) / steps, clock
+    return bare_ms, t0.elapsed_time(t1) / steps, clock
 
 
 def sample_clock(fn, seconds: float = 3.0) -> dict:
@@ -915,11 +938,13 @@ def phase_figures(ms: float, flop: float, nbytes: float) -> dict:
             "hbm_gbs": round(nbytes / ms / 1e6, 1), "hbm_frac": round(nbytes / ms / 1e6 / PEAK_HBM_GBS, 4)}
 
 
-def report_config(fa, w, dev, steps=20, warmup=3) -> dict:
-    """Forward and backward of one named workload, timed separately (whole calls, HIP events
-    on the launch stream), with each kernel's share from the library's per-kernel events.
-    TFLOP/s by the headline convention (dense N^2, halved for causal; kept blocks for a
-    block mask), and by allowed pairs for key padding; HBM GB/s of the compulsory bytes."""
+def report_config(fa, w, dev, steps=50, warmup=3) -> dict:
+    """Forward and backward of one named workload, timed separately: `steps` back-to-back
+    whole calls between two HIP events on the launch stream (the mean, `ms`), then `steps`
+    more with the library's per-kernel events armed (each kernel's mean, and the median of
+    the calls' first-to-last-kernel time, `median_call_ms`). TFLOP/s by the headline
+    convention (dense N^2, halved for causal; kept blocks for a block mask), and by allowed
+    pairs for key padding; HBM GB/s of the compulsory bytes."""
     import torch
     r = Runner(fa, w, dev)
     ff = attn_flops(w, r.kept)
@@ -937,16 +962,20 @@ def report_config(fa, w, dev, steps=20, warmup=3) -> dict:
     for phase in ("fwd", "bwd") if w.backward else ("fwd",):
         fn = r.fwd if phase == "fwd" else r.bwd
         warm_up(fn, warmup)
-        clock = KernelClock()
-        evs = [KernelClock.new_events(1 + len(kernels[phase])) for _ in range(steps)]
         a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         a.record()
-        for e in evs:
-            clock.arm(fa, phase, e)
+        for _ in range(steps):
             fn()
         b.record()
         torch.cuda.synchronize()
         ms = a.elapsed_time(b) / steps
+        clock = KernelClock()
+        evs = [KernelClock.new_events(1 + len(kernels[phase])) for _ in range(steps)]
+        torch.cuda.synchronize()
+        for e in evs:
+            clock.arm(fa, phase, e)
+            fn()
+        torch.cuda.synchronize()
         mult = 2.5 if phase == "bwd" else 1.0
         fig = phase_figures(ms, ff * mult, compulsory_bytes(w, phase))
         if kept_ff is not None:
@@ -954,6 +983,7 @@ def report_config(fa, w, dev, steps=20, warmup=3) -> dict:
             fig["frac_of_peak_kept_pairs"] = round(kept_ff * mult / ms / 1e9 / PEAK_BF16_TFLOPS, 4)
         if w.dtype == "f32":
             fig["us"] = round(ms * 1e3, 2)
+        fig["median_call_ms"] = round(clock.call_ms_median(phase), 4)
         for i, kname in enumerate(kernels[phase]):
             fig[kname + "_kernel_ms"] = round(clock.kernel_ms(phase, i), 4)
         res[phase] = fig
@@ -1055,7 +1085,7 @@ def main():
         torch.cuda.synchronize()
         print(f"pmc pass done: calibration copy of {CALIBRATION_BYTES} bytes, one step", flush=True)
         return
-    ms, clock = time_step(fa, runners, args.steps, args.warmup)
+    ms, ms_instr, clock = time_step(fa, runners, args.steps, args.warmup)
     step_flop = sum(3.5 * attn_flops(r.w) for r in runners)
     value = step_flop / (ms * 1e-3) / 1e12
 
@@ -1093,7 +1123,8 @@ def main():
             "vs_baseline": None, "dtype": "bf16", "data": "synthetic (iid N(0,1), seeded)",
             "config": {"workload": "long-sequence causal attention fwd+bwd, B=1 H=16 N=16384, d=64 and d=128",
                        "B": 1, "H": 16, "N": 16384, "d": [64, 128], "causal": True},
-            "frac_of_peak": round(value / PEAK_BF16_TFLOPS, 4), "phases": phases, "kernels": kern,
+            "frac_of_peak": round(value / PEAK_BF16_TFLOPS, 4),
+            "instrumented_ms_per_step": round(ms_instr, 4), "phases": phases, "kernels": kern,
             "roofline": roofline}
 
     def one_step():
