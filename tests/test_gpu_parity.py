@@ -103,6 +103,23 @@ def test_sweep_bf16(gpu_lib, name, params):
     full_check(gpu_lib, case, "bf16", label=name)
 
 
+# The dense bf16 forward without dropout stages three K/V tiles deep up to N = 4096 at
+# d <= 64 and two deep beyond (and at d = 128): both sides of that switch, with ragged ends.
+STAGE_SWITCH = [
+    ("stages-N4096-d64-causal", 4096, 64, True, None),
+    ("stages-N4097-d64-causal", 4097, 64, True, None),
+    ("stages-N4096-d32-padded", 4096, 32, False, [3001]),
+    ("stages-N4097-d32-padded", 4097, 32, False, [4097]),
+    ("stages-N4096-d16-causal", 4096, 16, True, None),
+]
+
+
+@pytest.mark.parametrize("name,N,d,causal,kv", STAGE_SWITCH, ids=[c[0] for c in STAGE_SWITCH])
+def test_stage_depth_switch(gpu_lib, name, N, d, causal, kv):
+    case = workloads.make_case(1, 2, N, d, seed=zlib.crc32(name.encode()) % 10000, causal=causal, kv_len=kv)
+    full_check(gpu_lib, case, "bf16", label=name)
+
+
 def _synthetic_mask(nb, seed):
     rng = np.random.default_rng(seed)
     m = (rng.random((nb, nb)) < 0.5).astype(np.uint8)
