@@ -296,3 +296,29 @@ def kvc_noalloc(lib, dt=fa.FA_BF16, B=1, H=1, Nq=1, Nk=256, d=64, q=P, o=P, lse=
 def test_kvcache_noalloc_rejects(lib, kwargs, status):
     assert kvc_noalloc(lib, **kwargs) == status
     assert lib.fa_last_error().decode()
+
+
+def test_last_error_is_per_thread(lib):
+    """fa_last_error keeps each thread's own reason: two threads that fail validation in
+    different ways, interleaved, always read back their own message (validation only; no
+    device is touched)."""
+    import threading
+    results = {}
+    barrier = threading.Barrier(2)
+
+    def worker(name, kwargs, pattern):
+        barrier.wait()
+        ok = True
+        for _ in range(300):
+            st = fwd(lib, **kwargs)
+            msg = lib.fa_last_error().decode()
+            ok &= st != fa.FA_OK and re.search(pattern, msg) is not None
+        results[name] = ok
+
+    t1 = threading.Thread(target=worker, args=("sizes", dict(B=0), r"sizes must be positive"))
+    t2 = threading.Thread(target=worker, args=("headdim", dict(d=96), r"head dimension 96"))
+    t1.start()
+    t2.start()
+    t1.join()
+    t2.join()
+    assert results == {"sizes": True, "headdim": True}
