@@ -54,6 +54,7 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 PEAK_BF16_TFLOPS = 2500.0  # MI355X dense bf16 MFMA
+PEAK_CLOCK_MHZ = 2400.0    # the engine clock that peak assumes
 DROPOUT_P, DROPOUT_SEED = 0.1, 1234  # the dropout report's probability and seed
 PEAK_HBM_GBS = 8000.0
 METRIC = "attention fwd+bwd TFLOP/s (bf16, causal) and % of MI355X bf16 MFMA peak"
@@ -1132,6 +1133,13 @@ def main():
             r.fwd()
             r.bwd()
     line["clock"] = sample_clock(one_step, 3.0)
+    mhz = line["clock"].get("sclk_mhz_mean")
+    if mhz:
+        # context only: the matrix rate the sampled clock allows, and the dominant kernel
+        # against it (the roofline fraction stays against the published peak)
+        at_clock = PEAK_BF16_TFLOPS * mhz / PEAK_CLOCK_MHZ
+        line["clock"]["bf16_peak_tflops_at_mean_clock"] = round(at_clock, 1)
+        line["roofline"]["frac_at_mean_clock"] = round(roofline["achieved"] / at_clock, 4)
     if not args.step_only:
         # every named workload, forward and backward separately (the step's own two from the
         # step above)
