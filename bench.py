@@ -405,6 +405,59 @@ def summarize_counters(sq_csv, fetch_csv, write_csv, trace_csv, valu_csv=None) -
     return "\n".join(lines)
 
 
+STALL_COUNTERS_A = ("SQ_WAVE_CYCLES", "SQ_WAIT_ANY", "SQ_WAIT_INST_ANY", "SQ_WAIT_INST_LDS", "SQ_ACTIVE_INST_ANY",
+                    "SQ_VALU_MFMA_COEXEC_CYCLES", "SQ_BUSY_CU_CYCLES", "SQ_VALU_MFMA_BUSY_CYCLES")
+STALL_COUNTERS_B = ("SQ_WAVE_CYCLES", "SQ_ACTIVE_INST_LDS", "SQ_ACTIVE_INST_VALU", "SQ_ACTIVE_INST_SCA",
+                    "SQ_ACTIVE_INST_MISC", "SQ_INST_LEVEL_LDS", "SQ_INSTS_LDS", "SQ_ACTIVE_INST_VMEM")
+
+
+def summarize_stalls(a_csv, b_csv) -> str:
+    """Markdown table per (workload, kernel) of the second round of `--counter-pass`, from two
+    counter files taken with STALL_COUNTERS_A and STALL_COUNTERS_B: where the waves' cycles go
+    (issuing an instruction, waiting for a wait count or the barrier, or holding an instruction
+    that does not issue), the share of MFMA-busy cycles in which a vector instruction issued
+    as well, and the cycles spent on vector, LDS and scalar instructions. Every share is of
+    SQ_WAVE_CYCLES of the same run (the SQ_WAIT_* and SQ_ACTIVE_INST_* counters are in the
+    same units)."""
+    import csv
+    from exact_tiled_attention_32_amd import workloads
+
+    def load(path):
+        per = {}
+        for row in csv.DictReader(open(path)):
+            if "fa::" not in row["Kernel_Name"]:
+                continue
+            d = per.setdefault(int(row["Dispatch_Id"]), {"name": row["Kernel_Name"]})
+            d[row["Counter_Name"]] = d.get(row["Counter_Name"], 0.0) + float(row["Counter_Value"])
+        return [per[k] for k in sorted(per)]
+
+    A, B = load(a_csv), load(b_csv)
+    seq = counter_sequence(workloads)
+    for what, rows, names in (("A", A, STALL_COUNTERS_A), ("B", B, STALL_COUNTERS_B)):
+        if len(rows) != len(seq):
+            raise RuntimeError(f"{what}: {len(rows)} library dispatches, expected {len(seq)}")
+        missing = [n for n in names if any(n not in r for r in rows)]
+        if missing:
+            raise RuntimeError(f"{what}: counters missing: {missing}")
+    pct = lambda x: f"{100 * x:.1f} %"
+    lines = ["| workload | kernel | MFMA busy | issuing | waiting (wait count, barrier) | ready, not issued "
+             "| LDS issue wait | vector co-issue / MFMA busy | vector | LDS | scalar |",
+             "|---|---|---|---|---|---|---|---|---|---|---|"]
+    for i in range(len(seq) // 2, len(seq)):
+        wname, kname = seq[i]
+        a, b = A[i], B[i]
+        if kname.split("<")[0] not in a["name"] or kname.split("<")[0] not in b["name"]:
+            raise RuntimeError(f"dispatch {i}: expected {kname}, found {a['name']} / {b['name']}")
+        wa, wb = max(a["SQ_WAVE_CYCLES"], 1.0), max(b["SQ_WAVE_CYCLES"], 1.0)
+        mfma = a["SQ_VALU_MFMA_BUSY_CYCLES"] / max(4.0 * a["SQ_BUSY_CU_CYCLES"], 1.0)
+        coex = a["SQ_VALU_MFMA_COEXEC_CYCLES"] / max(a["SQ_VALU_MFMA_BUSY_CYCLES"], 1.0)
+        lines.append(f"| {wname} | {kname} | {pct(mfma)} | {pct(a['SQ_ACTIVE_INST_ANY'] / wa)} | "
+                     f"{pct(a['SQ_WAIT_ANY'] / wa)} | {pct(a['SQ_WAIT_INST_ANY'] / wa)} | "
+                     f"{pct(a['SQ_WAIT_INST_LDS'] / wa)} | {pct(coex)} | {pct(b['SQ_ACTIVE_INST_VALU'] / wb)} | "
+                     f"{pct(b['SQ_ACTIVE_INST_LDS'] / wb)} | {pct(b['SQ_ACTIVE_INST_SCA'] / wb)} |")
+    return "\n".join(lines)
+
+
 def kernel_source_digest() -> str:
     """Digest of the step kernels' code: comments and whitespace are left out, so that
     only a change of the code itself invalidates counter data taken on it."""
@@ -1031,6 +1084,9 @@ def main():
     ap.add_argument("--summarize-counters", nargs="+", metavar="CSV",
                     help="SQ_CSV FETCH_CSV WRITE_CSV TRACE_CSV [VALU_CSV]: print the per-kernel counter table "
                          "of a --counter-pass and exit")
+    ap.add_argument("--summarize-stalls", nargs=2, metavar=("A_CSV", "B_CSV"),
+                    help="print the per-kernel wave-cycle table of a --counter-pass taken with the "
+                         "STALL_COUNTERS_A and STALL_COUNTERS_B sets, and exit")
     ap.add_argument("--step-only", action="store_true",
                     help="time the step alone (no decode or packed workloads), e.g. under a kernel trace")
     ap.add_argument("--decode-only", action="store_true",
@@ -1046,6 +1102,9 @@ def main():
     args = ap.parse_args()
     if args.summarize_counters:
         print(summarize_counters(*args.summarize_counters))
+        return
+    if args.summarize_stalls:
+        print(summarize_stalls(*args.summarize_stalls))
         return
     if args.summarize_graph_trace:
         print(summarize_graph_trace(args.summarize_graph_trace, args.steps))

@@ -202,3 +202,44 @@ def test_summarize_graph_trace(tmp_path):
         else:
             assert vals[3] == 2.0 and vals[4] == 0.0
             assert vals[5] == 10.0 * (wi + 1) + 52.0
+
+
+def test_summarize_stalls(tmp_path):
+    """The wave-cycle table of a --counter-pass: synthetic counter files laid out as its
+    library dispatches (two rounds), each counter set to a value that makes every share known;
+    a missing dispatch is an error."""
+    seq = bench.counter_sequence(workloads)
+
+    def write(path, names, values, drop_last=False):
+        rows = seq[:-1] if drop_last else seq
+        with open(path, "w") as f:
+            f.write("Dispatch_Id,Kernel_Name,Counter_Name,Counter_Value\n")
+            f.write("0,__amd_rocclr_copyBuffer,SQ_WAVE_CYCLES,1\n")  # not a library kernel
+            for i, (_, k) in enumerate(rows):
+                for n in names:
+                    f.write(f"{i + 1},void fa::(anonymous namespace)::{k}(fa::Args),{n},{values[n](i)}\n")
+
+    a_vals = {"SQ_WAVE_CYCLES": lambda i: 1000.0, "SQ_WAIT_ANY": lambda i: 200.0,
+              "SQ_WAIT_INST_ANY": lambda i: 450.0, "SQ_WAIT_INST_LDS": lambda i: 90.0,
+              "SQ_ACTIVE_INST_ANY": lambda i: 350.0, "SQ_VALU_MFMA_COEXEC_CYCLES": lambda i: 60.0,
+              "SQ_BUSY_CU_CYCLES": lambda i: 100.0, "SQ_VALU_MFMA_BUSY_CYCLES": lambda i: 240.0 + i}
+    b_vals = {"SQ_WAVE_CYCLES": lambda i: 2000.0, "SQ_ACTIVE_INST_LDS": lambda i: 160.0,
+              "SQ_ACTIVE_INST_VALU": lambda i: 400.0, "SQ_ACTIVE_INST_SCA": lambda i: 120.0,
+              "SQ_ACTIVE_INST_MISC": lambda i: 1.0, "SQ_INST_LEVEL_LDS": lambda i: 1.0,
+              "SQ_INSTS_LDS": lambda i: 1.0, "SQ_ACTIVE_INST_VMEM": lambda i: 1.0}
+    a, b = tmp_path / "a.csv", tmp_path / "b.csv"
+    write(a, bench.STALL_COUNTERS_A, a_vals)
+    write(b, bench.STALL_COUNTERS_B, b_vals)
+    table = bench.summarize_stalls(str(a), str(b)).splitlines()
+    body = [[c.strip() for c in ln.split("|")[1:-1]] for ln in table[2:]]
+    half = len(seq) // 2
+    assert len(body) == len(seq) - half
+    for j, cells in enumerate(body):
+        i = half + j
+        assert (cells[0], cells[1]) == seq[i]
+        assert cells[2] == f"{100 * (240.0 + i) / 400.0:.1f} %"  # MFMA busy over 4 SIMDs
+        assert cells[3:8] == ["35.0 %", "20.0 %", "45.0 %", "9.0 %", f"{100 * 60.0 / (240.0 + i):.1f} %"]
+        assert cells[8:] == ["20.0 %", "8.0 %", "6.0 %"]
+    write(b, bench.STALL_COUNTERS_B, b_vals, drop_last=True)
+    with pytest.raises(RuntimeError, match="library dispatches"):
+        bench.summarize_stalls(str(a), str(b))
