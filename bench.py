@@ -184,10 +184,9 @@ class KernelClock:
 KERNEL_NAMES = {  # demangled kernel -> short name used by the bench and the traffic file
     # (template arguments: tile width, dropout flag, head dimension in memory; for the
     # forward also its K/V buffer count, two on these long workloads; for dK/dV the query
-    # halves, 1 for the dense 4-wave layout, the Q | dO buffer count, two on these long
-    # workloads, and the query-block override, 0 for none)
+    # halves, 1 for the dense 4-wave layout, and the query-block override, 0 for none)
     "fwd_bf16_kernel<64, false, 64, 2>": "fwd_d64", "fwd_bf16_kernel<128, false, 128, 2>": "fwd_d128",
-    "bwd_dkdv_kernel<64, false, 64, 1, 2, 0>": "bwd_dkdv_d64", "bwd_dkdv_kernel<128, false, 128, 1, 2, 0>": "bwd_dkdv_d128",
+    "bwd_dkdv_kernel<64, false, 64, 1, 0>": "bwd_dkdv_d64", "bwd_dkdv_kernel<128, false, 128, 1, 0>": "bwd_dkdv_d128",
     "bwd_dq_kernel<64, false, 64>": "bwd_dq_d64", "bwd_dq_kernel<128, false, 128>": "bwd_dq_d128",
     "kvc_split_kernel<64>": "kvc_split_d64", "kvc_split_kernel<128>": "kvc_split_d128",
     "kvc_merge_kernel<64>": "kvc_merge_d64", "kvc_merge_kernel<128>": "kvc_merge_d128",

@@ -113,8 +113,6 @@ __global__ __launch_bounds__(kThreads) void bwd_order_kernel(const uint8_t* __re
 // ---------------------------------------------------------------------------------------
 // s_waitcnt immediate for vmcnt(0), expcnt and lgkmcnt left free (gfx9 encoding).
 constexpr int kWaitVmcnt0 = 0x0F70;
-// s_waitcnt immediate for vmcnt(n) (n < 64: low four bits at [3:0], high two at [15:14]).
-constexpr int wait_vmcnt(int n) { return kWaitVmcnt0 | (n & 0xF) | ((n >> 4) << 14); }
 
 // Waves of a key group (32 keys) that split each query step between them (QH). With one,
 // a workgroup is 4 waves and two workgroups share a CU, so the two waves of a SIMD belong
@@ -157,20 +155,16 @@ __device__ int build_qtile_list(uint16_t* list, int* wcount, const uint8_t* mask
 }
 
 // DG: head dimension in memory; D: tile width (16 runs on 32-wide tiles, upper half zero).
-// NSQ: Q | dO buffers. With two, the loads of query tile t + 1 are issued at the start of
-// step t; that suffices when the tiles come from L2 (long sequences: a query tile is read by
-// every key tile of its head). Short sequences read them from HBM, whose latency is several
-// steps there, and use three: tile t + 2 is issued in step t and stays in flight across the
-// step's barrier, its row statistics a step later, with one 32-query block per step at
-// d = 64 (QBWO) so that two workgroups still fit in a CU. Those serve dense launches only
-// (no tile list).
-template <int D, bool DROP, int DG = D, int QH = dkdv_halves<D, DROP>(), int NSQ = 2, int QBWO = 0>
+// QBWO: 32-query blocks per wave and step when not the default (0). Short sequences at
+// d = 64 (dense, no dropout) take one instead of two, without the block-sparse tile list:
+// 48 KB of LDS and 168 registers, so that three workgroups share a CU instead of two and a
+// launch of up to three workgroups per CU is resident at once.
+template <int D, bool DROP, int DG = D, int QH = dkdv_halves<D, DROP>(), int QBWO = 0>
 __global__ __launch_bounds__(dkdv_threads(QH), QH == 1 ? 2 : 1) void bwd_dkdv_kernel(BwdArgs a) {
   static_assert(DG == D || (D == 32 && DG == 16), "narrow heads run on 32-wide tiles");
   static_assert(QH == 1 || QH == 2, "one or two query halves");
   static_assert(QH == 2 || dkdv_halves<D, DROP>() == 1, "this variant needs the 8-wave layout");
-  static_assert((NSQ == 2 || NSQ == 3) && (NSQ == 2 || QH == 1), "two or three Q | dO buffers");
-  constexpr bool LIST = NSQ == 2;  // block-sparse query-tile list
+  constexpr bool LIST = QBWO == 0;  // block-sparse query-tile list
   constexpr int kMainThreads = dkdv_threads(QH);
   constexpr int NW = 4 * QH;                  // waves per workgroup
   constexpr int KSG = (DG + 15) / 16;  // k-steps that carry data
@@ -191,14 +185,8 @@ __global__ __launch_bounds__(dkdv_threads(QH), QH == 1 ? 2 : 1) void bwd_dkdv_ke
   // touch the other, and does not wait for them before reading it.
   __shared__ __attribute__((aligned(16))) char qd0[2 * QT];
   __shared__ __attribute__((aligned(16))) char qd1[2 * QT];
-  __shared__ __attribute__((aligned(16))) char qd2[NSQ > 2 ? 2 * QT : 16];
   __shared__ __attribute__((aligned(16))) char kvt[KVT];
-  __shared__ __attribute__((aligned(16))) float stats[NSQ][2][BQ];  // [buf][lse2 | D][row]
-  // with three buffers, the raw lse | D rows of each buffer's tile, staged like the tiles
-  // (one array each)
-  __shared__ __attribute__((aligned(16))) float rst0[NSQ > 2 ? 2 * BQ : 1];
-  __shared__ __attribute__((aligned(16))) float rst1[NSQ > 2 ? 2 * BQ : 1];
-  __shared__ __attribute__((aligned(16))) float rst2[NSQ > 2 ? 2 * BQ : 1];
+  __shared__ __attribute__((aligned(16))) float stats[2][2][BQ];  // [buf][lse2 | D][row]
   __shared__ uint16_t qlist[LIST ? kMaxTileList : 1];
   __shared__ int wcount[8];
   FA_LDS char* const kt = (FA_LDS char*)kvt;  // (unused when K is in registers)
@@ -285,22 +273,9 @@ __global__ __launch_bounds__(dkdv_threads(QH), QH == 1 ? 2 : 1) void bwd_dkdv_ke
 
   float sr = 0.f;
   bool svalid = false;
-  // Buffer j mod NSQ (a compile-time index) and, with three buffers, its raw statistics.
-  auto qbuf = [&](auto jc) {
-    constexpr int J = decltype(jc)::value % NSQ;
-    if constexpr (J == 0) return (FA_LDS char*)qd0;
-    else if constexpr (J == 1) return (FA_LDS char*)qd1;
-    else return (FA_LDS char*)qd2;
-  };
-  auto rbuf = [&](auto jc) {
-    constexpr int J = decltype(jc)::value % NSQ;
-    if constexpr (J == 0) return (FA_LDS float*)rst0;
-    else if constexpr (J == 1) return (FA_LDS float*)rst1;
-    else return (FA_LDS float*)rst2;
-  };
   auto stage_q = [&](int it, auto bufc) {
     const int q0 = it * BQ;
-    FA_LDS char* qb = qbuf(bufc);
+    FA_LDS char* qb = (FA_LDS char*)(decltype(bufc)::value ? qd1 : qd0);
     // rows of the tile inside the slice (uniform: kept scalar, like the descriptors)
     const int rows = __builtin_amdgcn_readfirstlane(min(max(N - q0, 0), BQ));
     const uint32_t bytes = (uint32_t)rows * (uint32_t)(a.rs * 2);
@@ -315,40 +290,11 @@ __global__ __launch_bounds__(dkdv_threads(QH), QH == 1 ? 2 : 1) void bwd_dkdv_ke
     }
     // threads [0, BQ) stage lse, threads [BQ, 2 BQ) stage D (whole waves: 2 BQ is a
     // multiple of 64, so the other waves skip this by a scalar branch)
-    if constexpr (NSQ == 2) {
-      if (w * 64 < 2 * BQ) {
-        const int qq = q0 + (tid % BQ);
-        svalid = qq < N;
-        const float* src = tid < BQ ? lse : dsum;
-        sr = src[min(qq, N - 1)];
-      }
-    }
-  };
-  // Three buffers: the raw row statistics of query tile `it` into buffer J's raw array by
-  // direct buffer -> LDS loads (rows past N arrive as zeros), thread i writing element i,
-  // so that the same wait counts as the tiles' cover them (a load into a register makes the
-  // compiler wait for every load in flight before its use); published by store_stats_ring.
-  auto load_stats_ring = [&](int it, auto bufc) {
     if (w * 64 < 2 * BQ) {
-      const int q0 = it * BQ;
-      const uint32_t bytes = (uint32_t)__builtin_amdgcn_readfirstlane(min(max(N - q0, 0), BQ)) * 4u;
-      FA_LDS float* dst = rbuf(bufc) + 64 * w;  // lane l writes element 64 w + l = tid
-      const int voff = (tid % BQ) * 4;
-      if (tid < BQ)
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(make_rsrc(lse + q0, bytes), (FA_LDS void*)dst, 4, voff, 0, 0, 0);
-      else
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(make_rsrc(dsum + q0, bytes), (FA_LDS void*)dst, 4, voff, 0, 0, 0);
-    }
-  };
-  auto store_stats_ring = [&](int it, auto bufc) {
-    constexpr int J = decltype(bufc)::value % NSQ;
-    if (tid < 2 * BQ) {
-      const float r = rbuf(bufc)[tid];
-      const bool valid = it * BQ + tid % BQ < N;
-      float v;
-      if (tid < BQ) v = (!valid || r == kNegInf) ? __builtin_inff() : r * kLog2e;  // as store_stats
-      else v = valid ? r : 0.f;
-      stats[J][tid / BQ][tid % BQ] = v;
+      const int qq = q0 + (tid % BQ);
+      svalid = qq < N;
+      const float* src = tid < BQ ? lse : dsum;
+      sr = src[min(qq, N - 1)];
     }
   };
   auto store_stats = [&](int buf) {
@@ -363,10 +309,8 @@ __global__ __launch_bounds__(dkdv_threads(QH), QH == 1 ? 2 : 1) void bwd_dkdv_ke
       stats[buf][tid / BQ][tid % BQ] = v;
     }
   };
-  // Wait for this wave's staging loads before the barrier that publishes the staged tile
-  // (with three buffers: all but the newest tile's, issued after the next tile's statistics).
+  // Wait for this wave's staging loads before the barrier that publishes the staged tile.
   auto wait_loads = [&]() { __builtin_amdgcn_s_waitcnt(kWaitVmcnt0); };
-  auto wait_ahead = [&]() { __builtin_amdgcn_s_waitcnt(wait_vmcnt(2 * NDMA)); };
   // Query tiles are visited last-first.
   auto tile_at = [&](int t) {
     if constexpr (LIST) return a.mask ? __builtin_amdgcn_readfirstlane((int)qlist[nq - 1 - t]) : i0 + nq - 1 - t;
@@ -382,12 +326,8 @@ __global__ __launch_bounds__(dkdv_threads(QH), QH == 1 ? 2 : 1) void bwd_dkdv_ke
       kf[ks] = key < N ? __builtin_bit_cast(bf16x8, gload16(krow + 16 * ks)) : bf16x8{};
   }
   stage_q(nq > 0 ? tile_at(0) : 0, std::integral_constant<int, 0>{});
-  if constexpr (NSQ > 2) {  // the first tile's statistics and the second tile
-    load_stats_ring(nq > 0 ? tile_at(0) : 0, std::integral_constant<int, 0>{});
-    if (nq > 1) stage_q(tile_at(1), std::integral_constant<int, 1>{});
-  }
   // The V tile, and the K tile unless K is held in registers, stay in LDS for the whole
-  // kernel (rows past N are zero). Requested after the first query tiles' staging, so that
+  // kernel (rows past N are zero). Requested after the first query tile's staging, so that
   // the prologue waits for one memory latency, not two.
 #pragma unroll
   for (int c = 0; c < KCH; ++c) {
@@ -404,30 +344,20 @@ __global__ __launch_bounds__(dkdv_threads(QH), QH == 1 ? 2 : 1) void bwd_dkdv_ke
     lds_store16(vt + tile_off<D>(row, col), ok ? vv : u32x4{});
   }
   wait_loads();
-  if constexpr (NSQ == 2) store_stats(0);
-  else store_stats_ring(nq > 0 ? tile_at(0) : 0, std::integral_constant<int, 0>{});
+  store_stats(0);
   __syncthreads();
   asm volatile("" ::: "memory");
 
   auto step = [&](auto bufc, int t) {
-    constexpr int BUF = decltype(bufc)::value;  // t mod NSQ
+    constexpr int BUF = decltype(bufc)::value;
     const int it = tile_at(t);
     const int q0 = it * BQ;
-    bool more = true;
-    if constexpr (NSQ == 2) {
-      // buffer BUF ^ 1 was last read in step t - 1: stream the next query tile into it
-      stage_q(tile_at(min(t + 1, nq - 1)), std::integral_constant<int, BUF ^ 1>{});
-    } else {
-      // the next tile's statistics, then tile t + 2 into buffer (t + 2) mod 3, last read in
-      // step t - 1 (none once the last tile is staged)
-      more = t + 2 < nq;
-      if (t + 1 < nq) load_stats_ring(tile_at(t + 1), std::integral_constant<int, BUF + 1>{});
-      if (more) stage_q(tile_at(t + 2), std::integral_constant<int, BUF + 2>{});
-    }
+    // buffer BUF ^ 1 was last read in step t - 1: stream the next query tile into it
+    stage_q(tile_at(min(t + 1, nq - 1)), std::integral_constant<int, BUF ^ 1>{});
     // Offset bases made opaque once per step (no copy; the value is unchanged): keeps the
     // compiler from hoisting every derived offset out of the loop into its own register.
     asm volatile("" : "+v"(ro0), "+v"(ko0), "+v"(tl0), "+v"(th0));
-    const FA_LDS char* qb = qbuf(bufc);
+    const FA_LDS char* qb = (const FA_LDS char*)(BUF ? qd1 : qd0);
     const FA_LDS char* db = qb + QT;
 
     // S = Q K^T and dP = dO V^T: the wave's QBW query blocks x its 32 keys.
@@ -556,31 +486,14 @@ __global__ __launch_bounds__(dkdv_threads(QH), QH == 1 ? 2 : 1) void bwd_dkdv_ke
       dkt[md] = mfma32(to[j & 1].q, sb[s4], dkt[md]);
     }
     // Wait for the staged tile, publish it and its statistics.
-    if constexpr (NSQ == 2) {
-      wait_loads();
-      store_stats(BUF ^ 1);
-      __syncthreads();
-      asm volatile("" ::: "memory");
-    } else {
-      // tile t + 2's loads stay in flight: a barrier that waits only for LDS operations
-      // (__syncthreads' workgroup fence would wait for every load)
-      if (more) wait_ahead();
-      else wait_loads();
-      if (t + 1 < nq) store_stats_ring(tile_at(t + 1), std::integral_constant<int, BUF + 1>{});
-      lds_barrier();
-    }
+    wait_loads();
+    store_stats(BUF ^ 1);
+    __syncthreads();
+    asm volatile("" ::: "memory");
   };
-  if constexpr (NSQ == 2) {
-    for (int t = 0; t < nq; t += 2) {
-      step(std::integral_constant<int, 0>{}, t);
-      if (t + 1 < nq) step(std::integral_constant<int, 1>{}, t + 1);
-    }
-  } else {
-    for (int t = 0; t < nq; t += 3) {
-      step(std::integral_constant<int, 0>{}, t);
-      if (t + 1 < nq) step(std::integral_constant<int, 1>{}, t + 1);
-      if (t + 2 < nq) step(std::integral_constant<int, 2>{}, t + 2);
-    }
+  for (int t = 0; t < nq; t += 2) {
+    step(std::integral_constant<int, 0>{}, t);
+    if (t + 1 < nq) step(std::integral_constant<int, 1>{}, t + 1);
   }
 
   wait_loads();  // the last step's look-ahead staging must land before LDS is reused
@@ -917,10 +830,10 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dq_kernel(BwdArgs a) {
 
 }  // namespace
 
-// Dense dK/dV launches without dropout that stage query tiles three deep: head dimensions
-// up to 64 and sequences up to 4096 rows, whose query tiles mostly come from HBM.
+// Dense dK/dV launches without dropout at d = 64 up to this many rows take the three-per-CU
+// layout (one 32-query block per wave and step): at these lengths a causal or padded launch
+// holds at most three workgroups per CU, so all of them run from the start.
 constexpr int kShortBwdMaxQueries = 4096;
-constexpr int kShortBwdMaxD = 64;
 
 hipError_t launch_bwd(const BwdArgs& a, int d, hipStream_t stream, KernelTimer& tm) {
   const dim3 block(kThreads);
@@ -961,14 +874,10 @@ hipError_t launch_bwd(const BwdArgs& a, int d, hipStream_t stream, KernelTimer& 
     else if (d == 32) dkdv(bwd_dkdv_kernel<32, false, 32, 2>, 2);
     else if (d == 64) dkdv(bwd_dkdv_kernel<64, false, 64, 2>, 2);
     else dkdv(bwd_dkdv_kernel<128, false, 128, 2>, 2);
-  } else if (d <= kShortBwdMaxD && a.N <= kShortBwdMaxQueries) {
-    // short sequences: query tiles staged two steps ahead (see bwd_dkdv_kernel)
-    if (d == 16) dkdv(bwd_dkdv_kernel<32, false, 16, 1, 3>, 1);
-    else if (d == 32) dkdv(bwd_dkdv_kernel<32, false, 32, 1, 3>, 1);
-    else dkdv(bwd_dkdv_kernel<64, false, 64, 1, 3, 1>, 1);
   } else {
     if (d == 16) dkdv(bwd_dkdv_kernel<32, false, 16>, dkdv_halves<32, false>());
     else if (d == 32) dkdv(bwd_dkdv_kernel<32, false>, dkdv_halves<32, false>());
+    else if (d == 64 && a.N <= kShortBwdMaxQueries) dkdv(bwd_dkdv_kernel<64, false, 64, 1, 1>, 1);
     else if (d == 64) dkdv(bwd_dkdv_kernel<64, false>, dkdv_halves<64, false>());
     else dkdv(bwd_dkdv_kernel<128, false>, dkdv_halves<128, false>());
   }

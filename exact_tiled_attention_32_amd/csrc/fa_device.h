@@ -44,19 +44,6 @@ __device__ __forceinline__ int lane_id() { return threadIdx.x & 63; }
 // that depend on it stay scalar branches instead of per-lane exec masking.
 __device__ __forceinline__ int wave_id() { return __builtin_amdgcn_readfirstlane(threadIdx.x >> 6); }
 
-// Workgroup barrier for LDS hand-offs between the steps of a tile loop: waits for this
-// wave's own LDS operations only, then meets the other waves. __syncthreads() also waits
-// for every global load in flight (its workgroup-scope fence), which would drain the
-// direct-to-LDS staging of the tiles after the next one; here a tile's staging loads are
-// waited for by their count before the barrier that publishes it. The empty asm statements
-// keep the compiler from moving memory accesses across the barrier.
-__device__ __forceinline__ void lds_barrier() {
-  asm volatile("" ::: "memory");
-  __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0); vmcnt and expcnt left free (gfx9 encoding)
-  __builtin_amdgcn_s_barrier();
-  asm volatile("" ::: "memory");
-}
-
 // Raw buffer resource over [base, base + bytes). Loads through it at a byte offset >= bytes
 // return zero instead of touching memory (the hardware range check of raw buffers), which
 // zero-fills tiles that run past the end of a sequence without any per-lane test.
