@@ -178,9 +178,8 @@ fa_status check_varlen(fa_dtype dt, int nseq, int H, int total, int max_seqlen, 
 size_t kvcache_ws(int B, int H, int Nq, int Nk, int d, size_t* off_m, size_t* off_l) {
   if (B <= 0 || H <= 0 || Nq <= 0 || Nk <= 0 || d <= 0) return 0;
   if ((long double)B * H * (long double)(Nq > Nk ? Nq : Nk) * d * 4 > (long double)(1ull << 62)) return 0;
-  int chunk = 0, units = 0;
-  fa::kvcache_split_plan(B, H, Nk, d, &chunk, &units);
-  const size_t rows = (size_t)B * H * units * Nq;
+  const size_t slots = (size_t)fa::kvcache_max_waves(B, H, Nk) + (size_t)B * H - 1;
+  const size_t rows = slots * Nq;
   const size_t su = align256(rows * d * sizeof(float)), sm = align256(rows * sizeof(float));
   if (off_m) *off_m = su;
   if (off_l) *off_l = su + sm;
@@ -392,9 +391,9 @@ fa_status kvcache_impl(fa_dtype dt, int B, int H, int Nq, int Nk, int d, const v
   }
 
   fa::DecArgs a{};
-  fa::kvcache_split_plan(B, H, Nk, d, &a.chunk, &a.units);
-  if ((long long)a.units / fa::kvcache_split_waves(d) * B * H > 0x7fffffffLL || (long long)B * H * Nq > 0x7fffffffLL)
-    return fail(FA_ERR_INVALID, "grid too large (B*H*units/waves or B*H*Nq > 2^31-1)");
+  if ((long long)B * H * ((Nk + 31) / 32) > 0x7fffffffLL)
+    return fail(FA_ERR_UNSUPPORTED, "cache too large (B*H*ceil(Nk/32) > 2^31-1 key tiles)");
+  if ((long long)B * H * Nq > 0x7fffffffLL) return fail(FA_ERR_INVALID, "grid too large (B*H*Nq > 2^31-1)");
   if (use_scratch) {
     fa_status st = FA_OK;
     workspace = scratch_ptr(&st);

@@ -6,20 +6,29 @@
 // values are cached; query i attends key j iff j < L_b and, when causal, j <= L_b - Nq + i.
 //
 // Decoding reads every cached key and value once and does little arithmetic per byte (it
-// is bound by HBM bandwidth), so the work is split over the keys to occupy the whole GPU:
-//   1. kvc_split_kernel: each wave owns one "unit", a contiguous range of `chunk` keys of
-//      one (b, h), and runs the forward's tiled online softmax over it for all Nq queries
-//      (S^T = K Q^T and O^T += V^T P^T on v_mfma_f32_32x32x16_bf16, one query per lane,
-//      32-key tiles staged by direct buffer -> LDS loads into a ring of LDS stages that
-//      belongs to the wave alone, so no workgroup barrier is involved). It writes the
-//      unit's partial statistics (m, l) and unnormalised output u = sum_j e^(s_j - m) v_j.
-//   2. kvc_merge_kernel: per (b, h, query), combines the units with the online-softmax
-//      rule of aiwiki "FlashAttention", section "Tiling and online normalization":
+// is bound by HBM bandwidth), so the keys are split evenly over every wave the GPU holds:
+//   1. kvc_split_kernel: the valid 32-key tiles of all (b, h) are laid end to end
+//      ((b, h) in row-major order, keys in order within one), and wave w of G takes the
+//      contiguous tiles [w T / G, (w + 1) T / G) of that sequence (T tiles in all, G <= T,
+//      so every wave has work and all waves have the same amount, whatever the cache
+//      lengths). A wave streams its tiles through a ring of LDS stages of its own (direct
+//      buffer -> LDS loads, no workgroup barrier) without draining it at (b, h) borders,
+//      and runs the forward's tiled online softmax for all Nq queries (S^T = K Q^T and
+//      O^T += V^T P^T on v_mfma_f32_32x32x16_bf16, one query per lane). Each run of tiles
+//      of one (b, h) inside a wave (a "piece") ends with the piece's partial statistics
+//      (m, l) and unnormalised output u = sum_j e^(s_j - m) v_j written to slot w + bh:
+//      along the sequence w and bh never decrease and one of them grows from a piece to
+//      the next, so slots are distinct and fewer than G + B H.
+//   2. kvc_merge_kernel: per (b, h, query), finds the waves whose ranges meet the (b, h)
+//      (the same arithmetic) and combines their pieces with the online-softmax rule of
+//      aiwiki "FlashAttention", section "Tiling and online normalization":
 //      m = max_u m_u, l = sum_u e^(m_u - m) l_u, O = sum_u e^(m_u - m) u_u / l, and
 //      lse = m + ln l.
 #include "fa_device.h"
 #include "fa_launch.h"
 
+#include <algorithm>
+#include <atomic>
 #include <type_traits>
 
 namespace fa {
@@ -29,7 +38,6 @@ namespace {
 constexpr int kThreads = 256;    // merge kernel
 constexpr int kKT = 32;          // keys per tile
 constexpr float kRescaleLog2 = 8.0f;
-constexpr long long kTargetUnits = 4096;  // key ranges per call, over all (b, h)
 // s_waitcnt immediates (gfx9 encoding: vmcnt in bits 3:0 and 15:14, expcnt 6:4, lgkmcnt
 // 11:8); the unnamed counters are left free.
 constexpr int kWaitVmcnt0 = 0x0F70;
@@ -39,27 +47,114 @@ constexpr int kWaitLgkm0 = 0xC07F;
 // in whole 16-byte-per-lane rows, so nothing is lost by not keeping it in the caches).
 constexpr int kNonTemporal = 2;
 
-// Waves per workgroup (one unit each) and pipeline stages per wave of the key-split
-// kernel. A stage holds one K tile and one V tile (2 x 32 x D bf16) in LDS; a wave keeps
-// S - 1 tiles in flight while it computes one, so LDS bounds the bytes in flight.
+// Pipeline stages S of a key-split wave (one wave per workgroup) and the most waves
+// launched per CU. A stage holds one K tile and one V tile (2 x 32 x D bf16) in LDS; the
+// wave keeps S - 1 tiles in flight while it computes one. Each wave reads two sequential
+// streams (its K and V ranges), and HBM serves fewer, longer streams better: filling the CU
+// (5 or 6 waves) was 3-16 % slower on the decode workloads than 2 (d = 128) or 3 (d <= 64)
+// waves per CU.
 template <int D> struct SplitShape;
-template <> struct SplitShape<32> { static constexpr int W = 4, S = 4; };
-template <> struct SplitShape<64> { static constexpr int W = 4, S = 4; };
-template <> struct SplitShape<128> { static constexpr int W = 3, S = 3; };
+template <> struct SplitShape<32> { static constexpr int S = 3, PER_CU = 3; };
+template <> struct SplitShape<64> { static constexpr int S = 3, PER_CU = 3; };
+template <> struct SplitShape<128> { static constexpr int S = 2, PER_CU = 2; };
 
-// LDS of one pipeline stage of every wave; unused stages shrink to 16 bytes.
-template <int D, int STAGE, bool USED = (STAGE < SplitShape<D>::S)>
+// LDS of one pipeline stage; unused stages shrink to 16 bytes.
+template <int D, int STAGE>
 struct StageLds {
-  static constexpr int W = USED ? SplitShape<D>::W : 1;
-  static constexpr int BYTES = USED ? 2 * kKT * D * 2 : 16;
+  static constexpr int BYTES = STAGE < SplitShape<D>::S ? 2 * kKT * D * 2 : 16;
 };
+
+// Valid cached keys of batch b, and their 32-key tiles.
+__device__ __forceinline__ int cache_len(const DecArgs& a, int b) {
+  return a.kv_len ? min(max(a.kv_len[b], 0), a.Nk) : a.Nk;
+}
+__device__ __forceinline__ int cache_tiles(const DecArgs& a, int b) { return (cache_len(a, b) + kKT - 1) / kKT; }
+
+// Tiles of the batches below `bend` over all heads: H sum_{b < bend} tiles(b) (the lanes of
+// the wave share the batches; every lane returns the sum). bend = B gives T.
+__device__ int tiles_before(const DecArgs& a, int bend) {
+  if (!a.kv_len) return bend * a.H * ((a.Nk + kKT - 1) / kKT);
+  int sum = 0;
+  for (int c = 0; c < bend; c += 64) {
+    const int b = c + lane_id();
+    sum += b < bend ? cache_tiles(a, b) : 0;
+  }
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) sum += __shfl_xor(sum, off);
+  return __builtin_amdgcn_readfirstlane(a.H * sum);
+}
+
+// Batch b holding tile g of the sequence (0 <= g < T) and the tiles before it, P(b).
+__device__ void locate_tile(const DecArgs& a, int g, int& b_out, int& p_out) {
+  if (!a.kv_len) {
+    const int per = a.H * ((a.Nk + kKT - 1) / kKT);
+    b_out = g / per;
+    p_out = b_out * per;
+    return;
+  }
+  int base = 0;
+  for (int c = 0; c < a.B; c += 64) {
+    const int b = c + lane_id();
+    const int t = b < a.B ? a.H * cache_tiles(a, b) : 0;
+    int incl = t;  // inclusive prefix over the lanes
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) {
+      const int y = __shfl_up(incl, off);
+      if (lane_id() >= off) incl += y;
+    }
+    const unsigned long long hit = __ballot(b < a.B && base + incl > g);
+    if (hit) {
+      const int lane = __builtin_ctzll(hit);
+      b_out = __builtin_amdgcn_readfirstlane(c + lane);
+      p_out = __builtin_amdgcn_readfirstlane(base + __shfl(incl - t, lane));
+      return;
+    }
+    base += __builtin_amdgcn_readfirstlane(__shfl(incl, 63));
+  }
+  b_out = a.B;  // (g >= T: not reached by the kernels)
+  p_out = base;
+}
+
+// Wave-uniform position in the tile sequence: batch b, head h, tile j of (b, h), and the
+// batch's tile count and valid length. Past the last tile b = B (with tb = 1, L = 0).
+struct Cursor {
+  int b, h, j, tb, L;
+};
+
+__device__ __forceinline__ Cursor cursor_at(const DecArgs& a, int g) {
+  Cursor c;
+  int p = 0;
+  locate_tile(a, g, c.b, p);
+  c.L = __builtin_amdgcn_readfirstlane(cache_len(a, c.b));
+  c.tb = (c.L + kKT - 1) / kKT;
+  const int r = g - p;
+  c.h = r / c.tb;
+  c.j = r % c.tb;
+  return c;
+}
+
+__device__ __forceinline__ void cursor_next(const DecArgs& a, Cursor& c) {
+  if (++c.j < c.tb) return;
+  c.j = 0;
+  if (++c.h < a.H) return;
+  c.h = 0;
+  for (++c.b; c.b < a.B; ++c.b) {  // skip batches with an empty cache
+    c.L = __builtin_amdgcn_readfirstlane(cache_len(a, c.b));
+    c.tb = (c.L + kKT - 1) / kKT;
+    if (c.tb > 0) return;
+  }
+  c.L = 0;
+  c.tb = 1;
+}
+
+// Waves that take part: G = min(launched waves, T), so that every range is nonempty.
+__device__ __forceinline__ int active_waves(const DecArgs& a, int T) { return min(a.waves, T); }
 
 // DG: head dimension in memory; D: tile width (16 runs on 32-wide tiles, upper half zero).
 template <int D, int DG = D>
-__global__ __launch_bounds__(SplitShape<D>::W * 64, 1) void kvc_split_kernel(DecArgs a) {
+__global__ __launch_bounds__(64) void kvc_split_kernel(DecArgs a) {
   static_assert(DG == D || (D == 32 && DG == 16), "narrow heads run on 32-wide tiles");
   constexpr int KSG = (DG + 15) / 16;           // k-steps that carry data
-  constexpr int W = SplitShape<D>::W;
   constexpr int S = SplitShape<D>::S;
   static_assert(S >= 2 && S <= 4, "pipeline depth");
   constexpr int KS = D / 16;                    // k-steps of the score product
@@ -70,44 +165,51 @@ __global__ __launch_bounds__(SplitShape<D>::W * 64, 1) void kvc_split_kernel(Dec
   constexpr int NB = TILE / 1024;               // staging instructions per tile and tensor
   constexpr int NI = 2 * NB;                    // memory instructions per stage
   // One array per stage, so that the compiler can tell that staging into one stage does
-  // not touch the others. Stage layout per wave: [V tile | K tile], both swizzled.
-  __shared__ __attribute__((aligned(16))) char st0[StageLds<D, 0>::W][StageLds<D, 0>::BYTES];
-  __shared__ __attribute__((aligned(16))) char st1[StageLds<D, 1>::W][StageLds<D, 1>::BYTES];
-  __shared__ __attribute__((aligned(16))) char st2[StageLds<D, 2>::W][StageLds<D, 2>::BYTES];
-  __shared__ __attribute__((aligned(16))) char st3[StageLds<D, 3>::W][StageLds<D, 3>::BYTES];
+  // not touch the others. Stage layout: [V tile | K tile], both swizzled.
+  __shared__ __attribute__((aligned(16))) char st0[StageLds<D, 0>::BYTES];
+  __shared__ __attribute__((aligned(16))) char st1[StageLds<D, 1>::BYTES];
+  __shared__ __attribute__((aligned(16))) char st2[StageLds<D, 2>::BYTES];
+  __shared__ __attribute__((aligned(16))) char st3[StageLds<D, 3>::BYTES];
 
-  const int BH = a.B * a.H;
-  const int bh = blockIdx.x % BH;
-  const int b = bh / a.H;
-  const int w = wave_id(), l = lane_id(), h = l >> 5, ql = l & 31;
-  const int unit = W * (blockIdx.x / BH) + w;
-  int L = a.Nk;
-  if (a.kv_len) L = min(max(a.kv_len[b], 0), a.Nk);
-  const int kb = unit * a.chunk;
-  const int ke = min(kb + a.chunk, L);
-  const int ntiles = ke > kb ? (ke - kb + kKT - 1) / kKT : 0;
+  const int l = lane_id(), hl = l >> 5, ql = l & 31;
+  const int T = tiles_before(a, a.B);
+  const int G = active_waves(a, T);
+  const int w = blockIdx.x;
+  if (w >= G) return;  // (T = 0, or more waves launched than tiles)
+  const int s = (int)((long long)w * T / G);
+  const int ntiles = (int)((long long)(w + 1) * T / G) - s;
 
-  const __bf16* __restrict__ Q = reinterpret_cast<const __bf16*>(a.q) + (size_t)bh * a.Nq * DG;
-  const __bf16* __restrict__ K = reinterpret_cast<const __bf16*>(a.k) + (size_t)bh * a.Nk * DG;
-  const __bf16* __restrict__ V = reinterpret_cast<const __bf16*>(a.v) + (size_t)bh * a.Nk * DG;
+  const __bf16* __restrict__ Q = reinterpret_cast<const __bf16*>(a.q);
+  const __bf16* __restrict__ K = reinterpret_cast<const __bf16*>(a.k);
+  const __bf16* __restrict__ V = reinterpret_cast<const __bf16*>(a.v);
 
-  // Q fragments (B operand of S^T = K Q^T): lane holds query ql, columns 16 ks + 8 h .. + 7;
-  // query rows past Nq are zero (their results are never written). The loads are waited
-  // for after the first tiles' loads have been issued.
+  // Q fragments (B operand of S^T = K Q^T) of one (b, h): lane holds query ql, columns
+  // 16 ks + 8 hl .. + 7; query rows past Nq are zero (their results are never written).
   u32x4 qraw[KS];
-  {
-    const __bf16* qrow = Q + (size_t)min(ql, a.Nq - 1) * DG + 8 * h;
+  bf16x8 qf[KS];
+  auto q_load = [&](int bh) {
+    const __bf16* qrow = Q + ((size_t)bh * a.Nq + min(ql, a.Nq - 1)) * DG + 8 * hl;
 #pragma unroll
     for (int ks = 0; ks < KSG; ++ks) qraw[ks] = gload16(qrow + 16 * ks);
 #pragma unroll
     for (int ks = KSG; ks < KS; ++ks) qraw[ks] = u32x4{};
-  }
-  bf16x8 qf[KS];
+  };
+  auto q_set = [&]() {
+    const bool live = ql < a.Nq;
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) qf[ks] = __builtin_bit_cast(bf16x8, live ? qraw[ks] : u32x4{});
+    if (a.qmul != 1.0f) {
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks)
+#pragma unroll
+        for (int e = 0; e < 8; ++e) qf[ks][e] = (__bf16)((float)qf[ks][e] * a.qmul);
+    }
+  };
 
   // LDS operand offsets: K rows (A operand of S^T), V^T transpose reads (A operand of O^T).
   int k_off[KS];
 #pragma unroll
-  for (int ks = 0; ks < KS; ++ks) k_off[ks] = TILE + tile_off<D>(ql, 16 * ks + 8 * h);
+  for (int ks = 0; ks < KS; ++ks) k_off[ks] = TILE + tile_off<D>(ql, 16 * ks + 8 * hl);
   int v_lo[MD], v_hi[MD];
 #pragma unroll
   for (int md = 0; md < MD; ++md) tr8_offsets<D>(32 * md, v_lo[md], v_hi[md]);
@@ -123,29 +225,29 @@ __global__ __launch_bounds__(SplitShape<D>::W * 64, 1) void kvc_split_kernel(Dec
     st_off[c] = 8 * chunk < DG ? (row * DG + chunk * 8) * 2 : (int)0xFFFFFFF0u;
   }
   auto stage = [&](auto si) -> FA_LDS char* {
-    if constexpr (decltype(si)::value == 0) return (FA_LDS char*)st0[w];
-    else if constexpr (decltype(si)::value == 1) return (FA_LDS char*)st1[w];
-    else if constexpr (decltype(si)::value == 2) return (FA_LDS char*)st2[w];
-    else return (FA_LDS char*)st3[w];
+    if constexpr (decltype(si)::value == 0) return (FA_LDS char*)st0;
+    else if constexpr (decltype(si)::value == 1) return (FA_LDS char*)st1;
+    else if constexpr (decltype(si)::value == 2) return (FA_LDS char*)st2;
+    else return (FA_LDS char*)st3;
   };
-  // Tile t of the unit into a stage. Rows at or past the unit's end read as zero (buffer
-  // range check), so padding never reaches a sum, and a tile wholly past the end makes no
-  // memory access at all; it is issued anyway so that every iteration issues the same
-  // loads and the waits below stay exact. The wave's LDS reads of the stage (the tile
-  // computed last) have returned before new values are written into it.
-  auto load = [&](int t, FA_LDS char* dst) {
+  // Tile t of the wave (at cursor c) into a stage. Rows at or past the cache length read
+  // as zero (buffer range check), so padding never reaches a sum, and a tile past the
+  // wave's range makes no memory access at all; it is issued anyway so that every step
+  // issues the same loads and the waits below stay exact. The wave's LDS reads of the
+  // stage (the tile computed last) have returned before new values are written into it.
+  auto load = [&](int t, const Cursor& c, FA_LDS char* dst) {
     __builtin_amdgcn_s_waitcnt(kWaitLgkm0);
-    const int t0 = kb + t * kKT;
-    const int rows = __builtin_amdgcn_readfirstlane(t < ntiles ? min(L - t0, kKT) : 0);  // scalar
+    const int t0 = c.j * kKT;
+    const int rows = __builtin_amdgcn_readfirstlane(t < ntiles ? min(c.L - t0, kKT) : 0);  // scalar
     const uint32_t bytes = (uint32_t)rows * (uint32_t)(DG * 2);
-    const size_t base = t < ntiles ? (size_t)t0 * DG : 0;
+    const size_t base = t < ntiles ? ((size_t)(c.b * a.H + c.h) * a.Nk + t0) * DG : 0;
     const auto rv = make_rsrc(V + base, bytes);
     const auto rk = make_rsrc(K + base, bytes);
 #pragma unroll
-    for (int c = 0; c < NB; ++c) {
-      const int voff = st_off[c];
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(rv, (FA_LDS void*)(dst + c * 1024), 16, voff, 0, 0, kNonTemporal);
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(rk, (FA_LDS void*)(dst + TILE + c * 1024), 16, voff, 0, 0,
+    for (int c2i = 0; c2i < NB; ++c2i) {
+      const int voff = st_off[c2i];
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rv, (FA_LDS void*)(dst + c2i * 1024), 16, voff, 0, 0, kNonTemporal);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rk, (FA_LDS void*)(dst + TILE + c2i * 1024), 16, voff, 0, 0,
                                                kNonTemporal);
     }
   };
@@ -155,23 +257,24 @@ __global__ __launch_bounds__(SplitShape<D>::W * 64, 1) void kvc_split_kernel(Dec
   for (int md = 0; md < MD; ++md) o[md] = f32x16{};
   float m_run = kNegInf, l_run = 0.f;
   const float c2 = a.c2;
-  const int last = L - a.Nq;  // causal: query i sees keys j <= last + i
 
-  auto tile = [&](const FA_LDS char* vt, int t0) {
-    f32x16 s = f32x16{};
+  // One tile: keys t0 .. t0 + 31 of a (b, h) whose first L keys are valid.
+  auto tile = [&](const FA_LDS char* vt, int t0, int L) {
+    f32x16 sc = f32x16{};
 #pragma unroll
-    for (int ks = 0; ks < KSG; ++ks) s = mfma32(lds_ld8(vt + k_off[ks]), qf[ks], s);
+    for (int ks = 0; ks < KSG; ++ks) sc = mfma32(lds_ld8(vt + k_off[ks]), qf[ks], sc);
+    const int last = L - a.Nq;  // causal: query i sees keys j <= last + i
     // keys past the valid range, or (causal) past a query's position
     if (t0 + kKT > L || (a.causal && t0 + kKT - 1 > last)) {
 #pragma unroll
       for (int i = 0; i < 16; ++i) {
-        const int key = t0 + 8 * (i >> 2) + 4 * h + (i & 3);
-        if (key >= L || (a.causal && key > last + ql)) s[i] = kNegInf;
+        const int key = t0 + 8 * (i >> 2) + 4 * hl + (i & 3);
+        if (key >= L || (a.causal && key > last + ql)) sc[i] = kNegInf;
       }
     }
     float tmax = kNegInf;
 #pragma unroll
-    for (int i = 0; i < 16; ++i) tmax = fmaxf(tmax, s[i]);
+    for (int i = 0; i < 16; ++i) tmax = fmaxf(tmax, sc[i]);
     tmax = fmaxf(tmax, other_half(tmax));
     const float mcand = fmaxf(m_run, tmax);
     const bool need = (mcand - m_run) * c2 > kRescaleLog2;
@@ -187,7 +290,7 @@ __global__ __launch_bounds__(SplitShape<D>::W * 64, 1) void kvc_split_kernel(Dec
     float lsum = 0.f;
 #pragma unroll
     for (int i = 0; i < 16; ++i) {
-      const float p = fast_exp2(__builtin_fmaf(s[i], c2, -moff));
+      const float p = fast_exp2(__builtin_fmaf(sc[i], c2, -moff));
       lsum += p;
       pb[i >> 3][i & 7] = (__bf16)p;
     }
@@ -199,80 +302,109 @@ __global__ __launch_bounds__(SplitShape<D>::W * 64, 1) void kvc_split_kernel(Dec
         o[md] = mfma32(lds_tr8(vt + v_lo[md] + st * 16 * 2 * D, vt + v_hi[md] + st * 16 * 2 * D), pb[st], o[md]);
   };
 
-  // Ring of S stages: tile t lives in stage t % S; while it is computed, tiles t + 1 ..
-  // t + S - 1 are in flight. The loop is unrolled by S so that every stage is a distinct
-  // array at every access.
-  if (ntiles > 0) {
-    load(0, stage(std::integral_constant<int, 0>{}));
-    if constexpr (S > 2) load(1, stage(std::integral_constant<int, 1>{}));
-    if constexpr (S > 3) load(2, stage(std::integral_constant<int, 2>{}));
-    // the Q loads, issued before the tiles', have landed once at most the tiles' remain
-    __builtin_amdgcn_s_waitcnt(wait_vmcnt((S - 1) * NI));
-    const bool live = ql < a.Nq;
+  // Partial results of a piece into its slot, then a fresh state for the next piece.
+  auto finish_piece = [&](int slot) {
+    const float l_tot = l_run + other_half(l_run);
+    if (ql < a.Nq) {
+      const size_t pu = (size_t)slot * a.Nq + ql;
+      float* U = a.part_u + pu * DG;
 #pragma unroll
-    for (int ks = 0; ks < KS; ++ks) qf[ks] = __builtin_bit_cast(bf16x8, live ? qraw[ks] : u32x4{});
-    if (a.qmul != 1.0f) {
+      for (int md = 0; md < MD; ++md)
 #pragma unroll
-      for (int ks = 0; ks < KS; ++ks)
+        for (int g = 0; g < 4; ++g) {
+          f32x4 v4;
 #pragma unroll
-        for (int e = 0; e < 8; ++e) qf[ks][e] = (__bf16)((float)qf[ks][e] * a.qmul);
-    }
-    for (int t = 0; t < ntiles; t += S) {
-      auto step = [&](auto j) {
-        constexpr int J = decltype(j)::value;
-        load(t + J + S - 1, stage(std::integral_constant<int, (J + S - 1) % S>{}));
-        __builtin_amdgcn_s_waitcnt(wait_vmcnt((S - 1) * NI));
-        if (t + J < ntiles) tile(stage(j), kb + (t + J) * kKT);
-      };
-      step(std::integral_constant<int, 0>{});
-      step(std::integral_constant<int, 1>{});
-      if constexpr (S > 2) step(std::integral_constant<int, 2>{});
-      if constexpr (S > 3) step(std::integral_constant<int, 3>{});
-    }
-    // the last loads (all past the end) must land before the wave ends
-    __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
-  } else {
-    __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);  // the unused Q loads
-  }
-
-  // Partial results of the unit (an empty unit writes m = -inf, l = 0, u = 0).
-  const float l_tot = l_run + other_half(l_run);
-  if (ql < a.Nq) {
-    const size_t pu = ((size_t)bh * a.units + unit) * a.Nq + ql;
-    float* U = a.part_u + pu * DG;
-#pragma unroll
-    for (int md = 0; md < MD; ++md)
-#pragma unroll
-      for (int g = 0; g < 4; ++g) {
-        f32x4 v4;
-#pragma unroll
-        for (int e = 0; e < 4; ++e) v4[e] = o[md][4 * g + e];
-        if (32 * md + 8 * g < DG) *reinterpret_cast<f32x4*>(U + 32 * md + 8 * g + 4 * h) = v4;
+          for (int e = 0; e < 4; ++e) v4[e] = o[md][4 * g + e];
+          if (32 * md + 8 * g < DG) *reinterpret_cast<f32x4*>(U + 32 * md + 8 * g + 4 * hl) = v4;
+        }
+      if (hl == 0) {
+        a.part_m[pu] = m_run;
+        a.part_l[pu] = l_tot;
       }
-    if (h == 0) {
-      a.part_m[pu] = m_run;
-      a.part_l[pu] = l_tot;
     }
+#pragma unroll
+    for (int md = 0; md < MD; ++md) o[md] = f32x16{};
+    m_run = kNegInf;
+    l_run = 0.f;
+  };
+
+  // Ring of S stages: tile t lives in stage t % S; while it is computed, tiles t + 1 ..
+  // t + S - 1 are in flight. `lc` is the position of the next tile to load, `cc` that of
+  // the next tile to compute. The loop is unrolled by S so that every stage is a distinct
+  // array at every access.
+  Cursor lc = cursor_at(a, s);
+  Cursor cc = lc;
+  q_load(cc.b * a.H + cc.h);
+  load(0, lc, stage(std::integral_constant<int, 0>{}));
+  cursor_next(a, lc);
+  if constexpr (S > 2) {
+    load(1, lc, stage(std::integral_constant<int, 1>{}));
+    cursor_next(a, lc);
   }
+  if constexpr (S > 3) {
+    load(2, lc, stage(std::integral_constant<int, 2>{}));
+    cursor_next(a, lc);
+  }
+  // the Q loads, issued before the tiles', have landed once at most the tiles' remain
+  __builtin_amdgcn_s_waitcnt(wait_vmcnt((S - 1) * NI));
+  q_set();
+  for (int t = 0; t < ntiles; t += S) {
+    auto step = [&](auto jc) {
+      constexpr int J = decltype(jc)::value;
+      load(t + J + S - 1, lc, stage(std::integral_constant<int, (J + S - 1) % S>{}));
+      cursor_next(a, lc);
+      __builtin_amdgcn_s_waitcnt(wait_vmcnt((S - 1) * NI));
+      const int tt = t + J;
+      if (tt < ntiles) {
+        const int bh = cc.b * a.H + cc.h;
+        if (tt > 0 && cc.j == 0) {  // a new (b, h): its queries (waits for every load)
+          q_load(bh);
+          __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
+          q_set();
+        }
+        tile(stage(jc), cc.j * kKT, cc.L);
+        if (tt == ntiles - 1 || cc.j == cc.tb - 1) finish_piece(w + bh);
+        cursor_next(a, cc);
+      }
+    };
+    step(std::integral_constant<int, 0>{});
+    step(std::integral_constant<int, 1>{});
+    if constexpr (S > 2) step(std::integral_constant<int, 2>{});
+    if constexpr (S > 3) step(std::integral_constant<int, 3>{});
+  }
+  // the last loads (all past the range) must land before the wave ends
+  __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
 }
 
-// One workgroup per (b, h, query). The units are spread over the threads: first the
-// maximum of the units' maxima, then groups of D / 4 threads (one 4-column slice each)
-// accumulate every G-th unit's weighted output, and the G group sums are added in LDS.
+// One workgroup per (b, h, query). The pieces of (b, h) are those of waves w0 .. w1 (the
+// waves holding its first and last tile), in slots w + bh. They are spread over the
+// threads: first the maximum of their maxima, then groups of D / 4 threads (one 4-column
+// slice each) accumulate every G-th piece's weighted output, and the G group sums are
+// added in LDS. A (b, h) with an empty cache has no piece: O = 0, lse = -inf.
 template <int D>
 __global__ __launch_bounds__(kThreads) void kvc_merge_kernel(DecArgs a) {
   constexpr int C4 = D / 4;           // threads per output row
-  constexpr int G = kThreads / C4;    // unit groups
+  constexpr int G = kThreads / C4;    // piece groups
   __shared__ float wmax[kThreads / 64];
   __shared__ f32x4 gacc[G][C4];
   __shared__ float gl[G];
   const int bh = blockIdx.x / a.Nq, q = blockIdx.x % a.Nq;
+  const int b = bh / a.H, hd = bh % a.H;
   const int tid = threadIdx.x;
-  const size_t base = (size_t)bh * a.units * a.Nq + q;  // unit u at base + u Nq
-  const int U = a.units;
+
+  const int T = tiles_before(a, a.B);
+  const int tb = __builtin_amdgcn_readfirstlane(cache_tiles(a, b));
+  int w0 = 0, np = 0;
+  if (tb > 0) {
+    const int W = active_waves(a, T);
+    const int g0 = tiles_before(a, b) + hd * tb, g1 = g0 + tb - 1;
+    w0 = (int)(((long long)(g0 + 1) * W - 1) / T);
+    np = (int)(((long long)(g1 + 1) * W - 1) / T) - w0 + 1;
+  }
+  const size_t base = (size_t)(w0 + bh) * a.Nq + q;  // piece p at base + p Nq
 
   float m = kNegInf;
-  for (int u = tid; u < U; u += kThreads) m = fmaxf(m, a.part_m[base + (size_t)u * a.Nq]);
+  for (int p = tid; p < np; p += kThreads) m = fmaxf(m, a.part_m[base + (size_t)p * a.Nq]);
 #pragma unroll
   for (int off = 32; off > 0; off >>= 1) m = fmaxf(m, __shfl_xor(m, off));
   if (lane_id() == 0) wmax[wave_id()] = m;
@@ -283,10 +415,10 @@ __global__ __launch_bounds__(kThreads) void kvc_merge_kernel(DecArgs a) {
   f32x4 acc = f32x4{};
   float lsum = 0.f;
   if (m != kNegInf) {
-    // an empty unit has m_u = -inf (weight 0), l_u = 0 and u_u = 0
+    // a piece whose queries saw no key has m_u = -inf (weight 0), l_u = 0 and u_u = 0
 #pragma unroll 4
-    for (int u = g; u < U; u += G) {
-      const size_t pu = base + (size_t)u * a.Nq;
+    for (int p = g; p < np; p += G) {
+      const size_t pu = base + (size_t)p * a.Nq;
       const float wgt = fast_exp2((a.part_m[pu] - m) * a.c2);
       lsum += wgt * a.part_l[pu];
       const f32x4 uv = *reinterpret_cast<const f32x4*>(a.part_u + pu * D + 4 * c4);
@@ -316,31 +448,52 @@ __global__ __launch_bounds__(kThreads) void kvc_merge_kernel(DecArgs a) {
 
 }  // namespace
 
-void kvcache_split_plan(int B, int H, int Nk, int d, int* chunk, int* units) {
-  // about kTargetUnits units in all, each a multiple of the tile; the units of a (b, h)
-  // rounded up to whole workgroups
-  const int W = kvcache_split_waves(d);
-  const long long total = (long long)B * H * Nk;
-  long long c = (total + kTargetUnits - 1) / kTargetUnits;
-  c = (c + kKT - 1) / kKT * kKT;
-  if (c < kKT) c = kKT;
-  const long long u = (Nk + c - 1) / c;
-  *chunk = (int)c;
-  *units = (int)((u + W - 1) / W * W);
+int kvcache_max_waves(int B, int H, int Nk) {
+  const long long tiles = (long long)B * H * ((Nk + kKT - 1) / kKT);
+  return (int)std::max(1LL, std::min<long long>(kDecMaxWaves, tiles));
 }
 
-int kvcache_split_waves(int d) {
-  return d <= 32 ? SplitShape<32>::W : d == 64 ? SplitShape<64>::W : SplitShape<128>::W;
+namespace {
+
+// Waves of the key-split kernel to launch on the current device: CUs x min(workgroups
+// resident per CU, per_cu), looked up once per device and head-dimension variant. 0 if
+// unknown.
+constexpr int kMaxDevices = 64;
+std::atomic<int> g_resident[kMaxDevices][4];
+
+template <typename K>
+int resident_waves(K kernel, int variant, int per_cu_max) {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return 0;
+  int n = g_resident[dev][variant].load(std::memory_order_relaxed);
+  if (n > 0) return n;
+  int cus = 0, per_cu = 0;
+  if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return 0;
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, reinterpret_cast<const void*>(kernel), 64, 0) !=
+      hipSuccess)
+    return 0;
+  n = cus * std::min(per_cu, per_cu_max);
+  if (n > 0) g_resident[dev][variant].store(n, std::memory_order_relaxed);
+  return n;
 }
 
-hipError_t launch_kvcache(const DecArgs& a, int d, hipStream_t stream, KernelTimer& tm) {
-  const int W = kvcache_split_waves(d);
-  const dim3 gsplit((unsigned)(a.units / W * a.B * a.H)), gmerge((unsigned)(a.B * a.H * a.Nq));
+}  // namespace
+
+hipError_t launch_kvcache(const DecArgs& args, int d, hipStream_t stream, KernelTimer& tm) {
+  DecArgs a = args;
+  const int wmax = kvcache_max_waves(a.B, a.H, a.Nk);
+  int res = 0;
+  if (d == 16) res = resident_waves(kvc_split_kernel<32, 16>, 0, SplitShape<32>::PER_CU);
+  else if (d == 32) res = resident_waves(kvc_split_kernel<32>, 1, SplitShape<32>::PER_CU);
+  else if (d == 64) res = resident_waves(kvc_split_kernel<64>, 2, SplitShape<64>::PER_CU);
+  else res = resident_waves(kvc_split_kernel<128>, 3, SplitShape<128>::PER_CU);
+  a.waves = res > 0 ? std::min(res, wmax) : wmax;
+  const dim3 gsplit((unsigned)a.waves), gmerge((unsigned)(a.B * a.H * a.Nq));
   tm.mark(stream);
-  if (d == 16) hipLaunchKernelGGL((kvc_split_kernel<32, 16>), gsplit, dim3(64 * W), 0, stream, a);
-  else if (d == 32) hipLaunchKernelGGL(kvc_split_kernel<32>, gsplit, dim3(64 * W), 0, stream, a);
-  else if (d == 64) hipLaunchKernelGGL(kvc_split_kernel<64>, gsplit, dim3(64 * W), 0, stream, a);
-  else hipLaunchKernelGGL(kvc_split_kernel<128>, gsplit, dim3(64 * W), 0, stream, a);
+  if (d == 16) hipLaunchKernelGGL((kvc_split_kernel<32, 16>), gsplit, dim3(64), 0, stream, a);
+  else if (d == 32) hipLaunchKernelGGL(kvc_split_kernel<32>, gsplit, dim3(64), 0, stream, a);
+  else if (d == 64) hipLaunchKernelGGL(kvc_split_kernel<64>, gsplit, dim3(64), 0, stream, a);
+  else hipLaunchKernelGGL(kvc_split_kernel<128>, gsplit, dim3(64), 0, stream, a);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   tm.mark(stream);

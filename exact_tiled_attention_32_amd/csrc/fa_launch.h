@@ -75,12 +75,11 @@ struct DecArgs {
   void* o;                // [B, H, Nq, d]
   float* lse;             // [B, H, Nq]
   const int32_t* kv_len;  // nullptr: every cached key valid
-  float* part_u;          // workspace: [B, H, units, Nq, d] unnormalised partial outputs
-  float* part_m;          // workspace: [B, H, units, Nq] partial maxima (raw q.k units)
-  float* part_l;          // workspace: [B, H, units, Nq] partial sums
+  float* part_u;          // workspace: [slots, Nq, d] unnormalised partial outputs
+  float* part_m;          // workspace: [slots, Nq] partial maxima (raw q.k units)
+  float* part_l;          // workspace: [slots, Nq] partial sums
   int B, H, Nq, Nk;
-  int chunk;              // keys per unit (a multiple of the 32-key tile)
-  int units;              // units per (b, h), a multiple of the waves per workgroup
+  int waves;              // key-split waves launched (those past the tile count stay idle)
   int causal;
   float c2, sc_abs, qmul; // as in FwdArgs
 };
@@ -91,10 +90,11 @@ constexpr int kDecMaxQueries = 32;
 // or a window extent below it stay far from the int range.
 constexpr int kMaxSeqLen = 1 << 30;
 
-// Split of the cached keys into units: chunk keys each, units per (b, h).
-void kvcache_split_plan(int B, int H, int Nk, int d, int* chunk, int* units);
-// Waves (units) per workgroup of the key-split kernel for head dimension d.
-int kvcache_split_waves(int d);
+// Most key-split waves of one call; partial-result slots of a call number
+// kvcache_max_waves(B, H, Nk) + B H - 1.
+constexpr int kDecMaxWaves = 2048;
+// Waves a call may launch: min(kDecMaxWaves, the 32-key tiles of a full cache), at least 1.
+int kvcache_max_waves(int B, int H, int Nk);
 
 constexpr int kFwdRowsPerWG = 128;       // fp32 forward; also the mask-block granularity
 constexpr int kFwdRowsPerWGBF16 = 128;   // bf16 forward: 4 waves x 32 query rows

@@ -221,10 +221,10 @@ fa_status fa_bwd_varlen(fa_dtype dt, int nseq, int H, int total, int max_seqlen,
 
 /*
  * Bytes of device workspace fa_fwd_kvcache needs for the partial results of its key split:
- * B*H*units*Nq*(4d + 8) bytes (three regions, each rounded up to 256 bytes), where units
- * is the number of key ranges each (b, h) is split into, chosen from B, H and Nk (about
- * 8192 ranges in all, at least 32 keys each). Returns 0 for non-positive or overflowing
- * sizes.
+ * slots*Nq*(4d + 8) bytes (three regions, each rounded up to 256 bytes), where
+ * slots = min(2048, B*H*ceil(Nk/32)) + B*H - 1 (at most 2048 waves share the key tiles of
+ * all (b, h); each wave leaves one partial result per (b, h) its tiles touch). Returns 0
+ * for non-positive or overflowing sizes.
  */
 size_t fa_fwd_kvcache_workspace_bytes(int B, int H, int Nq, int Nk, int d);
 
@@ -244,10 +244,11 @@ size_t fa_fwd_kvcache_workspace_bytes(int B, int H, int Nq, int Nk, int d);
  *                     the bottom-right corner); zero: it attends every key j < L_b
  *   workspace         device memory of at least fa_fwd_kvcache_workspace_bytes(B,H,Nq,Nk,d)
  *                     bytes, 256-byte aligned, owned by the caller, overwritten
- * Each (b, h) splits its keys into ranges processed in parallel, each with the online
- * softmax of aiwiki "FlashAttention", section "Tiling and online normalization"; a second
- * kernel merges the ranges' (max, sum, unnormalised output) with the same update. A query
- * with no allowed key yields O = 0 and lse = -inf.
+ * The valid 32-key tiles of all (b, h) are split into equal contiguous ranges, one per
+ * wave, each run with the online softmax of aiwiki "FlashAttention", section "Tiling and
+ * online normalization"; a second kernel merges the partial (max, sum, unnormalised
+ * output) of each (b, h) with the same update. A query with no allowed key yields O = 0 and
+ * lse = -inf. Caches of more than 2^31-1 key tiles over all (b, h) give FA_ERR_UNSUPPORTED.
  */
 fa_status fa_fwd_kvcache(fa_dtype dt, int B, int H, int Nq, int Nk, int d,
                          const void* q, const void* k_cache, const void* v_cache,

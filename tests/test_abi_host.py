@@ -144,24 +144,21 @@ def test_binding_fails_loudly_without_library(monkeypatch, tmp_path):
         fa.load()
 
 
-def _kvcache_units(B, H, Nk, d):
-    # key ranges per (b, h): about 4096 ranges in all, each a multiple of 32 keys, the
-    # count per (b, h) rounded up to whole workgroups (4 ranges at d=64, 3 at d=128)
-    W = 4 if d == 64 else 3
-    chunk = max(32, -(-(-(-(B * H * Nk) // 4096)) // 32) * 32)
-    units = -(-Nk // chunk)
-    return chunk, -(-units // W) * W
+def _kvcache_slots(B, H, Nk):
+    # partial-result slots: at most 2048 waves (never more than the 32-key tiles of a full
+    # cache) share the tiles of all (b, h); each wave leaves one partial per (b, h) it
+    # touches, and slot w + bh is distinct for every such pair, so G + B H - 1 slots suffice
+    tiles = B * H * -(-Nk // 32)
+    return min(2048, max(tiles, 1)) + B * H - 1
 
 
 @pytest.mark.parametrize("B,H,Nq,Nk,d", [(1, 1, 1, 1, 64), (8, 16, 1, 16384, 128), (4, 32, 16, 32768, 64),
                                          (2, 3, 5, 70000, 128), (1, 1, 32, 1 << 24, 64)])
 def test_kvcache_workspace_bytes(lib, B, H, Nq, Nk, d):
     al = lambda x: (x + 255) // 256 * 256
-    chunk, units = _kvcache_units(B, H, Nk, d)
-    assert chunk * units >= Nk and chunk % 32 == 0
-    # the partial results stay bounded: at most ~4096 ranges plus rounding per (b, h)
-    assert B * H * units <= 4096 + 4 * B * H
-    rows = B * H * units * Nq
+    slots = _kvcache_slots(B, H, Nk)
+    assert slots <= 2048 + B * H - 1
+    rows = slots * Nq
     assert fa.fa_fwd_kvcache_workspace_bytes(B, H, Nq, Nk, d) == al(rows * d * 4) + 2 * al(rows * 4)
     assert fa.fa_fwd_kvcache_workspace_bytes(B, H, 0, Nk, d) == 0
     assert fa.fa_fwd_kvcache_workspace_bytes(B, H, Nq, -1, d) == 0
@@ -190,6 +187,8 @@ def kvc(lib, dt=fa.FA_BF16, B=1, H=1, Nq=1, Nk=256, d=64, q=P, k=P, v=P, o=P, ls
     (dict(dt=fa.FA_F32), fa.FA_ERR_UNSUPPORTED),
     (dict(d=96), fa.FA_ERR_UNSUPPORTED),
     (dict(Nq=33), fa.FA_ERR_UNSUPPORTED),
+    # 2^20 (b, h) x 2048 key tiles: the tile sequence would pass 2^31 - 1
+    (dict(B=1024, H=1024, Nk=65536), fa.FA_ERR_UNSUPPORTED),
 ])
 def test_kvcache_rejects(lib, kwargs, status):
     assert kvc(lib, **kwargs) == status
@@ -290,7 +289,7 @@ def kvc_noalloc(lib, dt=fa.FA_BF16, B=1, H=1, Nq=1, Nk=256, d=64, q=P, o=P, lse=
     (dict(scale=float("nan")), fa.FA_ERR_INVALID),
     (dict(d=96), fa.FA_ERR_UNSUPPORTED),
     (dict(Nq=33), fa.FA_ERR_UNSUPPORTED),
-    # partial results beyond the static scratch (204 MB for 12288 units x 32 queries x d=128)
+    # partial results beyond the static scratch (102 MB: 2048 + 4095 slots x 32 queries x d=128)
     (dict(B=64, H=64, Nq=32, Nk=32, d=128), fa.FA_ERR_UNSUPPORTED),
 ])
 def test_kvcache_noalloc_rejects(lib, kwargs, status):

@@ -2,8 +2,8 @@
 
 Bars (tests/parity.py): bf16 O within 1e-2 after discounting the output's own rounding,
 lse within 1e-3, rows without an allowed key O = 0 and lse = -inf. The sweep spans one to
-several key ranges per (b, h), ragged cache lengths (including 0 and lengths shorter than
-the number of queries) and both mask modes; the named decode workloads run at their full
+many waves per (b, h) and many (b, h) per wave, ragged cache lengths (including 0 and
+lengths shorter than the number of queries) and both mask modes; the named decode workloads run at their full
 sizes and are compared in full (the oracle handles a few queries per head quickly).
 """
 import sys
@@ -72,6 +72,18 @@ def test_many_key_ranges(gpu_lib, d):
     # combines many partial results, some of them empty (the second sequence is short)
     case = workloads.make_decode_case(2, 3, 5, 70000, d, seed=77 + d, causal=True, kv_len=[70000, 12345])
     check(gpu_lib, case, f"many_ranges_d{d}")
+
+
+@pytest.mark.parametrize("d,causal", [(16, True), (64, False), (64, True), (128, True)])
+def test_tile_stream_borders(gpu_lib, d, causal):
+    # many (b, h) with short caches, a fifth of them empty: the key tiles of all (b, h) are
+    # shared out in equal runs, so a wave's run crosses many (b, h) borders (reloading its
+    # queries and leaving a partial result at each) and skips empty batches inside it
+    rng = np.random.default_rng(900 + d)
+    B, H, Nq, Nk = 512, 8, 3, 80
+    kv = [int(x) if rng.random() > 0.2 else 0 for x in rng.integers(1, Nk + 1, size=B)]
+    case = workloads.make_decode_case(B, H, Nq, Nk, d, seed=31 + d, causal=causal, kv_len=kv)
+    check(gpu_lib, case, f"stream_borders_d{d}_{'causal' if causal else 'full'}")
 
 
 @pytest.mark.parametrize("d", [64, 128])

@@ -104,10 +104,14 @@ def test_sweep_bf16(gpu_lib, name, params):
 
 
 # The dense bf16 forward without dropout stages three K/V tiles deep up to N = 4096 at
-# d <= 64 and two deep beyond (and at d = 128): both sides of that switch, with ragged ends.
+# d <= 64 and two deep beyond (and at d = 128), and the dense d = 64 dK/dV kernel takes one
+# query block per step (three workgroups per CU) up to N = 4096 and two beyond: both sides
+# of those switches, with ragged ends.
 STAGE_SWITCH = [
     ("stages-N4096-d64-causal", 4096, 64, True, None),
     ("stages-N4097-d64-causal", 4097, 64, True, None),
+    ("stages-N4096-d64-padded", 4096, 64, False, [2501]),
+    ("stages-N4097-d64-padded", 4097, 64, False, [4097]),
     ("stages-N4096-d32-padded", 4096, 32, False, [3001]),
     ("stages-N4097-d32-padded", 4097, 32, False, [4097]),
     ("stages-N4096-d16-causal", 4096, 16, True, None),
