@@ -1,4 +1,5 @@
-"""HIP-graph capture of a forward + backward call pair.
+"""HIP-graph capture of a forward + backward call pair, and of the cache forward (with a
+workspace and through the entry point that allocates nothing).
 
 The library keeps no per-call state, allocates nothing and issues no memset, so a caller
 can capture its calls into a graph (torch.cuda.CUDAGraph records them on its capture
@@ -69,3 +70,48 @@ def test_graph_replay_matches_eager(gpu_lib, name):
         torch.cuda.synchronize()
         for n in NAMES:
             assert torch.equal(out[n], ref[n]), f"{name}: eager call after replay {rep}: {n} differs"
+
+
+@pytest.mark.parametrize("noalloc", [False, True])
+def test_graph_replay_cache_forward(gpu_lib, noalloc):
+    # the cache forward captured as a graph: with a caller workspace, and through the entry
+    # point that allocates nothing (its partial results in the library's static array)
+    fa = gpu_lib
+    print(f"[graph] cache forward noalloc={noalloc}", flush=True)
+    sys.stdout.flush()
+    case = workloads.make_decode_case(4, 8, 5, 3000, 128, seed=61, causal=True, kv_len=[3000, 17, 0, 2048])
+    q, k, v = (case[n].to(DEV) for n in ("q", "k", "v"))
+    kv = case["kv_len"].to(DEV)
+    o = torch.empty_like(q)
+    lse = torch.empty(q.shape[:3], dtype=torch.float32, device=DEV)
+    ws = torch.empty(fa.fa_fwd_kvcache_workspace_bytes(4, 8, 5, 3000, 128), dtype=torch.uint8, device=DEV)
+
+    def call():
+        if noalloc:
+            fa.fa_fwd_kvcache_noalloc(q, k, v, case["scale"], o, lse, True, kv)
+        else:
+            fa.fa_fwd_kvcache(q, k, v, case["scale"], True, kv, o=o, lse=lse, workspace=ws)
+
+    call()
+    torch.cuda.synchronize()
+    ref_o, ref_l = o.clone(), lse.clone()
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        call()
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        call()
+    torch.cuda.synchronize()
+    for rep in range(4):
+        o.fill_(float("nan"))
+        lse.fill_(float("nan"))
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(o, ref_o) and torch.equal(lse, ref_l), f"replay {rep} differs from the eager result"
+        call()  # eager work between replays
+        torch.cuda.synchronize()
+        assert torch.equal(o, ref_o) and torch.equal(lse, ref_l), f"eager call after replay {rep} differs"
