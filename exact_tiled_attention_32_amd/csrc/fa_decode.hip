@@ -244,10 +244,10 @@ __global__ __launch_bounds__(64) void kvc_split_kernel(DecArgs a) {
     const auto rv = make_rsrc(V + base, bytes);
     const auto rk = make_rsrc(K + base, bytes);
 #pragma unroll
-    for (int c2i = 0; c2i < NB; ++c2i) {
-      const int voff = st_off[c2i];
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(rv, (FA_LDS void*)(dst + c2i * 1024), 16, voff, 0, 0, kNonTemporal);
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(rk, (FA_LDS void*)(dst + TILE + c2i * 1024), 16, voff, 0, 0,
+    for (int blk = 0; blk < NB; ++blk) {
+      const int voff = st_off[blk];
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rv, (FA_LDS void*)(dst + blk * 1024), 16, voff, 0, 0, kNonTemporal);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rk, (FA_LDS void*)(dst + TILE + blk * 1024), 16, voff, 0, 0,
                                                kNonTemporal);
     }
   };
