@@ -48,14 +48,16 @@ constexpr int kWaitLgkm0 = 0xC07F;
 constexpr int kNonTemporal = 2;
 
 // Pipeline stages S of a key-split wave (one wave per workgroup) and the most waves
-// launched per CU. A stage holds one K tile and one V tile (2 x 32 x D bf16) in LDS; the
-// wave keeps S - 1 tiles in flight while it computes one. Each wave reads two sequential
-// streams (its K and V ranges), and HBM serves fewer, longer streams better: filling the CU
-// (5 or 6 waves) was 3-16 % slower on the decode workloads than 2 (d = 128) or 3 (d <= 64)
-// waves per CU.
+// launched per CU, as measured on the decode workloads. A stage holds one K tile and one V
+// tile (2 x 32 x D bf16) in LDS; the wave keeps S - 1 tiles in flight while it computes one,
+// and reads two sequential streams (its K and V runs). At d = 128 (16 KB stages) 2 waves
+// per CU were fastest: filling the CU (5) was 12-16 % slower, 3 or 4 no faster. At d = 64
+// 4 were fastest (3: up to 2 % slower; 5, unevenly spread over the four SIMDs: 8-12 %
+// slower). At d <= 32 a stage is only 4 KB, and 8 waves keep enough bytes in flight (3 per
+// CU: 14-46 % slower).
 template <int D> struct SplitShape;
-template <> struct SplitShape<32> { static constexpr int S = 3, PER_CU = 3; };
-template <> struct SplitShape<64> { static constexpr int S = 3, PER_CU = 3; };
+template <> struct SplitShape<32> { static constexpr int S = 3, PER_CU = 8; };
+template <> struct SplitShape<64> { static constexpr int S = 3, PER_CU = 4; };
 template <> struct SplitShape<128> { static constexpr int S = 2, PER_CU = 2; };
 
 // LDS of one pipeline stage; unused stages shrink to 16 bytes.

@@ -108,6 +108,14 @@ def test_query_count_beyond_cache(gpu_lib):
     check(gpu_lib, case, "nq_beyond_cache")
 
 
+@pytest.mark.parametrize("d", [16, 128])
+def test_all_caches_empty(gpu_lib, d):
+    # no valid key anywhere: no wave has a tile, and the merge alone writes O = 0, lse = -inf
+    case = workloads.make_decode_case(3, 2, 4, 64, d, seed=8 + d, causal=False, kv_len=[0, 0, 0])
+    o, lse = check(gpu_lib, case, f"all_empty_d{d}")
+    assert bool(torch.isneginf(lse).all()) and float(o.float().abs().max()) == 0.0
+
+
 def test_deterministic_and_workspace_reuse(gpu_lib):
     fa = gpu_lib
     big = workloads.make_decode_case(2, 4, 7, 20000, 128, seed=21, causal=True, kv_len=[20000, 9000])
