@@ -108,6 +108,14 @@ def test_query_count_beyond_cache(gpu_lib):
     check(gpu_lib, case, "nq_beyond_cache")
 
 
+@pytest.mark.parametrize("d,Nq", [(32, 2), (64, 32)])
+def test_many_heads_uniform_cache(gpu_lib, d, Nq):
+    # every cache full (no lengths given) and only 2 tiles long over 1024 (b, h): runs of
+    # one or two tiles, nearly every one crossing a (b, h) border
+    case = workloads.make_decode_case(64, 16, Nq, 40, d, seed=40 + d, causal=True)
+    check(gpu_lib, case, f"many_heads_uniform_d{d}_q{Nq}")
+
+
 @pytest.mark.parametrize("d", [16, 128])
 def test_all_caches_empty(gpu_lib, d):
     # no valid key anywhere: no wave has a tile, and the merge alone writes O = 0, lse = -inf
