@@ -391,8 +391,9 @@ fa_status kvcache_impl(fa_dtype dt, int B, int H, int Nq, int Nk, int d, const v
   }
 
   fa::DecArgs a{};
-  if ((long long)B * H * ((Nk + 31) / 32) > 0x7fffffffLL)
-    return fail(FA_ERR_UNSUPPORTED, "cache too large (B*H*ceil(Nk/32) > 2^31-1 key tiles)");
+  if ((long long)B * H * ((Nk + 31) / 32) > 0x7fffffffLL || (long long)B * H + fa::kDecMaxWaves > 0x7fffffffLL)
+    return fail(FA_ERR_UNSUPPORTED, "cache too large (B*H*ceil(Nk/32) key tiles or B*H + %d partial-result "
+                "slots beyond 2^31-1)", fa::kDecMaxWaves);
   if ((long long)B * H * Nq > 0x7fffffffLL) return fail(FA_ERR_INVALID, "grid too large (B*H*Nq > 2^31-1)");
   if (use_scratch) {
     fa_status st = FA_OK;
