@@ -3,7 +3,8 @@
 Bars (tests/parity.py): bf16 O within 1e-2 after discounting the output's own rounding,
 lse within 1e-3, rows without an allowed key O = 0 and lse = -inf. The sweep spans one to
 many waves per (b, h) and many (b, h) per wave, ragged cache lengths (including 0 and
-lengths shorter than the number of queries) and both mask modes; the named decode workloads run at their full
+lengths shorter than the number of queries) and both mask modes, plus 32 fixed-seed random
+shapes; the named decode workloads run at their full
 sizes and are compared in full (the oracle handles a few queries per head quickly).
 """
 import sys
@@ -143,3 +144,28 @@ def test_deterministic_and_workspace_reuse(gpu_lib):
 def test_decode_workload_full(gpu_lib, name):
     w = workloads.DECODE_WORKLOADS[name]
     check(gpu_lib, workloads.generate_decode(w), name)
+
+
+def _random_cases(n=32, seed=2024):
+    # fixed-seed random shapes: head counts, query counts, cache sizes and ragged lengths
+    # (zeros included) drawn together, so that runs start, end and cross (b, h) borders at
+    # arbitrary tile positions
+    rng = np.random.default_rng(seed)
+    cases = []
+    for i in range(n):
+        d = int(rng.choice([16, 32, 64, 128]))
+        B, H = int(rng.integers(1, 9)), int(rng.integers(1, 13))
+        Nq = int(rng.choice([1, 2, 5, 16, 32]))
+        Nk = int(rng.integers(1, 3000))
+        kv = None if rng.random() < 0.3 else [int(x) if rng.random() > 0.15 else 0 for x in rng.integers(0, Nk + 1, size=B)]
+        cases.append((f"rand{i}_d{d}_B{B}H{H}_q{Nq}_k{Nk}", d, B, H, Nq, Nk, kv, bool(rng.random() < 0.5)))
+    return cases
+
+
+RANDOM = _random_cases()
+
+
+@pytest.mark.parametrize("name,d,B,H,Nq,Nk,kv,causal", RANDOM, ids=[c[0] for c in RANDOM])
+def test_random_shapes(gpu_lib, name, d, B, H, Nq, Nk, kv, causal):
+    case = workloads.make_decode_case(B, H, Nq, Nk, d, seed=zlib.crc32(name.encode()) % 10007, causal=causal, kv_len=kv)
+    check(gpu_lib, case, name)
