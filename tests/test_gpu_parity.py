@@ -103,6 +103,33 @@ def test_sweep_bf16(gpu_lib, name, params):
     full_check(gpu_lib, case, "bf16", label=name)
 
 
+def _random_dense(n=24, seed=4242):
+    # fixed-seed random shapes for the dense path: head dimension, batch, heads, length,
+    # mask mode and ragged key lengths (zeros included) drawn together
+    rng = np.random.default_rng(seed)
+    out = []
+    for i in range(n):
+        d = int(rng.choice([16, 32, 64, 128, 64, 64]))
+        B, H = int(rng.integers(1, 4)), int(rng.integers(1, 4))
+        N = int(rng.integers(1, 1300))
+        causal = bool(rng.random() < 0.5)
+        kv = None if rng.random() < 0.5 else [int(x) for x in rng.integers(0, N + 1, size=B)]
+        out.append((f"rand{i}_d{d}_B{B}H{H}_N{N}_{'causal' if causal else 'full'}{'' if kv is None else '_padded'}",
+                    dict(B=B, H=H, N=N, d=d, causal=causal, kv_len=kv)))
+    return out
+
+
+RANDOM_DENSE = _random_dense()
+
+
+@pytest.mark.parametrize("name,params", RANDOM_DENSE, ids=[c[0] for c in RANDOM_DENSE])
+def test_random_dense_shapes(gpu_lib, name, params):
+    p = dict(params)
+    B, H, N, d = p.pop("B"), p.pop("H"), p.pop("N"), p.pop("d")
+    case = workloads.make_case(B, H, N, d, seed=zlib.crc32(name.encode()) % 10000, **p)
+    full_check(gpu_lib, case, "bf16", label=name)
+
+
 # The dense bf16 forward without dropout stages three K/V tiles deep up to N = 4096 at
 # d <= 64 and two deep beyond (and at d = 128), and the dense d = 64 dK/dV kernel takes one
 # query block per step (three workgroups per CU) up to N = 4096 and two beyond: both sides
