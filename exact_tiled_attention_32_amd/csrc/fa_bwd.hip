@@ -42,21 +42,25 @@ constexpr int kBK = kBwdKeyTile;  // keys per dK/dV workgroup (32 per wave)
 //     kept mask blocks first. The work of a key tile is proportional to the kept blocks of
 //     its mask column; a column kept for every query block (a "global" column) can take
 //     far longer than the rest, and started last it would set the end of the launch.
-//     One workgroup: column counts into LDS, then a bitonic sort of (count, tile) keys.
+//     One workgroup of 1024 threads: column counts into LDS (several 16-byte row loads in
+//     flight per thread), then a bitonic sort of (count, tile) keys.
 // ---------------------------------------------------------------------------------------
-__global__ __launch_bounds__(kThreads) void bwd_order_kernel(const uint8_t* __restrict__ mask, int nb, int mb,
+constexpr int kOrderThreads = 1024;
+
+__global__ __launch_bounds__(kOrderThreads) void bwd_order_kernel(const uint8_t* __restrict__ mask, int nb, int mb,
                                                              int ntk, uint32_t* __restrict__ order) {
   __shared__ uint32_t cnt[kMaxKeyTiles];   // kept blocks per mask column (nb <= ntk)
   __shared__ uint32_t keys[kMaxKeyTiles];
   const int tid = threadIdx.x;
-  for (int c = tid; c < nb; c += kThreads) cnt[c] = 0;
+  for (int c = tid; c < nb; c += kOrderThreads) cnt[c] = 0;
   __syncthreads();
   if (nb % 16 == 0 && (reinterpret_cast<uintptr_t>(mask) & 15) == 0) {
     // 16 columns per thread and 16-byte loads: column group g = tid % G, every R-th row
-    const int G = nb / 16, R = kThreads / G;
+    const int G = nb / 16, R = kOrderThreads / G;
     if (tid < G * R) {
       const int g = tid % G;
       uint32_t n[16] = {};
+#pragma unroll 4
       for (int r = tid / G; r < nb; r += R) {
         const u32x4 v = gload16(mask + (size_t)r * nb + 16 * g);
 #pragma unroll
@@ -67,7 +71,7 @@ __global__ __launch_bounds__(kThreads) void bwd_order_kernel(const uint8_t* __re
     }
   } else {
     // any width: each thread sums its columns down the rows
-    for (int c = tid; c < nb; c += kThreads) {
+    for (int c = tid; c < nb; c += kOrderThreads) {
       uint32_t n = 0;
       for (int r = 0; r < nb; ++r) n += mask[(size_t)r * nb + c] != 0;
       cnt[c] = n;
@@ -77,12 +81,12 @@ __global__ __launch_bounds__(kThreads) void bwd_order_kernel(const uint8_t* __re
   int P = 1;
   while (P < ntk) P <<= 1;
   // ascending order of (0xFFFF - count) << 16 | tile: most blocks first, ties by tile
-  for (int j = tid; j < P; j += kThreads)
+  for (int j = tid; j < P; j += kOrderThreads)
     keys[j] = j < ntk ? ((0xFFFFu - min(cnt[(j * kBwdKeyTile) / mb], 0xFFFFu)) << 16) | (uint32_t)j : 0xFFFFFFFFu;
   __syncthreads();
   for (int k = 2; k <= P; k <<= 1)
     for (int j = k >> 1; j > 0; j >>= 1) {
-      for (int i = tid; i < P; i += kThreads) {
+      for (int i = tid; i < P; i += kOrderThreads) {
         const int x = i ^ j;
         if (x > i) {
           const uint32_t a = keys[i], b = keys[x];
@@ -95,7 +99,7 @@ __global__ __launch_bounds__(kThreads) void bwd_order_kernel(const uint8_t* __re
       }
       __syncthreads();
     }
-  for (int i = tid; i < ntk; i += kThreads) order[i] = keys[i] & 0xFFFFu;
+  for (int i = tid; i < ntk; i += kOrderThreads) order[i] = keys[i] & 0xFFFFu;
 }
 
 // ---------------------------------------------------------------------------------------
@@ -842,7 +846,7 @@ hipError_t launch_bwd(const BwdArgs& a, int d, hipStream_t stream, KernelTimer& 
   tm.mark(stream);
   hipError_t e;
   if (a.order) {
-    hipLaunchKernelGGL(bwd_order_kernel, dim3(1), block, 0, stream, a.mask, a.nb, a.mb,
+    hipLaunchKernelGGL(bwd_order_kernel, dim3(1), dim3(kOrderThreads), 0, stream, a.mask, a.nb, a.mb,
                        (a.N + kBK - 1) / kBK, a.order);
     e = hipGetLastError();
     if (e != hipSuccess) return e;
