@@ -17,7 +17,7 @@ MAX_WAVES = 2048
 KT = 32
 
 
-def _check(lens, H, launched, Nk):
+def _check(lens, H, launched, Nk, slot=lambda w, b, h, H: w + b * H + h):
     tiles = [(L + KT - 1) // KT for L in lens]
     B = len(lens)
     BH = B * H
@@ -34,7 +34,7 @@ def _check(lens, H, launched, Nk):
             assert ((g + 1) * G - 1) // T == w
             b, h = seq[g]
             pieces.setdefault((w, b * H + h), 0)
-    slots = [w + bh for (w, bh) in pieces]
+    slots = [slot(w, bh // H, bh % H, H) for (w, bh) in pieces]
     assert len(set(slots)) == len(slots), "two pieces share a slot"
     wave_cap = min(MAX_WAVES, max(B * H * ((Nk + KT - 1) // KT), 1))
     assert launched <= wave_cap
@@ -69,3 +69,10 @@ def test_tile_runs_slots_and_merge_ranges(seed):
 def test_full_caches_many_heads():
     # 1024 (b, h) of two tiles each over 1024 waves: one piece per wave, slots w + bh
     _check([40] * 64, 16, 1024, 40)
+
+
+def test_planted_slot_mistake_is_caught():
+    # slot w + b (the batch instead of the (b, h) index) lets pieces of two heads of one
+    # batch share a slot; the distinct-slot check must fail on a case with several heads
+    with pytest.raises(AssertionError, match="share a slot"):
+        _check([40] * 4, 4, 16, 40, slot=lambda w, b, h, H: w + b)
