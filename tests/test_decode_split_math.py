@@ -72,7 +72,8 @@ def test_full_caches_many_heads():
 
 
 def test_planted_slot_mistake_is_caught():
-    # slot w + b (the batch instead of the (b, h) index) lets pieces of two heads of one
-    # batch share a slot; the distinct-slot check must fail on a case with several heads
+    # slot w + b (the batch instead of the (b, h) index) gives the pieces of two heads of
+    # one batch inside one wave the same slot: 4 batches x 4 heads of 2 tiles over 8 waves,
+    # so every wave holds two heads of one batch
     with pytest.raises(AssertionError, match="share a slot"):
-        _check([40] * 4, 4, 16, 40, slot=lambda w, b, h, H: w + b)
+        _check([40] * 4, 4, 8, 40, slot=lambda w, b, h, H: w + b)
