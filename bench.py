@@ -54,6 +54,7 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 PEAK_BF16_TFLOPS = 2500.0  # MI355X dense bf16 MFMA
+PEAK_F32_TFLOPS = 157.3    # MI355X dense fp32 (the fp32 forward's MFMA rate)
 PEAK_CLOCK_MHZ = 2400.0    # the engine clock that peak assumes
 DROPOUT_P, DROPOUT_SEED = 0.1, 1234  # the dropout report's probability and seed
 PEAK_HBM_GBS = 8000.0
@@ -986,9 +987,11 @@ def kept_pair_flops(w, kv_len) -> float:
     return 4.0 * w.H * w.d * w.N * float(sum(min(max(int(x), 0), w.N) for x in kv_len))
 
 
-def phase_figures(ms: float, flop: float, nbytes: float) -> dict:
+def phase_figures(ms: float, flop: float, nbytes: float, peak: float = PEAK_BF16_TFLOPS) -> dict:
+    """ms, TFLOP/s, fraction of `peak` (the dense MFMA peak of the call's dtype) and HBM rate
+    of the compulsory bytes."""
     return {"ms": round(ms, 4), "tflops": round(flop / ms / 1e9, 1),
-            "frac_of_peak": round(flop / ms / 1e9 / PEAK_BF16_TFLOPS, 4),
+            "frac_of_peak": round(flop / ms / 1e9 / peak, 4),
             "hbm_gbs": round(nbytes / ms / 1e6, 1), "hbm_frac": round(nbytes / ms / 1e6 / PEAK_HBM_GBS, 4)}
 
 
@@ -1002,8 +1005,9 @@ def report_config(fa, w, dev, steps=50, warmup=3) -> dict:
     import torch
     r = Runner(fa, w, dev)
     ff = attn_flops(w, r.kept)
+    peak = PEAK_F32_TFLOPS if w.dtype == "f32" else PEAK_BF16_TFLOPS
     res = {"shape": [w.B, w.H, w.N, w.d], "dtype": w.dtype, "causal": w.causal, "padding": w.padding,
-           "sparse": w.sparse, "fwd_gflop": round(ff / 1e9, 3)}
+           "sparse": w.sparse, "fwd_gflop": round(ff / 1e9, 3), "peak_tflops": peak}
     if r.kept is not None:
         res["kept_block_fraction"] = round(r.kept, 5)
         res["flop_convention"] = "kept 128x128 blocks only"
@@ -1031,10 +1035,10 @@ def report_config(fa, w, dev, steps=50, warmup=3) -> dict:
             fn()
         torch.cuda.synchronize()
         mult = 2.5 if phase == "bwd" else 1.0
-        fig = phase_figures(ms, ff * mult, compulsory_bytes(w, phase))
+        fig = phase_figures(ms, ff * mult, compulsory_bytes(w, phase), peak)
         if kept_ff is not None:
             fig["tflops_kept_pairs"] = round(kept_ff * mult / ms / 1e9, 1)
-            fig["frac_of_peak_kept_pairs"] = round(kept_ff * mult / ms / 1e9 / PEAK_BF16_TFLOPS, 4)
+            fig["frac_of_peak_kept_pairs"] = round(kept_ff * mult / ms / 1e9 / peak, 4)
         if w.dtype == "f32":
             fig["us"] = round(ms * 1e3, 2)
         fig["median_call_ms"] = round(clock.call_ms_median(phase), 4)

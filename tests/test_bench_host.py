@@ -243,3 +243,12 @@ def test_summarize_stalls(tmp_path):
     write(b, bench.STALL_COUNTERS_B, b_vals, drop_last=True)
     with pytest.raises(RuntimeError, match="library dispatches"):
         bench.summarize_stalls(str(a), str(b))
+
+
+def test_phase_figures_use_the_dtype_peak():
+    # 157.3 GFLOP in 1 ms is the whole fp32 peak and 6.3 % of the bf16 one
+    f32 = bench.phase_figures(1.0, 157.3e9, 8e9, bench.PEAK_F32_TFLOPS)
+    bf16 = bench.phase_figures(1.0, 157.3e9, 8e9)
+    assert f32["tflops"] == 157.3 and f32["frac_of_peak"] == 1.0
+    assert bf16["frac_of_peak"] == round(157.3 / bench.PEAK_BF16_TFLOPS, 4)
+    assert f32["hbm_frac"] == 1.0
