@@ -449,16 +449,36 @@ __global__ __launch_bounds__(kThreads) void fwd_f32_kernel(FwdArgs a) {
   float m_run = kNegInf, l_run = 0.f;
   const float c2 = a.c2;
 
+  // Tile t + 1 is read into registers while tile t is computed, then written to LDS after
+  // the step's last barrier: one memory latency per launch instead of one per tile.
+  constexpr int PER = BC * D / kThreads;  // elements of a tile per thread and tensor
+  float kr[PER], vr[PER];
+  auto fetch = [&](int t) {
+    const int key0 = (a.mask ? __builtin_amdgcn_readfirstlane((int)tlist[t]) : t) * BC;
+#pragma unroll
+    for (int i = 0; i < PER; ++i) {
+      const int e = tid + i * kThreads, key = key0 + e / D, col = e % D;
+      kr[i] = key < a.N ? K[(size_t)key * D + col] : 0.f;
+      vr[i] = key < a.N ? V[(size_t)key * D + col] : 0.f;
+    }
+  };
+  auto publish = [&]() {
+#pragma unroll
+    for (int i = 0; i < PER; ++i) {
+      const int e = tid + i * kThreads, row = e / D, col = e % D;
+      kt[row * LD + col] = kr[i];
+      vt[row * LD + col] = vr[i];
+    }
+  };
+  if (ntiles > 0) {
+    fetch(0);
+    publish();
+  }
   for (int t = 0; t < ntiles; ++t) {
     const int jt = a.mask ? __builtin_amdgcn_readfirstlane((int)tlist[t]) : t;
     const int key0 = jt * BC;
-    for (int e = tid; e < BC * D; e += kThreads) {
-      const int row = e / D, col = e % D;
-      const int key = key0 + row;
-      kt[row * LD + col] = key < a.N ? K[(size_t)key * D + col] : 0.f;
-      vt[row * LD + col] = key < a.N ? V[(size_t)key * D + col] : 0.f;
-    }
     __syncthreads();
+    if (t + 1 < ntiles) fetch(t + 1);
     if (!(a.causal && key0 > q0 + 32 * w + 31)) {
       f32x16 s = f32x16{};
 #pragma unroll
@@ -493,6 +513,7 @@ __global__ __launch_bounds__(kThreads) void fwd_f32_kernel(FwdArgs a) {
           o[md] = mfma32_f32(vt[(8 * (i >> 2) + 4 * h + (i & 3)) * LD + 32 * md + ql], s[i], o[md]);
     }
     __syncthreads();
+    if (t + 1 < ntiles) publish();
   }
 
   const float l_tot = l_run + wave_xor32(l_run);
